@@ -1,0 +1,388 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for the FP4 sparse-indexer scorer.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h). Deliberately slow and literal:
+ * every step is written the way its definition reads, in double precision,
+ * with no blocking, fusion or reordering. OpenMP only spreads independent
+ * rows / keys over threads; it does not change any arithmetic.
+ *
+ * Readings of the pages that this file commits to (the pages leave them open):
+ *   R1 scale rule: e = floor(log2(amax)) - 2 (E2M1's largest exponent is 2),
+ *      clamped to [-127, 127], stored as e + 127; amax == 0 gives byte 0.
+ *   R2 element rounding: nearest point of the E2M1 grid, ties to the even
+ *      code, magnitudes past 6 saturate to 6; the sign bit is the input's.
+ *   R3 nibble order: element 2i in the low nibble of byte i.
+ *   R4 query format: q is quantized by the same MXFP4 rule per (row, head).
+ *   R5 padding rows see an empty key range (they "read no key").
+ *   R6 score: sum over heads of w * max(0, q.k); no other factor.
+ *   R7 top-k ties: the lower column wins.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define KEY_DIM 128     /* index head dimension (Scope: index_head_dim == 128) */
+#define BLOCK_ELEMS 32  /* one e8m0 scale per 32 elements */
+#define PAGE_KEYS 64    /* block size 64 */
+
+/* E2M1 magnitudes by 3-bit code [OCP, E2M1]: 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static const double kE2M1[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_value(int code) {
+  double mag = kE2M1[code & 7];
+  return (code & 8) ? -mag : mag;
+}
+
+/* e8m0: byte b stands for 2^(b - 127) [OCP, E8M0]. */
+double oracle_e8m0_value(int byte) { return ldexp(1.0, (byte & 0xFF) - 127); }
+
+/* Scale-plane slot of key position pos inside its 64-key page: the scale
+ * plane stores the row axis as a 16x4 transpose, slot = (pos % 16) * 4 + pos / 16
+ * ([P2] second review finding; commit "Use the index scale plane's own row
+ * order when staging FP4 prefill under DCP"). */
+int oracle_scale_slot(int pos) { return (pos % 16) * 4 + pos / 16; }
+
+/* bf16 bit pattern -> double (exact: bf16 is the top half of an fp32). */
+static double bf16_to_double(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Nearest E2M1 magnitude code for a non-negative x, ties to the even code (R2).
+ * Past 6 the nearest grid point is 6 itself, which is the saturation. */
+static int e2m1_nearest_code(double x) {
+  int best = 0;
+  double best_d = fabs(x - kE2M1[0]);
+  for (int c = 1; c < 8; c++) {
+    double d = fabs(x - kE2M1[c]);
+    if (d < best_d || (d == best_d && (c % 2) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+/* One MX block: 32 values -> e8m0 byte + 32 E2M1 codes (R1, R2). */
+static void encode_block(const double *v, uint8_t *scale, uint8_t *codes) {
+  double amax = 0.0;
+  for (int i = 0; i < BLOCK_ELEMS; i++)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  int e;
+  if (amax == 0.0) {
+    e = -127;
+  } else {
+    int ex;
+    frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+    e = (ex - 1) - 2;
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+  }
+  *scale = (uint8_t)(e + 127);
+  for (int i = 0; i < BLOCK_ELEMS; i++) {
+    double x = ldexp(fabs(v[i]), -e); /* exact power-of-two rescale */
+    int code = e2m1_nearest_code(x);
+    if (signbit(v[i])) code |= 8;
+    codes[i] = (uint8_t)code;
+  }
+}
+
+int oracle_mx_encode_blocks(const uint16_t *vals, int64_t n_blocks, uint8_t *scale, uint8_t *codes) {
+  if (n_blocks < 0) return -1;
+  for (int64_t b = 0; b < n_blocks; b++) {
+    double v[BLOCK_ELEMS];
+    for (int i = 0; i < BLOCK_ELEMS; i++) v[i] = bf16_to_double(vals[b * BLOCK_ELEMS + i]);
+    encode_block(v, &scale[b], &codes[b * BLOCK_ELEMS]);
+  }
+  return 0;
+}
+
+/* One 128-dim vector -> 64 packed bytes (R3) + 4 scale bytes (one per 32). */
+static void encode_vector(const uint16_t *src, uint8_t *packed, uint8_t *scales) {
+  for (int g = 0; g < KEY_DIM / BLOCK_ELEMS; g++) {
+    double v[BLOCK_ELEMS];
+    uint8_t codes[BLOCK_ELEMS];
+    for (int i = 0; i < BLOCK_ELEMS; i++) v[i] = bf16_to_double(src[g * BLOCK_ELEMS + i]);
+    encode_block(v, &scales[g], codes);
+    for (int i = 0; i < BLOCK_ELEMS / 2; i++)
+      packed[g * (BLOCK_ELEMS / 2) + i] = (uint8_t)(codes[2 * i] | (codes[2 * i + 1] << 4));
+  }
+}
+
+/* Cache write ([P2] commit "Score a DSA sparse indexer in FP4": keys kept as
+ * packed E2M1 plus e8m0 scales in one index region declared as two planes;
+ * review fixes: the writer skips rows whose slot is negative). */
+int oracle_quant_and_cache(const uint16_t *k, int64_t n_tok, int64_t k_ld, const int64_t *slot,
+                           uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages) {
+  if (n_tok < 0 || k_ld < KEY_DIM || n_pages < 0) return -1;
+  for (int64_t t = 0; t < n_tok; t++) {
+    if (slot[t] < 0) continue;
+    int64_t page = slot[t] / PAGE_KEYS;
+    int pos = (int)(slot[t] % PAGE_KEYS);
+    if (page >= n_pages) return -2;
+    uint8_t packed[64], scales[4];
+    encode_vector(&k[t * k_ld], packed, scales);
+    memcpy(&kv_packed[(page * PAGE_KEYS + pos) * 64], packed, 64);
+    for (int g = 0; g < 4; g++) kv_scale[(page * 4 + g) * PAGE_KEYS + oracle_scale_slot(pos)] = scales[g];
+  }
+  return 0;
+}
+
+/* Query quantization (R4; the FP4 writer emits q_out with q_scale). */
+int oracle_quant_q(const uint16_t *q, int64_t n_rows, int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale) {
+  if (n_rows < 0 || n_heads <= 0) return -1;
+  for (int64_t r = 0; r < n_rows; r++)
+    for (int32_t h = 0; h < n_heads; h++) {
+      int64_t v = r * n_heads + h;
+      encode_vector(&q[v * KEY_DIM], &q_packed[v * 64], &q_scale[v * 4]);
+    }
+  return 0;
+}
+
+/* value of element d of a packed 128-dim vector with its 4 scale bytes */
+static double element(const uint8_t *packed, const uint8_t scales[4], int d) {
+  uint8_t byte = packed[d / 2];
+  int code = (d % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+  return oracle_e2m1_value(code) * oracle_e8m0_value(scales[d / BLOCK_ELEMS]);
+}
+
+int oracle_dequant_key(const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
+                       int64_t page, int pos, double *out) {
+  if (page < 0 || page >= n_pages || pos < 0 || pos >= PAGE_KEYS) return -1;
+  uint8_t scales[4];
+  for (int g = 0; g < 4; g++) scales[g] = kv_scale[(page * 4 + g) * PAGE_KEYS + oracle_scale_slot(pos)];
+  const uint8_t *packed = &kv_packed[(page * PAGE_KEYS + pos) * 64];
+  for (int d = 0; d < KEY_DIM; d++) out[d] = element(packed, scales, d);
+  return 0;
+}
+
+int oracle_dequant_q(const uint8_t *q_packed, const uint8_t *q_scale, int64_t row, int32_t n_heads,
+                     int32_t h, double *out) {
+  if (row < 0 || h < 0 || h >= n_heads) return -1;
+  int64_t v = row * n_heads + h;
+  for (int d = 0; d < KEY_DIM; d++) out[d] = element(&q_packed[v * 64], &q_scale[v * 4], d);
+  return 0;
+}
+
+/* Decode rows: a sequence contributes next_n query rows; row t of them sits
+ * next_n - 1 - t tokens before the end of the context ([P2] review fixes
+ * name next_n rows per sequence; the staggering is the usual layout of
+ * speculative rows). */
+int oracle_decode_geometry(const int32_t *ctx, int32_t batch, int32_t next_n, int32_t *row_seq,
+                           int32_t *row_len) {
+  if (batch < 0 || next_n <= 0) return -1;
+  for (int32_t b = 0; b < batch; b++)
+    for (int32_t t = 0; t < next_n; t++) {
+      int32_t len = ctx[b] - next_n + 1 + t;
+      if (len < 0) len = 0;
+      row_seq[b * next_n + t] = b;
+      row_len[b * next_n + t] = len;
+    }
+  return 0;
+}
+
+/* Prefill rows: causal, inclusive of the row's own position. Padding rows join
+ * the last request's group at position 0 and read no key ([P1] section 3). */
+int oracle_prefill_geometry(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
+                            int32_t n_rows_padded, int32_t *row_seq, int32_t *row_len) {
+  if (n_req <= 0 || cu_rows[0] != 0 || n_rows_padded < cu_rows[n_req]) return -1;
+  for (int32_t i = 0; i < n_req; i++) {
+    if (cu_rows[i + 1] < cu_rows[i]) return -1;
+    for (int32_t r = cu_rows[i]; r < cu_rows[i + 1]; r++) {
+      row_seq[r] = i;
+      row_len[r] = start_pos[i] + (r - cu_rows[i]) + 1;
+    }
+  }
+  for (int32_t r = cu_rows[n_req]; r < n_rows_padded; r++) {
+    row_seq[r] = n_req - 1;
+    row_len[r] = 0;
+  }
+  return 0;
+}
+
+/* s = sum_h w[h] * max(0, sum_d q[h][d] * k[d])  (R6). */
+static double score_one(const double *qd, const float *w, int32_t n_heads, const double *kd) {
+  double s = 0.0;
+  for (int32_t h = 0; h < n_heads; h++) {
+    double dot = 0.0;
+    for (int d = 0; d < KEY_DIM; d++) dot += qd[h * KEY_DIM + d] * kd[d];
+    s += (double)w[h] * (dot > 0.0 ? dot : 0.0);
+  }
+  return s;
+}
+
+static int dequant_row_q(const uint8_t *q_packed, const uint8_t *q_scale, int64_t r, int32_t n_heads,
+                         double *qd) {
+  for (int32_t h = 0; h < n_heads; h++)
+    if (oracle_dequant_q(q_packed, q_scale, r, n_heads, h, &qd[h * KEY_DIM])) return -1;
+  return 0;
+}
+
+/* Paged DSA index score ([P2] PR description: logits straight from the
+ * paged FP4 cache; the page table maps a row's keys to pages). */
+int oracle_score(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
+                 int64_t n_rows, const int32_t *row_seq, const int32_t *row_len,
+                 const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
+                 const int32_t *block_table, int64_t bt_ld, double *logits, int64_t ld,
+                 int64_t *reads) {
+  if (n_heads <= 0 || n_rows < 0) return -1;
+  double *qd = (double *)malloc(sizeof(double) * n_heads * KEY_DIM);
+  if (!qd) return -3;
+  int err = 0;
+  for (int64_t r = 0; r < n_rows && !err; r++) {
+    int64_t len = row_len[r];
+    if (len > ld || (len + PAGE_KEYS - 1) / PAGE_KEYS > bt_ld) { err = -1; break; }
+    if (dequant_row_q(q_packed, q_scale, r, n_heads, qd)) { err = -1; break; }
+    const int32_t *bt = &block_table[(int64_t)row_seq[r] * bt_ld];
+    int64_t nread = 0;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(+ : nread) reduction(| : bad)
+    for (int64_t j = 0; j < len; j++) {
+      double kd[KEY_DIM];
+      if (oracle_dequant_key(kv_packed, kv_scale, n_pages, bt[j / PAGE_KEYS], (int)(j % PAGE_KEYS), kd)) {
+        bad = 1;
+        continue;
+      }
+      nread += 1;
+      logits[r * ld + j] = score_one(qd, &w[r * n_heads], n_heads, kd);
+    }
+    if (bad) err = -2;
+    if (reads) reads[r] = nread;
+  }
+  free(qd);
+  return err;
+}
+
+int oracle_score_pairs(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
+                       const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
+                       const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table,
+                       int64_t bt_ld, const int64_t *rows, const int64_t *cols, int64_t n_pairs,
+                       double *out) {
+  if (n_heads <= 0 || n_pairs < 0) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+  for (int64_t i = 0; i < n_pairs; i++) {
+    int64_t r = rows[i], j = cols[i];
+    if (j < 0 || j >= row_len[r] || (j / PAGE_KEYS) >= bt_ld) { bad = 1; continue; }
+    double *qd = (double *)malloc(sizeof(double) * n_heads * KEY_DIM);
+    double kd[KEY_DIM];
+    if (!qd) { bad = 1; continue; }
+    if (dequant_row_q(q_packed, q_scale, r, n_heads, qd) ||
+        oracle_dequant_key(kv_packed, kv_scale, n_pages, block_table[(int64_t)row_seq[r] * bt_ld + j / PAGE_KEYS],
+                           (int)(j % PAGE_KEYS), kd)) {
+      bad = 1;
+    } else {
+      out[i] = score_one(qd, &w[r * n_heads], n_heads, kd);
+    }
+    free(qd);
+  }
+  return bad ? -2 : 0;
+}
+
+/* Top-k by a full sort of (score desc, column asc) (R7). The per-row scan is
+ * bounded by the row's own length ([P2] review fixes: the top-k bounds its
+ * scan by the context, so the logits tail is never read). */
+typedef struct {
+  double v;
+  int32_t j;
+} Cand;
+
+static int cand_cmp(const void *a, const void *b) {
+  const Cand *x = (const Cand *)a, *y = (const Cand *)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+int oracle_topk(const double *s, int64_t ld, int64_t n_rows, const int32_t *row_len, int32_t k,
+                int32_t *idx, int64_t idx_ld) {
+  if (k <= 0 || idx_ld < k || n_rows < 0) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < n_rows; r++) {
+    int64_t len = row_len[r];
+    if (len < 0 || len > ld) { bad = 1; continue; }
+    Cand *c = (Cand *)malloc(sizeof(Cand) * (len > 0 ? len : 1));
+    if (!c) { bad = 1; continue; }
+    for (int64_t j = 0; j < len; j++) {
+      c[j].v = s[r * ld + j];
+      c[j].j = (int32_t)j;
+    }
+    qsort(c, (size_t)len, sizeof(Cand), cand_cmp);
+    for (int32_t i = 0; i < k; i++) idx[r * idx_ld + i] = (i < len) ? c[i].j : -1;
+    free(c);
+  }
+  return bad ? -1 : 0;
+}
+
+/* Even split of n_items over n_units contiguous ranges: unit u starts at
+ * floor(u * n_items / n_units). (The pages publish a per-step CTA schedule
+ * with a persistent grid of max(floor, rows) units -- [P2] Decode grid floor
+ * -- but do not print how it divides the work; this even contiguous split is
+ * the plainest reading.) */
+static void even_split(int64_t n_items, int32_t n_units, int32_t *unit_begin) {
+  for (int32_t u = 0; u <= n_units; u++) unit_begin[u] = (int32_t)(((int64_t)u * n_items) / n_units);
+}
+
+int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, int32_t *cum_pages,
+                           int32_t *unit_begin, int32_t *unit_seq) {
+  if (batch < 0 || n_units <= 0) return -1;
+  cum_pages[0] = 0;
+  for (int32_t b = 0; b < batch; b++) {
+    if (ctx[b] < 0) return -1;
+    cum_pages[b + 1] = cum_pages[b] + (ctx[b] + PAGE_KEYS - 1) / PAGE_KEYS;
+  }
+  even_split(cum_pages[batch], n_units, unit_begin);
+  for (int32_t u = 0; u < n_units; u++) {
+    int32_t b = 0;
+    while (b < batch && cum_pages[b + 1] <= unit_begin[u]) b++;
+    unit_seq[u] = b;
+  }
+  return 0;
+}
+
+int oracle_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
+                            int32_t n_rows_padded, int32_t tile_rows, int32_t n_units,
+                            int32_t max_tiles, int32_t *n_tiles, int32_t *tiles, int32_t *cum_items,
+                            int32_t *unit_begin, int32_t *unit_tile) {
+  if (n_req <= 0 || tile_rows <= 0 || n_units <= 0 || cu_rows[0] != 0 || n_rows_padded < cu_rows[n_req])
+    return -1;
+  int32_t nt = 0;
+  cum_items[0] = 0;
+  for (int32_t i = 0; i < n_req; i++) {
+    int32_t first = cu_rows[i];
+    int32_t valid_end = cu_rows[i + 1];
+    /* the last request's group also holds the padding rows ([P1] section 3) */
+    int32_t group_end = (i == n_req - 1) ? n_rows_padded : cu_rows[i + 1];
+    if (valid_end < first) return -1;
+    for (int32_t r0 = first; r0 < group_end; r0 += tile_rows) {
+      int32_t rows = group_end - r0 < tile_rows ? group_end - r0 : tile_rows;
+      int32_t pages = 0;
+      for (int32_t r = r0; r < r0 + rows; r++) {
+        if (r >= valid_end) continue; /* padding row: no key */
+        int32_t len = start_pos[i] + (r - first) + 1;
+        int32_t p = (len + PAGE_KEYS - 1) / PAGE_KEYS;
+        if (p > pages) pages = p;
+      }
+      if (nt >= max_tiles) return -2; /* never truncate silently ([P2] review fixes) */
+      tiles[4 * nt + 0] = r0;
+      tiles[4 * nt + 1] = rows;
+      tiles[4 * nt + 2] = i;
+      tiles[4 * nt + 3] = pages;
+      cum_items[nt + 1] = cum_items[nt] + pages;
+      nt++;
+    }
+  }
+  *n_tiles = nt;
+  even_split(cum_items[nt], n_units, unit_begin);
+  for (int32_t u = 0; u < n_units; u++) {
+    int32_t t = 0;
+    while (t < nt && cum_items[t + 1] <= unit_begin[u]) t++;
+    unit_tile[u] = t;
+  }
+  return 0;
+}
