@@ -1,0 +1,217 @@
+/*
+ * indexer_fp4.h -- C ABI of the MI355X (gfx950) FP4 sparse-indexer library.
+ *
+ * What the library computes (sources are web pages, cited by title and section):
+ *   [P2] "Score a DSA sparse indexer in FP4" (ROCm/ATOM pull request #2216)
+ *   [P1] ROCm/ATOM pull request #2125, Technical Details section 3
+ *        "FP4 indexer padding rows"
+ *
+ * A DSA sparse indexer keeps one 128-dim index key per token. Here the keys are
+ * stored in FP4: packed E2M1 codes (64 bytes per key) plus one e8m0 scale byte per
+ * 32 elements, in 64-token pages ([P2] commit message and PR description intro).
+ * For every query row the scorer computes, per index head, the dot product of the
+ * row's query with every key the row may see, applies ReLU, and sums the heads with
+ * per-head weights into one fp32 logit per key; a top-k then keeps the index_topk
+ * best keys per row.
+ *
+ * Memory layout (one index region, two planes; [P2] PR description intro):
+ *   kv_packed  uint8 [n_pages][64 pos][64 B]  key (page,pos), element d in byte d/2,
+ *                                             even d in the low nibble
+ *   kv_scale   uint8 [n_pages][4 group][64 slot]  scale of elements 32g..32g+31 of
+ *                                             key (page,pos) at slot (pos%16)*4 + pos/16,
+ *                                             the 16x4 transpose of the row axis ([P2]
+ *                                             second review finding; commit "Use the
+ *                                             index scale plane's own row order ...")
+ *   q_packed   uint8 [rows][n_heads][64 B]    same packing as keys
+ *   q_scale    uint8 [rows][n_heads][4]       scale of elements 32g..32g+31 at [g]
+ *   weights    fp32  [rows][n_heads]          per-head weights
+ *   block_table int32 [seqs][bt_ld]           page of key j of sequence s at
+ *                                             block_table[s][j/64], position j%64
+ *   logits     fp32  [rows][logits_ld]        column j = key position j of the row's
+ *                                             sequence; only j < row_len[r] is written
+ *
+ * Encoding (the pages name the format but print no rule; OCP Microscaling v1.0):
+ *   scale exponent e = floor(log2(amax of the 32 elements)) - 2, clamped to
+ *   [-127, 127], byte e + 127 (0 for an all-zero block); each element is rounded to
+ *   the nearest of +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} * 2^e, ties to the even code,
+ *   larger magnitudes saturate to 6 * 2^e; the sign bit is the input's sign bit.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless marked [host]. The caller owns every buffer;
+ *     the library keeps no pointer past the call and allocates no device memory.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Calls are asynchronous on
+ *     it, never synchronize, and never read device memory on the host, so a sequence
+ *     of calls can be captured into a HIP graph and replayed.
+ *   - Return value: INDEXER_FP4_OK (0) or a negative code; nothing is launched when a
+ *     call returns an error. indexer_fp4_last_error() then holds a message (per host
+ *     thread) that names the offending quantities.
+ *   - Problems only visible on the device (a block-table entry outside [0, n_pages),
+ *     a context longer than the block table covers) never fault: the kernel skips the
+ *     page and ORs a flag into the error word of the schedule buffer it was given
+ *     (int32 at byte offset 4 of the buffer; see INDEXER_FP4_DEV_*).
+ *   - The library refuses what it cannot do (wrong geometry, wrong GPU); it has no
+ *     fallback path ([P2] Scope: the structural gate, with falling back to FP8 left
+ *     to the caller).
+ */
+#ifndef INDEXER_FP4_H
+#define INDEXER_FP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  INDEXER_FP4_OK = 0,
+  INDEXER_FP4_EINVAL = -1, /* an argument is out of range or inconsistent */
+  INDEXER_FP4_ENOSPC = -2, /* a buffer (schedule, workspace, logits, table) is too small */
+  INDEXER_FP4_EARCH = -3,  /* the current device is not gfx950 */
+  INDEXER_FP4_EHIP = -4    /* the HIP runtime reported an error */
+};
+
+/* Flags the kernels OR into the schedule buffer's error word (device-side problems). */
+enum {
+  INDEXER_FP4_DEV_BAD_PAGE = 1,      /* block-table entry outside [0, n_pages): page skipped */
+  INDEXER_FP4_DEV_TABLE_SHORT = 2,   /* a row needs more pages than bt_ld: rest skipped */
+  INDEXER_FP4_DEV_BAD_SCHEDULE = 4,  /* schedule built for other sizes than the call's */
+  INDEXER_FP4_DEV_BAD_LENGTH = 8     /* negative length or cu_rows not ascending */
+};
+
+#define INDEXER_FP4_PAGE 64       /* tokens per page ([P2] review fixes: block size 64) */
+#define INDEXER_FP4_HEAD_DIM 128  /* index head dimension ([P2] Scope) */
+#define INDEXER_FP4_HEAD_MULT 16  /* n_heads must be a multiple of this ([P2] Scope: MFMA_M) */
+#define INDEXER_FP4_MAX_HEADS 128
+#define INDEXER_FP4_TILE_ROWS 8   /* prefill rows per tile; n_rows_padded is a multiple */
+
+/* Message of the last failed call on this host thread ("" if none). [host] */
+const char *indexer_fp4_last_error(void);
+
+/* ---------------------------------------------------------------------------------
+ * Cache write and query quantization ([P2] commit message: the fused writer's FP4
+ * output mode stores keys as packed E2M1 plus e8m0 scales and emits the quantized
+ * query with its scales; review fixes: rows whose slot is negative are skipped).
+ *
+ *   k_bf16        bf16 [n_tok][k_ld]; elements 0..127 of each row are the key
+ *   slot_mapping  int64 [n_tok]; key t goes to page slot/64, position slot%64;
+ *                 slot < 0 is skipped, and so (device-side) is slot >= n_pages*64
+ *   kv_packed, kv_scale  the two planes (layout above), n_pages pages each; only the
+ *                 bytes of the written keys change
+ *   q_bf16        bf16 [n_q_rows][n_heads][128], or NULL (no query arm)
+ *   q_packed, q_scale  outputs [n_q_rows][n_heads][64] / [n_q_rows][n_heads][4]
+ * n_tok may be 0 (query arm only); n_q_rows may be 0 (key arm only).
+ * Errors: EINVAL (negative sizes, k_ld < 128, n_heads <= 0 with a query arm, NULL
+ * plane or output pointers that a non-empty arm needs), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
+                                const int64_t *slot_mapping, uint8_t *kv_packed,
+                                uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
+                                int64_t n_q_rows, int32_t n_heads, uint8_t *q_packed,
+                                uint8_t *q_scale, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Per-step schedules. The scorers run a persistent grid of n_units workgroups that
+ * splits the step's work evenly: unit u takes items [floor(u*W/n), floor((u+1)*W/n))
+ * of the W work items. The schedule is built once per step into a caller-owned
+ * buffer that stays at a fixed address, so a captured graph that reads it can be
+ * replayed for a new step after the schedule call is re-run ([P2] Decode grid floor:
+ * the CTA schedule is published once a step at a graph-stable address; the pages'
+ * floors are 512 units for decode and 4096 for prefill).
+ *
+ * Decode: rows are next_n query tokens per sequence ([P2] review fixes). A work item
+ * is (sequence b, page p < ceil(context_lens[b]/64)), b-major. row_len[b*next_n + t]
+ * = context_lens[b] - next_n + 1 + t (the context counts the token just written).
+ *   context_lens  int32 [batch]
+ *   sched         buffer of indexer_fp4_decode_sched_bytes(batch, next_n, n_units) bytes
+ *   row_len       int32 [batch*next_n] output (keys each row sees)
+ * Errors: EINVAL (batch < 0, next_n outside 1..4, n_units <= 0), ENOSPC (sched_bytes too
+ * small: a schedule is never silently truncated, [P2] review fixes), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int64_t indexer_fp4_decode_sched_bytes(int32_t batch, int32_t next_n, int32_t n_units);
+int indexer_fp4_decode_schedule(const int32_t *context_lens, int32_t batch, int32_t next_n,
+                                int32_t n_units, void *sched, int64_t sched_bytes,
+                                int32_t *row_len, void *stream);
+
+/* Prefill: the step's query rows are grouped by request: rows [cu_rows[i],
+ * cu_rows[i+1]) belong to request i, and row r sits at position start_pos[i] + r -
+ * cu_rows[i] and sees keys [0, position] (causal, inclusive). Rows [cu_rows[n_req],
+ * n_rows_padded) are padding: they join the last request's group and see no key
+ * ([P1] section 3: padding rows fold into the last request's group, sit at position 0
+ * and read no key). Each group is cut into tiles of up to 8 rows starting at the
+ * group's first row; a work item is (tile, page), tile-major.
+ *   cu_rows    int32 [n_req+1], cu_rows[0] = 0, ascending, cu_rows[n_req] <= n_rows_padded
+ *   start_pos  int32 [n_req]
+ *   n_rows_padded [host] multiple of 8
+ *   row_len    int32 [n_rows_padded] output (0 for padding rows)
+ * Errors: EINVAL (n_req <= 0, n_rows_padded not a positive multiple of 8, n_units <= 0),
+ * ENOSPC, EARCH, EHIP. Device-side: a descending cu_rows or negative start_pos sets
+ * INDEXER_FP4_DEV_BAD_LENGTH and empties the schedule.
+ * --------------------------------------------------------------------------------- */
+int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, int32_t n_units);
+int indexer_fp4_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
+                                 int32_t n_rows_padded, int32_t n_units, void *sched,
+                                 int64_t sched_bytes, int32_t *row_len, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Decode scorer ([P2] commit message and PR description: the FP4 mqa-logits kernel
+ * scores straight out of the paged FP4 cache on a persistent grid driven by the
+ * published CTA schedule).
+ *   logits[r][j] = sum_h weights[r][h] * max(0, sum_d q(r,h,d) * k(j,d)),  j < row_len[r]
+ * with q and k the dequantized FP4 values; row r = b*next_n + t reads its sequence's
+ * pages through block_table[b]. Columns >= row_len[r] are not written.
+ *   sched, row_len  as written by indexer_fp4_decode_schedule for the same batch,
+ *                   next_n and n_units (sched's error word may be updated)
+ * Errors: EINVAL (n_heads not a multiple of 16 or above 128, batch/next_n/n_units that
+ * are not those of the schedule's sizes, negative sizes), ENOSPC (logits_ld < 64*bt_ld
+ * or bt_ld <= 0), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale,
+                             const float *weights, int32_t n_heads, const uint8_t *kv_packed,
+                             const uint8_t *kv_scale, int64_t n_pages,
+                             const int32_t *block_table, int64_t bt_ld, int32_t batch,
+                             int32_t next_n, void *sched, int32_t n_units,
+                             const int32_t *row_len, float *logits, int64_t logits_ld,
+                             void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Prefill scorer ([P2] commit message: the FP4 prefill variant; [P1] section 3: the
+ * row-group kernel finds a group's page table as group b -> block_tables[b]).
+ * Same logit as decode for every valid row of the step; row r of request i reads its
+ * keys through block_table[i] (row i of the table = request i of the step). Padding
+ * rows read nothing and write nothing.
+ *   q_packed/q_scale/weights  [n_rows_padded][n_heads]...
+ *   sched, row_len            from indexer_fp4_prefill_schedule (same n_req,
+ *                             n_rows_padded, n_units)
+ * Errors: as decode.
+ * --------------------------------------------------------------------------------- */
+int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
+                              const float *weights, int32_t n_heads, const uint8_t *kv_packed,
+                              const uint8_t *kv_scale, int64_t n_pages,
+                              const int32_t *block_table, int64_t bt_ld, int32_t n_req,
+                              void *sched, int32_t n_units, int32_t n_rows_padded,
+                              const int32_t *row_len, float *logits, int64_t logits_ld,
+                              void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Per-row top-k ([P2] review fixes: top_k_per_row bounds its scan by the row's
+ * context, so the logits tail past it is never read; PR description Accuracy: a row
+ * with at most index_topk keys keeps them all).
+ * For row r, topk_idx[r][0 .. min(k, row_len[r])) receives the columns of the
+ * min(k, row_len[r]) largest logits[r][0 .. row_len[r]), in ascending column order;
+ * among equal logits the lower column is kept (-0.0 counts as equal to +0.0). The
+ * rest of the row, up to k, is -1. Logits must be finite.
+ *   row_len    int32 [n_rows] (e.g. a schedule's row_len output)
+ *   workspace  indexer_topk_workspace_bytes(n_rows, max_len, k) bytes, any content
+ * Errors: EINVAL (k <= 0, n_rows < 0, max_len < 0), ENOSPC (topk_ld < k, workspace
+ * too small), EARCH, EHIP. Rows longer than max_len are clamped to max_len
+ * (device-side; max_len must not exceed logits_ld).
+ * --------------------------------------------------------------------------------- */
+int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len, int32_t k);
+int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
+                 int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld,
+                 void *workspace, int64_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* INDEXER_FP4_H */

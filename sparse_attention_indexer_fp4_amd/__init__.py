@@ -1,0 +1,237 @@
+"""Python binding of the gfx950 FP4 sparse-indexer library (libindexer_fp4.so).
+
+Argument marshalling only: every function takes torch tensors that live on the GPU, checks
+their dtype/device/contiguity, and passes raw pointers, sizes and the current HIP stream to
+the C entry point of the same name (see include/indexer_fp4.h for the exact semantics). All
+computation happens in the library's HIP kernels; there is no fallback. If the shared
+library has not been built, importing this package raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libindexer_fp4.so")
+
+PAGE = 64
+HEAD_DIM = 128
+TILE_ROWS = 8
+DEV_BAD_PAGE, DEV_TABLE_SHORT, DEV_BAD_SCHEDULE, DEV_BAD_LENGTH = 1, 2, 4, 8
+# persistent-grid sizes the scorers default to (units = workgroups)
+DECODE_UNITS = 512
+PREFILL_UNITS = 512
+
+EXPORTS = (
+    "indexer_fp4_last_error",
+    "indexer_fp4_quant_and_cache",
+    "indexer_fp4_decode_sched_bytes",
+    "indexer_fp4_decode_schedule",
+    "indexer_fp4_prefill_sched_bytes",
+    "indexer_fp4_prefill_schedule",
+    "indexer_fp4_score_decode",
+    "indexer_fp4_score_prefill",
+    "indexer_topk_workspace_bytes",
+    "indexer_topk",
+)
+
+
+class IndexerError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    sig = {
+        "indexer_fp4_last_error": ([], ctypes.c_char_p),
+        "indexer_fp4_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
+        "indexer_fp4_decode_sched_bytes": ([I32, I32, I32], I64),
+        "indexer_fp4_decode_schedule": ([P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
+        "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32], I64),
+        "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
+        "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P], ctypes.c_int),
+        "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P], ctypes.c_int),
+        "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
+        "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, contiguous=True):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise IndexerError(rc, lib.indexer_fp4_last_error().decode())
+
+
+def indexer_fp4_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, q=None, q_packed=None, q_scale=None):
+    """k: bf16 [n_tok, >=128] (row stride k.stride(0)); slot_mapping int64 [n_tok];
+    kv_packed uint8 [n_pages, 64, 64]; kv_scale uint8 [n_pages, 4, 64];
+    q: bf16 [rows, H, 128] or None -> q_packed uint8 [rows, H, 64], q_scale uint8 [rows, H, 4]."""
+    _dev(kv_packed, "kv_packed", torch.uint8)
+    _dev(kv_scale, "kv_scale", torch.uint8)
+    n_tok = 0 if k is None else k.shape[0]
+    if k is not None:
+        _dev(k, "k", torch.bfloat16, contiguous=False)
+        if k.dim() != 2 or k.stride(1) != 1:
+            raise ValueError("k must be 2-D with unit stride along the head dimension")
+        _dev(slot_mapping, "slot_mapping", torch.int64)
+    rows, heads = 0, 0
+    if q is not None:
+        _dev(q, "q", torch.bfloat16)
+        rows, heads, d = q.shape
+        if d != HEAD_DIM:
+            raise ValueError("q must be [rows, heads, 128]")
+        _dev(q_packed, "q_packed", torch.uint8)
+        _dev(q_scale, "q_scale", torch.uint8)
+    _check(lib.indexer_fp4_quant_and_cache(
+        _ptr(k), n_tok, 0 if k is None else k.stride(0), _ptr(slot_mapping), _ptr(kv_packed), _ptr(kv_scale),
+        kv_packed.shape[0], _ptr(q), rows, heads, _ptr(q_packed), _ptr(q_scale), _stream(kv_packed)))
+
+
+def indexer_fp4_decode_sched_bytes(batch: int, next_n: int, n_units: int) -> int:
+    return int(lib.indexer_fp4_decode_sched_bytes(batch, next_n, n_units))
+
+
+def indexer_fp4_prefill_sched_bytes(n_req: int, n_rows_padded: int, n_units: int) -> int:
+    return int(lib.indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units))
+
+
+def indexer_fp4_decode_schedule(context_lens, next_n, n_units, sched, row_len):
+    """context_lens int32 [B]; sched uint8/int32 buffer; row_len int32 [B*next_n] (outputs)."""
+    _dev(context_lens, "context_lens", torch.int32)
+    _dev(sched, "sched")
+    _dev(row_len, "row_len", torch.int32)
+    _check(lib.indexer_fp4_decode_schedule(
+        _ptr(context_lens), context_lens.shape[0], next_n, n_units, _ptr(sched),
+        sched.numel() * sched.element_size(), _ptr(row_len), _stream(sched)))
+
+
+def indexer_fp4_prefill_schedule(cu_rows, start_pos, n_rows_padded, n_units, sched, row_len):
+    _dev(cu_rows, "cu_rows", torch.int32)
+    _dev(start_pos, "start_pos", torch.int32)
+    _dev(sched, "sched")
+    _dev(row_len, "row_len", torch.int32)
+    _check(lib.indexer_fp4_prefill_schedule(
+        _ptr(cu_rows), _ptr(start_pos), start_pos.shape[0], n_rows_padded, n_units, _ptr(sched),
+        sched.numel() * sched.element_size(), _ptr(row_len), _stream(sched)))
+
+
+def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched, n_units,
+                             row_len, logits):
+    """q_packed [B*next_n, H, 64], q_scale [B*next_n, H, 4], weights fp32 [B*next_n, H],
+    block_table int32 [B, W], logits fp32 [B*next_n, LD] (row stride logits.stride(0))."""
+    _dev(q_packed, "q_packed", torch.uint8)
+    _dev(q_scale, "q_scale", torch.uint8)
+    _dev(weights, "weights", torch.float32)
+    _dev(kv_packed, "kv_packed", torch.uint8)
+    _dev(kv_scale, "kv_scale", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(sched, "sched")
+    _dev(row_len, "row_len", torch.int32)
+    _dev(logits, "logits", torch.float32, contiguous=False)
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    batch, bt_ld = block_table.shape
+    _check(lib.indexer_fp4_score_decode(
+        _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
+        kv_packed.shape[0], _ptr(block_table), bt_ld, batch, next_n, _ptr(sched), n_units, _ptr(row_len),
+        _ptr(logits), logits.stride(0), _stream(logits)))
+
+
+def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, sched, n_units,
+                              n_rows_padded, row_len, logits):
+    """block_table int32 [n_req, W] with row i = request i of the step; q/weights/logits have
+    n_rows_padded rows."""
+    _dev(q_packed, "q_packed", torch.uint8)
+    _dev(q_scale, "q_scale", torch.uint8)
+    _dev(weights, "weights", torch.float32)
+    _dev(kv_packed, "kv_packed", torch.uint8)
+    _dev(kv_scale, "kv_scale", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(sched, "sched")
+    _dev(row_len, "row_len", torch.int32)
+    _dev(logits, "logits", torch.float32, contiguous=False)
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    n_req, bt_ld = block_table.shape
+    _check(lib.indexer_fp4_score_prefill(
+        _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
+        kv_packed.shape[0], _ptr(block_table), bt_ld, n_req, _ptr(sched), n_units, n_rows_padded, _ptr(row_len),
+        _ptr(logits), logits.stride(0), _stream(logits)))
+
+
+def indexer_topk_workspace_bytes(n_rows: int, max_len: int, k: int) -> int:
+    return int(lib.indexer_topk_workspace_bytes(n_rows, max_len, k))
+
+
+def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None):
+    """logits fp32 [rows, LD]; row_len int32 [rows]; topk_idx int32 [rows, >=k] (output)."""
+    _dev(logits, "logits", torch.float32, contiguous=False)
+    _dev(row_len, "row_len", torch.int32)
+    _dev(topk_idx, "topk_idx", torch.int32, contiguous=False)
+    if logits.stride(1) != 1 or topk_idx.stride(1) != 1:
+        raise ValueError("logits and topk_idx rows must be contiguous")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.indexer_topk(
+        _ptr(logits), logits.stride(0), logits.shape[0], _ptr(row_len), max_len, k, _ptr(topk_idx),
+        topk_idx.stride(0), _ptr(workspace), ws_bytes, _stream(logits)))
+
+
+# ---- schedule-buffer inspection (host copies; for tests and diagnostics) -----------------
+
+def sched_error(sched) -> int:
+    """Device-side error flags of a schedule buffer (synchronizes)."""
+    return int(sched.view(torch.int32)[1].item())
+
+
+def read_decode_schedule(sched, batch: int, n_units: int) -> dict:
+    w = sched.view(torch.int32).cpu().numpy()
+    cum = 8
+    ub = cum + batch + 1
+    us = ub + n_units + 1
+    return {"header": w[:8].copy(), "cum_pages": w[cum:cum + batch + 1].copy(),
+            "unit_begin": w[ub:ub + n_units + 1].copy(), "unit_seq": w[us:us + n_units].copy()}
+
+
+def read_prefill_schedule(sched, n_req: int, n_rows_padded: int, n_units: int) -> dict:
+    w = sched.view(torch.int32).cpu().numpy()
+    max_tiles = n_rows_padded // TILE_ROWS + n_req
+    tiles = 8
+    cum = tiles + 4 * max_tiles
+    ub = cum + max_tiles + 1
+    ut = ub + n_units + 1
+    n_tiles = int(w[5])
+    return {"header": w[:8].copy(), "tiles": w[tiles:tiles + 4 * n_tiles].reshape(n_tiles, 4).copy(),
+            "cum_items": w[cum:cum + n_tiles + 1].copy(), "unit_begin": w[ub:ub + n_units + 1].copy(),
+            "unit_tile": w[ut:ut + n_units].copy()}

@@ -1,0 +1,102 @@
+// Internal helpers of the gfx950 FP4 indexer library: error reporting, device checks,
+// schedule-buffer layouts, and the block-scaled FP4 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "indexer_fp4.h"
+
+namespace ifp4 {
+
+constexpr int kPage = INDEXER_FP4_PAGE;          // tokens per page
+constexpr int kHeadDim = INDEXER_FP4_HEAD_DIM;   // elements per key / query head
+constexpr int kKeyBytes = kHeadDim / 2;          // packed E2M1 bytes per key (64)
+constexpr int kGroups = kHeadDim / 32;           // e8m0 scales per key (4)
+constexpr int kPageBytes = kPage * kKeyBytes;    // packed plane bytes per page (4096)
+constexpr int kPageScaleBytes = kPage * kGroups; // scale plane bytes per page (256)
+constexpr int kTileRows = INDEXER_FP4_TILE_ROWS; // prefill rows per tile
+
+// ---- errors (thread-local message, see indexer_fp4_last_error) -------------------------
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+int check_device();                 // INDEXER_FP4_EARCH unless the current device is gfx950
+int launch_status(const char *what);  // INDEXER_FP4_EHIP if the last launch failed
+
+// ---- schedule buffers (int32 words) ------------------------------------------------------
+// Decode: [0] magic, [1] error word, [2] batch, [3] next_n, [4] n_units, [5] items,
+//         [6..7] 0, then cum_pages[batch+1], unit_begin[n_units+1], unit_seq[n_units].
+constexpr int32_t kDecodeMagic = 0x34504644;   // "DFP4"
+constexpr int32_t kPrefillMagic = 0x34504650;  // "PFP4"
+constexpr int kHdrWords = 8;
+
+struct DecodeSchedLayout {
+  int64_t cum, unit_begin, unit_seq, words;
+  __host__ __device__ DecodeSchedLayout(int32_t batch, int32_t n_units) {
+    cum = kHdrWords;
+    unit_begin = cum + (int64_t)batch + 1;
+    unit_seq = unit_begin + (int64_t)n_units + 1;
+    words = unit_seq + n_units;
+  }
+};
+
+// Prefill: [0] magic, [1] error word, [2] n_req, [3] n_rows_padded, [4] n_units,
+//          [5] n_tiles, [6] items, [7] tile rows, then tiles[max_tiles] as int4
+//          {first row, rows, request, pages}, cum_items[max_tiles+1],
+//          unit_begin[n_units+1], unit_tile[n_units], req_tile[n_req+1].
+struct PrefillSchedLayout {
+  int64_t max_tiles, tiles, cum, unit_begin, unit_tile, req_tile, words;
+  __host__ __device__ PrefillSchedLayout(int32_t n_req, int32_t n_rows_padded, int32_t n_units) {
+    max_tiles = (int64_t)n_rows_padded / kTileRows + n_req;
+    tiles = kHdrWords;
+    cum = tiles + 4 * max_tiles;
+    unit_begin = cum + max_tiles + 1;
+    unit_tile = unit_begin + (int64_t)n_units + 1;
+    req_tile = unit_tile + n_units;
+    words = req_tile + (int64_t)n_req + 1;
+  }
+};
+
+// ---- block-scaled FP4 MFMA ----------------------------------------------------------------
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// 16x16x128 MXFP4 x MXFP4 -> fp32. Lane l supplies row (A) / column (B) l%16 and the 32
+// K-elements [32*(l/16), 32*(l/16)+32) as 16 bytes, element 2i in the low nibble of byte
+// i; its scale operand carries that (row, 32-block)'s e8m0 byte in byte SA / SB. The
+// result holds C[4*(l/16)+i][l%16] in element i. Only the first four dwords of the A/B
+// operands are read for FP4.
+template <int SA, int SB>
+__device__ __forceinline__ floatx4 mfma_fp4(const uint4 &a, const uint4 &b, floatx4 c, uint32_t sa,
+                                            uint32_t sb) {
+  intx8 av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  intx8 bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, SA, (int)sa, SB, (int)sb);
+}
+
+// compile-time loop: f(std::integral_constant<int, I>{}) for I = 0..N-1
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Read-only view in the constant address space: wave-uniform reads through it become scalar
+// loads, which do not wait behind the vector-memory queue (the page prefetches). Only for
+// memory the kernel does not write.
+template <class T>
+using const_ptr = const __attribute__((address_space(4))) T *;
+template <class T>
+__device__ __forceinline__ const_ptr<T> as_const(const T *p) {
+  return (const_ptr<T>)p;
+}
+
+}  // namespace ifp4

@@ -1,0 +1,87 @@
+// Register-level building blocks shared by the decode and prefill scorers: a 64-key
+// page of the FP4 cache held as MFMA B operands, query rows held as MFMA A operands, and
+// the per-page logit (block-scaled FP4 MFMAs, ReLU, head-weighted sum, cross-lane
+// reduction). See score_decode.hip for the data movement these registers encode.
+#pragma once
+#include "common.h"
+
+namespace ifp4 {
+
+struct PageRegs {
+  uint4 k[4];  // 4 key tiles x 16 bytes
+  uint32_t s;  // scales: byte t = tile t
+};
+
+template <int NH16, int NN>
+struct RowRegs {
+  uint4 qa[NN][NH16];                // query operand per M-tile (16 heads)
+  uint32_t qs[NN][(NH16 + 3) / 4];   // query scales, byte m%4 of word m/4
+  float4 w[NN][NH16];                // weights of heads 16m + 4(l/16) + i
+};
+
+template <int NH16, int NN>
+__device__ __forceinline__ void load_rows(RowRegs<NH16, NN> &R, const uint8_t *__restrict__ qp,
+                                          const uint8_t *__restrict__ qs, const float *__restrict__ w,
+                                          int64_t row0, int n_valid, int n_heads, int lane) {
+  const int hl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < NN; n++) {
+    if (n >= n_valid) break;  // rows past the tile are never read
+    const int64_t r = row0 + n;
+#pragma unroll
+    for (int j = 0; j < (NH16 + 3) / 4; j++) R.qs[n][j] = 0;
+#pragma unroll
+    for (int m = 0; m < NH16; m++) {
+      const int64_t v = r * n_heads + 16 * m + hl;
+      R.qa[n][m] = *reinterpret_cast<const uint4 *>(qp + v * kKeyBytes + 16 * g);
+      R.qs[n][m / 4] |= (uint32_t)qs[v * kGroups + g] << (8 * (m % 4));
+      R.w[n][m] = *reinterpret_cast<const float4 *>(w + r * n_heads + 16 * m + 4 * g);
+    }
+  }
+  // Wait for the query loads here (vmcnt 0; expcnt and lgkmcnt left free). Rows are
+  // reloaded only when a wave moves to another sequence or tile; without this wait the
+  // compiler would have to assume at every page that the query loads are the youngest in
+  // flight and drain the whole page prefetch ring before each page's MFMAs.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+__device__ __forceinline__ void load_page(PageRegs &P, const uint8_t *__restrict__ kvp,
+                                          const uint8_t *__restrict__ kvs, int64_t phys, int lane) {
+  const uint8_t *base = kvp + phys * kPageBytes + (lane & 15) * kKeyBytes + (lane >> 4) * 16;
+#pragma unroll
+  for (int t = 0; t < 4; t++) P.k[t] = *reinterpret_cast<const uint4 *>(base + 1024 * t);
+  P.s = *reinterpret_cast<const uint32_t *>(kvs + phys * kPageScaleBytes + 4 * lane);
+}
+
+// Logit of key `lane` of the page for row n: sum over heads of w * ReLU(q . k).
+template <int NH16, int NN, int N>
+__device__ __forceinline__ float page_logit(const PageRegs &P, const RowRegs<NH16, NN> &R, int lane) {
+  float acc[4];
+  static_for<4>([&](auto tt) {
+    constexpr int T = decltype(tt)::value;
+    float a = 0.f;
+    static_for<NH16>([&](auto mm) {
+      constexpr int M = decltype(mm)::value;
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      const floatx4 c = mfma_fp4<M % 4, T>(R.qa[N][M], P.k[T], zero, R.qs[N][M / 4], P.s);
+      a += R.w[N][M].x * fmaxf(c[0], 0.f);
+      a += R.w[N][M].y * fmaxf(c[1], 0.f);
+      a += R.w[N][M].z * fmaxf(c[2], 0.f);
+      a += R.w[N][M].w * fmaxf(c[3], 0.f);
+    });
+    acc[T] = a;
+  });
+  // lanes 16G..16G+15 hold, for every tile, partial sums over their heads; reduce across
+  // the four lane groups so that lane 16G+j ends with tile G's full sum for key j
+  const int G = lane >> 4;
+  const bool lo = G < 2;
+  float kx = lo ? acc[0] : acc[2];
+  float ky = lo ? acc[1] : acc[3];
+  kx += __shfl_xor(lo ? acc[2] : acc[0], 32, 64);
+  ky += __shfl_xor(lo ? acc[3] : acc[1], 32, 64);
+  const bool odd = G & 1;
+  const float keep = odd ? ky : kx;
+  return keep + __shfl_xor(odd ? kx : ky, 16, 64);
+}
+
+}  // namespace ifp4

@@ -1,0 +1,97 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports every entry
+point declared in include/indexer_fp4.h, and its size queries and argument checks behave as
+documented (every error path below returns before any device call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "indexer_fp4.h")
+LIB = os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "libindexer_fp4.so")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        from sparse_attention_indexer_fp4_amd import build
+
+        build.build()
+    lib = ctypes.CDLL(LIB)
+    lib.indexer_fp4_last_error.restype = ctypes.c_char_p
+    for name in ("indexer_fp4_decode_sched_bytes", "indexer_fp4_prefill_sched_bytes",
+                 "indexer_topk_workspace_bytes"):
+        getattr(lib, name).restype = ctypes.c_int64
+    lib.indexer_topk_workspace_bytes.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|char|void)\s*\*?\s*(indexer_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(L, n), n
+    import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
+
+    assert set(pkg_module.EXPORTS) == set(names)
+
+
+def test_size_queries(L):
+    # decode: 8-word header + cum[B+1] + unit_begin[U+1] + unit_seq[U]
+    assert L.indexer_fp4_decode_sched_bytes(8, 1, 512) == 4 * (8 + 9 + 513 + 512)
+    assert L.indexer_fp4_decode_sched_bytes(-1, 1, 512) < 0
+    assert L.indexer_fp4_decode_sched_bytes(8, 1, 0) < 0
+    # prefill: header + tiles[max] x4 + cum[max+1] + unit_begin[U+1] + unit_tile[U] + req_tile[R+1]
+    mt = 2048 // 8 + 4
+    assert L.indexer_fp4_prefill_sched_bytes(4, 2048, 4096) == 4 * (8 + 4 * mt + mt + 1 + 4097 + 4096 + 5)
+    assert L.indexer_fp4_prefill_sched_bytes(0, 2048, 4096) < 0
+    assert L.indexer_topk_workspace_bytes(8, 131072, 2048) >= 0
+    assert L.indexer_topk_workspace_bytes(8, 131072, 0) < 0
+
+
+def _err(L):
+    return L.indexer_fp4_last_error().decode()
+
+
+def test_host_argument_errors(L):
+    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.indexer_fp4_decode_schedule.argtypes = [P, I32, I32, I32, P, I64, P, P]
+    # next_n out of range
+    assert L.indexer_fp4_decode_schedule(None, 8, 5, 512, None, 0, None, None) == -1
+    assert "next_n=5" in _err(L)
+    # schedule buffer too small: never silently truncated
+    assert L.indexer_fp4_decode_schedule(None, 8, 1, 512, None, 100, None, None) == -2
+    assert "needs" in _err(L) and "100" in _err(L)
+    L.indexer_fp4_prefill_schedule.argtypes = [P, P, I32, I32, I32, P, I64, P, P]
+    assert L.indexer_fp4_prefill_schedule(None, None, 4, 1001, 4096, None, 0, None, None) == -1
+    assert "multiple of 8" in _err(L)
+    L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P]
+    # head count not a multiple of 16 (the MFMA tile height)
+    assert L.indexer_fp4_score_decode(None, None, None, 24, None, None, 0, None, 8, 1, 1, None, 512, None,
+                                      None, 512, None) == -1
+    assert "n_heads=24" in _err(L)
+    # logits row too short for the block table
+    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 1, 1, None, 512, None,
+                                      None, 500, None) == -2
+    assert "logits_ld=500" in _err(L)
+    L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P]
+    assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, None, 8, 0, None, 512, 8, None,
+                                       None, 512, None) == -1
+    L.indexer_topk.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, I64, P]
+    assert L.indexer_topk(None, 100, 4, None, 100, 0, None, 16, None, 0, None) == -1
+    assert "k=0" in _err(L)
+    assert L.indexer_topk(None, 100, 4, None, 100, 32, None, 16, None, 0, None) == -2
+    assert "topk_ld=16" in _err(L)
+    assert L.indexer_topk(None, 100, 4, None, 200, 32, None, 32, None, 0, None) == -1
+    L.indexer_fp4_quant_and_cache.argtypes = [P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P]
+    assert L.indexer_fp4_quant_and_cache(None, 4, 128, None, None, None, 1, None, 0, 0, None, None, None) == -1
+    assert L.indexer_fp4_quant_and_cache(P(16), 4, 100, P(16), P(16), P(16), 1, None, 0, 0, None, None, None) == -1
+    assert "k_ld=100" in _err(L)

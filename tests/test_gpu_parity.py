@@ -1,0 +1,249 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
+inputs. Bit-exact for bytes, schedules and indices; 1e-3 relative for logits; top-k sets
+equal up to near-ties of the k-th score (see helpers.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from helpers import (bf16_tensor, check_logits, check_topk, dev, gpu_decode, gpu_prefill_step, oracle_decode,
+                     oracle_prefill_step, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ifp4():
+    import sparse_attention_indexer_fp4_amd as m
+
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------- cache write
+
+@pytest.mark.parametrize("sens", [False, True])
+def test_cache_and_query_bytes_exact(ifp4, sens):
+    case = W.decode_config("decode_tiny", swizzle_sensitive=sens)
+    _say(f"decode_tiny swizzle_sensitive={sens}")
+    g = gpu_decode(case, run_topk=False)
+    o = oracle_decode(case, scores=False)
+    assert np.array_equal(g["kp"].cpu().numpy(), o["kp"])
+    assert np.array_equal(g["ks"].cpu().numpy(), o["ks"])
+    assert np.array_equal(g["qp"].cpu().numpy(), o["qp"])
+    assert np.array_equal(g["qs"].cpu().numpy(), o["qs"])
+
+
+def _all_finite_bf16():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    return b[((b.astype(np.int64) >> 7) & 0xFF) != 0xFF]
+
+
+def test_quantizer_exhaustive_bf16(ifp4):
+    """Every finite bf16 value alone in its block, in a random block mix, and under fixed
+    block scales 2^e (e = -10..10), through the query arm: bytes equal the oracle's."""
+    bits = _all_finite_bf16()
+    rng = np.random.default_rng(11)
+    vecs = []
+    alone = np.zeros((bits.size, 32), np.uint16)
+    alone[:, 0] = bits
+    vecs.append(alone.reshape(-1, 128))
+    vecs.append(rng.permutation(np.concatenate([bits, bits[: (-bits.size) % 128]])).reshape(-1, 128))
+    for e in range(-10, 11):
+        v = W.bf16_to_f32(bits).astype(np.float64)
+        sel = bits[np.abs(v) < 2.0 ** (e + 2)]
+        blk = np.zeros((sel.size, 32), np.uint16)
+        blk[:, 0] = W.bf16_bits(np.full(sel.size, 2.0 ** (e + 2), np.float32))
+        blk[:, 1] = sel
+        blk = np.concatenate([blk, np.zeros(((-sel.size) % 4, 32), np.uint16)])
+        vecs.append(blk.reshape(-1, 128))
+    q = np.concatenate(vecs)[:, None, :]  # [rows, 1 head, 128]
+    _say(f"exhaustive quantizer rows={q.shape[0]}")
+    qp = torch.empty((q.shape[0], 1, 64), dtype=torch.uint8, device=dev())
+    qs = torch.empty((q.shape[0], 1, 4), dtype=torch.uint8, device=dev())
+    kp = torch.zeros((1, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((1, 4, 64), dtype=torch.uint8, device=dev())
+    ifp4.indexer_fp4_quant_and_cache(None, None, kp, ks, bf16_tensor(q), qp, qs)
+    oqp, oqs = oracle.quant_q(q)
+    assert np.array_equal(qs.cpu().numpy(), oqs)
+    assert np.array_equal(qp.cpu().numpy(), oqp)
+
+
+def test_writer_skips_negative_and_out_of_pool_slots(ifp4):
+    keys = W.normal_bf16(np.random.default_rng(5), (6, 128))
+    slots = np.array([-1, 3, 64 * 2, -5, 64 * 2 + 70, 127], np.int64)  # page 2 does not exist
+    kp = torch.full((2, 64, 64), 0xA5, dtype=torch.uint8, device=dev())
+    ks = torch.full((2, 4, 64), 0x5A, dtype=torch.uint8, device=dev())
+    ifp4.indexer_fp4_quant_and_cache(bf16_tensor(keys), to_dev(slots), kp, ks)
+    okp = np.full((2, 64, 64), 0xA5, np.uint8)
+    oks = np.full((2, 4, 64), 0x5A, np.uint8)
+    ok = slots < 128
+    oracle.quant_and_cache(keys[ok], slots[ok], okp, oks)
+    assert np.array_equal(kp.cpu().numpy(), okp)
+    assert np.array_equal(ks.cpu().numpy(), oks)
+
+
+# ---------------------------------------------------------------------------- schedules
+
+@pytest.mark.parametrize("ctx,units,next_n", [([300, 512], 512, 1), ([4096], 512, 1), ([0, 65, 64, 1, 0], 7, 1),
+                                              ([131072] * 8, 512, 1), ([5] * 3000, 512, 1), ([200, 77], 64, 3)])
+def test_decode_schedule_exact(ifp4, ctx, units, next_n):
+    ctx = np.array(ctx, np.int32)
+    sched = torch.full((ifp4.indexer_fp4_decode_sched_bytes(len(ctx), next_n, units),), 0xEE, dtype=torch.uint8,
+                       device=dev())
+    row_len = torch.empty(len(ctx) * next_n, dtype=torch.int32, device=dev())
+    ifp4.indexer_fp4_decode_schedule(to_dev(ctx), next_n, units, sched, row_len)
+    got = ifp4.read_decode_schedule(sched, len(ctx), units)
+    want = oracle.decode_schedule(ctx, units)
+    for key in ("cum_pages", "unit_begin", "unit_seq"):
+        assert np.array_equal(got[key], want[key]), key
+    assert got["header"][1] == 0
+    _, rl = oracle.decode_geometry(ctx, next_n)
+    assert np.array_equal(row_len.cpu().numpy(), rl)
+
+
+@pytest.mark.parametrize("which", ["prefill_tiny", "prefill_4req"])
+@pytest.mark.parametrize("units", [13, 512, 4096])
+def test_prefill_schedule_exact(ifp4, which, units):
+    case = W.prefill_config(which, heads=16)
+    for st in case.steps:
+        R, NP = len(st.req_ids), st.n_rows_padded
+        sched = torch.full((ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units),), 0xEE, dtype=torch.uint8,
+                           device=dev())
+        row_len = torch.empty(NP, dtype=torch.int32, device=dev())
+        ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, sched, row_len)
+        got = ifp4.read_prefill_schedule(sched, R, NP, units)
+        want = oracle.prefill_schedule(st.cu_rows, st.start_pos, NP, 8, units)
+        assert got["header"][1] == 0
+        for key in ("tiles", "cum_items", "unit_begin", "unit_tile"):
+            assert np.array_equal(got[key], want[key]), key
+        _, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, NP)
+        assert np.array_equal(row_len.cpu().numpy(), rl)
+
+
+# ---------------------------------------------------------------------------- decode scores
+
+DECODE_CASES = [
+    dict(name="decode_tiny"),
+    dict(name="decode_tiny", swizzle_sensitive=True),
+    dict(name="h64_ragged", ctx=[1000, 64, 1, 129, 4095], heads=64, topk=256),
+    dict(name="h32_small_k", ctx=[700, 70], heads=32, topk=16),
+    dict(name="h128", ctx=[513, 2000], heads=128, topk=300),
+    dict(name="next_n2", ctx=[300, 191], heads=64, topk=64, next_n=2),
+    dict(name="next_n4", ctx=[520, 4], heads=16, topk=32, next_n=4),
+]
+
+
+@pytest.mark.parametrize("p", DECODE_CASES, ids=lambda p: p["name"] + ("_sens" if p.get("swizzle_sensitive") else ""))
+@pytest.mark.parametrize("units", [512, 5])
+def test_decode_scores_and_topk(ifp4, p, units):
+    p = dict(p)
+    name = p.pop("name")
+    case = W.decode_config(name, **p) if name in W.DECODE_CONFIGS else W.decode_case(name=name, **p)
+    _say(f"decode {name} ctx={list(case.ctx)} H={case.heads} next_n={case.next_n} units={units}")
+    g = gpu_decode(case, units=units)
+    o = oracle_decode(case)
+    assert g["err"] == 0
+    assert np.array_equal(g["row_len"].cpu().numpy(), o["row_len"])
+    check_logits(g["logits"].cpu().numpy(), o["s"], o["row_len"])
+    check_topk(g["top"].cpu().numpy(), o["top"], o["s"], o["row_len"], case.topk)
+
+
+def test_topk_is_exact_on_the_same_logits(ifp4):
+    """Selection itself is exact: on the GPU's own fp32 logits the GPU top-k equals the oracle's
+    full sort (ties to the lower column), returned in ascending column order."""
+    case = W.decode_case([3000, 4096, 2049, 100], heads=16, topk=2048, seed=9)
+    g = gpu_decode(case)
+    lg = g["logits"].cpu().numpy().astype(np.float64)
+    rl = g["row_len"].cpu().numpy()
+    want = oracle.topk(lg, rl, case.topk)
+    top = g["top"].cpu().numpy()
+    for r in range(case.rows):
+        n = min(case.topk, int(rl[r]))
+        assert list(top[r][:n]) == sorted(want[r][:n].tolist())
+        assert (top[r][n:] == -1).all()
+
+
+def test_topk_ties_and_signed_zero(ifp4):
+    rng = np.random.default_rng(3)
+    rows, n = 6, 5000
+    lg = rng.integers(-3, 4, size=(rows, n)).astype(np.float32)  # heavy ties
+    lg[1] = 0.0
+    lg[1, ::2] = -0.0                                          # -0 ranks with +0
+    lg[2] = rng.standard_normal(n).astype(np.float32)
+    lg[3, :] = 7.0
+    lg[4] = -np.abs(rng.standard_normal(n)).astype(np.float32)  # all negative
+    rl = np.array([n, n, 2500, 4097, n, 10], np.int32)
+    k = 2048
+    t = to_dev(lg)
+    top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk(t, to_dev(rl), n, k, top)
+    want = oracle.topk(lg.astype(np.float64), rl, k)
+    got = top.cpu().numpy()
+    for r in range(rows):
+        m = min(k, int(rl[r]))
+        assert list(got[r][:m]) == sorted(want[r][:m].tolist()), r
+        assert (got[r][m:] == -1).all()
+
+
+def test_device_side_errors_flag_and_skip(ifp4):
+    case = W.decode_config("decode_tiny")
+    bt = case.block_table.copy()
+    bt[0, 1] = 10_000   # outside the pool
+    bt[1, 2] = -3
+    case.block_table = bt
+    g = gpu_decode(case, run_topk=False)
+    assert g["err"] & ifp4.DEV_BAD_PAGE
+    lg = g["logits"].cpu().numpy()
+    assert np.isnan(lg[0, 64:128]).all() and np.isnan(lg[1, 128:192]).all()  # skipped, not faulted
+    o = oracle_decode(W.decode_config("decode_tiny"))
+    good = np.ones_like(lg, bool)
+    good[0, 64:128] = False
+    good[1, 128:192] = False
+    for r in range(2):
+        L = int(o["row_len"][r])
+        m = good[r, :L]
+        assert np.allclose(lg[r, :L][m], o["s"][r, :L][m], rtol=1e-3, atol=0)
+
+
+# ---------------------------------------------------------------------------- prefill scores
+
+@pytest.mark.parametrize("which,heads,units", [("prefill_tiny", 16, 512), ("prefill_tiny", 64, 7),
+                                               ("prefill_tiny", 64, 4096)])
+def test_prefill_scores_and_topk(ifp4, which, heads, units):
+    case = W.prefill_config(which, heads=heads)
+    kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((case.n_pages, 4, 64), dtype=torch.uint8, device=dev())
+    okp = np.zeros((case.n_pages, 64, 64), np.uint8)
+    oks = np.zeros((case.n_pages, 4, 64), np.uint8)
+    for si, st in enumerate(case.steps):
+        _say(f"prefill {which} H={heads} units={units} step {si} rows={st.n_rows}/{st.n_rows_padded}")
+        g = gpu_prefill_step(case, st, kp, ks, units=units)
+        o = oracle_prefill_step(case, st, okp, oks)
+        assert g["err"] == 0
+        assert np.array_equal(kp.cpu().numpy(), okp) and np.array_equal(ks.cpu().numpy(), oks)
+        assert np.array_equal(g["qp"].cpu().numpy(), o["qp"])
+        assert np.array_equal(g["row_len"].cpu().numpy(), o["row_len"])
+        check_logits(g["logits"].cpu().numpy(), o["s"], o["row_len"])
+        check_topk(g["top"].cpu().numpy(), o["top"], o["s"], o["row_len"], case.topk)
+        pad = np.arange(st.n_rows_padded) >= st.n_rows
+        assert (g["top"].cpu().numpy()[pad] == -1).all()  # padding rows select nothing
+
+
+# ---------------------------------------------------------------------------- full sizes
+
+@pytest.mark.parametrize("name", ["decode_b1_4k", "decode_b8_128k"])
+def test_full_size_decode(ifp4, name):
+    case = W.decode_config(name)
+    _say(f"full-size {name}: B={case.batch} ctx={int(case.ctx[0])}")
+    g = gpu_decode(case)
+    assert g["err"] == 0
+    o = oracle_decode(case)
+    assert np.array_equal(g["kp"].cpu().numpy(), o["kp"])
+    assert np.array_equal(g["ks"].cpu().numpy(), o["ks"])
+    check_logits(g["logits"].cpu().numpy(), o["s"], o["row_len"])
+    check_topk(g["top"].cpu().numpy(), o["top"], o["s"], o["row_len"], case.topk)
