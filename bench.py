@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP4 sparse-indexer hot path on one MI355X.
+
+A step is one decode step of the indexer over 21 layers at batch 8 x context 131072 (64
+index heads x 128, index_topk 2048): the decode schedule is published once, then every
+layer writes its 8 new keys and quantizes its queries (indexer_fp4_quant_and_cache),
+scores all keys (indexer_fp4_score_decode) and selects the top-k (indexer_topk). Each layer
+has its own key cache (21 x 78 MB), so the scan streams from HBM instead of the 256 MB
+last-level cache. The pages' indexer has 21 layers ("Score a DSA sparse indexer in FP4",
+PR description: 21 layers x 5.8 us of grid overhead a step).
+
+Steps run as replays of a HIP graph captured from the library calls (the calls are
+capturable: fixed grids, lengths read on the device, no host reads or allocations), as a
+serving engine would run them. Printed: one JSON line with the throughput (keys scored per
+second over whole steps), the decode scorer's roofline (algorithmic bytes per launch over
+its mean launch time: HIP events around replays of a graph holding the step's 21 scorer
+launches), the prefill path's time per layer and FP4 MFMA roofline (4 requests of
+3420..4213 tokens, 512-token chunks), and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4
+METRIC = "indexer keys scored/sec + µs/layer decode & prefill; % HBM / MFMA roofline"
+
+
+def kernel_source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_scorer_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -> int:
+    """Algorithmic HBM bytes of one decode-scorer launch: every key's 64 packed + 4 scale
+    bytes read once and its fp32 logit written once; one block-table entry per page; per
+    row the quantized query (64 + 4 bytes per head), its fp32 head weights and its length."""
+    return n_keys * (64 + 4 + 4) + n_pages * 4 + rows * (heads * (64 + 4) + heads * 4 + 4)
+
+
+def build_decode(torch, ifp4, W, layers, units, seed):
+    dev = torch.device("cuda:0")
+    case_ctx = W.DECODE_CONFIGS["decode_b8_128k"]
+    ctx = np.array(case_ctx["ctx"], np.int32)
+    H, k = case_ctx["heads"], case_ctx["topk"]
+    B = ctx.shape[0]
+    rng = np.random.default_rng(seed)
+    # one shuffled block table shared by the layers (each layer has its own cache buffers)
+    pages_per = (ctx + 63) // 64
+    need = int(pages_per.sum())
+    n_pages = need + need // 10
+    perm = rng.permutation(n_pages).astype(np.int32)
+    bt = perm[:need].reshape(B, -1)
+    bt_t = torch.from_numpy(bt).to(dev)
+    slots_all = (bt.astype(np.int64)[:, :, None] * 64 + np.arange(64)).reshape(B, -1)
+    slots_all_t = torch.from_numpy(slots_all.reshape(-1).copy()).to(dev)
+    new_slots = torch.from_numpy(slots_all[np.arange(B), ctx - 1].copy()).to(dev)
+    gen = torch.Generator(device=dev)
+    L = []
+    for layer in range(layers):
+        gen.manual_seed(seed * 1000 + layer)
+        kp = torch.empty((n_pages, 64, 64), dtype=torch.uint8, device=dev)
+        ks = torch.empty((n_pages, 4, 64), dtype=torch.uint8, device=dev)
+        keys = torch.randn((B * int(ctx[0]), 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ifp4.indexer_fp4_quant_and_cache(keys, slots_all_t, kp, ks)
+        del keys
+        q = torch.randn((B, H, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        w = torch.rand((B, H), generator=gen, device=dev, dtype=torch.float32)
+        knew = torch.randn((B, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        L.append(dict(kp=kp, ks=ks, q=q, w=w, knew=knew,
+                      qp=torch.empty((B, H, 64), dtype=torch.uint8, device=dev),
+                      qs=torch.empty((B, H, 4), dtype=torch.uint8, device=dev)))
+    ld = bt.shape[1] * 64
+    shared = dict(
+        ctx=torch.from_numpy(ctx).to(dev), bt=bt_t, new_slots=new_slots,
+        sched=torch.empty(ifp4.indexer_fp4_decode_sched_bytes(B, 1, units), dtype=torch.uint8, device=dev),
+        row_len=torch.empty(B, dtype=torch.int32, device=dev),
+        logits=torch.empty((B, ld), dtype=torch.float32, device=dev),
+        top=torch.empty((B, k), dtype=torch.int32, device=dev),
+        ws=torch.empty(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 1), dtype=torch.uint8, device=dev),
+    )
+    torch.cuda.synchronize()
+    meta = dict(B=B, H=H, k=k, ctx=int(ctx[0]), n_keys=int(ctx.astype(np.int64).sum()), n_pages_read=need,
+                ld=ld, units=units)
+    return L, shared, meta
+
+
+def decode_step(ifp4, L, S, meta):
+    """One decode step over all layers: schedule once, then per layer write + score + select."""
+    units, ld, k = meta["units"], meta["ld"], meta["k"]
+    ifp4.indexer_fp4_decode_schedule(S["ctx"], 1, units, S["sched"], S["row_len"])
+    for lay in L:
+        ifp4.indexer_fp4_quant_and_cache(lay["knew"], S["new_slots"], lay["kp"], lay["ks"], lay["q"], lay["qp"],
+                                         lay["qs"])
+        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
+                                      units, S["row_len"], S["logits"])
+        ifp4.indexer_topk(S["logits"], S["row_len"], ld, k, S["top"], S["ws"])
+
+
+def decode_scorers(ifp4, L, S, meta):
+    """The step's 21 scorer launches alone (one per layer cache)."""
+    for lay in L:
+        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
+                                      meta["units"], S["row_len"], S["logits"])
+
+
+def capture(torch, fn):
+    """Capture fn() into a HIP graph (after one run on the capture side stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def timed_replays(torch, g, reps):
+    """Milliseconds per replay, HIP events on the replay stream, synchronized on both sides."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def bench_decode(torch, ifp4, W, args):
+    L, S, meta = build_decode(torch, ifp4, W, args.layers, args.units, args.seed)
+    for _ in range(args.warmup):
+        decode_step(ifp4, L, S, meta)
+    torch.cuda.synchronize()
+    if ifp4.sched_error(S["sched"]) != 0:
+        raise RuntimeError(f"device error flags {ifp4.sched_error(S['sched'])}")
+    step_graph = capture(torch, lambda: decode_step(ifp4, L, S, meta))
+    for _ in range(args.warmup):
+        step_graph.replay()
+    wall0 = time.perf_counter()
+    ms_per_step = timed_replays(torch, step_graph, args.steps)
+    wall = time.perf_counter() - wall0
+    # the dominant kernel alone: 21 scorer launches per replay, averaged over the replays
+    scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
+    scorer_graph.replay()
+    scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / args.layers
+    keys_per_step = meta["n_keys"] * args.layers
+    alg_bytes = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
+    achieved = alg_bytes / (scorer_us * 1e-6) / 1e9
+    return dict(meta=meta, ms_per_step=ms_per_step, wall_s=wall, keys_per_s=keys_per_step / (ms_per_step * 1e-3),
+                scorer_us=scorer_us, alg_bytes=alg_bytes, achieved_gbs=achieved)
+
+
+def bench_prefill(torch, ifp4, W, args):
+    dev = torch.device("cuda:0")
+    case = W.prefill_config("prefill_4req", seed=args.seed)
+    units = args.prefill_units
+    kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev)
+    ks = torch.zeros((case.n_pages, 4, 64), dtype=torch.uint8, device=dev)
+    ld = case.block_table.shape[1] * 64
+    steps = []
+    pairs = 0
+    for st in case.steps:
+        NP, R = st.n_rows_padded, len(st.req_ids)
+        keys, slots = W.step_keys(case, st)
+        bt = W.step_block_table(case, st)
+        rl = np.zeros(NP, np.int64)
+        for i in range(R):
+            n = int(st.cu_rows[i + 1] - st.cu_rows[i])
+            rl[st.cu_rows[i]:st.cu_rows[i + 1]] = st.start_pos[i] + np.arange(n) + 1
+        pairs += int(rl.sum())
+        steps.append(dict(
+            NP=NP, R=R,
+            keys=torch.from_numpy(keys.view(np.int16)).view(torch.bfloat16).to(dev),
+            slots=torch.from_numpy(slots).to(dev),
+            q=torch.from_numpy(st.q.view(np.int16)).view(torch.bfloat16).to(dev),
+            w=torch.from_numpy(st.w).to(dev),
+            cu=torch.from_numpy(st.cu_rows).to(dev), sp=torch.from_numpy(st.start_pos).to(dev),
+            bt=torch.from_numpy(bt).to(dev),
+            qp=torch.empty((NP, case.heads, 64), dtype=torch.uint8, device=dev),
+            qs=torch.empty((NP, case.heads, 4), dtype=torch.uint8, device=dev),
+            sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8, device=dev),
+            row_len=torch.empty(NP, dtype=torch.int32, device=dev),
+            logits=torch.empty((NP, ld), dtype=torch.float32, device=dev),
+            top=torch.empty((NP, case.topk), dtype=torch.int32, device=dev)))
+
+    def run():
+        for s in steps:
+            ifp4.indexer_fp4_quant_and_cache(s["keys"], s["slots"], kp, ks, s["q"], s["qp"], s["qs"])
+            ifp4.indexer_fp4_prefill_schedule(s["cu"], s["sp"], s["NP"], units, s["sched"], s["row_len"])
+            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["bt"], s["sched"], units, s["NP"],
+                                           s["row_len"], s["logits"])
+            ifp4.indexer_topk(s["logits"], s["row_len"], ld, case.topk, s["top"])
+
+    def scorers():
+        for s in steps:
+            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["bt"], s["sched"], units, s["NP"],
+                                           s["row_len"], s["logits"])
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    reps = max(1, args.prefill_reps)
+    layer_graph = capture(torch, run)
+    layer_us = 1e3 * timed_replays(torch, layer_graph, reps)
+    scorer_graph = capture(torch, scorers)
+    scorer_us = 1e3 * timed_replays(torch, scorer_graph, reps)
+    flops = 16384 * pairs
+    tflops = flops / (scorer_us * 1e-6) / 1e12
+    return dict(workload="prefill_4req", lengths=[int(x) for x in case.lengths], chunk=case.chunk,
+                steps=len(steps), causal_pairs=pairs, us_per_layer=round(layer_us, 2),
+                scorer_us_per_layer=round(scorer_us, 2), keys_scored_per_s=pairs / (layer_us * 1e-6),
+                roofline={"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP4_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)})
+
+
+def cpu_baseline(W, seconds: float):
+    """The oracle on the decode workload's first sequences: score every key (fp64) and run
+    the full-sort top-k, repeated until `seconds` of work; returns keys scored per second."""
+    import oracle
+
+    case = W.decode_config("decode_b8_128k", seed=0)
+    kp = np.zeros((case.n_pages, 64, 64), np.uint8)
+    ks = np.zeros((case.n_pages, 4, 64), np.uint8)
+    oracle.quant_and_cache(case.keys, case.slots, kp, ks)
+    qp, qs = oracle.quant_q(case.q)
+    rs, rl = oracle.decode_geometry(case.ctx)
+    done_keys, t0 = 0, time.perf_counter()
+    reps = 0
+    while True:
+        s, _ = oracle.score(qp, qs, case.w, rs, rl, kp, ks, case.block_table)
+        oracle.topk(s, rl, case.topk)
+        done_keys += int(rl.sum())
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(done_keys / dt, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} pass(es) of fp64 score + full-sort top-k over one layer of the 8 x 131072 decode "
+                      f"workload ({int(rl.sum())} keys each), cache already written; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--layers", type=int, default=21)
+    ap.add_argument("--units", type=int, default=None)
+    ap.add_argument("--prefill-units", type=int, default=None)
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 256 MiB device-to-device copy, a kernel of known traffic "
+                         "for scaling hardware byte counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (this build has no "
+              f"multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+
+    import sparse_attention_indexer_fp4_amd as ifp4
+    import workloads as W
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("bench: copy calibration kernel: 268435456 bytes read, 268435456 written", file=sys.stderr, flush=True)
+        del src, dst
+    args.units = args.units or ifp4.DECODE_UNITS
+    args.prefill_units = args.prefill_units or ifp4.PREFILL_UNITS
+    print(f"bench: decode 8 x 131072, {args.layers} layers, steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    d = bench_decode(torch, ifp4, W, args)
+    print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scorer {d['scorer_us']:.2f} us "
+          f"({d['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    pre = None
+    if not args.no_prefill:
+        pre = bench_prefill(torch, ifp4, W, args)
+        print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us",
+              file=sys.stderr, flush=True)
+
+    # HBM traffic of the scorer from rocprofv3 counters, valid only for the kernel they were taken on
+    traffic = None
+    tf = os.path.join(ROOT, "profiles", "decode_scorer_traffic.json")
+    if os.path.exists(tf):
+        with open(tf) as f:
+            rec = json.load(f)
+        if rec.get("kernel_hash") == kernel_source_hash(["score_decode.hip", "score_common.h", "common.h"]):
+            traffic = rec.get("bytes_per_launch")
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(W, args.cpu_seconds)
+
+    m = d["meta"]
+    line = {
+        "metric": METRIC,
+        "value": round(d["keys_per_s"], 1),
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": "decode_b8_128k", "batch": m["B"], "context": m["ctx"], "heads": m["H"],
+                   "head_dim": 128, "index_topk": m["k"], "layers": args.layers, "page": 64,
+                   "units": m["units"]},
+        "decode_us_per_layer": round(1e3 * d["ms_per_step"] / args.layers, 3),
+        "roofline": {"bound": "hbm", "achieved": round(d["achieved_gbs"], 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(d["achieved_gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "score_decode", "launch_us_mean": round(d["scorer_us"], 3),
+                     "alg_bytes_per_launch": d["alg_bytes"]},
+        "cpu_baseline": cpu,
+        "prefill": pre,
+    }
+    if rank == 0:
+        print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
