@@ -68,7 +68,7 @@ def _declare(L):
         "oracle_score": [P, P, P, I32, I64, P, P, P, P, I64, P, I64, P, I64, P],
         "oracle_score_pairs": [P, P, P, I32, P, P, P, P, I64, P, I64, P, P, I64, P],
         "oracle_topk": [P, I64, I64, P, I32, P, I64],
-        "oracle_decode_schedule": [P, I32, I32, P, P, P],
+        "oracle_decode_schedule": [P, I32, I32, P, P, P, P, P],
         "oracle_prefill_schedule": [P, P, I32, I32, I32, I32, I32, P, P, P, P, P],
     }
     for name, args in sigs.items():
@@ -230,8 +230,11 @@ def decode_schedule(ctx, n_units):
     cum = np.zeros(b + 1, np.int32)
     ub = np.zeros(n_units + 1, np.int32)
     us = np.zeros(n_units, np.int32)
-    _check(lib().oracle_decode_schedule(_p(ctx), b, n_units, _p(cum), _p(ub), _p(us)), "decode_schedule")
-    return {"cum_pages": cum, "unit_begin": ub, "unit_seq": us}
+    up = np.zeros(n_units, np.int32)
+    ur = np.zeros(n_units, np.int32)
+    _check(lib().oracle_decode_schedule(_p(ctx), b, n_units, _p(cum), _p(ub), _p(us), _p(up), _p(ur)),
+           "decode_schedule")
+    return {"cum_pages": cum, "unit_begin": ub, "unit_seq": us, "unit_page": up, "unit_run": ur}
 
 
 def prefill_schedule(cu_rows, start_pos, n_rows_padded, tile_rows, n_units):

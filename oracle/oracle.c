@@ -329,7 +329,7 @@ static void even_split(int64_t n_items, int32_t n_units, int32_t *unit_begin) {
 }
 
 int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, int32_t *cum_pages,
-                           int32_t *unit_begin, int32_t *unit_seq) {
+                           int32_t *unit_begin, int32_t *unit_seq, int32_t *unit_page, int32_t *unit_run) {
   if (batch < 0 || n_units <= 0) return -1;
   cum_pages[0] = 0;
   for (int32_t b = 0; b < batch; b++) {
@@ -341,6 +341,8 @@ int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, i
     int32_t b = 0;
     while (b < batch && cum_pages[b + 1] <= unit_begin[u]) b++;
     unit_seq[u] = b;
+    unit_page[u] = (b < batch) ? unit_begin[u] - cum_pages[b] : 0;  /* page of the first item */
+    unit_run[u] = (b < batch) ? cum_pages[b + 1] - unit_begin[u] : 0; /* items left in sequence b */
   }
   return 0;
 }

@@ -89,9 +89,11 @@ int oracle_topk(const double *s, int64_t ld, int64_t n_rows, const int32_t *row_
 /* Decode work split: items are (sequence b, page p < ceil(ctx[b]/64)) in
  * b-major order, cum_pages[b] = first item of b (B+1 entries). Unit u covers
  * items [unit_begin[u], unit_begin[u+1]) with unit_begin[u] = floor(u*W/U);
- * unit_seq[u] = sequence that holds item unit_begin[u] (batch if none). */
+ * unit_seq[u] = sequence that holds item unit_begin[u] (batch if none), unit_page[u] = that
+ * item's page index in it, unit_run[u] = items from it to the end of that sequence (both 0
+ * if none). */
 int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, int32_t *cum_pages,
-                           int32_t *unit_begin, int32_t *unit_seq);
+                           int32_t *unit_begin, int32_t *unit_seq, int32_t *unit_page, int32_t *unit_run);
 
 /* Prefill work split: tiles of at most tile_rows rows that stay inside one
  * request's group and start at the group's first row (the last group runs to

@@ -220,8 +220,11 @@ def read_decode_schedule(sched, batch: int, n_units: int) -> dict:
     cum = 8
     ub = cum + batch + 1
     us = ub + n_units + 1
+    up = us + n_units
+    ur = up + n_units
     return {"header": w[:8].copy(), "cum_pages": w[cum:cum + batch + 1].copy(),
-            "unit_begin": w[ub:ub + n_units + 1].copy(), "unit_seq": w[us:us + n_units].copy()}
+            "unit_begin": w[ub:ub + n_units + 1].copy(), "unit_seq": w[us:us + n_units].copy(),
+            "unit_page": w[up:up + n_units].copy(), "unit_run": w[ur:ur + n_units].copy()}
 
 
 def read_prefill_schedule(sched, n_req: int, n_rows_padded: int, n_units: int) -> dict:

@@ -28,18 +28,23 @@ int launch_status(const char *what);  // INDEXER_FP4_EHIP if the last launch fai
 
 // ---- schedule buffers (int32 words) ------------------------------------------------------
 // Decode: [0] magic, [1] error word, [2] batch, [3] next_n, [4] n_units, [5] items,
-//         [6..7] 0, then cum_pages[batch+1], unit_begin[n_units+1], unit_seq[n_units].
+//         [6..7] 0, then cum_pages[batch+1], unit_begin[n_units+1], unit_seq[n_units],
+//         unit_page[n_units], unit_run[n_units]: the sequence holding the unit's first
+//         item, that item's page index in it, and how many items from it on stay in that
+//         sequence (so a unit finds its first pages without walking cum_pages).
 constexpr int32_t kDecodeMagic = 0x34504644;   // "DFP4"
 constexpr int32_t kPrefillMagic = 0x34504650;  // "PFP4"
 constexpr int kHdrWords = 8;
 
 struct DecodeSchedLayout {
-  int64_t cum, unit_begin, unit_seq, words;
+  int64_t cum, unit_begin, unit_seq, unit_page, unit_run, words;
   __host__ __device__ DecodeSchedLayout(int32_t batch, int32_t n_units) {
     cum = kHdrWords;
     unit_begin = cum + (int64_t)batch + 1;
     unit_seq = unit_begin + (int64_t)n_units + 1;
-    words = unit_seq + n_units;
+    unit_page = unit_seq + n_units;
+    unit_run = unit_page + n_units;
+    words = unit_run + n_units;
   }
 };
 
@@ -97,6 +102,21 @@ using const_ptr = const __attribute__((address_space(4))) T *;
 template <class T>
 __device__ __forceinline__ const_ptr<T> as_const(const T *p) {
   return (const_ptr<T>)p;
+}
+
+// Raw buffer view of [base, base + bytes) for range-checked stores: a store at a byte
+// offset past `bytes` is dropped by the hardware. Used to mask logits past a row's length
+// without a branch (branches around stores make the compiler's memory-wait analysis fall
+// back to waiting for every outstanding load). Descriptor word 3 is the gfx9-family raw
+// 32-bit buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+#ifndef IFP4_STORE_POLICY
+#define IFP4_STORE_POLICY 0
+#endif
+__device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)byte_offset, 0, IFP4_STORE_POLICY);
 }
 
 }  // namespace ifp4

@@ -99,7 +99,12 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(const in
   for (int u = threadIdx.x; u <= n_units; u += kSchedThreads) {
     const int64_t ib = (int64_t)u * items / n_units;
     sched[L.unit_begin + u] = (int32_t)ib;
-    if (u < n_units) sched[L.unit_seq + u] = count_le(cum + 1, batch, ib);
+    if (u < n_units) {
+      const int b = count_le(cum + 1, batch, ib);
+      sched[L.unit_seq + u] = b;
+      sched[L.unit_page + u] = b < batch ? (int32_t)ib - cum[b] : 0;
+      sched[L.unit_run + u] = b < batch ? cum[b + 1] - (int32_t)ib : 0;
+    }
   }
 }
 

@@ -7,7 +7,7 @@
 // per-head weights).
 //
 // Design for gfx950. The work items are (sequence, page) pairs; unit u of the grid owns a
-// contiguous range of them (see schedule.hip) and its waves take every NW-th item. A wave
+// contiguous range of them (see schedule.hip) and each of its waves a contiguous share. A wave
 // scores one whole 64-key page for all heads of all next_n rows of that sequence:
 //   - the page is read once, straight into MFMA operand registers: for the 16-key tile t
 //     lane l loads the 16 bytes of key 16t + l%16 that hold elements [32(l/16), +32), so
@@ -19,10 +19,18 @@
 //   - ReLU and the head weights are applied in registers, partial head sums are
 //     exchanged across the four 16-lane groups, and lane l ends with the logit of key l
 //     of the page: one 256-byte store per row.
-// A wave loads D pages at a time into registers, then scores them. A unit with no work exits before
+// Each wave keeps D pages in flight in a register ring. A unit with no work exits before
 // any other load (empty CTAs of a large grid must cost nothing: the pages measured 8.75
 // against 2.99 us per layer at 4096 against 512 units).
 #include "score_common.h"
+
+// waves per unit and pages in flight per wave (tuned on MI355X at 8 x 131072, 64 heads)
+#ifndef IFP4_DECODE_WAVES
+#define IFP4_DECODE_WAVES 4
+#endif
+#ifndef IFP4_DECODE_RING
+#define IFP4_DECODE_RING 2
+#endif
 
 namespace ifp4 {
 
@@ -33,7 +41,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     const int32_t *__restrict__ bt_g, int64_t bt_ld, int batch, int n_units, const int32_t *__restrict__ sched_g,
     int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g, float *__restrict__ logits, int64_t ld) {
   const DecodeSchedLayout L(batch, n_units);
-  const const_ptr<int32_t> sched = as_const(sched_g), bt = as_const(bt_g), row_len = as_const(row_len_g);
+  const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
   const int it0 = sched[L.unit_begin + u];
   const int it1 = sched[L.unit_begin + u + 1];
@@ -44,69 +52,100 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
     return;
   }
-  const int first = it0 + wv;
-  if (first >= it1) return;
-  const int n_my = (it1 - first + NW - 1) / NW;
-  const const_ptr<int32_t> cum = sched + L.cum;
+  if (n_pages <= 0) {
+    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
+    return;
+  }
+  // this wave's contiguous share of the unit's items
+  const int per = (it1 - it0 + NW - 1) / NW;
+  const int w0 = it0 + wv * per;
+  const int w1 = min(it1, w0 + per);
+  if (w0 >= w1) return;
+  const int n_my = w1 - w0;
+  const int32_t *cum = sched_g + L.cum;
 
-  // sequence of this wave's first item; its query rows are loaded before any page so
-  // that no wait for them ever drains the page prefetch queue
-  int ib = sched[L.unit_seq + u];  // issue-side sequence cursor
-  while (ib < batch - 1 && first >= cum[ib + 1]) ib++;
+  // Item table, one lane per item, for 64 items at a time: sequence, page index within
+  // it, and physical page (-1 if the page cannot be read). Built with one round of
+  // per-lane loads instead of a chain of dependent scalar loads per page.
+  int seq0 = sched[L.unit_seq + u];  // sequence of the unit's first item
+  const int page0 = sched[L.unit_page + u];
+  const int run0 = sched[L.unit_run + u];
+  int tab_base = -64;
+  int v_seq = 0, v_page = 0, v_phys = -1;
+  auto fill = [&](int base) {
+    tab_base = base;
+    const int it = w0 + base + lane;
+    int b = seq0, p = 0, phys = -1;
+    if (it < w1) {
+      const int k = it - it0;  // items past the unit's first one
+      if (k < run0) {          // still in the unit's first sequence: no lookup
+        b = sched[L.unit_seq + u];
+        p = page0 + k;
+      } else {
+        while (b < batch - 1 && it >= cum[b + 1]) b++;
+        p = it - cum[b];
+      }
+      if (p >= 0 && p < bt_ld) {
+        phys = bt_g[(int64_t)b * bt_ld + p];
+        if (phys < 0 || phys >= n_pages) {
+          atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
+          phys = -1;
+        }
+      } else {
+        atomicOr(err, p < 0 ? INDEXER_FP4_DEV_BAD_SCHEDULE : INDEXER_FP4_DEV_TABLE_SHORT);
+      }
+    }
+    v_seq = b;
+    v_page = p;
+    v_phys = phys;
+    seq0 = __builtin_amdgcn_readlane(b, 63);  // sequences only advance with the items
+  };
+
+  // Software pipeline over a ring of D pages: scoring slot K overlaps the loads of the
+  // other D-1 slots. Every slot refill is unconditional -- past the wave's last item it
+  // reloads that item (a cache hit) and its logits are dropped -- so the compiler waits
+  // only for the slot being scored.
+  PageRegs P[D];
+  int sb[D], sp[D];
+  bool sok[D];
+  auto issue = [&](auto kk, int i) {
+    constexpr int K = decltype(kk)::value;
+    const bool live = i < n_my;
+    const int ii = live ? i : n_my - 1;
+    if (ii - tab_base >= 64) fill(ii & ~63);
+    const int l = ii - tab_base;
+    const int phys = __builtin_amdgcn_readlane(v_phys, l);
+    sb[K] = __builtin_amdgcn_readlane(v_seq, l);
+    sp[K] = __builtin_amdgcn_readlane(v_page, l);
+    sok[K] = live && phys >= 0;
+    load_page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);
+  };
   RowRegs<NH16, NN> R;
-  int qb = ib;
-  load_rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
-
-  // Batches of D pages: issue all D loads, then score the D pages. Several waves per
-  // SIMD overlap one wave's scoring with the others' loads.
-  for (int i0 = 0; i0 < n_my; i0 += D) {
-    PageRegs P[D];
-    int sb[D], sp[D];
-    bool sok[D];
-    static_for<D>([&](auto kk) {
-      constexpr int K = decltype(kk)::value;
-      sok[K] = false;
-      sb[K] = ib;
-      sp[K] = 0;
-      if (i0 + K < n_my) {
-        const int it = first + NW * (i0 + K);
-        while (ib < batch - 1 && it >= cum[ib + 1]) ib++;
-        const int p = it - cum[ib];
-        sb[K] = ib;
-        sp[K] = p;
-        if (p < 0) {
-          if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
-        } else if (p >= bt_ld) {
-          if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_TABLE_SHORT);
-        } else {
-          const int64_t phys = bt[(int64_t)ib * bt_ld + p];
-          if (phys < 0 || phys >= n_pages) {
-            if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
-          } else {
-            sok[K] = true;
-            load_page(P[K], kvp, kvs, phys, lane);
-          }
-        }
-      }
+  int qb = -1;
+  auto score = [&](auto kk) {
+    constexpr int K = decltype(kk)::value;
+    if (sb[K] != qb) {  // a new sequence: its query rows (waits for everything in flight)
+      qb = sb[K];
+      load_rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
+    }
+    const uint32_t col = (uint32_t)(sp[K] * kPage + lane);
+    static_for<NN>([&](auto nn) {
+      constexpr int N = decltype(nn)::value;
+      const int64_t r = (int64_t)qb * NN + N;
+      const int len = row_len[r];
+      // logits past the row's length (or of a dropped slot) fall outside the view
+      const uint32_t bytes = sok[K] ? 4u * (uint32_t)max(len, 0) : 0u;
+      const float v = page_logit<NH16, NN, N>(P[K], R, lane);
+      buffer_store_f32(v, buffer_view(logits + r * ld, bytes), 4u * col);
     });
+  };
+
+  // the first pages are in flight before the query rows are fetched
+  static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
+  for (int i0 = 0; i0 < n_my; i0 += D) {
     static_for<D>([&](auto kk) {
-      constexpr int K = decltype(kk)::value;
-      if (sok[K]) {
-        if (sb[K] != qb) {
-          qb = sb[K];
-          load_rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
-        }
-        const int col = sp[K] * kPage + lane;
-        static_for<NN>([&](auto nn) {
-          constexpr int N = decltype(nn)::value;
-          const int64_t r = (int64_t)qb * NN + N;
-          const int len = row_len[r];
-          if (sp[K] * kPage < len) {
-            const float v = page_logit<NH16, NN, N>(P[K], R, lane);
-            if (col < len) logits[r * ld + col] = v;
-          }
-        });
-      }
+      score(kk);
+      issue(kk, i0 + decltype(kk)::value + D);
     });
   }
 }
@@ -116,7 +155,7 @@ static void launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const 
                           int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                           int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len, float *logits,
                           int64_t ld) {
-  constexpr int NW = 4, D = 4;
+  constexpr int NW = IFP4_DECODE_WAVES, D = IFP4_DECODE_RING;
   hipLaunchKernelGGL((score_decode_kernel<NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
                      n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len, logits, ld);
 }

@@ -45,8 +45,8 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_size_queries(L):
-    # decode: 8-word header + cum[B+1] + unit_begin[U+1] + unit_seq[U]
-    assert L.indexer_fp4_decode_sched_bytes(8, 1, 512) == 4 * (8 + 9 + 513 + 512)
+    # decode: 8-word header + cum[B+1] + unit_begin[U+1] + unit_seq/unit_page/unit_run[U]
+    assert L.indexer_fp4_decode_sched_bytes(8, 1, 512) == 4 * (8 + 9 + 513 + 3 * 512)
     assert L.indexer_fp4_decode_sched_bytes(-1, 1, 512) < 0
     assert L.indexer_fp4_decode_sched_bytes(8, 1, 0) < 0
     # prefill: header + tiles[max] x4 + cum[max+1] + unit_begin[U+1] + unit_tile[U] + req_tile[R+1]

@@ -99,7 +99,7 @@ def test_decode_schedule_exact(ifp4, ctx, units, next_n):
     ifp4.indexer_fp4_decode_schedule(to_dev(ctx), next_n, units, sched, row_len)
     got = ifp4.read_decode_schedule(sched, len(ctx), units)
     want = oracle.decode_schedule(ctx, units)
-    for key in ("cum_pages", "unit_begin", "unit_seq"):
+    for key in ("cum_pages", "unit_begin", "unit_seq", "unit_page", "unit_run"):
         assert np.array_equal(got[key], want[key]), key
     assert got["header"][1] == 0
     _, rl = oracle.decode_geometry(ctx, next_n)
@@ -247,3 +247,43 @@ def test_full_size_decode(ifp4, name):
     assert np.array_equal(g["ks"].cpu().numpy(), o["ks"])
     check_logits(g["logits"].cpu().numpy(), o["s"], o["row_len"])
     check_topk(g["top"].cpu().numpy(), o["top"], o["s"], o["row_len"], case.topk)
+
+
+# ---------------------------------------------------------------------------- long-row top-k
+
+def _topk_exact(ifp4, lg, rl, k, max_len):
+    rows, n = lg.shape
+    t = to_dev(lg)
+    top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
+    ws = torch.empty(max(ifp4.indexer_topk_workspace_bytes(rows, max_len, k), 16), dtype=torch.uint8, device=dev())
+    ifp4.indexer_topk(t, to_dev(rl), max_len, k, top, ws)
+    got = top.cpu().numpy()
+    want = oracle.topk(lg.astype(np.float64), np.minimum(rl, max_len).astype(np.int32), k)
+    for r in range(rows):
+        m = min(k, int(min(rl[r], max_len)))
+        assert list(got[r][:m]) == sorted(want[r][:m].tolist()), f"row {r} len {rl[r]}"
+        assert (got[r][m:] == -1).all(), f"row {r}: tail"
+
+
+@pytest.mark.parametrize("n,k", [(131072, 2048), (262144, 2048), (20000, 64), (50000, 10000)])
+def test_topk_long_rows_exact(ifp4, n, k):
+    rng = np.random.default_rng(n + k)
+    rows = 8
+    _say(f"long top-k n={n} k={k}")
+    lg = rng.standard_normal((rows, n)).astype(np.float32)
+    lg[1] = 3.0                                              # all ties
+    lg[2] = rng.integers(-2, 3, n).astype(np.float32)        # heavy ties
+    lg[3, ::3] = -0.0
+    lg[3, 1::3] = 0.0                                        # signed zeros rank equal
+    lg[4] = -np.abs(lg[4])                                   # all negative
+    lg[5] = np.abs(lg[5]) * 1e-30                            # tiny magnitudes
+    rl = np.array([n, n, n - 5, n - 4096 - 1, k, k + 1, 17, n + 100], np.int32)  # last row clamps to max_len
+    _topk_exact(ifp4, lg, rl, k, n)
+
+
+def test_topk_long_row_at_the_bitmap_limit(ifp4):
+    n, k = 1 << 20, 2048
+    rng = np.random.default_rng(1)
+    lg = rng.standard_normal((2, n)).astype(np.float32)
+    lg[1] = np.repeat(rng.standard_normal(n // 1024).astype(np.float32), 1024)  # blocks of ties
+    _topk_exact(ifp4, lg, np.array([n, n - 1], np.int32), k, n)

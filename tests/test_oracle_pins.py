@@ -472,8 +472,10 @@ def test_decode_schedule_covers_every_page_once(ctx, units):
         seq = sch["unit_seq"][u]
         if a < n_items:
             assert sch["cum_pages"][seq] <= a < sch["cum_pages"][seq + 1]
+            assert sch["unit_page"][u] == a - sch["cum_pages"][seq] < pages[seq]
+            assert sch["unit_run"][u] == pages[seq] - sch["unit_page"][u]
         else:
-            assert seq == len(ctx)
+            assert seq == len(ctx) and sch["unit_page"][u] == 0 and sch["unit_run"][u] == 0
     assert (covered == 1).all()
 
 
