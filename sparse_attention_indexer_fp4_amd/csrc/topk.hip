@@ -6,20 +6,18 @@
 // index_topk short-circuit).
 //
 // Exact selection by radix select on order-preserving 32-bit keys (flip the sign bit of
-// non-negative floats, invert negative ones; -0.0 is folded onto +0.0): three histogram
-// passes (11, 11 and 10 bits) narrow the key of the k-th largest value to one value T,
-// then a gather keeps every key above T plus the lowest-column keys equal to T, writing
-// columns in ascending order. Rows up to 16384 keys take one 1024-thread workgroup per
-// row, with the histograms in LDS (several copies spread the atomic traffic of lanes that
-// hit the same bin); longer rows take the chunked path further below.
+// non-negative floats, invert negative ones; -0.0 is folded onto +0.0): histogram passes
+// over 8-bit digits narrow the key of the k-th largest value to one value T (bits that
+// all keys of the row share are skipped), then every key above T is kept together with
+// the lowest-column keys equal to T, and the columns are written in ascending order.
+//
+// Rows up to 16384 keys: one 1024-thread workgroup per row with the row's keys held in
+// LDS. Longer rows: the chunked path further below. Every loop that reads global memory
+// issues all of a thread's loads before it uses them, so a pass costs one memory latency
+// rather than one per element.
 #include "common.h"
 
 namespace ifp4 {
-
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kBins = 2048;
-constexpr int kCopies = 4;
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -31,104 +29,185 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float *__restrict__ logits, int64_t ld,
-                                                               const int32_t *__restrict__ row_len, int64_t max_len,
-                                                               int k, int32_t *__restrict__ out, int64_t out_ld) {
-  __shared__ uint32_t hist[kCopies][kBins];
-  __shared__ int s_scan[kTopkWaves];
-  __shared__ int s_digit, s_above;
-  __shared__ int s_gt[kTopkWaves], s_eq[kTopkWaves];
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
+// Inclusive suffix sum of v over the workgroup's threads (threads >= tid).
+template <int NT>
+__device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_down(v, off, 64);
+    if (lane + off < 64) v += y;
+  }
+  if (lane == 0) s_scan[wv] = v;
+  __syncthreads();
+  for (int w2 = wv + 1; w2 < NT / 64; w2++) v += s_scan[w2];
+  __syncthreads();
+  return v;
+}
+
+// Histogram increment of digit d (for lanes with `active`). Keys of one row cluster in a
+// few digits, so plain LDS atomics from a wave would mostly hit one address and serialize;
+// the two most common digits of the wave are added once each by a leader lane.
+__device__ __forceinline__ void hist_add(uint32_t *h, uint32_t d, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t act = __ballot(active);
+#pragma unroll
+  for (int round = 0; round < 2; round++) {
+    if (!act) break;
+    const int leader = __ffsll((unsigned long long)act) - 1;
+    const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+    const uint64_t m = __ballot(active && d == dl);
+    if (lane == leader) atomicAdd(&h[dl], (uint32_t)__popcll(m));
+    if ((m >> lane) & 1ull) active = false;
+    act &= ~m;
+  }
+  if (active) atomicAdd(&h[d], 1u);
+}
+
+// Radix select over items i < n whose key bits under `pmask` equal `prefix`: resolves the
+// bits below bit `top` of the rem-th largest such key, 8 bits a pass. Returns that key T;
+// *rem becomes how many keys equal to T still have to be taken, *n_eq how many equal T.
+// Callers pass a prefix that every item matches or top > 0 (with top == 0 every item then
+// equals T). hist has 4 x 256 words.
+template <int NT, class KeyOf>
+__device__ uint32_t block_select(int n, KeyOf key_of, uint32_t prefix, uint32_t pmask, int top, int *rem, int *n_eq,
+                                 uint32_t *hist, int *s_scan, int *s_misc) {
+  const int tid = threadIdx.x;
+  *n_eq = n;
+  while (top > 0) {
+    const int nbits = top >= 8 ? 8 : top;
+    const int shift = top - nbits;
+    const uint32_t nb = 1u << nbits;
+    for (int i = tid; i < 4 * 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    uint32_t *h = hist + 256 * ((tid >> 6) & 3);
+    for (int i0 = 0; i0 < n; i0 += NT) {
+      const int i = i0 + tid;
+      const uint32_t key = i < n ? key_of(i) : 0u;
+      hist_add(h, (key >> shift) & (nb - 1), i < n && (key & pmask) == prefix);
+    }
+    __syncthreads();
+    const int c = (uint32_t)tid < nb ? (int)(hist[tid] + hist[256 + tid] + hist[512 + tid] + hist[768 + tid]) : 0;
+    const int s = block_suffix_sum<NT>(c, s_scan);  // count(digit >= tid)
+    if ((uint32_t)tid < nb && s >= *rem && s - c < *rem) {
+      s_misc[0] = tid;
+      s_misc[1] = s - c;
+      s_misc[2] = c;
+    }
+    __syncthreads();
+    *rem -= s_misc[1];
+    *n_eq = s_misc[2];
+    prefix |= (uint32_t)s_misc[0] << shift;
+    pmask |= (nb - 1) << shift;
+    top = shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+// Number of leading bits shared by every key of a set (from its smallest and largest key):
+// the search can start below them. __clz(0) is 32.
+__device__ __forceinline__ int shared_bits(uint32_t kmin, uint32_t kmax) { return __clz((int)(kmin ^ kmax)); }
+
+// Mask of the top sb bits, sb in [0, 32]. Written with a 64-bit shift instead of a select:
+// this compiler turned the select form `sb >= 32 ? ~0u : ~(~0u >> sb)` into a scalar
+// conditional move that read a stale condition code and returned ~0u for sb = 6.
+__device__ __forceinline__ uint32_t top_bits_mask(int sb) { return (uint32_t)~(0xFFFFFFFFull >> sb); }
+
+// Block-wide min and max, returned to every thread.
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uint32_t *s_mm) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
+  }
+  if (lane == 0) {
+    s_mm[2 * wv] = kmin;
+    s_mm[2 * wv + 1] = kmax;
+  }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu;
+  kmax = 0u;
+  for (int w2 = 0; w2 < NT / 64; w2++) {
+    kmin = min(kmin, s_mm[2 * w2]);
+    kmax = max(kmax, s_mm[2 * w2 + 1]);
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------
+// Rows up to kShortMax keys: one workgroup per row, keys staged in LDS (dynamic: max_len
+// words), then radix passes and an ordered gather from LDS.
+constexpr int kShortThreads = 1024;
+constexpr int kShortWaves = kShortThreads / 64;
+constexpr int64_t kShortMax = 16384;
+
+__global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__restrict__ logits, int64_t ld,
+                                                                const int32_t *__restrict__ row_len, int64_t max_len,
+                                                                int k, int32_t *__restrict__ out, int64_t out_ld) {
+  extern __shared__ uint32_t keys[];
+  __shared__ uint32_t hist[4 * 256];
+  __shared__ int s_scan[kShortWaves], s_misc[4];
+  __shared__ uint32_t s_mm[2 * kShortWaves];
+  __shared__ int s_gt[kShortWaves], s_eq[kShortWaves];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int64_t len = row_len[r];
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
-  const float *row = logits + r * ld;
+  int64_t len64 = row_len[r];
+  len64 = len64 < 0 ? 0 : (len64 > max_len ? max_len : len64);
+  const int n = (int)len64;
   int32_t *o = out + r * out_ld;
-
-  if (len <= k) {  // short row: every key is kept
-    for (int j = tid; j < k; j += kTopkThreads) o[j] = j < len ? j : -1;
+  if (n <= k) {  // short row: every key is kept
+    for (int j = tid; j < k; j += kShortThreads) o[j] = j < n ? j : -1;
     return;
   }
-  const int n = (int)len;
-
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; pass++) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);  // digits of 11, 11, 10 bits
-    const uint32_t nb = pass == 2 ? 1024u : 2048u;
-    for (int i = tid; i < kCopies * kBins; i += kTopkThreads) (&hist[0][0])[i] = 0;
-    __syncthreads();
-    uint32_t *h = hist[tid & (kCopies - 1)];
-    for (int j = tid; j < n; j += kTopkThreads) {
-      const uint32_t key = order_key(row[j]);
-      if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    // Digit d with count(digit >= d) >= remaining > count(digit > d). Thread t owns bins
-    // 2t, 2t+1; a suffix scan over threads (reversed thread order) gives counts from the top.
-    const int b0 = 2 * tid, b1 = 2 * tid + 1;
-    int c0 = 0, c1 = 0;
-    if ((uint32_t)b1 < nb) {
+  // stage the row: 16 loads in flight per thread and round
+  const float *row = logits + r * ld;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int base = 0; base < n; base += 16 * kShortThreads) {
+    float v[16];
 #pragma unroll
-      for (int c = 0; c < kCopies; c++) {
-        c0 += hist[c][b0];
-        c1 += hist[c][b1];
-      }
+    for (int u = 0; u < 16; u++) {
+      const int j = base + u * kShortThreads + tid;
+      v[u] = j < n ? row[j] : 0.f;
     }
-    int v = c0 + c1;
-    {
-      // suffix scan: x = sum of v over lanes >= this lane, then add the waves above
-      int x = v;
 #pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_down(x, off, 64);
-        if (lane + off < 64) x += y;
-      }
-      if (lane == 0) s_scan[wv] = x;  // sum of this wave
-      __syncthreads();
-      int above_waves = 0;
-      for (int w2 = wv + 1; w2 < kTopkWaves; w2++) above_waves += s_scan[w2];
-      v = x + above_waves;  // count of bins >= b0 (held by threads >= tid)
-    }
-    const int s_b0 = v;        // count(digit >= b0)
-    const int s_b1 = v - c0;   // count(digit >= b1)
-    const int s_b2 = s_b1 - c1;  // count(digit >= b1 + 1)
-    if ((uint32_t)b1 < nb) {
-      if (s_b1 >= remaining && s_b2 < remaining) {
-        s_digit = b1;
-        s_above = s_b2;
-      } else if (s_b0 >= remaining && s_b1 < remaining) {
-        s_digit = b0;
-        s_above = s_b1;
+    for (int u = 0; u < 16; u++) {
+      const int j = base + u * kShortThreads + tid;
+      if (j < n) {
+        const uint32_t key = order_key(v[u]);
+        keys[j] = key;
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
       }
     }
-    __syncthreads();
-    remaining -= s_above;
-    prefix |= (uint32_t)s_digit << shift;
-    pmask |= (nb - 1) << shift;
-    __syncthreads();
   }
-  const uint32_t T = prefix;
-  const int need_eq = remaining;  // keys equal to T still to take, lowest columns first
+  block_minmax<kShortThreads>(kmin, kmax, s_mm);  // its barrier also publishes the staged keys
+  const int sb = shared_bits(kmin, kmax);
+  const uint32_t pmask = top_bits_mask(sb);
+  int rem = k, n_eq = 0;
+  const uint32_t T = block_select<kShortThreads>(n, [&](int i) { return keys[i]; }, kmax & pmask, pmask, 32 - sb,
+                                                 &rem, &n_eq, hist, s_scan, s_misc);
+  const int need_eq = rem;  // keys equal to T still to take, lowest columns first
 
   // gather: wave wv owns the contiguous column range [c_lo, c_hi)
-  const int chunk = ((n + kTopkWaves - 1) / kTopkWaves + 63) & ~63;
+  const int chunk = ((n + kShortWaves - 1) / kShortWaves + 63) & ~63;
   const int c_lo = min(n, wv * chunk), c_hi = min(n, c_lo + chunk);
-  int n_gt = 0, n_eq = 0;
+  int n_gt = 0, n_eqw = 0;
   for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
     const int j = j0 + lane;
-    uint32_t key = 0;
-    if (j < c_hi) key = order_key(row[j]);
-    const uint64_t gt = __ballot(j < c_hi && key > T);
-    const uint64_t eq = __ballot(j < c_hi && key == T);
-    n_gt += __popcll(gt);
-    n_eq += __popcll(eq);
+    const uint32_t key = j < c_hi ? keys[j] : 0u;
+    n_gt += __popcll(__ballot(j < c_hi && key > T));
+    n_eqw += __popcll(__ballot(j < c_hi && key == T));
   }
   if (lane == 0) {
     s_gt[wv] = n_gt;
-    s_eq[wv] = n_eq;
+    s_eq[wv] = n_eqw;
   }
   __syncthreads();
   int eq_base = 0, out_base = 0;
@@ -139,8 +218,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float *__r
   }
   for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
     const int j = j0 + lane;
-    uint32_t key = 0;
-    if (j < c_hi) key = order_key(row[j]);
+    const uint32_t key = j < c_hi ? keys[j] : 0u;
     const bool is_gt = j < c_hi && key > T;
     const bool is_eq = j < c_hi && key == T;
     const uint64_t eq = __ballot(is_eq);
@@ -162,17 +240,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_row_kernel(const float *__r
 //            the last chunk to finish (atomic ticket) picks the bin b1 that holds the k-th
 //            largest key and the count of keys above it;
 //   collect  every chunk appends its keys above b1 ("sure") and its keys in b1
-//            ("candidates") to the workspace; the last chunk to finish selects the
-//            remaining keys exactly among the candidates (radix select on the low 20 bits,
-//            ties resolved to the lowest columns by a second radix select on the column),
-//            marks the chosen columns in an LDS bitmap and writes them out in ascending
-//            order.
+//            ("candidates") to the workspace; the last chunk to finish stages the
+//            candidates in LDS, selects the remaining keys exactly among them (radix select
+//            on the low 20 bits, ties resolved to the lowest columns by a radix select on
+//            the column), marks the chosen columns in an LDS bitmap and writes them out in
+//            ascending order.
 constexpr int kLongThreads = 256;
 constexpr int kLongWaves = kLongThreads / 64;
 constexpr int kChunk = 4096;
-constexpr int kBins1 = 4096;                  // first digit: key bits 31..20
-constexpr int64_t kShortMax = 16384;          // longer rows take the chunked path
-constexpr int64_t kLongMaxLen = 1 << 20;      // bitmap of the finishing workgroup fits LDS
+constexpr int kPerThread = kChunk / kLongThreads;  // 16
+constexpr int kBins1 = 4096;                        // first digit: key bits 31..20
+constexpr int kCopies1 = 4;
+constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
+constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the collect kernel
+constexpr int kMaxStaged = 16384;                   // candidates staged in LDS
 constexpr int kStateWords = 8;
 enum { kTicket1 = 0, kTicket2 = 1, kBin1 = 2, kAbove1 = 3, kNSure = 4, kNCand = 5 };
 
@@ -188,23 +269,10 @@ struct LongWs {  // word offsets of the per-row areas in the workspace
   }
 };
 
-__device__ __forceinline__ uint32_t coherent_load(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Inclusive suffix sum of v over the workgroup's threads (threads >= tid).
-__device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += y;
-  }
-  if (lane == 0) s_scan[wv] = v;
-  __syncthreads();
-  for (int w2 = wv + 1; w2 < kLongWaves; w2++) v += s_scan[w2];
-  __syncthreads();
-  return v;
+__host__ __device__ inline int long_bitmap_words(int64_t max_len) { return (int)((max_len + 31) / 32); }
+__host__ __device__ inline int long_staged_cap(int64_t max_len) {
+  const int64_t room = ((int64_t)kLdsBudget - 4 * (int64_t)long_bitmap_words(max_len)) / 8;
+  return (int)(room < 0 ? 0 : (room > kMaxStaged ? kMaxStaged : room));
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_clear_kernel(uint32_t *__restrict__ ws, int rows) {
@@ -219,7 +287,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
                                                                 const int32_t *__restrict__ row_len,
                                                                 int64_t max_len, int k, uint32_t *ws, int rows,
                                                                 int64_t cap) {
-  __shared__ uint32_t h[kCopies][kBins1];
+  __shared__ uint32_t h[kCopies1][kBins1];
   __shared__ int s_scan[kLongWaves];
   __shared__ int s_last, s_bin, s_above;
   const int r = blockIdx.y, tid = threadIdx.x;
@@ -230,12 +298,22 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
   len = len < 0 ? 0 : (len > max_len ? max_len : len);
   const int64_t start = (int64_t)blockIdx.x * kChunk;
   if (len > k && start < len) {
-    for (int i = tid; i < kCopies * kBins1; i += kLongThreads) (&h[0][0])[i] = 0;
-    __syncthreads();
     const float *row = logits + r * ld;
     const int64_t end = min(len, start + kChunk);
-    uint32_t *hc = h[tid & (kCopies - 1)];
-    for (int64_t j = start + tid; j < end; j += kLongThreads) atomicAdd(&hc[order_key(row[j]) >> 20], 1u);
+    float v[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t j = start + u * kLongThreads + tid;
+      v[u] = j < end ? row[j] : 0.f;
+    }
+    for (int i = tid; i < kCopies1 * kBins1; i += kLongThreads) (&h[0][0])[i] = 0;
+    __syncthreads();
+    uint32_t *hc = h[(tid >> 6) & (kCopies1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t j = start + u * kLongThreads + tid;
+      hist_add(hc, order_key(v[u]) >> 20, j < end);
+    }
     __syncthreads();
     for (int b = tid; b < kBins1; b += kLongThreads) {
       const uint32_t c = h[0][b] + h[1][b] + h[2][b] + h[3][b];
@@ -253,11 +331,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
   uint32_t cnt[kPer];
   int sum = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    cnt[i] = coherent_load(&gh[kPer * tid + i]);
-    sum += (int)cnt[i];
-  }
-  int acc = block_suffix_sum(sum, s_scan);  // keys in bins >= kPer*tid
+  for (int i = 0; i < kPer; i++) cnt[i] = coherent_load(&gh[kPer * tid + i]);
+#pragma unroll
+  for (int i = 0; i < kPer; i++) sum += (int)cnt[i];
+  int acc = block_suffix_sum<kLongThreads>(sum, s_scan);  // keys in bins >= kPer*tid
 #pragma unroll
   for (int i = 0; i < kPer; i++) {
     if (acc >= k && acc - (int)cnt[i] < k) {
@@ -273,52 +350,17 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
   }
 }
 
-// Radix select inside the finishing workgroup: among keys[i] (i < n) whose bits under
-// `pmask` equal `prefix`, find the value of the bits below bit `top` that makes the
-// `rem`-th largest key; returns the full key and leaves in *rem how many keys equal to it
-// are still to be taken, in *n_eq how many keys equal it.
-template <class KeyOf>
-__device__ uint32_t block_select(int n, KeyOf key_of, uint32_t prefix, uint32_t pmask, int top, int *rem, int *n_eq,
-                                 uint32_t *hist, int *s_scan, int *s_digit, int *s_above, int *s_cnt) {
-  const int tid = threadIdx.x;
-  while (top > 0) {
-    const int nbits = top >= 8 ? 8 : top;
-    const int shift = top - nbits;
-    const uint32_t nb = 1u << nbits;
-    for (uint32_t i = tid; i < 256; i += kLongThreads) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kLongThreads) {
-      const uint32_t key = key_of(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    const int c = (uint32_t)tid < nb ? (int)hist[tid] : 0;
-    const int s = block_suffix_sum(c, s_scan);  // count(digit >= tid)
-    if ((uint32_t)tid < nb && s >= *rem && s - c < *rem) {
-      *s_digit = tid;
-      *s_above = s - c;
-      *s_cnt = c;
-    }
-    __syncthreads();
-    *rem -= *s_above;
-    *n_eq = *s_cnt;
-    prefix |= (uint32_t)*s_digit << shift;
-    pmask |= (nb - 1) << shift;
-    top = shift;
-    __syncthreads();
-  }
-  return prefix;
-}
-
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float *__restrict__ logits, int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
                                                                    int64_t max_len, int k, uint32_t *ws, int rows,
                                                                    int64_t cap, int32_t *__restrict__ out,
                                                                    int64_t out_ld) {
-  extern __shared__ uint32_t bitmap[];  // ceil(max_len / 32) words, used by the finishing chunk
-  __shared__ uint32_t hist[256];
-  __shared__ int s_scan[kLongWaves];
-  __shared__ int s_last, s_digit, s_above, s_cnt;
+  // dynamic LDS of the finishing chunk: bitmap of the row's columns, staged candidates
+  extern __shared__ uint32_t lds[];
+  __shared__ uint32_t hist[4 * 256];
+  __shared__ int s_scan[kLongWaves], s_misc[4];
+  __shared__ uint32_t s_mm[2 * kLongWaves];
+  __shared__ int s_last;
   const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const LongWs L(rows, cap, k);
   uint32_t *st = ws + L.state + (int64_t)r * kStateWords;
@@ -332,9 +374,17 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     const uint32_t bin1 = st[kBin1];
     const float *row = logits + r * ld;
     const int64_t end = min(len, start + kChunk);
-    for (int64_t j0 = start + 64 * wv; j0 < end; j0 += kLongThreads) {
-      const int64_t j = j0 + lane;
-      const uint32_t key = j < end ? order_key(row[j]) : 0u;
+    // wave wv takes the 64-key steps wv, wv + 4, ...; all its loads first
+    float v[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+      v[u] = j < end ? row[j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) {
+      const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+      const uint32_t key = order_key(v[u]);
       const uint32_t d = key >> 20;
       const bool is_sure = j < end && d > bin1;
       const bool is_cand = j < end && d == bin1;
@@ -372,31 +422,68 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   const int n_cand = (int)coherent_load(&st[kNCand]);
   const uint32_t bin1 = coherent_load(&st[kBin1]);
   const int nwords = (int)((len + 31) / 32);
+  uint32_t *bitmap = lds;
+  const int cap_lds = long_staged_cap(max_len);
+  uint32_t *skey = lds + long_bitmap_words(max_len);
+  uint32_t *sidx = skey + cap_lds;
+  const bool staged = n_cand <= cap_lds;
   for (int i = tid; i < nwords; i += kLongThreads) bitmap[i] = 0;
-  __syncthreads();
-  for (int i = tid; i < n_sure; i += kLongThreads) {
-    const uint32_t j = coherent_load(&sure[i]);
-    atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+  // candidates into LDS (16 loads in flight per thread), with their smallest and largest key
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int base = 0; base < n_cand; base += 16 * kLongThreads) {
+    uint32_t kk[16], jj[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int i = base + u * kLongThreads + tid;
+      kk[u] = i < n_cand ? coherent_load(&ckey[i]) : 0u;
+      jj[u] = (staged && i < n_cand) ? coherent_load(&cidx[i]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int i = base + u * kLongThreads + tid;
+      if (i < n_cand) {
+        kmin = min(kmin, kk[u]);
+        kmax = max(kmax, kk[u]);
+        if (staged) {
+          skey[i] = kk[u];
+          sidx[i] = jj[u];
+        }
+      }
+    }
   }
+  block_minmax<kLongThreads>(kmin, kmax, s_mm);  // its barriers also publish the bitmap reset
+  for (int base = 0; base < n_sure; base += 16 * kLongThreads) {
+    uint32_t jj[16];
+#pragma unroll
+    for (int u = 0; u < 16; u++) {
+      const int i = base + u * kLongThreads + tid;
+      jj[u] = i < n_sure ? coherent_load(&sure[i]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; u++)
+      if (base + u * kLongThreads + tid < n_sure) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+  }
+  auto key_at = [&](int i) { return staged ? skey[i] : coherent_load(&ckey[i]); };
+  auto col_at = [&](int i) { return staged ? sidx[i] : coherent_load(&cidx[i]); };
   // the remaining k - n_sure keys come from the candidates (all in bin b1)
+  const int sb = max(shared_bits(kmin, kmax), 12);  // the top 12 bits are b1 for every candidate
+  const uint32_t pmask = top_bits_mask(sb);
   int rem = k - n_sure, n_eq = 0;
-  const uint32_t T = block_select(n_cand, [&](int i) { return coherent_load(&ckey[i]); }, bin1 << 20, 0xFFF00000u,
-                                  20, &rem, &n_eq, hist, s_scan, &s_digit, &s_above, &s_cnt);
-  // keys equal to T: keep the rem lowest columns (select the largest of 2^20-1-column)
-  uint32_t cut = 0;  // ties with column <= cut are kept
+  const uint32_t T = block_select<kLongThreads>(n_cand, key_at, kmax & pmask, pmask, 32 - sb, &rem, &n_eq, hist,
+                                                s_scan, s_misc);
+  (void)bin1;
+  // keys equal to T: keep the rem lowest columns (the largest of 2^20 - 1 - column)
+  uint32_t cut = 0xFFFFFFFFu;  // ties with column <= cut are kept
   if (rem < n_eq) {
     int rem2 = rem, n_eq2 = 0;
-    const uint32_t sel = block_select(
-        n_cand,
-        [&](int i) { return coherent_load(&ckey[i]) == T ? (0xFFFFFu - coherent_load(&cidx[i])) : 0xFFFFFFFFu; },
-        0u, 0xFFF00000u, 20, &rem2, &n_eq2, hist, s_scan, &s_digit, &s_above, &s_cnt);
+    const uint32_t sel = block_select<kLongThreads>(
+        n_cand, [&](int i) { return key_at(i) == T ? (0xFFFFFu - col_at(i)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
+        &rem2, &n_eq2, hist, s_scan, s_misc);
     cut = 0xFFFFFu - sel;
-  } else {
-    cut = 0xFFFFFFFFu;
   }
   for (int i = tid; i < n_cand; i += kLongThreads) {
-    const uint32_t key = coherent_load(&ckey[i]);
-    const uint32_t j = coherent_load(&cidx[i]);
+    const uint32_t key = key_at(i);
+    const uint32_t j = col_at(i);
     if (key > T || (key == T && j <= cut)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
   __syncthreads();
@@ -407,10 +494,10 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   for (int i = w0; i < w1; i++) mine += __popc(bitmap[i]);
   // exclusive prefix over threads = total - suffix(tid); the total is exactly k when the
   // selection is consistent, and the bounds below hold either way
-  const int suffix = block_suffix_sum(mine, s_scan);
-  if (tid == 0) s_cnt = suffix;
+  const int suffix = block_suffix_sum<kLongThreads>(mine, s_scan);
+  if (tid == 0) s_misc[3] = suffix;
   __syncthreads();
-  const int total = s_cnt;
+  const int total = s_misc[3];
   int pos = total - suffix;
   for (int i = w0; i < w1; i++) {
     uint32_t m = bitmap[i];
@@ -442,14 +529,15 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
                             int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, void *workspace,
                             int64_t ws_bytes, void *stream) {
   clear_error();
-  (void)workspace;
   if (k <= 0 || n_rows < 0 || max_len < 0)
     return fail(INDEXER_FP4_EINVAL, "topk: k=%d must be > 0, n_rows=%d >= 0, max_len=%lld >= 0", k, n_rows,
                 (long long)max_len);
   if (max_len > logits_ld)
     return fail(INDEXER_FP4_EINVAL, "topk: max_len=%lld exceeds logits_ld=%lld", (long long)max_len,
                 (long long)logits_ld);
-  if (max_len > INT32_MAX) return fail(INDEXER_FP4_EINVAL, "topk: max_len=%lld too large", (long long)max_len);
+  if (max_len > kLongMaxLen)
+    return fail(INDEXER_FP4_EINVAL, "topk: max_len=%lld above the supported %lld", (long long)max_len,
+                (long long)kLongMaxLen);
   if (topk_ld < k) return fail(INDEXER_FP4_ENOSPC, "topk: topk_ld=%lld < k=%d", (long long)topk_ld, k);
   const int64_t need = indexer_topk_workspace_bytes(n_rows, max_len, k);
   if (ws_bytes < need)
@@ -459,23 +547,30 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   if (rc) return rc;
   if (n_rows == 0) return INDEXER_FP4_OK;
   hipStream_t st = (hipStream_t)stream;
+  // both kernels size their dynamic LDS from max_len; raise the launch limit once
+  static bool lds_set = false;
+  if (!lds_set) {
+    hipError_t e = hipFuncSetAttribute((const void *)topk_collect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kLdsBudget);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)topk_row_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(4 * kShortMax));
+    if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
+    lds_set = true;
+  }
   if (!use_long_path(max_len, k)) {
-    hipLaunchKernelGGL(topk_row_kernel, dim3(n_rows), dim3(kTopkThreads), 0, st, logits, logits_ld, row_len, max_len,
-                       k, topk_idx, topk_ld);
+    // rows of at most kShortMax keys, or k >= max_len (every row keeps all its keys and
+    // the kernel returns before staging anything)
+    const size_t lds = max_len <= kShortMax ? (size_t)(4 * max_len) : 0;
+    hipLaunchKernelGGL(topk_row_kernel, dim3(n_rows), dim3(kShortThreads), lds, st, logits, logits_ld, row_len,
+                       max_len, k, topk_idx, topk_ld);
     return launch_status("topk");
   }
   if (!workspace || (uintptr_t)workspace % 16 != 0)
     return fail(INDEXER_FP4_EINVAL, "topk: rows up to %lld keys need a 16-byte aligned workspace", (long long)max_len);
   uint32_t *ws = (uint32_t *)workspace;
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
-  const size_t lds = 4 * (size_t)((max_len + 31) / 32);
-  static bool lds_set = false;  // the bitmap may exceed the default LDS limit of a launch
-  if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)topk_collect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)(4 * ((kLongMaxLen + 31) / 32)));
-    if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
-    lds_set = true;
-  }
+  const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_staged_cap(max_len));
   hipLaunchKernelGGL(topk_clear_kernel, dim3(n_rows), dim3(kLongThreads), 0, st, ws, n_rows);
   hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
                      max_len, k, ws, n_rows, max_len);

@@ -287,3 +287,15 @@ def test_topk_long_row_at_the_bitmap_limit(ifp4):
     lg = rng.standard_normal((2, n)).astype(np.float32)
     lg[1] = np.repeat(rng.standard_normal(n // 1024).astype(np.float32), 1024)  # blocks of ties
     _topk_exact(ifp4, lg, np.array([n, n - 1], np.int32), k, n)
+
+
+@pytest.mark.parametrize("n,k", [(3000, 64), (16000, 2048), (131072, 2048)])
+def test_topk_rows_sharing_leading_bits(ifp4, n, k):
+    """Regression: rows whose keys all share their top bits (positive logits in a narrow band,
+    as the scorer produces) once met a miscompiled select in the mask of the shared bits and
+    selected nothing."""
+    rng = np.random.default_rng(n)
+    lg = np.stack([5.0 + 45.0 * rng.random(n), 1000.0 + rng.random(n), np.full(n, 7.5) + 1e-3 * rng.random(n),
+                   -(5.0 + 45.0 * rng.random(n))]).astype(np.float32)
+    rl = np.array([n, n - 1, n // 2 + k, n], np.int32)
+    _topk_exact(ifp4, lg, rl, k, n)
