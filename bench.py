@@ -90,7 +90,7 @@ def build_decode(torch, ifp4, W, layers, units, seed):
         row_len=torch.empty(B, dtype=torch.int32, device=dev),
         logits=torch.empty((B, ld), dtype=torch.float32, device=dev),
         top=torch.empty((B, k), dtype=torch.int32, device=dev),
-        ws=torch.empty(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 1), dtype=torch.uint8, device=dev),
+        ws=torch.zeros(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 1), dtype=torch.uint8, device=dev),
     )
     torch.cuda.synchronize()
     meta = dict(B=B, H=H, k=k, ctx=int(ctx[0]), n_keys=int(ctx.astype(np.int64).sum()), n_pages_read=need,

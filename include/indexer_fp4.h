@@ -201,10 +201,15 @@ int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
  * among equal logits the lower column is kept (-0.0 counts as equal to +0.0). The
  * rest of the row, up to k, is -1. Logits must be finite.
  *   row_len    int32 [n_rows] (e.g. a schedule's row_len output)
- *   workspace  indexer_topk_workspace_bytes(n_rows, max_len, k) bytes, any content
- * Errors: EINVAL (k <= 0, n_rows < 0, max_len < 0), ENOSPC (topk_ld < k, workspace
- * too small), EARCH, EHIP. Rows longer than max_len are clamped to max_len
- * (device-side; max_len must not exceed logits_ld).
+ *   workspace  indexer_topk_workspace_bytes(n_rows, max_len, k) bytes (0 when every
+ *              row fits one workgroup: max_len <= 16384 or k >= max_len). It must be
+ *              zero-filled before its first use; every call that returns OK leaves it
+ *              zero-filled again, so one buffer serves any number of calls on one
+ *              stream. Calls that share it must not overlap; after an EHIP error zero
+ *              it again.
+ * Errors: EINVAL (k <= 0, n_rows < 0, max_len < 0, max_len > 2^20 with k < max_len),
+ * ENOSPC (topk_ld < k, workspace too small), EARCH, EHIP. Rows longer than max_len
+ * are clamped to max_len (device-side; max_len must not exceed logits_ld).
  * --------------------------------------------------------------------------------- */
 int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len, int32_t k);
 int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,

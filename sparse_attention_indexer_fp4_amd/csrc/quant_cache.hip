@@ -8,74 +8,76 @@
 // floor(log2 amax) - 2 clamped to [-127, 127]; elements rounded to the nearest E2M1
 // value, ties to the even code, saturating at 6.
 //
-// One thread encodes one 32-element block: 64 input bytes in, 16 packed bytes and one
-// scale byte out. All decisions are made on the bf16 bit patterns in integer
+// Four lanes encode one 32-element block (eight elements, one 16-byte load and one 4-byte
+// store each), sixteen lanes one 128-element vector: the block maximum is a two-step
+// cross-lane reduction. All decisions are made on the bf16 bit patterns in integer
 // arithmetic, so the result does not depend on the FP denormal mode.
 #include "common.h"
 
 namespace ifp4 {
 
-// E2M1 magnitude code of a bf16 magnitude `mag` (15 bits: exponent << 7 | mantissa) at
-// block scale 2^e. With sig the significand (implicit bit included) and ep the
-// effective exponent field, |v| = sig * 2^(ep-134) and 4|v|/2^e = sig * 2^sh. The code
-// counts the decision points {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} that the scaled
-// magnitude passes; at the points with an even code below (0.25, 1.25, 2.5, 5) the
-// tie stays below, at the others (0.75, 1.75, 3.5) it goes up.
-__device__ __forceinline__ uint32_t e2m1_magnitude_code(uint32_t mag, int e) {
-  const uint32_t ex = mag >> 7;
-  const uint32_t sig = ex ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
-  const int ep = ex ? (int)ex : 1;
-  const int sh = ep - 134 - e + 2;
-  uint32_t c;
-  if (sh >= 0) {
-    const uint32_t x = sig << (sh < 20 ? sh : 20);  // 4x, saturated well past 20
-    c = (x > 1u) + (x >= 3u) + (x > 5u) + (x >= 7u) + (x > 10u) + (x >= 14u) + (x > 20u);
-  } else {
-    const int n = -sh;  // compare sig against threshold * 2^n
-    if (n > 20) return 0u;
-    c = (sig > (1u << n)) + (sig >= (3u << n)) + (sig > (5u << n)) + (sig >= (7u << n)) +
-        (sig > (10u << n)) + (sig >= (14u << n)) + (sig > (20u << n));
-  }
-  return c;
+constexpr int kLanesPerVec = kHeadDim / 8;  // 16
+
+// bf16 bit pattern of the exact value m * 2^p (m in {1, 3, 5, 7}, m * 2^p >= 2^-133; the
+// callers keep it below the largest finite bf16).
+__device__ __forceinline__ uint32_t bf16_pattern(uint32_t m, int p) {
+  const int lm = m >= 4 ? 2 : (m >= 2 ? 1 : 0);  // floor(log2 m)
+  const int E = p + lm;
+  if (E >= -126) return ((uint32_t)(E + 127) << 7) | ((m << (7 - lm)) & 0x7Fu);
+  return m << (p + 133);  // subnormal: the last mantissa bit is 2^-133
 }
 
-// 32 bf16 (as 4 x uint4) -> 16 packed bytes (element 2i low nibble of byte i) + scale
-__device__ __forceinline__ void encode_block32(const uint4 in[4], uint4 &packed, uint32_t &scale) {
+// The decision points of rounding a magnitude to E2M1 at block scale 2^e, as bf16 bit
+// patterns: {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5} * 2^e. Bit patterns of non-negative
+// bf16 values order like the values, so a magnitude's code is the number of points it
+// passes: at the points with an even code below (0.25, 1.25, 2.5, 5) a tie stays below,
+// at the others (0.75, 1.75, 3.5) it goes up.
+struct E2M1Points {
+  uint32_t t[7];
+  __device__ __forceinline__ explicit E2M1Points(int e) {
+    t[0] = bf16_pattern(1, e - 2);
+    t[1] = bf16_pattern(3, e - 2);
+    t[2] = bf16_pattern(5, e - 2);
+    t[3] = bf16_pattern(7, e - 2);
+    t[4] = bf16_pattern(5, e - 1);
+    t[5] = bf16_pattern(7, e - 1);
+    t[6] = bf16_pattern(5, e);
+  }
+  __device__ __forceinline__ uint32_t code(uint32_t bits) const {  // bf16 bits -> 4-bit code
+    const uint32_t mag = bits & 0x7FFFu;
+    const uint32_t c = (mag > t[0]) + (mag >= t[1]) + (mag > t[2]) + (mag >= t[3]) + (mag > t[4]) + (mag >= t[5]) +
+                       (mag > t[6]);
+    return c | ((bits >> 12) & 8u);
+  }
+};
+
+// Scale exponent of a block from its largest magnitude (15-bit bf16 pattern):
+// floor(log2 amax) - 2, clamped to [-127, 127]; -127 for an all-zero block.
+__device__ __forceinline__ int block_exponent(uint32_t amag) {
+  if (amag == 0) return -127;
+  const uint32_t ex = amag >> 7;
+  const uint32_t sig = ex ? (0x80u | (amag & 0x7Fu)) : (amag & 0x7Fu);
+  const int ep = ex ? (int)ex : 1;
+  const int e = (31 - __builtin_clz(sig)) + ep - 134 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// This lane's eight bf16 (one uint4) -> four packed bytes (element 2i in the low nibble of
+// byte i) and the block's scale byte; the four lanes of a block must be active together.
+__device__ __forceinline__ uint32_t encode_lane8(uint4 in, uint32_t &scale) {
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
   uint32_t amag = 0;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const uint32_t w[4] = {in[j].x, in[j].y, in[j].z, in[j].w};
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      amag = max(amag, w[h] & 0x7FFFu);
-      amag = max(amag, (w[h] >> 16) & 0x7FFFu);
-    }
-  }
-  int e = -127;
-  if (amag != 0) {
-    const uint32_t ex = amag >> 7;
-    const uint32_t sig = ex ? (0x80u | (amag & 0x7Fu)) : (amag & 0x7Fu);
-    const int ep = ex ? (int)ex : 1;
-    const int fl = (31 - __builtin_clz(sig)) + ep - 134;  // floor(log2 amax)
-    e = fl - 2;
-    e = e < -127 ? -127 : (e > 127 ? 127 : e);
-  }
+  for (int h = 0; h < 4; h++) amag = max(amag, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
+  amag = max(amag, (uint32_t)__shfl_xor((int)amag, 1, 64));
+  amag = max(amag, (uint32_t)__shfl_xor((int)amag, 2, 64));
+  const int e = block_exponent(amag);
   scale = (uint32_t)(e + 127);
-  uint32_t out[4];
+  const E2M1Points pts(e);
+  uint32_t d = 0;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const uint32_t w[4] = {in[j].x, in[j].y, in[j].z, in[j].w};
-    uint32_t d = 0;
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      const uint32_t lo = w[h] & 0xFFFFu, hi = w[h] >> 16;
-      const uint32_t clo = e2m1_magnitude_code(lo & 0x7FFFu, e) | ((lo >> 12) & 8u);
-      const uint32_t chi = e2m1_magnitude_code(hi & 0x7FFFu, e) | ((hi >> 12) & 8u);
-      d |= (clo | (chi << 4)) << (8 * h);
-    }
-    out[j] = d;
-  }
-  packed = make_uint4(out[0], out[1], out[2], out[3]);
+  for (int h = 0; h < 4; h++) d |= (pts.code(w[h] & 0xFFFFu) | (pts.code(w[h] >> 16) << 4)) << (8 * h);
+  return d;
 }
 
 __global__ __launch_bounds__(256) void quant_cache_kernel(
@@ -83,34 +85,30 @@ __global__ __launch_bounds__(256) void quant_cache_kernel(
     uint8_t *__restrict__ kv_packed, uint8_t *__restrict__ kv_scale, int64_t n_pages,
     const uint16_t *__restrict__ q, int64_t n_q_vec, uint8_t *__restrict__ q_packed,
     uint8_t *__restrict__ q_scale) {
-  const int64_t total = (n_tok + n_q_vec) * kGroups;
+  // every 16-lane group walks whole vectors, so the four lanes of a block stay together
+  const int64_t total = (n_tok + n_q_vec) * kLanesPerVec;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
-    const int64_t v = i >> 2;
-    const int g = (int)(i & 3);
-    uint4 in[4];
-    uint4 packed;
+    const int64_t v = i / kLanesPerVec;
+    const int l = (int)(i % kLanesPerVec);  // elements 8l .. 8l+7 of the vector
+    const int g = l >> 2;                   // its 32-element block
     uint32_t sc;
     if (v < n_tok) {
       const int64_t slot = slots[v];
-      if (slot < 0 || slot >= n_pages * kPage) continue;
-      const uint4 *src = reinterpret_cast<const uint4 *>(k + v * k_ld + 32 * g);
-#pragma unroll
-      for (int j = 0; j < 4; j++) in[j] = src[j];
-      encode_block32(in, packed, sc);
+      if (slot < 0 || slot >= n_pages * kPage) continue;  // uniform over the vector's lanes
+      const uint4 in = *reinterpret_cast<const uint4 *>(k + v * k_ld + 8 * l);
+      const uint32_t d = encode_lane8(in, sc);
       const int64_t page = slot / kPage;
       const int pos = (int)(slot % kPage);
-      *reinterpret_cast<uint4 *>(kv_packed + (page * kPage + pos) * kKeyBytes + 16 * g) = packed;
+      *reinterpret_cast<uint32_t *>(kv_packed + (page * kPage + pos) * kKeyBytes + 4 * l) = d;
       // scale plane: the 64-row axis is stored as a 16x4 transpose
-      kv_scale[(page * kGroups + g) * kPage + (pos % 16) * 4 + pos / 16] = (uint8_t)sc;
+      if ((l & 3) == 0) kv_scale[(page * kGroups + g) * kPage + (pos % 16) * 4 + pos / 16] = (uint8_t)sc;
     } else {
       const int64_t vq = v - n_tok;
-      const uint4 *src = reinterpret_cast<const uint4 *>(q + vq * kHeadDim + 32 * g);
-#pragma unroll
-      for (int j = 0; j < 4; j++) in[j] = src[j];
-      encode_block32(in, packed, sc);
-      *reinterpret_cast<uint4 *>(q_packed + vq * kKeyBytes + 16 * g) = packed;
-      q_scale[vq * kGroups + g] = (uint8_t)sc;
+      const uint4 in = *reinterpret_cast<const uint4 *>(q + vq * kHeadDim + 8 * l);
+      const uint32_t d = encode_lane8(in, sc);
+      *reinterpret_cast<uint32_t *>(q_packed + vq * kKeyBytes + 4 * l) = d;
+      if ((l & 3) == 0) q_scale[vq * kGroups + g] = (uint8_t)sc;
     }
   }
 }
@@ -147,7 +145,7 @@ extern "C" int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, in
   int rc = check_device();
   if (rc) return rc;
   const int64_t n_q_vec = q_arm ? n_q_rows * (int64_t)n_heads : 0;
-  const int64_t total = (n_tok + n_q_vec) * kGroups;
+  const int64_t total = (n_tok + n_q_vec) * kLanesPerVec;
   if (total == 0) return INDEXER_FP4_OK;
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;

@@ -29,10 +29,6 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint32_t coherent_load(const uint32_t *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Inclusive suffix sum of v over the workgroup's threads (threads >= tid).
 template <int NT>
 __device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
@@ -234,36 +230,40 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 // ---------------------------------------------------------------------------------------
 // Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). One workgroup per row
 // would leave the GPU idle, so each row is cut into chunks of kChunk keys, one workgroup
-// each, in three launches and without any grid-wide barrier:
-//   clear    zero the row's histogram, counters and tickets in the workspace;
-//   hist     histogram the top 12 key bits per chunk and add them into the row's histogram;
-//            the last chunk to finish (atomic ticket) picks the bin b1 that holds the k-th
-//            largest key and the count of keys above it;
-//   collect  every chunk appends its keys above b1 ("sure") and its keys in b1
-//            ("candidates") to the workspace; the last chunk to finish stages the
-//            candidates in LDS, selects the remaining keys exactly among them (radix select
-//            on the low 20 bits, ties resolved to the lowest columns by a radix select on
-//            the column), marks the chosen columns in an LDS bitmap and writes them out in
-//            ascending order.
+// each. Three launches, ordered by the stream (no fences, tickets or contended atomics):
+//   hist     histogram the top 12 key bits of each chunk into the row's histogram;
+//   collect  every chunk finds the bin b1 that holds the row's k-th largest key (from the
+//            full histogram) and writes its keys above b1 ("sure") and in b1
+//            ("candidates") into its own region of the workspace, with their counts;
+//   finish   (one workgroup per row) gathers the chunks' results, stages the candidates
+//            in LDS, selects the remaining keys exactly among them (radix select on the low
+//            20 bits, ties resolved to the lowest columns by a radix select on the column),
+//            marks the chosen columns in an LDS bitmap, writes them out in ascending order
+//            and zeroes the row's histogram for the next call.
 constexpr int kLongThreads = 256;
 constexpr int kLongWaves = kLongThreads / 64;
+constexpr int kFinishThreads = 1024;
 constexpr int kChunk = 4096;
 constexpr int kPerThread = kChunk / kLongThreads;  // 16
 constexpr int kBins1 = 4096;                        // first digit: key bits 31..20
 constexpr int kCopies1 = 4;
 constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
-constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the collect kernel
+constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
+constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the finish kernel
 constexpr int kMaxStaged = 16384;                   // candidates staged in LDS
-constexpr int kStateWords = 8;
-enum { kTicket1 = 0, kTicket2 = 1, kBin1 = 2, kAbove1 = 3, kNSure = 4, kNCand = 5 };
 
-struct LongWs {  // word offsets of the per-row areas in the workspace
-  int64_t state, hist, sure, ckey, cidx, words;
-  __host__ __device__ LongWs(int rows, int64_t cap, int k) {
-    state = 0;
-    hist = state + (int64_t)rows * kStateWords;
-    sure = hist + (int64_t)rows * kBins1;
-    ckey = sure + (int64_t)rows * k;
+// Workspace: the row histograms come first at a fixed stride (they must be zero when a call
+// starts and every call leaves them zero), then per row the chunk counts and the chunks'
+// regions for sure columns and candidate keys / columns.
+struct LongWs {
+  int64_t hist, counts, sure, ckey, cidx, words;
+  __host__ __device__ LongWs(int rows, int64_t max_len) {
+    const int64_t chunks = (max_len + kChunk - 1) / kChunk;
+    const int64_t cap = chunks * kChunk;
+    hist = 0;
+    counts = hist + (int64_t)rows * kBins1;
+    sure = counts + (int64_t)rows * 2 * chunks;
+    ckey = sure + (int64_t)rows * cap;
     cidx = ckey + (int64_t)rows * cap;
     words = cidx + (int64_t)rows * cap;
   }
@@ -275,226 +275,275 @@ __host__ __device__ inline int long_staged_cap(int64_t max_len) {
   return (int)(room < 0 ? 0 : (room > kMaxStaged ? kMaxStaged : room));
 }
 
-__global__ __launch_bounds__(kLongThreads) void topk_clear_kernel(uint32_t *__restrict__ ws, int rows) {
-  const int r = blockIdx.x;
-  uint32_t *st = ws + (int64_t)r * kStateWords;
-  uint32_t *h = ws + (int64_t)rows * kStateWords + (int64_t)r * kBins1;
-  if (threadIdx.x < kStateWords) st[threadIdx.x] = 0;
-  for (int i = threadIdx.x; i < kBins1; i += kLongThreads) h[i] = 0;
+__device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
+  const int64_t len = row_len[r];
+  return len < 0 ? 0 : (len > max_len ? max_len : len);
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len,
-                                                                int64_t max_len, int k, uint32_t *ws, int rows,
-                                                                int64_t cap) {
+                                                                int64_t max_len, int k, uint32_t *__restrict__ ws) {
   __shared__ uint32_t h[kCopies1][kBins1];
-  __shared__ int s_scan[kLongWaves];
-  __shared__ int s_last, s_bin, s_above;
   const int r = blockIdx.y, tid = threadIdx.x;
-  const LongWs L(rows, cap, k);
-  uint32_t *st = ws + L.state + (int64_t)r * kStateWords;
-  uint32_t *gh = ws + L.hist + (int64_t)r * kBins1;
-  int64_t len = row_len[r];
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
+  const int64_t len = clamped_len(row_len, r, max_len);
   const int64_t start = (int64_t)blockIdx.x * kChunk;
-  if (len > k && start < len) {
-    const float *row = logits + r * ld;
-    const int64_t end = min(len, start + kChunk);
-    float v[kPerThread];
+  if (len <= k || start >= len) return;
+  uint32_t *gh = ws + (int64_t)r * kBins1;
+  const float *row = logits + r * ld;
+  const int64_t end = min(len, start + kChunk);
+  float v[kPerThread];
 #pragma unroll
-    for (int u = 0; u < kPerThread; u++) {
-      const int64_t j = start + u * kLongThreads + tid;
-      v[u] = j < end ? row[j] : 0.f;
-    }
-    for (int i = tid; i < kCopies1 * kBins1; i += kLongThreads) (&h[0][0])[i] = 0;
-    __syncthreads();
-    uint32_t *hc = h[(tid >> 6) & (kCopies1 - 1)];
-#pragma unroll
-    for (int u = 0; u < kPerThread; u++) {
-      const int64_t j = start + u * kLongThreads + tid;
-      hist_add(hc, order_key(v[u]) >> 20, j < end);
-    }
-    __syncthreads();
-    for (int b = tid; b < kBins1; b += kLongThreads) {
-      const uint32_t c = h[0][b] + h[1][b] + h[2][b] + h[3][b];
-      if (c) atomicAdd(&gh[b], c);
-    }
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t j = start + u * kLongThreads + tid;
+    v[u] = j < end ? row[j] : 0.f;
   }
-  __threadfence();
+  for (int i = tid; i < kCopies1 * kBins1; i += kLongThreads) (&h[0][0])[i] = 0;
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&st[kTicket1], 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last || len <= k) return;
-  __threadfence();
-  // the last chunk: bin holding the k-th largest key, from the row's full histogram
-  constexpr int kPer = kBins1 / kLongThreads;  // bins per thread, consecutive
-  uint32_t cnt[kPer];
-  int sum = 0;
+  uint32_t *hc = h[(tid >> 6) & (kCopies1 - 1)];
 #pragma unroll
-  for (int i = 0; i < kPer; i++) cnt[i] = coherent_load(&gh[kPer * tid + i]);
-#pragma unroll
-  for (int i = 0; i < kPer; i++) sum += (int)cnt[i];
-  int acc = block_suffix_sum<kLongThreads>(sum, s_scan);  // keys in bins >= kPer*tid
-#pragma unroll
-  for (int i = 0; i < kPer; i++) {
-    if (acc >= k && acc - (int)cnt[i] < k) {
-      s_bin = kPer * tid + i;
-      s_above = acc - (int)cnt[i];
-    }
-    acc -= (int)cnt[i];
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t j = start + u * kLongThreads + tid;
+    hist_add(hc, order_key(v[u]) >> 20, j < end);
   }
   __syncthreads();
-  if (tid == 0) {
-    st[kBin1] = (uint32_t)s_bin;
-    st[kAbove1] = (uint32_t)s_above;
+  for (int b = tid; b < kBins1; b += kLongThreads) {
+    const uint32_t c = h[0][b] + h[1][b] + h[2][b] + h[3][b];
+    if (c) atomicAdd(&gh[b], c);
   }
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float *__restrict__ logits, int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
-                                                                   int64_t max_len, int k, uint32_t *ws, int rows,
-                                                                   int64_t cap, int32_t *__restrict__ out,
-                                                                   int64_t out_ld) {
-  // dynamic LDS of the finishing chunk: bitmap of the row's columns, staged candidates
+                                                                   int64_t max_len, int k, uint32_t *__restrict__ ws,
+                                                                   int rows) {
+  __shared__ int s_scan[kLongWaves];
+  __shared__ int s_bin;
+  __shared__ uint32_t s_ws[kLongWaves], s_wc[kLongWaves];
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t len = clamped_len(row_len, r, max_len);
+  const int64_t start = (int64_t)c * kChunk;
+  if (len <= k || start >= len) return;
+  const LongWs L(rows, max_len);
+  const int64_t chunks = (max_len + kChunk - 1) / kChunk;
+  const int64_t cap = chunks * kChunk;
+  const float *row = logits + r * ld;
+  const int64_t end = min(len, start + kChunk);
+  // this chunk's keys, wave wv taking the 64-key steps wv, wv + 4, ...
+  uint32_t key[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+    key[u] = order_key(j < end ? row[j] : 0.f);
+  }
+  // the bin of the row's k-th largest key, from the row's full histogram
+  {
+    const uint32_t *gh = ws + L.hist + (int64_t)r * kBins1;
+    constexpr int kPer = kBins1 / kLongThreads;
+    uint32_t cnt[kPer];
+    int sum = 0;
+    if (tid == 0) s_bin = 0;  // published by the scan's barriers
+#pragma unroll
+    for (int i = 0; i < kPer; i++) cnt[i] = gh[kPer * tid + i];
+#pragma unroll
+    for (int i = 0; i < kPer; i++) sum += (int)cnt[i];
+    int acc = block_suffix_sum<kLongThreads>(sum, s_scan);  // keys in bins >= kPer*tid
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      if (acc >= k && acc - (int)cnt[i] < k) s_bin = kPer * tid + i;
+      acc -= (int)cnt[i];
+    }
+    __syncthreads();
+  }
+  const uint32_t bin1 = (uint32_t)s_bin;
+  uint64_t ms[kPerThread], mc[kPerThread];
+  uint32_t n_s = 0, n_c = 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+    const uint32_t d = key[u] >> 20;
+    ms[u] = __ballot(j < end && d > bin1);
+    mc[u] = __ballot(j < end && d == bin1);
+    n_s += (uint32_t)__popcll(ms[u]);
+    n_c += (uint32_t)__popcll(mc[u]);
+  }
+  if (lane == 0) {
+    s_ws[wv] = n_s;
+    s_wc[wv] = n_c;
+  }
+  __syncthreads();
+  uint32_t bs = 0, bc = 0, ts = 0, tc = 0;
+  for (int w2 = 0; w2 < kLongWaves; w2++) {
+    if (w2 < wv) {
+      bs += s_ws[w2];
+      bc += s_wc[w2];
+    }
+    ts += s_ws[w2];
+    tc += s_wc[w2];
+  }
+  uint32_t *sure = ws + L.sure + (int64_t)r * cap + start;
+  uint32_t *ckey = ws + L.ckey + (int64_t)r * cap + start;
+  uint32_t *cidx = ws + L.cidx + (int64_t)r * cap + start;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const uint32_t j = (uint32_t)(start + 64 * (wv + kLongWaves * u) + lane);
+    if ((ms[u] >> lane) & 1ull) sure[bs + lanes_below(ms[u])] = j;
+    if ((mc[u] >> lane) & 1ull) {
+      ckey[bc + lanes_below(mc[u])] = key[u];
+      cidx[bc + lanes_below(mc[u])] = j;
+    }
+    bs += (uint32_t)__popcll(ms[u]);
+    bc += (uint32_t)__popcll(mc[u]);
+  }
+  if (tid == 0) {
+    uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
+    cnt[2 * c] = ts;
+    cnt[2 * c + 1] = tc;
+  }
+}
+
+__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32_t *__restrict__ row_len,
+                                                                    int64_t max_len, int k, uint32_t *__restrict__ ws,
+                                                                    int rows, int32_t *__restrict__ out,
+                                                                    int64_t out_ld) {
+  // dynamic LDS: bitmap of the row's columns, then the staged candidates (keys, columns)
   extern __shared__ uint32_t lds[];
   __shared__ uint32_t hist[4 * 256];
-  __shared__ int s_scan[kLongWaves], s_misc[4];
-  __shared__ uint32_t s_mm[2 * kLongWaves];
-  __shared__ int s_last;
-  const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const LongWs L(rows, cap, k);
-  uint32_t *st = ws + L.state + (int64_t)r * kStateWords;
-  uint32_t *sure = ws + L.sure + (int64_t)r * k;
-  uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
-  uint32_t *cidx = ws + L.cidx + (int64_t)r * cap;
-  int64_t len = row_len[r];
-  len = len < 0 ? 0 : (len > max_len ? max_len : len);
-  const int64_t start = (int64_t)blockIdx.x * kChunk;
-  if (len > k && start < len) {
-    const uint32_t bin1 = st[kBin1];
-    const float *row = logits + r * ld;
-    const int64_t end = min(len, start + kChunk);
-    // wave wv takes the 64-key steps wv, wv + 4, ...; all its loads first
-    float v[kPerThread];
-#pragma unroll
-    for (int u = 0; u < kPerThread; u++) {
-      const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
-      v[u] = j < end ? row[j] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kPerThread; u++) {
-      const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
-      const uint32_t key = order_key(v[u]);
-      const uint32_t d = key >> 20;
-      const bool is_sure = j < end && d > bin1;
-      const bool is_cand = j < end && d == bin1;
-      const uint64_t ms = __ballot(is_sure);
-      const uint64_t mc = __ballot(is_cand);
-      if (ms) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&st[kNSure], (uint32_t)__popcll(ms));
-        base = __shfl(base, 0, 64);
-        if (is_sure) sure[base + lanes_below(ms)] = (uint32_t)j;
-      }
-      if (mc) {
-        uint32_t base = 0;
-        if (lane == 0) base = atomicAdd(&st[kNCand], (uint32_t)__popcll(mc));
-        base = __shfl(base, 0, 64);
-        if (is_cand) {
-          ckey[base + lanes_below(mc)] = key;
-          cidx[base + lanes_below(mc)] = (uint32_t)j;
-        }
-      }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&st[kTicket2], 1u) == gridDim.x - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  __shared__ int s_scan[kFinishThreads / 64], s_misc[4];
+  __shared__ uint32_t s_mm[2 * (kFinishThreads / 64)];
+  __shared__ int s_sure_off[kMaxChunks + 1], s_cand_off[kMaxChunks + 1];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t len = clamped_len(row_len, r, max_len);
   int32_t *o = out + r * out_ld;
   if (len <= k) {  // short row: every key is kept
-    for (int j = tid; j < k; j += kLongThreads) o[j] = j < len ? j : -1;
+    for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
     return;
   }
-  const int n_sure = (int)coherent_load(&st[kNSure]);
-  const int n_cand = (int)coherent_load(&st[kNCand]);
-  const uint32_t bin1 = coherent_load(&st[kBin1]);
+  const LongWs L(rows, max_len);
+  const int chunks = (int)((max_len + kChunk - 1) / kChunk);
+  const int64_t cap = (int64_t)chunks * kChunk;
+  const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
+  // exclusive offsets of each chunk's sure columns and candidates (one thread per chunk)
+  {
+    const uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
+    int a = 0, b = 0;
+    if (tid < used) {
+      a = (int)cnt[2 * tid];
+      b = (int)cnt[2 * tid + 1];
+    }
+    const int sa = block_suffix_sum<kFinishThreads>(a, s_scan);
+    const int sb2 = block_suffix_sum<kFinishThreads>(b, s_scan);
+    if (tid == 0) {
+      s_sure_off[used] = sa;
+      s_cand_off[used] = sb2;
+    }
+    __syncthreads();
+    if (tid < used) {
+      s_sure_off[tid] = s_sure_off[used] - sa;
+      s_cand_off[tid] = s_cand_off[used] - sb2;
+    }
+    __syncthreads();
+  }
+  const int n_sure = s_sure_off[used];
+  const int n_cand = s_cand_off[used];
+  // g-th candidate / sure column of the row: find its chunk in the offsets
+  auto chunk_of = [&](const int *off, int g) {
+    int lo = 0, hi = used;  // largest c with off[c] <= g
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= g) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
+  const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
+  const uint32_t *cidx = ws + L.cidx + (int64_t)r * cap;
   const int nwords = (int)((len + 31) / 32);
   uint32_t *bitmap = lds;
   const int cap_lds = long_staged_cap(max_len);
   uint32_t *skey = lds + long_bitmap_words(max_len);
   uint32_t *sidx = skey + cap_lds;
   const bool staged = n_cand <= cap_lds;
-  for (int i = tid; i < nwords; i += kLongThreads) bitmap[i] = 0;
-  // candidates into LDS (16 loads in flight per thread), with their smallest and largest key
+  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0;
+  auto cand_pos = [&](int g) {
+    const int c = chunk_of(s_cand_off, g);
+    return (int64_t)c * kChunk + (g - s_cand_off[c]);
+  };
+  // candidates into LDS (8 loads in flight per thread), with their smallest and largest key
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int base = 0; base < n_cand; base += 16 * kLongThreads) {
-    uint32_t kk[16], jj[16];
+  for (int base = 0; base < n_cand; base += 8 * kFinishThreads) {
+    uint32_t kk[8], jj[8];
 #pragma unroll
-    for (int u = 0; u < 16; u++) {
-      const int i = base + u * kLongThreads + tid;
-      kk[u] = i < n_cand ? coherent_load(&ckey[i]) : 0u;
-      jj[u] = (staged && i < n_cand) ? coherent_load(&cidx[i]) : 0u;
+    for (int u = 0; u < 8; u++) {
+      const int g = base + u * kFinishThreads + tid;
+      const int64_t p = g < n_cand ? cand_pos(g) : 0;
+      kk[u] = g < n_cand ? ckey[p] : 0u;
+      jj[u] = (staged && g < n_cand) ? cidx[p] : 0u;
     }
 #pragma unroll
-    for (int u = 0; u < 16; u++) {
-      const int i = base + u * kLongThreads + tid;
-      if (i < n_cand) {
+    for (int u = 0; u < 8; u++) {
+      const int g = base + u * kFinishThreads + tid;
+      if (g < n_cand) {
         kmin = min(kmin, kk[u]);
         kmax = max(kmax, kk[u]);
         if (staged) {
-          skey[i] = kk[u];
-          sidx[i] = jj[u];
+          skey[g] = kk[u];
+          sidx[g] = jj[u];
         }
       }
     }
   }
-  block_minmax<kLongThreads>(kmin, kmax, s_mm);  // its barriers also publish the bitmap reset
-  for (int base = 0; base < n_sure; base += 16 * kLongThreads) {
-    uint32_t jj[16];
+  block_minmax<kFinishThreads>(kmin, kmax, s_mm);  // its barriers also publish the bitmap reset
+  for (int base = 0; base < n_sure; base += 8 * kFinishThreads) {
+    uint32_t jj[8];
 #pragma unroll
-    for (int u = 0; u < 16; u++) {
-      const int i = base + u * kLongThreads + tid;
-      jj[u] = i < n_sure ? coherent_load(&sure[i]) : 0u;
+    for (int u = 0; u < 8; u++) {
+      const int g = base + u * kFinishThreads + tid;
+      if (g < n_sure) {
+        const int c = chunk_of(s_sure_off, g);
+        jj[u] = sure[(int64_t)c * kChunk + (g - s_sure_off[c])];
+      } else {
+        jj[u] = 0u;
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 16; u++)
-      if (base + u * kLongThreads + tid < n_sure) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+    for (int u = 0; u < 8; u++)
+      if (base + u * kFinishThreads + tid < n_sure) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
   }
-  auto key_at = [&](int i) { return staged ? skey[i] : coherent_load(&ckey[i]); };
-  auto col_at = [&](int i) { return staged ? sidx[i] : coherent_load(&cidx[i]); };
+  auto key_at = [&](int g) { return staged ? skey[g] : ckey[cand_pos(g)]; };
+  auto col_at = [&](int g) { return staged ? sidx[g] : cidx[cand_pos(g)]; };
   // the remaining k - n_sure keys come from the candidates (all in bin b1)
   const int sb = max(shared_bits(kmin, kmax), 12);  // the top 12 bits are b1 for every candidate
   const uint32_t pmask = top_bits_mask(sb);
   int rem = k - n_sure, n_eq = 0;
-  const uint32_t T = block_select<kLongThreads>(n_cand, key_at, kmax & pmask, pmask, 32 - sb, &rem, &n_eq, hist,
-                                                s_scan, s_misc);
-  (void)bin1;
+  const uint32_t T = block_select<kFinishThreads>(n_cand, key_at, kmax & pmask, pmask, 32 - sb, &rem, &n_eq, hist,
+                                                  s_scan, s_misc);
   // keys equal to T: keep the rem lowest columns (the largest of 2^20 - 1 - column)
   uint32_t cut = 0xFFFFFFFFu;  // ties with column <= cut are kept
   if (rem < n_eq) {
     int rem2 = rem, n_eq2 = 0;
-    const uint32_t sel = block_select<kLongThreads>(
-        n_cand, [&](int i) { return key_at(i) == T ? (0xFFFFFu - col_at(i)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
+    const uint32_t sel = block_select<kFinishThreads>(
+        n_cand, [&](int g) { return key_at(g) == T ? (0xFFFFFu - col_at(g)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
         &rem2, &n_eq2, hist, s_scan, s_misc);
     cut = 0xFFFFFu - sel;
   }
-  for (int i = tid; i < n_cand; i += kLongThreads) {
-    const uint32_t key = key_at(i);
-    const uint32_t j = col_at(i);
+  for (int g = tid; g < n_cand; g += kFinishThreads) {
+    const uint32_t key = key_at(g);
+    const uint32_t j = col_at(g);
     if (key > T || (key == T && j <= cut)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
   }
+  // the row's histogram is left zero for the next call
+  uint32_t *gh = ws + L.hist + (int64_t)r * kBins1;
+  for (int i = tid; i < kBins1; i += kFinishThreads) gh[i] = 0;
   __syncthreads();
   // columns out in ascending order: each thread owns a contiguous run of bitmap words
-  const int per = (nwords + kLongThreads - 1) / kLongThreads;
+  const int per = (nwords + kFinishThreads - 1) / kFinishThreads;
   const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
   int mine = 0;
   for (int i = w0; i < w1; i++) mine += __popc(bitmap[i]);
   // exclusive prefix over threads = total - suffix(tid); the total is exactly k when the
   // selection is consistent, and the bounds below hold either way
-  const int suffix = block_suffix_sum<kLongThreads>(mine, s_scan);
+  const int suffix = block_suffix_sum<kFinishThreads>(mine, s_scan);
   if (tid == 0) s_misc[3] = suffix;
   __syncthreads();
   const int total = s_misc[3];
@@ -508,7 +557,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
       pos++;
     }
   }
-  for (int j = max(total, 0) + tid; j < k; j += kLongThreads) o[j] = -1;
+  for (int j = max(total, 0) + tid; j < k; j += kFinishThreads) o[j] = -1;
 }
 
 }  // namespace ifp4
@@ -522,7 +571,7 @@ static bool use_long_path(int64_t max_len, int32_t k) {
 extern "C" int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len, int32_t k) {
   if (n_rows < 0 || max_len < 0 || k <= 0) return -1;
   if (!use_long_path(max_len, k)) return 0;
-  return 4 * LongWs(n_rows, max_len, k).words;
+  return 4 * LongWs(n_rows, max_len).words;
 }
 
 extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
@@ -550,7 +599,7 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   // both kernels size their dynamic LDS from max_len; raise the launch limit once
   static bool lds_set = false;
   if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)topk_collect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+    hipError_t e = hipFuncSetAttribute((const void *)topk_finish_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kLdsBudget);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void *)topk_row_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -571,10 +620,11 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   uint32_t *ws = (uint32_t *)workspace;
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
   const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_staged_cap(max_len));
-  hipLaunchKernelGGL(topk_clear_kernel, dim3(n_rows), dim3(kLongThreads), 0, st, ws, n_rows);
   hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
-                     max_len, k, ws, n_rows, max_len);
-  hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), lds, st, logits, logits_ld,
-                     row_len, max_len, k, ws, n_rows, max_len, topk_idx, topk_ld);
+                     max_len, k, ws);
+  hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld,
+                     row_len, max_len, k, ws, n_rows);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3(n_rows), dim3(kFinishThreads), lds, st, row_len, max_len, k, ws,
+                     n_rows, topk_idx, topk_ld);
   return launch_status("topk");
 }

@@ -55,7 +55,7 @@ def gpu_decode(case: W.DecodeCase, units=None, ld=None, fill=float("nan"), cache
     if run_topk:
         top = torch.full((rows, case.topk), -7, dtype=torch.int32, device=dev())
         ws_bytes = ifp4.indexer_topk_workspace_bytes(rows, ld, case.topk)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev())
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev())
         ifp4.indexer_topk(logits, row_len, ld, case.topk, top, ws)
         out["top"] = top
     torch.cuda.synchronize()
@@ -100,7 +100,7 @@ def gpu_prefill_step(case: W.PrefillCase, step: W.PrefillStep, kp, ks, units=Non
     out = dict(qp=qp, qs=qs, sched=sched, row_len=row_len, logits=logits, units=units, ld=ld)
     if run_topk:
         top = torch.full((NP, case.topk), -7, dtype=torch.int32, device=dev())
-        ws = torch.empty(max(ifp4.indexer_topk_workspace_bytes(NP, ld, case.topk), 1), dtype=torch.uint8,
+        ws = torch.zeros(max(ifp4.indexer_topk_workspace_bytes(NP, ld, case.topk), 1), dtype=torch.uint8,
                          device=dev())
         ifp4.indexer_topk(logits, row_len, ld, case.topk, top, ws)
         out["top"] = top

@@ -251,11 +251,13 @@ def test_full_size_decode(ifp4, name):
 
 # ---------------------------------------------------------------------------- long-row top-k
 
-def _topk_exact(ifp4, lg, rl, k, max_len):
+def _topk_exact(ifp4, lg, rl, k, max_len, ws=None):
     rows, n = lg.shape
     t = to_dev(lg)
     top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
-    ws = torch.empty(max(ifp4.indexer_topk_workspace_bytes(rows, max_len, k), 16), dtype=torch.uint8, device=dev())
+    if ws is None:
+        ws = torch.zeros(max(ifp4.indexer_topk_workspace_bytes(rows, max_len, k), 16), dtype=torch.uint8,
+                         device=dev())
     ifp4.indexer_topk(t, to_dev(rl), max_len, k, top, ws)
     got = top.cpu().numpy()
     want = oracle.topk(lg.astype(np.float64), np.minimum(rl, max_len).astype(np.int32), k)
@@ -263,6 +265,7 @@ def _topk_exact(ifp4, lg, rl, k, max_len):
         m = min(k, int(min(rl[r], max_len)))
         assert list(got[r][:m]) == sorted(want[r][:m].tolist()), f"row {r} len {rl[r]}"
         assert (got[r][m:] == -1).all(), f"row {r}: tail"
+    return ws
 
 
 @pytest.mark.parametrize("n,k", [(131072, 2048), (262144, 2048), (20000, 64), (50000, 10000)])
@@ -278,7 +281,9 @@ def test_topk_long_rows_exact(ifp4, n, k):
     lg[4] = -np.abs(lg[4])                                   # all negative
     lg[5] = np.abs(lg[5]) * 1e-30                            # tiny magnitudes
     rl = np.array([n, n, n - 5, n - 4096 - 1, k, k + 1, 17, n + 100], np.int32)  # last row clamps to max_len
-    _topk_exact(ifp4, lg, rl, k, n)
+    ws = _topk_exact(ifp4, lg, rl, k, n)
+    # the workspace is left ready for the next call: reuse it on different rows
+    _topk_exact(ifp4, -lg[::-1].copy(), rl[::-1].copy(), k, n, ws)
 
 
 def test_topk_long_row_at_the_bitmap_limit(ifp4):
