@@ -228,51 +228,57 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 }
 
 // ---------------------------------------------------------------------------------------
-// Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). One workgroup per row
-// would leave the GPU idle, so each row is cut into chunks of kChunk keys, one workgroup
-// each. Three launches, ordered by the stream (no fences, tickets or contended atomics):
-//   hist     histogram the top 12 key bits of each chunk into the row's histogram;
-//   collect  every chunk finds the bin b1 that holds the row's k-th largest key (from the
-//            full histogram) and writes its keys above b1 ("sure") and in b1
-//            ("candidates") into its own region of the workspace, with their counts;
-//   finish   (one workgroup per row) gathers the chunks' results, stages the candidates
-//            in LDS, selects the remaining keys exactly among them (radix select on the low
-//            20 bits, ties resolved to the lowest columns by a radix select on the column),
-//            marks the chosen columns in an LDS bitmap, writes them out in ascending order
-//            and zeroes the row's histogram for the next call.
+// Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). A workgroup retires
+// only 64 lanes of arithmetic a cycle, so one workgroup per row would be bound by its own
+// ALUs; each row is cut into chunks of kChunk keys, one workgroup each, and the selection
+// is a two-level radix select over the key bits, in three launches ordered by the stream:
+//   hist     histogram of digit 1 (key bits 31..20) of every chunk, merged into the row's
+//            histogram with one atomic per occupied bin;
+//   collect  every chunk finds the bin b1 that holds the row's k-th largest key and writes,
+//            in column order, its keys above b1 ("sure") and in b1 ("candidates") into its
+//            own region of the workspace with their counts; the candidates are also
+//            histogrammed on digit 2 (key bits 19..8) into the row's second histogram;
+//   finish   (one workgroup per row) finds the digit-2 bin b2 that holds the remaining
+//            k - sure keys, marks sure keys and candidates above b2 in an LDS bitmap of
+//            the row's columns, selects among the few candidates in b2 exactly (by counting
+//            ranks, ties to the lowest columns; radix select when there are many), writes
+//            the columns in ascending order and zeroes both histograms for the next call.
+// Device-wide atomics on one cache line serialize, so the merges are kept to one atomic
+// instruction per workgroup and 64-bin block.
 constexpr int kLongThreads = 256;
 constexpr int kLongWaves = kLongThreads / 64;
 constexpr int kFinishThreads = 1024;
 constexpr int kChunk = 4096;
 constexpr int kPerThread = kChunk / kLongThreads;  // 16
-constexpr int kBins1 = 4096;                        // first digit: key bits 31..20
-constexpr int kCopies1 = 4;
+constexpr int kBins = 4096;                         // 12-bit digits
 constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
 constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
 constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the finish kernel
-constexpr int kMaxStaged = 16384;                   // candidates staged in LDS
+constexpr int kSubMax = 8192;                       // candidates of bin b2 staged in LDS
+constexpr int kRankMax = 256;                       // ... ranked by counting
 
-// Workspace: the row histograms come first at a fixed stride (they must be zero when a call
-// starts and every call leaves them zero), then per row the chunk counts and the chunks'
-// regions for sure columns and candidate keys / columns.
+// Workspace words: both row histograms first (zero when a call starts, zeroed again by the
+// finish), then per row the chunk counts and the chunks' regions for sure columns and
+// candidate keys / columns.
 struct LongWs {
-  int64_t hist, counts, sure, ckey, cidx, words;
+  int64_t hist1, hist2, counts, sure, ckey, ccol, words;
   __host__ __device__ LongWs(int rows, int64_t max_len) {
     const int64_t chunks = (max_len + kChunk - 1) / kChunk;
     const int64_t cap = chunks * kChunk;
-    hist = 0;
-    counts = hist + (int64_t)rows * kBins1;
+    hist1 = 0;
+    hist2 = hist1 + (int64_t)rows * kBins;
+    counts = hist2 + (int64_t)rows * kBins;
     sure = counts + (int64_t)rows * 2 * chunks;
     ckey = sure + (int64_t)rows * cap;
-    cidx = ckey + (int64_t)rows * cap;
-    words = cidx + (int64_t)rows * cap;
+    ccol = ckey + (int64_t)rows * cap;
+    words = ccol + (int64_t)rows * cap;
   }
 };
 
 __host__ __device__ inline int long_bitmap_words(int64_t max_len) { return (int)((max_len + 31) / 32); }
-__host__ __device__ inline int long_staged_cap(int64_t max_len) {
+__host__ __device__ inline int long_sub_cap(int64_t max_len) {
   const int64_t room = ((int64_t)kLdsBudget - 4 * (int64_t)long_bitmap_words(max_len)) / 8;
-  return (int)(room < 0 ? 0 : (room > kMaxStaged ? kMaxStaged : room));
+  return (int)(room < 0 ? 0 : (room > kSubMax ? kSubMax : room));
 }
 
 __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
@@ -280,15 +286,65 @@ __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, in
   return len < 0 ? 0 : (len > max_len ? max_len : len);
 }
 
+// LDS histogram increment of digit d for lanes with `ok`. A wave whose counted keys all share
+// one digit (ties, constant rows) adds them with one atomic instead of 64 conflicting ones.
+__device__ __forceinline__ void hist_put(uint32_t *h, uint32_t d, bool ok) {
+  const uint64_t act = __ballot(ok);
+  if (act == 0) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+  if (__ballot(ok && d != d0) == 0) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
+  } else if (ok) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
+// Adds an LDS histogram's occupied bins into a global one: each wave instruction covers 64
+// consecutive bins, so a workgroup sends at most one atomic instruction per 256-byte block.
+template <int NT>
+__device__ __forceinline__ void hist_flush(const uint32_t *h, uint32_t *g) {
+  for (int b = threadIdx.x; b < kBins; b += NT) {
+    const uint32_t c = h[b];
+    if (c) atomicAdd(&g[b], c);
+  }
+}
+
+// Suffix sums of three values over the workgroup's threads (threads >= tid), one barrier pair.
+template <int NT>
+__device__ __forceinline__ void block_suffix_sum3(int &a, int &b, int &c, int *s_scan) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int ya = __shfl_down(a, off, 64), yb = __shfl_down(b, off, 64), yc = __shfl_down(c, off, 64);
+    if (lane + off < 64) {
+      a += ya;
+      b += yb;
+      c += yc;
+    }
+  }
+  if (lane == 0) {
+    s_scan[3 * wv] = a;
+    s_scan[3 * wv + 1] = b;
+    s_scan[3 * wv + 2] = c;
+  }
+  __syncthreads();
+  for (int w2 = wv + 1; w2 < NT / 64; w2++) {
+    a += s_scan[3 * w2];
+    b += s_scan[3 * w2 + 1];
+    c += s_scan[3 * w2 + 2];
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len,
                                                                 int64_t max_len, int k, uint32_t *__restrict__ ws) {
-  __shared__ uint32_t h[kCopies1][kBins1];
+  __shared__ uint32_t h[kBins];
   const int r = blockIdx.y, tid = threadIdx.x;
   const int64_t len = clamped_len(row_len, r, max_len);
   const int64_t start = (int64_t)blockIdx.x * kChunk;
   if (len <= k || start >= len) return;
-  uint32_t *gh = ws + (int64_t)r * kBins1;
   const float *row = logits + r * ld;
   const int64_t end = min(len, start + kChunk);
   float v[kPerThread];
@@ -297,25 +353,19 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
     const int64_t j = start + u * kLongThreads + tid;
     v[u] = j < end ? row[j] : 0.f;
   }
-  for (int i = tid; i < kCopies1 * kBins1; i += kLongThreads) (&h[0][0])[i] = 0;
+  for (int i = tid; i < kBins; i += kLongThreads) h[i] = 0u;
   __syncthreads();
-  uint32_t *hc = h[(tid >> 6) & (kCopies1 - 1)];
 #pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + u * kLongThreads + tid;
-    hist_add(hc, order_key(v[u]) >> 20, j < end);
-  }
+  for (int u = 0; u < kPerThread; u++) hist_put(h, order_key(v[u]) >> 20, start + u * kLongThreads + tid < end);
   __syncthreads();
-  for (int b = tid; b < kBins1; b += kLongThreads) {
-    const uint32_t c = h[0][b] + h[1][b] + h[2][b] + h[3][b];
-    if (c) atomicAdd(&gh[b], c);
-  }
+  hist_flush<kLongThreads>(h, ws + (int64_t)r * kBins);  // hist1 leads the workspace
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float *__restrict__ logits, int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
                                                                    int64_t max_len, int k, uint32_t *__restrict__ ws,
                                                                    int rows) {
+  __shared__ uint32_t h2[kBins];
   __shared__ int s_scan[kLongWaves];
   __shared__ int s_bin;
   __shared__ uint32_t s_ws[kLongWaves], s_wc[kLongWaves];
@@ -328,17 +378,19 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   const int64_t cap = chunks * kChunk;
   const float *row = logits + r * ld;
   const int64_t end = min(len, start + kChunk);
-  // this chunk's keys, wave wv taking the 64-key steps wv, wv + 4, ...
+  // wave wv holds the chunk's columns [1024 wv, 1024 wv + 1024) in 64-column steps, so
+  // wave-major order is column order
   uint32_t key[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+    const int64_t j = start + 1024 * wv + 64 * u + lane;
     key[u] = order_key(j < end ? row[j] : 0.f);
   }
-  // the bin of the row's k-th largest key, from the row's full histogram
+  for (int i = tid; i < kBins; i += kLongThreads) h2[i] = 0u;
+  // the bin of the row's k-th largest key, from the row's digit-1 histogram
   {
-    const uint32_t *gh = ws + L.hist + (int64_t)r * kBins1;
-    constexpr int kPer = kBins1 / kLongThreads;
+    const uint32_t *gh = ws + L.hist1 + (int64_t)r * kBins;
+    constexpr int kPer = kBins / kLongThreads;
     uint32_t cnt[kPer];
     int sum = 0;
     if (tid == 0) s_bin = 0;  // published by the scan's barriers
@@ -359,18 +411,19 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   uint32_t n_s = 0, n_c = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + 64 * (wv + kLongWaves * u) + lane;
+    const bool ok = start + 1024 * wv + 64 * u + lane < end;
     const uint32_t d = key[u] >> 20;
-    ms[u] = __ballot(j < end && d > bin1);
-    mc[u] = __ballot(j < end && d == bin1);
+    ms[u] = __ballot(ok && d > bin1);
+    mc[u] = __ballot(ok && d == bin1);
     n_s += (uint32_t)__popcll(ms[u]);
     n_c += (uint32_t)__popcll(mc[u]);
+    if (mc[u]) hist_put(h2, (key[u] >> 8) & (kBins - 1), ok && d == bin1);
   }
   if (lane == 0) {
     s_ws[wv] = n_s;
     s_wc[wv] = n_c;
   }
-  __syncthreads();
+  __syncthreads();  // also completes h2
   uint32_t bs = 0, bc = 0, ts = 0, tc = 0;
   for (int w2 = 0; w2 < kLongWaves; w2++) {
     if (w2 < wv) {
@@ -382,14 +435,14 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   }
   uint32_t *sure = ws + L.sure + (int64_t)r * cap + start;
   uint32_t *ckey = ws + L.ckey + (int64_t)r * cap + start;
-  uint32_t *cidx = ws + L.cidx + (int64_t)r * cap + start;
+  uint32_t *ccol = ws + L.ccol + (int64_t)r * cap + start;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const uint32_t j = (uint32_t)(start + 64 * (wv + kLongWaves * u) + lane);
+    const uint32_t j = (uint32_t)(start + 1024 * wv + 64 * u + lane);
     if ((ms[u] >> lane) & 1ull) sure[bs + lanes_below(ms[u])] = j;
     if ((mc[u] >> lane) & 1ull) {
       ckey[bc + lanes_below(mc[u])] = key[u];
-      cidx[bc + lanes_below(mc[u])] = j;
+      ccol[bc + lanes_below(mc[u])] = j;
     }
     bs += (uint32_t)__popcll(ms[u]);
     bc += (uint32_t)__popcll(mc[u]);
@@ -399,22 +452,22 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     cnt[2 * c] = ts;
     cnt[2 * c + 1] = tc;
   }
+  if (tc) hist_flush<kLongThreads>(h2, ws + L.hist2 + (int64_t)r * kBins);
 }
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32_t *__restrict__ row_len,
                                                                     int64_t max_len, int k, uint32_t *__restrict__ ws,
                                                                     int rows, int32_t *__restrict__ out,
                                                                     int64_t out_ld) {
-  // dynamic LDS: bitmap of the row's columns, then the staged candidates (keys, columns)
+  // dynamic LDS: bitmap of the row's columns, then the candidates of bin b2 (keys, columns)
   extern __shared__ uint32_t lds[];
   __shared__ uint32_t hist[4 * 256];
-  __shared__ int s_scan[kFinishThreads / 64], s_misc[4];
-  __shared__ uint32_t s_mm[2 * (kFinishThreads / 64)];
+  __shared__ int s_scan[3 * (kFinishThreads / 64)], s_misc[8];
   __shared__ int s_sure_off[kMaxChunks + 1], s_cand_off[kMaxChunks + 1];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int64_t len = clamped_len(row_len, r, max_len);
   int32_t *o = out + r * out_ld;
-  if (len <= k) {  // short row: every key is kept
+  if (len <= k) {  // short row: every key is kept (the other kernels left it alone)
     for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
     return;
   }
@@ -422,7 +475,10 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   const int chunks = (int)((max_len + kChunk - 1) / kChunk);
   const int64_t cap = (int64_t)chunks * kChunk;
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
-  // exclusive offsets of each chunk's sure columns and candidates (one thread per chunk)
+  uint32_t *g1 = ws + L.hist1 + (int64_t)r * kBins;
+  uint32_t *g2 = ws + L.hist2 + (int64_t)r * kBins;
+  // chunk counts (one thread per chunk) and digit-2 bins 4 tid .. 4 tid + 3, scanned together
+  uint32_t h2[4];
   {
     const uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
     int a = 0, b = 0;
@@ -430,10 +486,12 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
       a = (int)cnt[2 * tid];
       b = (int)cnt[2 * tid + 1];
     }
-    const int sa = block_suffix_sum<kFinishThreads>(a, s_scan);
-    const int sb2 = block_suffix_sum<kFinishThreads>(b, s_scan);
+#pragma unroll
+    for (int i = 0; i < 4; i++) h2[i] = g2[4 * tid + i];
+    int sa = a, sb2 = b, sh = (int)(h2[0] + h2[1] + h2[2] + h2[3]);
+    block_suffix_sum3<kFinishThreads>(sa, sb2, sh, s_scan);
     if (tid == 0) {
-      s_sure_off[used] = sa;
+      s_sure_off[used] = sa;  // totals
       s_cand_off[used] = sb2;
     }
     __syncthreads();
@@ -441,100 +499,127 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
       s_sure_off[tid] = s_sure_off[used] - sa;
       s_cand_off[tid] = s_cand_off[used] - sb2;
     }
+    // bin b2 of the (k - sure)-th largest candidate
+    const int rem = k - s_sure_off[used];
+    int acc = sh;  // candidates in digit-2 bins >= 4 tid
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (acc >= rem && acc - (int)h2[i] < rem) {
+        s_misc[0] = 4 * tid + i;          // b2
+        s_misc[1] = rem - (acc - (int)h2[i]);  // keys of b2 still to take
+        s_misc[2] = (int)h2[i];           // keys in b2
+      }
+      acc -= (int)h2[i];
+    }
+    if (tid == 0) s_misc[3] = 0;  // staged candidates of b2
     __syncthreads();
   }
-  const int n_sure = s_sure_off[used];
-  const int n_cand = s_cand_off[used];
-  // g-th candidate / sure column of the row: find its chunk in the offsets
-  auto chunk_of = [&](const int *off, int g) {
-    int lo = 0, hi = used;  // largest c with off[c] <= g
+  // both histograms are left zero for the next call
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    g1[4 * tid + i] = 0u;
+    g2[4 * tid + i] = 0u;
+  }
+  const int n_sure = s_sure_off[used], n_cand = s_cand_off[used];
+  const uint32_t b2 = (uint32_t)s_misc[0];
+  const int need = s_misc[1], n2 = s_misc[2];
+  const int nwords = (int)((len + 31) / 32);
+  uint32_t *bitmap = lds;
+  const int sub_cap = long_sub_cap(max_len);
+  const bool staged = n2 <= sub_cap;
+  uint32_t *sub_key = lds + long_bitmap_words(max_len);
+  uint32_t *sub_col = sub_key + sub_cap;
+  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0u;
+  __syncthreads();
+  // g-th entry of a list split over chunks: the chunk is found for the wave's first lane by
+  // bisection and advanced per lane (a wave's 64 consecutive entries span few chunks)
+  auto locate = [&](const int *off, int g) {
+    const int g0 = __builtin_amdgcn_readfirstlane(g);
+    int lo = 0, hi = used;  // largest c with off[c] <= g0
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (off[mid] <= g) lo = mid;
+      if (off[mid] <= g0) lo = mid;
       else hi = mid;
     }
-    return lo;
+    int c = lo;
+    while (c + 1 < used && off[c + 1] <= g) c++;
+    return (int64_t)c * kChunk + (g - off[c]);
   };
   const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
   const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
-  const uint32_t *cidx = ws + L.cidx + (int64_t)r * cap;
-  const int nwords = (int)((len + 31) / 32);
-  uint32_t *bitmap = lds;
-  const int cap_lds = long_staged_cap(max_len);
-  uint32_t *skey = lds + long_bitmap_words(max_len);
-  uint32_t *sidx = skey + cap_lds;
-  const bool staged = n_cand <= cap_lds;
-  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0;
-  auto cand_pos = [&](int g) {
-    const int c = chunk_of(s_cand_off, g);
-    return (int64_t)c * kChunk + (g - s_cand_off[c]);
-  };
-  // candidates into LDS (8 loads in flight per thread), with their smallest and largest key
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int base = 0; base < n_cand; base += 8 * kFinishThreads) {
-    uint32_t kk[8], jj[8];
+  const uint32_t *ccol = ws + L.ccol + (int64_t)r * cap;
+  // sure columns and candidates above b2 into the bitmap; candidates in b2 into LDS
+  for (int base = 0; base < n_sure + n_cand; base += 4 * kFinishThreads) {
+    uint32_t kk[4], jj[4];
+    bool is_c[4];
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
+    for (int u = 0; u < 4; u++) {
       const int g = base + u * kFinishThreads + tid;
-      const int64_t p = g < n_cand ? cand_pos(g) : 0;
-      kk[u] = g < n_cand ? ckey[p] : 0u;
-      jj[u] = (staged && g < n_cand) ? cidx[p] : 0u;
+      is_c[u] = g >= n_sure;
+      kk[u] = 0xFFFFFFFFu;
+      jj[u] = 0xFFFFFFFFu;
+      if (g < n_sure) {
+        jj[u] = sure[locate(s_sure_off, g)];
+      } else if (g < n_sure + n_cand) {
+        const int64_t p = locate(s_cand_off, g - n_sure);
+        kk[u] = ckey[p];
+        jj[u] = ccol[p];
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int g = base + u * kFinishThreads + tid;
-      if (g < n_cand) {
-        kmin = min(kmin, kk[u]);
-        kmax = max(kmax, kk[u]);
-        if (staged) {
-          skey[g] = kk[u];
-          sidx[g] = jj[u];
+    for (int u = 0; u < 4; u++) {
+      const bool valid = jj[u] != 0xFFFFFFFFu;
+      const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
+      if (valid && (!is_c[u] || d2 > b2)) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+      const bool in_b2 = valid && is_c[u] && d2 == b2;
+      const uint64_t m = __ballot(in_b2 && staged);
+      if (m) {
+        int at = 0;
+        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
+        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+        if (in_b2 && at < n2) {
+          sub_key[at] = kk[u];
+          sub_col[at] = jj[u];
         }
       }
     }
   }
-  block_minmax<kFinishThreads>(kmin, kmax, s_mm);  // its barriers also publish the bitmap reset
-  for (int base = 0; base < n_sure; base += 8 * kFinishThreads) {
-    uint32_t jj[8];
-#pragma unroll
-    for (int u = 0; u < 8; u++) {
-      const int g = base + u * kFinishThreads + tid;
-      if (g < n_sure) {
-        const int c = chunk_of(s_sure_off, g);
-        jj[u] = sure[(int64_t)c * kChunk + (g - s_sure_off[c])];
-      } else {
-        jj[u] = 0u;
+  __syncthreads();
+  // the `need` largest candidates of b2, ties to the lowest columns
+  if (staged && n2 <= kRankMax) {
+    if (tid < n2) {
+      const uint32_t key = sub_key[tid], col = sub_col[tid];
+      int rank = 0;
+      for (int g = 0; g < n2; g++) {
+        const uint32_t kg = sub_key[g];
+        rank += (kg > key || (kg == key && sub_col[g] < col)) ? 1 : 0;
       }
+      if (rank < need) atomicOr(&bitmap[col >> 5], 1u << (col & 31));
     }
-#pragma unroll
-    for (int u = 0; u < 8; u++)
-      if (base + u * kFinishThreads + tid < n_sure) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+  } else {
+    // radix select over the low 8 key bits (the top 24 are b1 and b2): from the staged list,
+    // or straight from the candidate lists, where keys outside b2 do not match the prefix
+    const int n_sel = staged ? n2 : n_cand;
+    auto key_at = [&](int g) { return staged ? sub_key[g] : ckey[locate(s_cand_off, g)]; };
+    auto col_at = [&](int g) { return staged ? sub_col[g] : ccol[locate(s_cand_off, g)]; };
+    const uint32_t prefix = (ckey[locate(s_cand_off, 0)] & 0xFFF00000u) | (b2 << 8);
+    int rem = need, n_eq = 0;
+    const uint32_t T = block_select<kFinishThreads>(n_sel, key_at, prefix, 0xFFFFFF00u, 8, &rem, &n_eq, hist, s_scan,
+                                                    s_misc + 4);
+    uint32_t cut = 0xFFFFFFFFu;  // keys equal to T with column <= cut are kept
+    if (rem < n_eq) {            // keep the rem lowest columns: the largest 2^20 - 1 - column
+      int rem2 = rem, n_eq2 = 0;
+      const uint32_t sel = block_select<kFinishThreads>(
+          n_sel, [&](int g) { return key_at(g) == T ? (0xFFFFFu - col_at(g)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
+          &rem2, &n_eq2, hist, s_scan, s_misc + 4);
+      cut = 0xFFFFFu - sel;
+    }
+    for (int g = tid; g < n_sel; g += kFinishThreads) {
+      const uint32_t key = key_at(g);
+      const uint32_t j = col_at(g);
+      if (key > T || (key == T && j <= cut)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    }
   }
-  auto key_at = [&](int g) { return staged ? skey[g] : ckey[cand_pos(g)]; };
-  auto col_at = [&](int g) { return staged ? sidx[g] : cidx[cand_pos(g)]; };
-  // the remaining k - n_sure keys come from the candidates (all in bin b1)
-  const int sb = max(shared_bits(kmin, kmax), 12);  // the top 12 bits are b1 for every candidate
-  const uint32_t pmask = top_bits_mask(sb);
-  int rem = k - n_sure, n_eq = 0;
-  const uint32_t T = block_select<kFinishThreads>(n_cand, key_at, kmax & pmask, pmask, 32 - sb, &rem, &n_eq, hist,
-                                                  s_scan, s_misc);
-  // keys equal to T: keep the rem lowest columns (the largest of 2^20 - 1 - column)
-  uint32_t cut = 0xFFFFFFFFu;  // ties with column <= cut are kept
-  if (rem < n_eq) {
-    int rem2 = rem, n_eq2 = 0;
-    const uint32_t sel = block_select<kFinishThreads>(
-        n_cand, [&](int g) { return key_at(g) == T ? (0xFFFFFu - col_at(g)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
-        &rem2, &n_eq2, hist, s_scan, s_misc);
-    cut = 0xFFFFFu - sel;
-  }
-  for (int g = tid; g < n_cand; g += kFinishThreads) {
-    const uint32_t key = key_at(g);
-    const uint32_t j = col_at(g);
-    if (key > T || (key == T && j <= cut)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
-  }
-  // the row's histogram is left zero for the next call
-  uint32_t *gh = ws + L.hist + (int64_t)r * kBins1;
-  for (int i = tid; i < kBins1; i += kFinishThreads) gh[i] = 0;
   __syncthreads();
   // columns out in ascending order: each thread owns a contiguous run of bitmap words
   const int per = (nwords + kFinishThreads - 1) / kFinishThreads;
@@ -544,9 +629,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   // exclusive prefix over threads = total - suffix(tid); the total is exactly k when the
   // selection is consistent, and the bounds below hold either way
   const int suffix = block_suffix_sum<kFinishThreads>(mine, s_scan);
-  if (tid == 0) s_misc[3] = suffix;
+  if (tid == 0) s_misc[7] = suffix;
   __syncthreads();
-  const int total = s_misc[3];
+  const int total = s_misc[7];
   int pos = total - suffix;
   for (int i = w0; i < w1; i++) {
     uint32_t m = bitmap[i];
@@ -619,7 +704,7 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
     return fail(INDEXER_FP4_EINVAL, "topk: rows up to %lld keys need a 16-byte aligned workspace", (long long)max_len);
   uint32_t *ws = (uint32_t *)workspace;
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
-  const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_staged_cap(max_len));
+  const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_sub_cap(max_len));
   hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
                      max_len, k, ws);
   hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld,

@@ -251,9 +251,10 @@ def test_full_size_decode(ifp4, name):
 
 # ---------------------------------------------------------------------------- long-row top-k
 
-def _topk_exact(ifp4, lg, rl, k, max_len, ws=None):
+def _topk_exact(ifp4, lg, rl, k, max_len, ws=None, pad=0):
     rows, n = lg.shape
-    t = to_dev(lg)
+    # pad > 0 gives the rows a stride that is not a multiple of 4 floats
+    t = to_dev(np.pad(lg, ((0, 0), (0, pad)))) if pad else to_dev(lg)
     top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
     if ws is None:
         ws = torch.zeros(max(ifp4.indexer_topk_workspace_bytes(rows, max_len, k), 16), dtype=torch.uint8,
@@ -284,6 +285,25 @@ def test_topk_long_rows_exact(ifp4, n, k):
     ws = _topk_exact(ifp4, lg, rl, k, n)
     # the workspace is left ready for the next call: reuse it on different rows
     _topk_exact(ifp4, -lg[::-1].copy(), rl[::-1].copy(), k, n, ws)
+
+
+def test_topk_long_rows_second_level_paths(ifp4):
+    """Rows built so the k-th key's second-level bin holds (a) a few thousand keys (radix select
+    staged in LDS), (b) a handful with exact ties at the threshold (ranking by counting), (c) more
+    than LDS holds (radix select straight from the chunk lists); rows of odd stride."""
+    n, k = 131072, 2048
+    rng = np.random.default_rng(11)
+    lg = rng.random((4, n)).astype(np.float32)
+    idx = rng.permutation(n)[:6072]
+    lg[0, idx] = 7.5 + 1e-4 * rng.random(6072)                          # (a) dense cluster at the top
+    lg[1] = np.round(rng.standard_normal(n) * 64.0) / 64.0               # (b) ties everywhere
+    lg[2, idx] = 7.5                                                     # (c) 6072 equal keys on top
+    lg[2, rng.permutation(n)[:20000]] = 7.5
+    lg[3] = rng.standard_normal(n)
+    rl = np.array([n, n - 1, n, n - 333], np.int32)
+    ws = _topk_exact(ifp4, lg, rl, k, n)
+    _topk_exact(ifp4, lg[::-1].copy(), rl, k, n, ws)
+    _topk_exact(ifp4, lg, rl, k, n, pad=1)
 
 
 def test_topk_long_row_at_the_bitmap_limit(ifp4):

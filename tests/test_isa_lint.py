@@ -40,7 +40,10 @@ def suspicious_selects(asm_text):
         if j < 0 or re.match(r"^\S", lines[j]):
             continue  # condition code comes from another block
         between = lines[j + 1:i]
-        if not lines[j].strip().startswith("s_cmp") and any(x.strip().startswith("v_cmp") for x in between):
+        # a compare, or a uniform lane-mask condition turned into SCC by ANDing it with exec,
+        # is the select's intended condition
+        intended = lines[j].strip().startswith("s_cmp") or re.match(r"^\s+s_and_b(32|64) [^,]+, [^,]+, exec", lines[j])
+        if not intended and any(x.strip().startswith("v_cmp") for x in between):
             hits.append((i, lines[j].strip(), line.strip()))
     return hits
 
@@ -49,7 +52,9 @@ def test_lint_flags_the_known_bad_pattern():
     bad = "\n".join(["\ts_lshr_b32 s4, -1, s30", "\ts_not_b32 s31, s4", "\tv_cmp_eq_u32_e32 vcc, v8, v7",
                      "\ts_cselect_b32 s29, -1, s31"])
     good = "\n".join(["\tv_cmp_eq_u32_e32 vcc, v8, v7", "\ts_cmp_eq_u32 s4, s5", "\ts_cselect_b32 s29, -1, s31"])
-    assert suspicious_selects(bad) and not suspicious_selects(good)
+    mask = "\n".join(["\ts_and_b64 s[0:1], s[20:21], exec", "\tv_cmp_lt_i32_e32 vcc, v3, v4",
+                      "\ts_cselect_b32 s0, s4, 0"])
+    assert suspicious_selects(bad) and not suspicious_selects(good) and not suspicious_selects(mask)
 
 
 def test_kernels_have_no_stale_condition_selects():
