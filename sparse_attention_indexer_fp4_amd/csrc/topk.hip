@@ -245,11 +245,12 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 //            the columns in ascending order and zeroes both histograms for the next call.
 // Device-wide atomics on one cache line serialize, so the merges are kept to one atomic
 // instruction per workgroup and 64-bin block.
-constexpr int kLongThreads = 256;
+constexpr int kLongThreads = 1024;  // four waves per SIMD hide each other's latencies
 constexpr int kLongWaves = kLongThreads / 64;
 constexpr int kFinishThreads = 1024;
 constexpr int kChunk = 4096;
-constexpr int kPerThread = kChunk / kLongThreads;  // 16
+constexpr int kPerThread = kChunk / kLongThreads;  // 4
+constexpr int kWaveCols = kChunk / kLongWaves;      // columns of a chunk held by one wave
 constexpr int kBins = 4096;                         // 12-bit digits
 constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
 constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
@@ -378,12 +379,12 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   const int64_t cap = chunks * kChunk;
   const float *row = logits + r * ld;
   const int64_t end = min(len, start + kChunk);
-  // wave wv holds the chunk's columns [1024 wv, 1024 wv + 1024) in 64-column steps, so
-  // wave-major order is column order
+  // wave wv holds the chunk's columns [kWaveCols wv, kWaveCols (wv + 1)) in 64-column steps,
+  // so wave-major order is column order
   uint32_t key[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + 1024 * wv + 64 * u + lane;
+    const int64_t j = start + kWaveCols * wv + 64 * u + lane;
     key[u] = order_key(j < end ? row[j] : 0.f);
   }
   for (int i = tid; i < kBins; i += kLongThreads) h2[i] = 0u;
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   uint32_t n_s = 0, n_c = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const bool ok = start + 1024 * wv + 64 * u + lane < end;
+    const bool ok = start + kWaveCols * wv + 64 * u + lane < end;
     const uint32_t d = key[u] >> 20;
     ms[u] = __ballot(ok && d > bin1);
     mc[u] = __ballot(ok && d == bin1);
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   uint32_t *ccol = ws + L.ccol + (int64_t)r * cap + start;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const uint32_t j = (uint32_t)(start + 1024 * wv + 64 * u + lane);
+    const uint32_t j = (uint32_t)(start + kWaveCols * wv + 64 * u + lane);
     if ((ms[u] >> lane) & 1ull) sure[bs + lanes_below(ms[u])] = j;
     if ((mc[u] >> lane) & 1ull) {
       ckey[bc + lanes_below(mc[u])] = key[u];
@@ -520,7 +521,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
     g1[4 * tid + i] = 0u;
     g2[4 * tid + i] = 0u;
   }
-  const int n_sure = s_sure_off[used], n_cand = s_cand_off[used];
+  const int n_cand = s_cand_off[used];
   const uint32_t b2 = (uint32_t)s_misc[0];
   const int need = s_misc[1], n2 = s_misc[2];
   const int nwords = (int)((len + 31) / 32);
@@ -531,60 +532,66 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   uint32_t *sub_col = sub_key + sub_cap;
   for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0u;
   __syncthreads();
-  // g-th entry of a list split over chunks: the chunk is found for the wave's first lane by
-  // bisection and advanced per lane (a wave's 64 consecutive entries span few chunks)
-  auto locate = [&](const int *off, int g) {
-    const int g0 = __builtin_amdgcn_readfirstlane(g);
-    int lo = 0, hi = used;  // largest c with off[c] <= g0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= g0) lo = mid;
-      else hi = mid;
-    }
-    int c = lo;
-    while (c + 1 < used && off[c + 1] <= g) c++;
-    return (int64_t)c * kChunk + (g - off[c]);
-  };
   const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
   const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
   const uint32_t *ccol = ws + L.ccol + (int64_t)r * cap;
-  // sure columns and candidates above b2 into the bitmap; candidates in b2 into LDS
-  for (int base = 0; base < n_sure + n_cand; base += 4 * kFinishThreads) {
-    uint32_t kk[4], jj[4];
-    bool is_c[4];
+  // Sure columns and candidates above b2 go into the bitmap, candidates in b2 into LDS.
+  // Thread group c (tpc threads) walks chunk c's two lists; the first kBatch entries per
+  // thread of each list are loaded together.
+  {
+    constexpr int kBatch = 4;
+    const int tpc = max(1, kFinishThreads / used);
+    const int c = tid / tpc, t0 = tid % tpc;
+    const bool mine = c < used;
+    const int ns = mine ? s_sure_off[c + 1] - s_sure_off[c] : 0;
+    const int nc = mine ? s_cand_off[c + 1] - s_cand_off[c] : 0;
+    const uint32_t *cs = sure + (int64_t)(mine ? c : 0) * kChunk;
+    const uint32_t *ck = ckey + (int64_t)(mine ? c : 0) * kChunk;
+    const uint32_t *cc = ccol + (int64_t)(mine ? c : 0) * kChunk;
+    for (int t1 = t0; __syncthreads_or(t1 < ns || t1 < nc); t1 += kBatch * tpc) {
+      uint32_t sj[kBatch], kk[kBatch], jj[kBatch];
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const int g = base + u * kFinishThreads + tid;
-      is_c[u] = g >= n_sure;
-      kk[u] = 0xFFFFFFFFu;
-      jj[u] = 0xFFFFFFFFu;
-      if (g < n_sure) {
-        jj[u] = sure[locate(s_sure_off, g)];
-      } else if (g < n_sure + n_cand) {
-        const int64_t p = locate(s_cand_off, g - n_sure);
-        kk[u] = ckey[p];
-        jj[u] = ccol[p];
+      for (int u = 0; u < kBatch; u++) {
+        const int t = t1 + u * tpc;
+        sj[u] = t < ns ? cs[t] : 0xFFFFFFFFu;
+        kk[u] = t < nc ? ck[t] : 0u;
+        jj[u] = t < nc ? cc[t] : 0xFFFFFFFFu;
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const bool valid = jj[u] != 0xFFFFFFFFu;
-      const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
-      if (valid && (!is_c[u] || d2 > b2)) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
-      const bool in_b2 = valid && is_c[u] && d2 == b2;
-      const uint64_t m = __ballot(in_b2 && staged);
-      if (m) {
-        int at = 0;
-        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
-        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
-        if (in_b2 && at < n2) {
-          sub_key[at] = kk[u];
-          sub_col[at] = jj[u];
+      for (int u = 0; u < kBatch; u++) {
+        if (sj[u] != 0xFFFFFFFFu) atomicOr(&bitmap[sj[u] >> 5], 1u << (sj[u] & 31));
+        const bool valid = jj[u] != 0xFFFFFFFFu;
+        const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
+        if (valid && d2 > b2) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+        const bool in_b2 = valid && d2 == b2;
+        const uint64_t m = __ballot(in_b2 && staged);
+        if (m) {
+          int at = 0;
+          if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
+          at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+          if (in_b2 && at < n2) {
+            sub_key[at] = kk[u];
+            sub_col[at] = jj[u];
+          }
         }
       }
     }
   }
   __syncthreads();
+  // g-th candidate of the row (list split over chunks), for the radix fallback below: the
+  // chunk is found for the wave's first lane by bisection and advanced per lane
+  auto locate = [&](int g) {
+    const int g0 = __builtin_amdgcn_readfirstlane(g);
+    int lo = 0, hi = used;  // largest c with offset <= g0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cand_off[mid] <= g0) lo = mid;
+      else hi = mid;
+    }
+    int c = lo;
+    while (c + 1 < used && s_cand_off[c + 1] <= g) c++;
+    return (int64_t)c * kChunk + (g - s_cand_off[c]);
+  };
   // the `need` largest candidates of b2, ties to the lowest columns
   if (staged && n2 <= kRankMax) {
     if (tid < n2) {
@@ -600,9 +607,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
     // radix select over the low 8 key bits (the top 24 are b1 and b2): from the staged list,
     // or straight from the candidate lists, where keys outside b2 do not match the prefix
     const int n_sel = staged ? n2 : n_cand;
-    auto key_at = [&](int g) { return staged ? sub_key[g] : ckey[locate(s_cand_off, g)]; };
-    auto col_at = [&](int g) { return staged ? sub_col[g] : ccol[locate(s_cand_off, g)]; };
-    const uint32_t prefix = (ckey[locate(s_cand_off, 0)] & 0xFFF00000u) | (b2 << 8);
+    auto key_at = [&](int g) { return staged ? sub_key[g] : ckey[locate(g)]; };
+    auto col_at = [&](int g) { return staged ? sub_col[g] : ccol[locate(g)]; };
+    const uint32_t prefix = (ckey[locate(0)] & 0xFFF00000u) | (b2 << 8);
     int rem = need, n_eq = 0;
     const uint32_t T = block_select<kFinishThreads>(n_sel, key_at, prefix, 0xFFFFFF00u, 8, &rem, &n_eq, hist, s_scan,
                                                     s_misc + 4);
