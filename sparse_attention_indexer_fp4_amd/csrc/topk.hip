@@ -466,39 +466,63 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   __shared__ int s_scan[3 * (kFinishThreads / 64)], s_misc[8];
   __shared__ int s_sure_off[kMaxChunks + 1], s_cand_off[kMaxChunks + 1];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const LongWs L(rows, max_len);
+  const int chunks = (int)((max_len + kChunk - 1) / kChunk);
+  const int64_t cap = (int64_t)chunks * kChunk;
+  uint32_t *g1 = ws + L.hist1 + (int64_t)r * kBins;
+  uint32_t *g2 = ws + L.hist2 + (int64_t)r * kBins;
+  const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
+  const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
+  const uint32_t *ccol = ws + L.ccol + (int64_t)r * cap;
+  // Everything the kernel reads is requested at once: the row length, the chunk counts, the
+  // digit-2 histogram and the first entries of each chunk's two lists. Thread group c (tpc
+  // threads) owns chunk c; every chunk's list regions hold kChunk entries and
+  // kBatch * tpc <= kChunk, so reading past a count stays in bounds.
+  constexpr int kBatch = 4;
+  const int tpc = max(1, kFinishThreads / chunks);
+  const int c = tid / tpc, t0 = tid % tpc;
+  const int cq = min(c, chunks - 1);
+  const uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
+  const uint32_t *cs = sure + (int64_t)cq * kChunk;
+  const uint32_t *ck = ckey + (int64_t)cq * kChunk;
+  const uint32_t *cc = ccol + (int64_t)cq * kChunk;
   const int64_t len = clamped_len(row_len, r, max_len);
+  const int ns_raw = (int)cnt[2 * cq], nc_raw = (int)cnt[2 * cq + 1];
+  uint32_t h2[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) h2[i] = g2[4 * tid + i];
+  uint32_t sj[kBatch], kk[kBatch], jj[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; u++) {
+    sj[u] = cs[t0 + u * tpc];
+    kk[u] = ck[t0 + u * tpc];
+    jj[u] = cc[t0 + u * tpc];
+  }
   int32_t *o = out + r * out_ld;
   if (len <= k) {  // short row: every key is kept (the other kernels left it alone)
     for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
     return;
   }
-  const LongWs L(rows, max_len);
-  const int chunks = (int)((max_len + kChunk - 1) / kChunk);
-  const int64_t cap = (int64_t)chunks * kChunk;
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
-  uint32_t *g1 = ws + L.hist1 + (int64_t)r * kBins;
-  uint32_t *g2 = ws + L.hist2 + (int64_t)r * kBins;
-  // chunk counts (one thread per chunk) and digit-2 bins 4 tid .. 4 tid + 3, scanned together
-  uint32_t h2[4];
+  const bool mine = c < used;
+  const int ns = mine ? ns_raw : 0, nc = mine ? nc_raw : 0;
+  const int nwords = (int)((len + 31) / 32);
+  uint32_t *bitmap = lds;
+  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0u;
+  // chunk offsets (first thread of each group) and digit-2 bins 4 tid .. 4 tid + 3, scanned
+  // together; the scan's barriers also publish the cleared bitmap
   {
-    const uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
-    int a = 0, b = 0;
-    if (tid < used) {
-      a = (int)cnt[2 * tid];
-      b = (int)cnt[2 * tid + 1];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) h2[i] = g2[4 * tid + i];
-    int sa = a, sb2 = b, sh = (int)(h2[0] + h2[1] + h2[2] + h2[3]);
+    const bool lead = mine && t0 == 0;
+    int sa = lead ? ns : 0, sb2 = lead ? nc : 0, sh = (int)(h2[0] + h2[1] + h2[2] + h2[3]);
     block_suffix_sum3<kFinishThreads>(sa, sb2, sh, s_scan);
     if (tid == 0) {
       s_sure_off[used] = sa;  // totals
       s_cand_off[used] = sb2;
     }
     __syncthreads();
-    if (tid < used) {
-      s_sure_off[tid] = s_sure_off[used] - sa;
-      s_cand_off[tid] = s_cand_off[used] - sb2;
+    if (lead) {
+      s_sure_off[c] = s_sure_off[used] - sa;
+      s_cand_off[c] = s_cand_off[used] - sb2;
     }
     // bin b2 of the (k - sure)-th largest candidate
     const int rem = k - s_sure_off[used];
@@ -506,9 +530,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       if (acc >= rem && acc - (int)h2[i] < rem) {
-        s_misc[0] = 4 * tid + i;          // b2
+        s_misc[0] = 4 * tid + i;               // b2
         s_misc[1] = rem - (acc - (int)h2[i]);  // keys of b2 still to take
-        s_misc[2] = (int)h2[i];           // keys in b2
+        s_misc[2] = (int)h2[i];                // keys in b2
       }
       acc -= (int)h2[i];
     }
@@ -524,58 +548,43 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   const int n_cand = s_cand_off[used];
   const uint32_t b2 = (uint32_t)s_misc[0];
   const int need = s_misc[1], n2 = s_misc[2];
-  const int nwords = (int)((len + 31) / 32);
-  uint32_t *bitmap = lds;
   const int sub_cap = long_sub_cap(max_len);
   const bool staged = n2 <= sub_cap;
   uint32_t *sub_key = lds + long_bitmap_words(max_len);
   uint32_t *sub_col = sub_key + sub_cap;
-  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0u;
-  __syncthreads();
-  const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
-  const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
-  const uint32_t *ccol = ws + L.ccol + (int64_t)r * cap;
-  // Sure columns and candidates above b2 go into the bitmap, candidates in b2 into LDS.
-  // Thread group c (tpc threads) walks chunk c's two lists; the first kBatch entries per
-  // thread of each list are loaded together.
-  {
-    constexpr int kBatch = 4;
-    const int tpc = max(1, kFinishThreads / used);
-    const int c = tid / tpc, t0 = tid % tpc;
-    const bool mine = c < used;
-    const int ns = mine ? s_sure_off[c + 1] - s_sure_off[c] : 0;
-    const int nc = mine ? s_cand_off[c + 1] - s_cand_off[c] : 0;
-    const uint32_t *cs = sure + (int64_t)(mine ? c : 0) * kChunk;
-    const uint32_t *ck = ckey + (int64_t)(mine ? c : 0) * kChunk;
-    const uint32_t *cc = ccol + (int64_t)(mine ? c : 0) * kChunk;
-    for (int t1 = t0; __syncthreads_or(t1 < ns || t1 < nc); t1 += kBatch * tpc) {
-      uint32_t sj[kBatch], kk[kBatch], jj[kBatch];
+  // sure columns and candidates above b2 go into the bitmap, candidates in b2 into LDS
+  auto place = [&](int t1) {
 #pragma unroll
-      for (int u = 0; u < kBatch; u++) {
-        const int t = t1 + u * tpc;
-        sj[u] = t < ns ? cs[t] : 0xFFFFFFFFu;
-        kk[u] = t < nc ? ck[t] : 0u;
-        jj[u] = t < nc ? cc[t] : 0xFFFFFFFFu;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; u++) {
-        if (sj[u] != 0xFFFFFFFFu) atomicOr(&bitmap[sj[u] >> 5], 1u << (sj[u] & 31));
-        const bool valid = jj[u] != 0xFFFFFFFFu;
-        const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
-        if (valid && d2 > b2) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
-        const bool in_b2 = valid && d2 == b2;
-        const uint64_t m = __ballot(in_b2 && staged);
-        if (m) {
-          int at = 0;
-          if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
-          at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
-          if (in_b2 && at < n2) {
-            sub_key[at] = kk[u];
-            sub_col[at] = jj[u];
-          }
+    for (int u = 0; u < kBatch; u++) {
+      const int t = t1 + u * tpc;
+      if (t < ns) atomicOr(&bitmap[sj[u] >> 5], 1u << (sj[u] & 31));
+      const bool cand = t < nc;
+      const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
+      if (cand && d2 > b2) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
+      const bool in_b2 = cand && d2 == b2;
+      const uint64_t m = __ballot(in_b2 && staged);
+      if (m) {
+        int at = 0;
+        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
+        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+        if (in_b2 && at < n2) {
+          sub_key[at] = kk[u];
+          sub_col[at] = jj[u];
         }
       }
     }
+  };
+  place(t0);
+  // chunks with more entries than the first batch covered (rare)
+  for (int t1 = t0 + kBatch * tpc; __syncthreads_or(t1 < ns || t1 < nc); t1 += kBatch * tpc) {
+#pragma unroll
+    for (int u = 0; u < kBatch; u++) {
+      const int t = t1 + u * tpc;
+      sj[u] = t < ns ? cs[t] : 0u;
+      kk[u] = t < nc ? ck[t] : 0u;
+      jj[u] = t < nc ? cc[t] : 0u;
+    }
+    place(t1);
   }
   __syncthreads();
   // g-th candidate of the row (list split over chunks), for the radix fallback below: the
@@ -631,11 +640,11 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   // columns out in ascending order: each thread owns a contiguous run of bitmap words
   const int per = (nwords + kFinishThreads - 1) / kFinishThreads;
   const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  int mine = 0;
-  for (int i = w0; i < w1; i++) mine += __popc(bitmap[i]);
+  int bits = 0;
+  for (int i = w0; i < w1; i++) bits += __popc(bitmap[i]);
   // exclusive prefix over threads = total - suffix(tid); the total is exactly k when the
   // selection is consistent, and the bounds below hold either way
-  const int suffix = block_suffix_sum<kFinishThreads>(mine, s_scan);
+  const int suffix = block_suffix_sum<kFinishThreads>(bits, s_scan);
   if (tid == 0) s_misc[7] = suffix;
   __syncthreads();
   const int total = s_misc[7];
