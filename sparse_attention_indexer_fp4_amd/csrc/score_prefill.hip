@@ -7,17 +7,25 @@
 // at position p sees keys [0, p] (causal, inclusive).
 //
 // Design for gfx950. Work items are (tile, page) pairs where a tile is up to 8 rows of one
-// request's group (schedule.hip). A unit (workgroup of NW waves) takes a contiguous range
-// of items; all its waves walk the same items and wave w scores rows w*RPW .. w*RPW+RPW-1
-// of the tile, so one key page feeds 8 rows x n_heads query heads of MFMA work while its
-// bytes come from HBM once (later waves of the workgroup hit the CU's cache). Query rows
-// stay in registers while the unit stays on a tile. A wave skips a page that none of its
-// rows reaches (the causal triangle) and rows past a row's length are never stored.
+// request's group (schedule.hip). A unit (workgroup of 8 waves) takes a contiguous range of
+// items; all its waves walk the same items and wave w scores row w of the tile, so one key
+// page feeds 8 rows x n_heads query heads of MFMA work while its bytes come from HBM once
+// (the other waves of the workgroup hit the CU's caches). As in the decode scorer, each
+// wave builds a table of 64 items at a time with one round of per-lane loads (tile, page,
+// physical page, and whether its row reaches the page: the causal triangle) and keeps D
+// pages in flight in a register ring with unconditional, clamped refills, so the compiler
+// waits only for the page being scored; logits past a row's length fall outside the
+// store's range. The query row stays in registers while the wave stays on a tile.
 #include "score_common.h"
+
+// pages in flight per wave
+#ifndef IFP4_PREFILL_RING
+#define IFP4_PREFILL_RING 2
+#endif
 
 namespace ifp4 {
 
-template <int NH16, int RPW, int NW, int D>
+template <int NH16, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
@@ -25,97 +33,94 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const int32_t *__restrict__ sched_g, int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g,
     float *__restrict__ logits, int64_t ld) {
   const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
-  const const_ptr<int32_t> sched = as_const(sched_g), bt = as_const(bt_g), row_len = as_const(row_len_g);
+  const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
   const int it0 = sched[L.unit_begin + u];
   const int it1 = sched[L.unit_begin + u + 1];
   if (it0 >= it1) return;  // empty unit: nothing else is touched
   const int lane = threadIdx.x & 63;
-  const int wv = uniform(threadIdx.x >> 6);
+  const int my_row = uniform(threadIdx.x >> 6);  // this wave's row inside a tile
   if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units) {
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
     return;
   }
   const int n_tiles = sched[5];
-  const const_ptr<int32_t> tiles = sched + L.tiles;  // {first row, rows, request, pages} per tile
-  auto tile = [&](int t) { return make_int4(tiles[4 * t], tiles[4 * t + 1], tiles[4 * t + 2], tiles[4 * t + 3]); };
-  const const_ptr<int32_t> cum = sched + L.cum;
-  const int n_items = it1 - it0;
-  const int my_row0 = wv * RPW;  // this wave's first row inside a tile
+  const int32_t *tiles = sched_g + L.tiles;  // {first row, rows, request, pages} per tile
+  const int32_t *cum = sched_g + L.cum;
+  const int n_my = it1 - it0;
 
-  int tb = sched[L.unit_tile + u];  // issue-side tile cursor
-  // query rows of the unit's first tile, loaded before any page (see score_decode.hip)
-  RowRegs<NH16, RPW> R;
-  int qt = tb;
-  int row0, n_valid;
-  {
-    const int4 T = tile(qt);
-    row0 = T.x + my_row0;
-    n_valid = min(RPW, T.y - my_row0);
-    load_rows<NH16, RPW>(R, qp, qs, w, row0, n_valid, n_heads, lane);
-  }
-
-  // Batches of D items: issue the page loads this wave needs, then score them.
-  for (int i0 = 0; i0 < n_items; i0 += D) {
-    PageRegs P[D];
-    int st[D], sp[D];
-    bool sok[D];
-    static_for<D>([&](auto kk) {
-      constexpr int K = decltype(kk)::value;
-      sok[K] = false;
-      st[K] = tb;
-      sp[K] = 0;
-      if (i0 + K < n_items) {
-        const int it = it0 + i0 + K;
-        while (tb < n_tiles - 1 && it >= cum[tb + 1]) tb++;
-        const int4 T = tile(tb);
-        const int p = it - cum[tb];
-        st[K] = tb;
-        sp[K] = p;
-        bool need = false;
-#pragma unroll
-        for (int j = 0; j < RPW; j++)
-          if (my_row0 + j < T.y && row_len[T.x + my_row0 + j] > p * kPage) need = true;
-        if (need && p < 0) {
-          if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
-        } else if (need) {
-          if (p >= bt_ld) {
-            if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_TABLE_SHORT);
-          } else {
-            const int64_t phys = bt[(int64_t)T.z * bt_ld + p];
-            if (phys < 0 || phys >= n_pages) {
-              if (lane == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
-            } else {
-              sok[K] = true;
-              load_page(P[K], kvp, kvs, phys, lane);
-            }
-          }
+  // Item table, one lane per item, for 64 items at a time.
+  int tcur = sched[L.unit_tile + u];  // tile of the next item to look up
+  int tab_base = -64;
+  int v_tile = 0, v_page = 0, v_phys = -1, v_need = 0;
+  auto fill = [&](int base) {
+    tab_base = base;
+    const int it = it0 + base + lane;
+    int t = tcur, p = 0, phys = -1, need = 0;
+    if (it < it1) {
+      while (t < n_tiles - 1 && it >= cum[t + 1]) t++;
+      p = it - cum[t];
+      const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * t);
+      need = my_row < T.y && row_len[T.x + my_row] > p * kPage;
+      if (p < 0) {
+        atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
+        need = 0;
+      } else if (p >= bt_ld) {
+        if (need) atomicOr(err, INDEXER_FP4_DEV_TABLE_SHORT);
+        need = 0;
+      } else {
+        phys = bt_g[(int64_t)T.z * bt_ld + p];
+        if (phys < 0 || phys >= n_pages) {
+          if (need) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
+          phys = -1;
+          need = 0;
         }
       }
-    });
+    }
+    v_tile = t;
+    v_page = p;
+    v_phys = phys;
+    v_need = need;
+    tcur = __builtin_amdgcn_readlane(t, 63);  // tiles only advance with the items
+  };
+
+  PageRegs P[D];
+  int st[D], sp[D];
+  bool sok[D];
+  auto issue = [&](auto kk, int i) {
+    constexpr int K = decltype(kk)::value;
+    const bool live = i < n_my;
+    const int ii = live ? i : n_my - 1;
+    if (ii - tab_base >= 64) fill(ii & ~63);
+    const int l = ii - tab_base;
+    const int phys = __builtin_amdgcn_readlane(v_phys, l);
+    st[K] = __builtin_amdgcn_readlane(v_tile, l);
+    sp[K] = __builtin_amdgcn_readlane(v_page, l);
+    sok[K] = live && __builtin_amdgcn_readlane(v_need, l) != 0;
+    load_page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);  // a page some row of the tile reads
+  };
+  RowRegs<NH16, 1> R;
+  int qt = -1, row = 0, row_bytes = 0;
+  auto score = [&](auto kk) {
+    constexpr int K = decltype(kk)::value;
+    if (!sok[K]) return;
+    if (st[K] != qt) {  // a new tile: this wave's query row (waits for everything in flight)
+      qt = st[K];
+      const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * qt);
+      row = T.x + my_row;  // sok implies my_row < T.y
+      row_bytes = 4 * max(row_len[row], 0);
+      load_rows<NH16, 1>(R, qp, qs, w, row, 1, n_heads, lane);
+    }
+    const uint32_t col = (uint32_t)(sp[K] * kPage + lane);
+    const float v = page_logit<NH16, 1, 0>(P[K], R, lane);
+    buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
+  };
+
+  static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
+  for (int i0 = 0; i0 < n_my; i0 += D) {
     static_for<D>([&](auto kk) {
-      constexpr int K = decltype(kk)::value;
-      if (sok[K]) {
-        if (st[K] != qt) {
-          qt = st[K];
-          const int4 T = tile(qt);
-          row0 = T.x + my_row0;
-          n_valid = min(RPW, T.y - my_row0);
-          load_rows<NH16, RPW>(R, qp, qs, w, row0, n_valid, n_heads, lane);
-        }
-        const int col = sp[K] * kPage + lane;
-        static_for<RPW>([&](auto jj) {
-          constexpr int J = decltype(jj)::value;
-          if (J < n_valid) {
-            const int64_t r = row0 + J;
-            const int len = row_len[r];
-            if (sp[K] * kPage < len) {
-              const float v = page_logit<NH16, RPW, J>(P[K], R, lane);
-              if (col < len) logits[r * ld + col] = v;
-            }
-          }
-        });
-      }
+      score(kk);
+      issue(kk, i0 + decltype(kk)::value + D);
     });
   }
 }
@@ -125,8 +130,8 @@ static void launch_prefill(hipStream_t st, int n_units, const uint8_t *qp, const
                            int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                            int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched, const int32_t *row_len,
                            float *logits, int64_t ld) {
-  constexpr int RPW = 1, NW = kTileRows / RPW, D = 2;
-  hipLaunchKernelGGL((score_prefill_kernel<NH16, RPW, NW, D>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
+  constexpr int NW = kTileRows, D = IFP4_PREFILL_RING;
+  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, D>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
                      n_heads, kvp, kvs, n_pages, bt, bt_ld, n_req, n_rows_padded, n_units, sched, sched + 1, row_len,
                      logits, ld);
 }
