@@ -137,21 +137,43 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
   __syncthreads();
 }
 
+// LDS histogram increment of digit d for lanes with `ok`. A wave whose counted keys all share
+// one digit (ties, constant rows) adds them with one atomic instead of 64 conflicting ones.
+__device__ __forceinline__ void hist_put(uint32_t *h, uint32_t d, bool ok) {
+  const uint64_t act = __ballot(ok);
+  if (act == 0) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+  if (__ballot(ok && d != d0) == 0) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
+  } else if (ok) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
-// Rows up to kShortMax keys: one workgroup per row, keys staged in LDS (dynamic: max_len
-// words), then radix passes and an ordered gather from LDS.
-constexpr int kShortThreads = 1024;
+// Rows up to kShortMax keys: one 256-thread workgroup per row (several rows share a CU). The
+// row's keys are staged in LDS with their smallest and largest value; a 1024-bin histogram
+// spread linearly over that range (d = min((key - kmin) >> s, 1023)) finds the bin b that
+// holds the k-th largest key; keys in higher bins are kept and the few keys in b are ranked
+// by counting (radix select when there are many), ties to the lowest columns. The kept
+// columns are then gathered in ascending order, one contiguous column range per wave.
+constexpr int kShortThreads = 256;
 constexpr int kShortWaves = kShortThreads / 64;
 constexpr int64_t kShortMax = 16384;
+constexpr int kShortBins = 1024;
+constexpr int kShortRank = 256;  // bin-b keys ranked by counting
 
 __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len, int64_t max_len,
                                                                 int k, int32_t *__restrict__ out, int64_t out_ld) {
-  extern __shared__ uint32_t keys[];
-  __shared__ uint32_t hist[4 * 256];
-  __shared__ int s_scan[kShortWaves], s_misc[4];
+  extern __shared__ uint32_t keys[];  // max_len words
+  __shared__ uint32_t hist[kShortBins];
+  __shared__ uint32_t sel[kShortMax / 32];  // chosen bin-b keys, by column
+  __shared__ uint32_t ckey[kShortRank], ccol[kShortRank];
+  __shared__ int s_scan[3 * kShortWaves], s_misc[8];
   __shared__ uint32_t s_mm[2 * kShortWaves];
-  __shared__ int s_gt[kShortWaves], s_eq[kShortWaves];
+  __shared__ int s_gt[kShortWaves];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int64_t len64 = row_len[r];
@@ -162,7 +184,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
     for (int j = tid; j < k; j += kShortThreads) o[j] = j < n ? j : -1;
     return;
   }
-  // stage the row: 16 loads in flight per thread and round
+  // stage the row (16 loads in flight per thread and round), clear the histogram and bitmap
   const float *row = logits + r * ld;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
   for (int base = 0; base < n; base += 16 * kShortThreads) {
@@ -183,47 +205,115 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
       }
     }
   }
-  block_minmax<kShortThreads>(kmin, kmax, s_mm);  // its barrier also publishes the staged keys
-  const int sb = shared_bits(kmin, kmax);
-  const uint32_t pmask = top_bits_mask(sb);
-  int rem = k, n_eq = 0;
-  const uint32_t T = block_select<kShortThreads>(n, [&](int i) { return keys[i]; }, kmax & pmask, pmask, 32 - sb,
-                                                 &rem, &n_eq, hist, s_scan, s_misc);
-  const int need_eq = rem;  // keys equal to T still to take, lowest columns first
-
+  for (int i = tid; i < kShortBins; i += kShortThreads) hist[i] = 0u;
+  const int nwords = (n + 31) / 32;
+  for (int i = tid; i < nwords; i += kShortThreads) sel[i] = 0u;
+  if (tid == 0) s_misc[3] = 0;
+  block_minmax<kShortThreads>(kmin, kmax, s_mm);  // its barriers publish all of the above
+  const int bl = 32 - __clz((int)(kmax - kmin));
+  const int sh = bl > 10 ? bl - 10 : 0;
+  auto digit = [&](uint32_t key) { return min((key - kmin) >> sh, (uint32_t)(kShortBins - 1)); };
+  for (int i0 = 0; i0 < n; i0 += kShortThreads) {
+    const int i = i0 + tid;
+    hist_put(hist, i < n ? digit(keys[i]) : 0u, i < n);
+  }
+  __syncthreads();
+  // the bin b of the k-th largest key (thread t owns bins 4t .. 4t+3)
+  {
+    uint32_t c[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) c[i] = hist[4 * tid + i];
+    int acc = block_suffix_sum<kShortThreads>((int)(c[0] + c[1] + c[2] + c[3]), s_scan);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (acc >= k && acc - (int)c[i] < k) {
+        s_misc[0] = 4 * tid + i;          // b
+        s_misc[1] = k - (acc - (int)c[i]);  // keys of b to take
+        s_misc[2] = (int)c[i];            // keys in b
+      }
+      acc -= (int)c[i];
+    }
+    __syncthreads();
+  }
+  const uint32_t b = (uint32_t)s_misc[0];
+  const int need = s_misc[1], nb = s_misc[2];
+  if (nb <= kShortRank) {
+    // list the keys of bin b, then keep those ranked below `need` (key descending, column
+    // ascending)
+    for (int i0 = 0; i0 < n; i0 += kShortThreads) {
+      const int i = i0 + tid;
+      const bool in_b = i < n && digit(keys[i]) == b;
+      const uint64_t m = __ballot(in_b);
+      if (m) {
+        int at = 0;
+        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
+        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+        if (in_b && at < nb) {
+          ckey[at] = keys[i];
+          ccol[at] = (uint32_t)i;
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < nb) {
+      const uint32_t key = ckey[tid], col = ccol[tid];
+      int rank = 0;
+      for (int g = 0; g < nb; g++) {
+        const uint32_t kg = ckey[g];
+        rank += (kg > key || (kg == key && ccol[g] < col)) ? 1 : 0;
+      }
+      if (rank < need) atomicOr(&sel[col >> 5], 1u << (col & 31));
+    }
+  } else {
+    // many keys in b (ties, clusters): radix select over key - kmin among them. Their offsets
+    // lie in [b << sh, (b + 1) << sh), so they share the top 32 - sh bits (b); keys of other
+    // bins are mapped to a value whose top bits differ from b's
+    const uint32_t other = b == 0 ? 0xFFFFFFFFu : 0u;
+    auto off_of = [&](int i) {
+      const uint32_t key = keys[i];
+      return digit(key) == b ? key - kmin : other;
+    };
+    int rem = need, n_eq = 0;
+    const uint32_t T = kmin + block_select<kShortThreads>(n, off_of, b << sh, top_bits_mask(32 - sh), sh, &rem,
+                                                          &n_eq, hist, s_scan, s_misc + 4);
+    uint32_t cut = 0xFFFFFFFFu;  // keys equal to T with column <= cut are kept
+    if (rem < n_eq) {
+      int rem2 = rem, n_eq2 = 0;
+      const uint32_t selc = block_select<kShortThreads>(
+          n, [&](int i) { return keys[i] == T ? (0xFFFFFu - (uint32_t)i) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
+          &rem2, &n_eq2, hist, s_scan, s_misc + 4);
+      cut = 0xFFFFFu - selc;
+    }
+    for (int i = tid; i < n; i += kShortThreads) {
+      const uint32_t key = keys[i];
+      if (digit(key) == b && (key > T || (key == T && (uint32_t)i <= cut)))
+        atomicOr(&sel[i >> 5], 1u << (i & 31));
+    }
+  }
+  __syncthreads();
   // gather: wave wv owns the contiguous column range [c_lo, c_hi)
   const int chunk = ((n + kShortWaves - 1) / kShortWaves + 63) & ~63;
   const int c_lo = min(n, wv * chunk), c_hi = min(n, c_lo + chunk);
-  int n_gt = 0, n_eqw = 0;
+  auto take = [&](int j) {
+    const uint32_t key = keys[j];
+    return digit(key) > b || ((sel[j >> 5] >> (j & 31)) & 1u);
+  };
+  int n_take = 0;
   for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
     const int j = j0 + lane;
-    const uint32_t key = j < c_hi ? keys[j] : 0u;
-    n_gt += __popcll(__ballot(j < c_hi && key > T));
-    n_eqw += __popcll(__ballot(j < c_hi && key == T));
+    n_take += __popcll(__ballot(j < c_hi && take(j)));
   }
-  if (lane == 0) {
-    s_gt[wv] = n_gt;
-    s_eq[wv] = n_eqw;
-  }
+  if (lane == 0) s_gt[wv] = n_take;
   __syncthreads();
-  int eq_base = 0, out_base = 0;
-  for (int w2 = 0; w2 < wv; w2++) {
-    const int take_eq = min(max(need_eq - eq_base, 0), s_eq[w2]);
-    out_base += s_gt[w2] + take_eq;
-    eq_base += s_eq[w2];
-  }
+  int out_base = 0;
+  for (int w2 = 0; w2 < wv; w2++) out_base += s_gt[w2];
   for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
     const int j = j0 + lane;
-    const uint32_t key = j < c_hi ? keys[j] : 0u;
-    const bool is_gt = j < c_hi && key > T;
-    const bool is_eq = j < c_hi && key == T;
-    const uint64_t eq = __ballot(is_eq);
-    const bool take = is_gt || (is_eq && eq_base + (int)lanes_below(eq) < need_eq);
-    const uint64_t tk = __ballot(take);
+    const bool t = j < c_hi && take(j);
+    const uint64_t tk = __ballot(t);
     const int pos = out_base + (int)lanes_below(tk);
-    if (take && pos < k) o[pos] = j;  // exactly k are taken; the bound is insurance
+    if (t && pos < k) o[pos] = j;  // exactly k are taken; the bound is insurance
     out_base += __popcll(tk);
-    eq_base += __popcll(eq);
   }
 }
 
@@ -285,20 +375,6 @@ __host__ __device__ inline int long_sub_cap(int64_t max_len) {
 __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
   const int64_t len = row_len[r];
   return len < 0 ? 0 : (len > max_len ? max_len : len);
-}
-
-// LDS histogram increment of digit d for lanes with `ok`. A wave whose counted keys all share
-// one digit (ties, constant rows) adds them with one atomic instead of 64 conflicting ones.
-__device__ __forceinline__ void hist_put(uint32_t *h, uint32_t d, bool ok) {
-  const uint64_t act = __ballot(ok);
-  if (act == 0) return;
-  const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
-  if (__ballot(ok && d != d0) == 0) {
-    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
-  } else if (ok) {
-    atomicAdd(&h[d], 1u);
-  }
 }
 
 // Adds an LDS histogram's occupied bins into a global one: each wave instruction covers 64
