@@ -9,59 +9,107 @@
 // Design for gfx950. Work items are (tile, page) pairs where a tile is up to 8 rows of one
 // request's group (schedule.hip). A unit (workgroup of 8 waves) takes a contiguous range of
 // items; all its waves walk the same items and wave w scores row w of the tile, so one key
-// page feeds 8 rows x n_heads query heads of MFMA work while its bytes come from HBM once
-// (the other waves of the workgroup hit the CU's caches). As in the decode scorer, each
-// wave builds a table of 64 items at a time with one round of per-lane loads (tile, page,
-// physical page, and whether its row reaches the page: the causal triangle) and keeps D
-// pages in flight in a register ring with unconditional, clamped refills, so the compiler
-// waits only for the page being scored; logits past a row's length fall outside the
-// store's range. The query row stays in registers while the wave stays on a tile.
+// page feeds 8 rows x n_heads query heads of MFMA work. Pages go through a ring of P slots
+// in LDS filled by direct global-to-LDS loads (no registers held while in flight, so the
+// ring can be deep): four waves each copy one 1 KiB key tile, a fifth the 256-byte scale
+// block, with lane i fetching exactly the 16 bytes that lane i of every wave later reads as
+// its MFMA operand (same layout as the decode scorer's direct loads), so the LDS reads are
+// linear. Per item the loader waves wait until their copy of the item has landed
+// (vmcnt counting in issue order), the unit meets at a barrier, the slot freed by the
+// previous item is refilled P-1 items ahead, and every wave scores the item from LDS. Each
+// wave keeps a table of 64 items at a time (tile, page, physical page, whether its row
+// reaches the page), built with one round of per-lane loads. Logits past a row's length
+// fall outside the store's range; the query row stays in registers while the wave stays
+// on a tile.
 #include "score_common.h"
 
-// pages in flight per wave
+// pages in the LDS ring of a unit
 #ifndef IFP4_PREFILL_RING
-#define IFP4_PREFILL_RING 2
+#define IFP4_PREFILL_RING 4
 #endif
 
 namespace ifp4 {
 
-template <int NH16, int NW, int D>
+constexpr int kPrefillMaxRing = 8;
+
+// One LDS array per ring slot: with every slot access indexed by a constant the compiler
+// can tell the slots apart and adds no waits of its own between a slot's reads and the
+// loads in flight into other slots.
+#define IFP4_SLOT(I)                                                   \
+  __shared__ __attribute__((aligned(16))) uint4 pf_keys##I[kPage * 4]; \
+  __shared__ uint32_t pf_scales##I[kPage];
+IFP4_SLOT(0) IFP4_SLOT(1) IFP4_SLOT(2) IFP4_SLOT(3) IFP4_SLOT(4) IFP4_SLOT(5) IFP4_SLOT(6) IFP4_SLOT(7)
+#undef IFP4_SLOT
+
+template <int S>
+__device__ __forceinline__ uint4 *slot_keys() {
+  static_assert(S >= 0 && S < kPrefillMaxRing, "ring slot");
+  if constexpr (S == 0) return pf_keys0;
+  else if constexpr (S == 1) return pf_keys1;
+  else if constexpr (S == 2) return pf_keys2;
+  else if constexpr (S == 3) return pf_keys3;
+  else if constexpr (S == 4) return pf_keys4;
+  else if constexpr (S == 5) return pf_keys5;
+  else if constexpr (S == 6) return pf_keys6;
+  else return pf_keys7;
+}
+template <int S>
+__device__ __forceinline__ uint32_t *slot_scales() {
+  if constexpr (S == 0) return pf_scales0;
+  else if constexpr (S == 1) return pf_scales1;
+  else if constexpr (S == 2) return pf_scales2;
+  else if constexpr (S == 3) return pf_scales3;
+  else if constexpr (S == 4) return pf_scales4;
+  else if constexpr (S == 5) return pf_scales5;
+  else if constexpr (S == 6) return pf_scales6;
+  else return pf_scales7;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int NH16, int NW, int P>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
     const int32_t *__restrict__ bt_g, int64_t bt_ld, int n_req, int n_rows_padded, int n_units,
     const int32_t *__restrict__ sched_g, int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g,
     float *__restrict__ logits, int64_t ld) {
+  static_assert(P >= 2 && P <= kPrefillMaxRing && NW >= 5, "ring depth and loader waves");
   const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
   const int it0 = sched[L.unit_begin + u];
   const int it1 = sched[L.unit_begin + u + 1];
-  if (it0 >= it1) return;  // empty unit: nothing else is touched
+  if (it0 >= it1) return;  // empty unit (uniform over the workgroup): nothing else is touched
   const int lane = threadIdx.x & 63;
-  const int my_row = uniform(threadIdx.x >> 6);  // this wave's row inside a tile
+  const int wv = uniform(threadIdx.x >> 6);  // this wave's row inside a tile
   if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units) {
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
+    return;
+  }
+  if (n_pages <= 0) {  // the ring always copies some page: there must be one
+    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
     return;
   }
   const int n_tiles = sched[5];
   const int32_t *tiles = sched_g + L.tiles;  // {first row, rows, request, pages} per tile
   const int32_t *cum = sched_g + L.cum;
   const int n_my = it1 - it0;
+  const bool loader = wv < 5;  // waves 0-3 copy key tiles, wave 4 the scale block
 
   // Item table, one lane per item, for 64 items at a time.
   int tcur = sched[L.unit_tile + u];  // tile of the next item to look up
   int tab_base = -64;
-  int v_tile = 0, v_page = 0, v_phys = -1, v_need = 0;
+  int v_tile = 0, v_page = 0, v_phys = 0, v_need = 0;
   auto fill = [&](int base) {
     tab_base = base;
     const int it = it0 + base + lane;
-    int t = tcur, p = 0, phys = -1, need = 0;
+    int t = tcur, p = 0, phys = 0, need = 0;
     if (it < it1) {
       while (t < n_tiles - 1 && it >= cum[t + 1]) t++;
       p = it - cum[t];
       const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * t);
-      need = my_row < T.y && row_len[T.x + my_row] > p * kPage;
+      need = wv < T.y && row_len[T.x + wv] > p * kPage;
       if (p < 0) {
         atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
         need = 0;
@@ -72,7 +120,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
         phys = bt_g[(int64_t)T.z * bt_ld + p];
         if (phys < 0 || phys >= n_pages) {
           if (need) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
-          phys = -1;
+          phys = 0;  // a page that exists; nobody scores it
           need = 0;
         }
       }
@@ -84,43 +132,73 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     tcur = __builtin_amdgcn_readlane(t, 63);  // tiles only advance with the items
   };
 
-  PageRegs P[D];
-  int st[D], sp[D];
-  bool sok[D];
-  auto issue = [&](auto kk, int i) {
-    constexpr int K = decltype(kk)::value;
+  int st[P], sp[P];
+  bool sok[P];
+  // copy item i (clamped to the unit's last item) into ring slot S, and note what scoring it
+  // needs; every wave records the item, the loader waves issue one direct load each
+  auto issue = [&](auto ss, int i) {
+    constexpr int S = decltype(ss)::value;
     const bool live = i < n_my;
     const int ii = live ? i : n_my - 1;
     if (ii - tab_base >= 64) fill(ii & ~63);
     const int l = ii - tab_base;
     const int phys = __builtin_amdgcn_readlane(v_phys, l);
-    st[K] = __builtin_amdgcn_readlane(v_tile, l);
-    sp[K] = __builtin_amdgcn_readlane(v_page, l);
-    sok[K] = live && __builtin_amdgcn_readlane(v_need, l) != 0;
-    load_page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);  // a page some row of the tile reads
+    st[S] = __builtin_amdgcn_readlane(v_tile, l);
+    sp[S] = __builtin_amdgcn_readlane(v_page, l);
+    sok[S] = live && __builtin_amdgcn_readlane(v_need, l) != 0;
+    if (wv < 4) {
+      const uint8_t *src = kvp + (int64_t)phys * kPageBytes + 1024 * wv + 64 * (lane & 15) + 16 * (lane >> 4);
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)(slot_keys<S>() + 64 * wv), 16, 0, 0);
+    } else if (wv == 4) {
+      const uint8_t *src = kvs + (int64_t)phys * kPageScaleBytes + 4 * lane;
+      __builtin_amdgcn_global_load_lds(src, (lds_void *)slot_scales<S>(), 4, 0, 0);
+    }
   };
+  // a store that writes nothing (empty range): keeps every wave at one store per item
+  auto idle_store = [&]() { buffer_store_f32(0.f, buffer_view(logits, 0u), 0u); };
+
   RowRegs<NH16, 1> R;
   int qt = -1, row = 0, row_bytes = 0;
-  auto score = [&](auto kk) {
-    constexpr int K = decltype(kk)::value;
-    if (!sok[K]) return;
-    if (st[K] != qt) {  // a new tile: this wave's query row (waits for everything in flight)
-      qt = st[K];
+  auto score = [&](auto ss) {
+    constexpr int S = decltype(ss)::value;
+    if (!sok[S]) {
+      idle_store();
+      return;
+    }
+    if (st[S] != qt) {  // a new tile: this wave's query row (waits for everything in flight)
+      qt = st[S];
       const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * qt);
-      row = T.x + my_row;  // sok implies my_row < T.y
+      row = T.x + wv;  // sok implies wv < T.y
       row_bytes = 4 * max(row_len[row], 0);
       load_rows<NH16, 1>(R, qp, qs, w, row, 1, n_heads, lane);
     }
-    const uint32_t col = (uint32_t)(sp[K] * kPage + lane);
-    const float v = page_logit<NH16, 1, 0>(P[K], R, lane);
+    PageRegs pg;
+#pragma unroll
+    for (int t = 0; t < 4; t++) pg.k[t] = slot_keys<S>()[64 * t + lane];
+    pg.s = slot_scales<S>()[lane];
+    const uint32_t col = (uint32_t)(sp[S] * kPage + lane);
+    const float v = page_logit<NH16, 1, 0>(pg, R, lane);
     buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
   };
 
-  static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
-  for (int i0 = 0; i0 < n_my; i0 += D) {
-    static_for<D>([&](auto kk) {
-      score(kk);
-      issue(kk, i0 + decltype(kk)::value + D);
+  // Prologue: items 0 .. P-2 into slots 0 .. P-2, each followed by an idle store so that a
+  // loader wave issues the same sequence (one load, one store) before every item.
+  static_for<P - 1>([&](auto ss) {
+    issue(ss, decltype(ss)::value);
+    if (loader) idle_store();
+  });
+  for (int i0 = 0; i0 < n_my; i0 += P) {
+    static_for<P>([&](auto ss) {
+      constexpr int S = decltype(ss)::value;
+      // After item i0+S's load this wave issued the loads of the next P-2 items and the
+      // stores of the P-1 items before it, and memory operations complete in issue order:
+      // at most 2P-3 outstanding means the item's copy is in LDS.
+      if (loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * P - 3));
+      __builtin_amdgcn_s_barrier();  // every copy of this item landed; the previous slot is free
+      asm volatile("" ::: "memory");
+      issue(std::integral_constant<int, (S + P - 1) % P>{}, i0 + S + P - 1);
+      score(ss);
+
     });
   }
 }
@@ -130,8 +208,8 @@ static void launch_prefill(hipStream_t st, int n_units, const uint8_t *qp, const
                            int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                            int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched, const int32_t *row_len,
                            float *logits, int64_t ld) {
-  constexpr int NW = kTileRows, D = IFP4_PREFILL_RING;
-  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, D>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
+  constexpr int NW = kTileRows, P = IFP4_PREFILL_RING;
+  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, P>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
                      n_heads, kvp, kvs, n_pages, bt, bt_ld, n_req, n_rows_padded, n_units, sched, sched + 1, row_len,
                      logits, ld);
 }
@@ -174,3 +252,4 @@ extern "C" int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t 
   }
   return launch_status("score_prefill");
 }
+
