@@ -14,18 +14,21 @@
 // ring can be deep): four waves each copy one 1 KiB key tile, a fifth the 256-byte scale
 // block, with lane i fetching exactly the 16 bytes that lane i of every wave later reads as
 // its MFMA operand (same layout as the decode scorer's direct loads), so the LDS reads are
-// linear. Per item the loader waves wait until their copy of the item has landed
-// (vmcnt counting in issue order), the unit meets at a barrier, the slot freed by the
-// previous item is refilled P-1 items ahead, and every wave scores the item from LDS. Each
-// wave keeps a table of 64 items at a time (tile, page, physical page, whether its row
-// reaches the page), built with one round of per-lane loads. Logits past a row's length
-// fall outside the store's range; the query row stays in registers while the wave stays
-// on a tile.
+// linear. Items go in groups of B: per group the loader waves wait until their copies have
+// landed (vmcnt counting in issue order), the unit meets at one barrier, the slots of the
+// previous group are refilled P-B items ahead, and every wave scores its row for the whole
+// group from LDS without further synchronisation. Each wave keeps a table of 64 items at a
+// time (tile, page, physical page, whether its row reaches the page), built with one round
+// of per-lane loads. Logits past a row's length fall outside the store's range; the query
+// row stays in registers while the wave stays on a tile.
 #include "score_common.h"
 
-// pages in the LDS ring of a unit
+// pages in the LDS ring of a unit, and items between the unit's barriers (divides the ring)
 #ifndef IFP4_PREFILL_RING
-#define IFP4_PREFILL_RING 4
+#define IFP4_PREFILL_RING 8
+#endif
+#ifndef IFP4_PREFILL_GROUP
+#define IFP4_PREFILL_GROUP 4
 #endif
 
 namespace ifp4 {
@@ -67,14 +70,14 @@ __device__ __forceinline__ uint32_t *slot_scales() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NH16, int NW, int P>
+template <int NH16, int NW, int P, int B>
 __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
     const int32_t *__restrict__ bt_g, int64_t bt_ld, int n_req, int n_rows_padded, int n_units,
     const int32_t *__restrict__ sched_g, int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g,
     float *__restrict__ logits, int64_t ld) {
-  static_assert(P >= 2 && P <= kPrefillMaxRing && NW >= 5, "ring depth and loader waves");
+  static_assert(P <= kPrefillMaxRing && B >= 1 && P % B == 0 && P / B >= 2 && NW >= 5, "ring, groups, loaders");
   const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
@@ -181,24 +184,33 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
   };
 
-  // Prologue: items 0 .. P-2 into slots 0 .. P-2, each followed by an idle store so that a
-  // loader wave issues the same sequence (one load, one store) before every item.
-  static_for<P - 1>([&](auto ss) {
-    issue(ss, decltype(ss)::value);
-    if (loader) idle_store();
+  // Items go in groups of B; the ring holds G = P / B groups. At the start of group k the
+  // loader waves wait until the group's copies have landed, the unit meets once, the slots
+  // of group k-1 are refilled with group k+G-1, and every wave scores its row for the B
+  // items of group k without further synchronisation.
+  constexpr int G = P / B;
+  // Prologue: groups 0 .. G-2, each followed by B idle stores so that a loader wave issues
+  // the same sequence (B loads, then B stores) before every group.
+  static_for<G - 1>([&](auto gg) {
+    constexpr int GG = decltype(gg)::value;
+    static_for<B>([&](auto bb) { issue(std::integral_constant<int, GG * B + decltype(bb)::value>{}, GG * B + decltype(bb)::value); });
+    if (loader) static_for<B>([&](auto) { idle_store(); });
   });
   for (int i0 = 0; i0 < n_my; i0 += P) {
-    static_for<P>([&](auto ss) {
-      constexpr int S = decltype(ss)::value;
-      // After item i0+S's load this wave issued the loads of the next P-2 items and the
-      // stores of the P-1 items before it, and memory operations complete in issue order:
-      // at most 2P-3 outstanding means the item's copy is in LDS.
-      if (loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * P - 3));
-      __builtin_amdgcn_s_barrier();  // every copy of this item landed; the previous slot is free
+    static_for<G>([&](auto gg) {
+      constexpr int GG = decltype(gg)::value;
+      // After the last load of this group a loader wave issued the stores of the G-1 groups
+      // before it and the loads of the G-2 groups after it, B each, and memory operations
+      // complete in issue order: at most B(2G-3) outstanding means the group is in LDS.
+      if (loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (B * (2 * G - 3)));
+      __builtin_amdgcn_s_barrier();  // the group landed; the previous group's slots are free
       asm volatile("" ::: "memory");
-      issue(std::integral_constant<int, (S + P - 1) % P>{}, i0 + S + P - 1);
-      score(ss);
-
+      constexpr int GR = (GG + G - 1) % G;  // slots of the previous group
+      static_for<B>([&](auto bb) {
+        constexpr int BB = decltype(bb)::value;
+        issue(std::integral_constant<int, GR * B + BB>{}, i0 + (GG + G - 1) * B + BB);
+      });
+      static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}); });
     });
   }
 }
@@ -208,8 +220,8 @@ static void launch_prefill(hipStream_t st, int n_units, const uint8_t *qp, const
                            int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                            int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched, const int32_t *row_len,
                            float *logits, int64_t ld) {
-  constexpr int NW = kTileRows, P = IFP4_PREFILL_RING;
-  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, P>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
+  constexpr int NW = kTileRows, P = IFP4_PREFILL_RING, B = IFP4_PREFILL_GROUP;
+  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, P, B>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
                      n_heads, kvp, kvs, n_pages, bt, bt_ld, n_req, n_rows_padded, n_units, sched, sched + 1, row_len,
                      logits, ld);
 }
