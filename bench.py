@@ -238,6 +238,7 @@ def bench_prefill(torch, ifp4, W, args):
                 steps=len(steps), causal_pairs=pairs, us_per_layer=round(layer_us, 2),
                 schedule_us_per_pass=round(sched_us, 2), layers_sharing_schedule=layers,
                 scorer_us_per_layer=round(scorer_us, 2), keys_scored_per_s=pairs / (layer_us * 1e-6),
+                scorer_keys_per_s=round(pairs / (scorer_us * 1e-6), 1),
                 roofline={"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP4_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)})
 
@@ -264,9 +265,19 @@ def cpu_baseline(W, seconds: float):
             break
     dt = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(done_keys / dt, 1), "unit": "keys/s", "cores": threads, "kind": "oracle",
             "sample": f"{reps} pass(es) of fp64 score + full-sort top-k over one layer of the 8 x 131072 decode "
-                      f"workload ({int(rl.sum())} keys each), cache already written; {dt:.1f} s"}
+                      f"workload ({int(rl.sum())} keys each), cache already written; {dt:.1f} s on {threads} "
+                      f"threads of {model}"}
 
 
 def main():
@@ -348,6 +359,7 @@ def main():
                    "head_dim": 128, "index_topk": m["k"], "layers": args.layers, "page": 64,
                    "units": m["units"]},
         "decode_us_per_layer": round(1e3 * d["ms_per_step"] / args.layers, 3),
+        "decode_scorer_keys_per_s": round(d["meta"]["n_keys"] / (d["scorer_us"] * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(d["achieved_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(d["achieved_gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "score_decode", "launch_us_mean": round(d["scorer_us"], 3),

@@ -213,7 +213,8 @@ def test_device_side_errors_flag_and_skip(ifp4):
 # ---------------------------------------------------------------------------- prefill scores
 
 @pytest.mark.parametrize("which,heads,units", [("prefill_tiny", 16, 512), ("prefill_tiny", 64, 7),
-                                               ("prefill_tiny", 64, 4096)])
+                                               ("prefill_tiny", 64, 4096),
+                                               ("prefill_4req", 64, 512)])  # full size, as benched
 def test_prefill_scores_and_topk(ifp4, which, heads, units):
     case = W.prefill_config(which, heads=heads)
     kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev())
@@ -236,7 +237,7 @@ def test_prefill_scores_and_topk(ifp4, which, heads, units):
 
 # ---------------------------------------------------------------------------- full sizes
 
-@pytest.mark.parametrize("name", ["decode_b1_4k", "decode_b8_128k"])
+@pytest.mark.parametrize("name", ["decode_b1_4k", "decode_b8_128k", "decode_b16_128k", "decode_b8_256k"])
 def test_full_size_decode(ifp4, name):
     case = W.decode_config(name)
     _say(f"full-size {name}: B={case.batch} ctx={int(case.ctx[0])}")
