@@ -325,3 +325,82 @@ def test_topk_rows_sharing_leading_bits(ifp4, n, k):
                    -(5.0 + 45.0 * rng.random(n))]).astype(np.float32)
     rl = np.array([n, n - 1, n // 2 + k, n], np.int32)
     _topk_exact(ifp4, lg, rl, k, n)
+
+
+# ---------------------------------------------------------------------------- graph replay
+
+def test_graph_replay_bitwise_stable(ifp4):
+    """One decode step (schedule, key/query write, scorer, top-k) captured once at fixed
+    addresses and replayed under four context-length vectors written in place: every replay
+    equals an eager run of the same inputs bit for bit (the schedule is what lets a captured
+    graph follow changing lengths). Eager work and synchronizations run between replays."""
+    B, H, k, max_ctx, units = 4, 64, 2048, 20000, 64
+    rng = np.random.default_rng(21)
+    pages = -(-max_ctx // 64)
+    n_pages = B * pages + 8
+    bt_np = rng.permutation(n_pages)[:B * pages].astype(np.int32).reshape(B, pages)
+    ld = pages * 64
+    kp = torch.zeros((n_pages, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((n_pages, 4, 64), dtype=torch.uint8, device=dev())
+    all_slots = (bt_np.astype(np.int64)[:, :, None] * 64 + np.arange(64)).reshape(B, -1)[:, :max_ctx]
+    keys = torch.from_numpy(W.bf16_bits(rng.standard_normal((B * max_ctx, 128)).astype(np.float32)).view(np.int16))
+    ifp4.indexer_fp4_quant_and_cache(keys.view(torch.bfloat16).to(dev()), to_dev(all_slots.reshape(-1).copy()), kp, ks)
+    bt = to_dev(bt_np)
+    ctx = torch.zeros(B, dtype=torch.int32, device=dev())
+    slots = torch.zeros(B, dtype=torch.int64, device=dev())
+    knew = torch.from_numpy(W.bf16_bits(rng.standard_normal((B, 128)).astype(np.float32)).view(np.int16)).view(
+        torch.bfloat16).to(dev())
+    q = torch.from_numpy(W.bf16_bits(rng.standard_normal((B, H, 128)).astype(np.float32)).view(np.int16)).view(
+        torch.bfloat16).to(dev())
+    w = to_dev(rng.random((B, H), dtype=np.float32))
+
+    def buffers():
+        return dict(sched=torch.empty(ifp4.indexer_fp4_decode_sched_bytes(B, 1, units), dtype=torch.uint8, device=dev()),
+                    row_len=torch.empty(B, dtype=torch.int32, device=dev()),
+                    qp=torch.empty((B, H, 64), dtype=torch.uint8, device=dev()),
+                    qs=torch.empty((B, H, 4), dtype=torch.uint8, device=dev()),
+                    logits=torch.full((B, ld), float("nan"), dtype=torch.float32, device=dev()),
+                    top=torch.full((B, k), -7, dtype=torch.int32, device=dev()),
+                    ws=torch.zeros(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 16), dtype=torch.uint8,
+                                   device=dev()))
+
+    def step(o):
+        ifp4.indexer_fp4_decode_schedule(ctx, 1, units, o["sched"], o["row_len"])
+        ifp4.indexer_fp4_quant_and_cache(knew, slots, kp, ks, q, o["qp"], o["qs"])
+        ifp4.indexer_fp4_score_decode(o["qp"], o["qs"], w, kp, ks, bt, 1, o["sched"], units, o["row_len"],
+                                      o["logits"])
+        ifp4.indexer_topk(o["logits"], o["row_len"], ld, k, o["top"], o["ws"])
+
+    def set_ctx(c):
+        ctx.copy_(to_dev(np.asarray(c, np.int32)))
+        slots.copy_(to_dev(all_slots[np.arange(B), np.asarray(c) - 1].copy()))
+
+    g_out, e_out = buffers(), buffers()
+    set_ctx([4096, 100, 17000, 2049])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(g_out)  # warm-up on the capture stream
+        with torch.cuda.graph(graph, stream=side):
+            step(g_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for c in ([4096, 100, 17000, 2049], [20000, 64, 1, 9000], [3000, 19999, 2048, 2047], [65, 12345, 20000, 300]):
+        _say(f"graph replay ctx={c}")
+        set_ctx(c)
+        e_out["logits"].fill_(float("nan"))
+        g_out["logits"].fill_(float("nan"))
+        step(e_out)  # eager, same inputs
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ifp4.sched_error(g_out["sched"]) == 0
+        gl, el = g_out["logits"].cpu().numpy(), e_out["logits"].cpu().numpy()
+        for r in range(B):
+            n = int(c[r])
+            assert np.array_equal(gl[r, :n].view(np.uint32), el[r, :n].view(np.uint32)), f"row {r}: logits differ"
+            assert np.isnan(gl[r, n:]).all()
+        assert np.array_equal(g_out["top"].cpu().numpy(), e_out["top"].cpu().numpy())
+        assert np.array_equal(g_out["row_len"].cpu().numpy(), np.asarray(c, np.int32))
