@@ -68,6 +68,7 @@ def _declare(L):
         "oracle_score": [P, P, P, I32, I64, P, P, P, P, I64, P, I64, P, I64, P],
         "oracle_score_pairs": [P, P, P, I32, P, P, P, P, I64, P, I64, P, P, I64, P],
         "oracle_topk": [P, I64, I64, P, I32, P, I64],
+        "oracle_topk_merge": [P, P, I64, I64, I32, I32, P, I64],
         "oracle_decode_schedule": [P, I32, I32, P, P, P, P, P],
         "oracle_prefill_schedule": [P, P, I32, I32, I32, I32, I32, P, P, P, P, P],
     }
@@ -220,6 +221,16 @@ def topk(s, row_len, k):
     idx = np.full((rows, k), -7, np.int32)
     _check(lib().oracle_topk(_p(s), ld, rows, _p(rl), k, _p(idx), k), "topk")
     return idx
+
+
+def topk_merge(score, index, k):
+    """score float [rows, n_cand], index int32 [rows, n_cand] (< 0: empty) -> int32 [rows, k]."""
+    sc = _c(score, np.float64)
+    ix = _c(index, np.int32)
+    rows, n = sc.shape
+    out = np.full((rows, k), -7, np.int32)
+    _check(lib().oracle_topk_merge(_p(sc), _p(ix), n, rows, n, k, _p(out), k), "topk_merge")
+    return out
 
 
 # ---- schedules ------------------------------------------------------------------------

@@ -319,6 +319,34 @@ int oracle_topk(const double *s, int64_t ld, int64_t n_rows, const int32_t *row_
   return bad ? -1 : 0;
 }
 
+/* Candidate merge for context-parallel decode ([P2] DCP commit: each rank takes a local
+ * top-k over its share of a sequence's pages, the ranks exchange candidates, and a merge
+ * top-k reads the exchanged fp32 scores). For row r the candidates are
+ * (score[r*ld + c], index[r*ld + c]) for c < n_cand; an index < 0 is an empty slot. The
+ * result lists the indices of the min(k, #valid) candidates with the largest score, ties to
+ * the smaller index (R7), in that order; entries past them are -1. */
+int oracle_topk_merge(const double *score, const int32_t *index, int64_t ld, int64_t n_rows, int32_t n_cand,
+                      int32_t k, int32_t *idx, int64_t idx_ld) {
+  if (k <= 0 || idx_ld < k || n_rows < 0 || n_cand < 0 || ld < n_cand) return -1;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t r = 0; r < n_rows; r++) {
+    Cand *c = (Cand *)malloc(sizeof(Cand) * (n_cand > 0 ? (size_t)n_cand : 1));
+    if (!c) { bad = 1; continue; }
+    int32_t n = 0;
+    for (int32_t j = 0; j < n_cand; j++) {
+      if (index[r * ld + j] < 0) continue;
+      c[n].v = score[r * ld + j];
+      c[n].j = index[r * ld + j];
+      n++;
+    }
+    qsort(c, (size_t)n, sizeof(Cand), cand_cmp);
+    for (int32_t i = 0; i < k; i++) idx[r * idx_ld + i] = (i < n) ? c[i].j : -1;
+    free(c);
+  }
+  return bad ? -1 : 0;
+}
+
 /* Even split of n_items over n_units contiguous ranges: unit u starts at
  * floor(u * n_items / n_units). (The pages publish a per-step CTA schedule
  * with a persistent grid of max(floor, rows) units -- [P2] Decode grid floor

@@ -86,6 +86,12 @@ int oracle_score_pairs(const uint8_t *q_packed, const uint8_t *q_scale, const fl
 int oracle_topk(const double *s, int64_t ld, int64_t n_rows, const int32_t *row_len, int32_t k,
                 int32_t *idx, int64_t idx_ld);
 
+/* Candidate merge: among the candidates (score[r*ld + c], index[r*ld + c]), c < n_cand, whose
+ * index is >= 0, idx[r*idx_ld + i], i < k, holds the index of the i-th largest score, ties to
+ * the smaller index; entries past the valid candidates are -1. */
+int oracle_topk_merge(const double *score, const int32_t *index, int64_t ld, int64_t n_rows, int32_t n_cand,
+                      int32_t k, int32_t *idx, int64_t idx_ld);
+
 /* Decode work split: items are (sequence b, page p < ceil(ctx[b]/64)) in
  * b-major order, cum_pages[b] = first item of b (B+1 entries). Unit u covers
  * items [unit_begin[u], unit_begin[u+1]) with unit_begin[u] = floor(u*W/U);

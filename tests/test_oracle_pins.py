@@ -517,3 +517,57 @@ def test_prefill_schedule_covers_rows_and_pages_once(which):
         for r in range(st.n_rows_padded):
             npg = (int(rl[r]) + 63) // 64
             assert (need[r, :npg] == 1).all() and not need[r, npg:].any()
+
+
+# ---------------------------------------------------------------------------- candidate merge
+
+def _shard_candidates(s, n, W, k):
+    """Split columns [0, n) of a row by pages over W shards (page p on shard p % W), take
+    each shard's oracle top-k in its local column order, and map it back to global columns;
+    returns (scores, indices) of the W*k candidates (-1 = empty)."""
+    sc = np.zeros(W * k)
+    ix = np.full(W * k, -1, np.int32)
+    cols = np.arange(n)
+    for sh in range(W):
+        g = cols[(cols // 64) % W == sh]  # global columns of the shard, ascending
+        if g.size == 0:
+            continue
+        top = oracle.topk(s[g][None, :], np.array([g.size], np.int32), k)[0]
+        m = top >= 0
+        sc[sh * k: sh * k + m.sum()] = s[g[top[m]]]
+        ix[sh * k: sh * k + m.sum()] = g[top[m]]
+    return sc, ix
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_topk_merge_of_shard_topks_equals_the_unsharded_topk(W):
+    """Context parallelism is exact: merging the shards' local top-k candidates gives the
+    unsharded top-k, order and tie-break included (ties cross shard boundaries here)."""
+    rng = np.random.default_rng(W)
+    k = 50
+    for n in [1, 49, 50, 64, 65, 300, 1000, 2047]:
+        for kind in range(3):
+            if kind == 0:
+                s = rng.standard_normal(n)
+            elif kind == 1:
+                s = rng.integers(-3, 4, n).astype(np.float64)  # heavy ties
+            else:
+                s = np.full(n, 2.5)  # one value
+            want = oracle.topk(s[None, :], np.array([n], np.int32), k)[0]
+            sc, ix = _shard_candidates(s, n, W, k)
+            got = oracle.topk_merge(sc[None, :], ix[None, :], k)[0]
+            assert np.array_equal(got, want), (W, n, kind)
+
+
+def test_topk_merge_skips_empty_slots_and_pads():
+    sc = np.array([[5.0, 9.0, 1.0, 9.0, 7.0, 0.0], [1.0, 2.0, 3.0, 4.0, 5.0, 6.0]])
+    ix = np.array([[10, -1, 3, 7, -1, 2], [-1, -1, -1, -1, -1, -1]], np.int32)
+    got = oracle.topk_merge(sc, ix, 4)
+    # valid: (5,10) (1,3) (9,7) (0,2): by score desc -> 7, 10, 3, 2
+    assert got[0].tolist() == [7, 10, 3, 2]
+    assert got[1].tolist() == [-1, -1, -1, -1]
+    got = oracle.topk_merge(sc[:1], ix[:1], 6)
+    assert got[0].tolist() == [7, 10, 3, 2, -1, -1]
+    # equal scores: the smaller index first
+    got = oracle.topk_merge(np.array([[1.0, 1.0, 1.0]]), np.array([[8, 3, 5]], np.int32), 2)
+    assert got[0].tolist() == [3, 5]
