@@ -243,6 +243,21 @@ def bench_prefill(torch, ifp4, W, args):
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)})
 
 
+def bench_dcp_merge(torch, ifp4, args, shards=4, rows=8, k=2048):
+    """Merge of `shards` local top-k candidate lists per row (context-parallel decode on one
+    GPU's share; the exchange itself is not timed): one launch per layer."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    sc = torch.randn((rows, shards * k), generator=g, device=dev, dtype=torch.float32)
+    ix = torch.randperm(rows * shards * k * 2, generator=g, device=dev)[: rows * shards * k].view(rows, -1).int()
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    ifp4.indexer_topk_merge(sc, ix, k, out)
+    graph = capture(torch, lambda: [ifp4.indexer_topk_merge(sc, ix, k, out) for _ in range(args.layers)])
+    us = 1e3 * timed_replays(torch, graph, args.steps) / args.layers
+    return {"shards": shards, "rows": rows, "candidates_per_row": shards * k, "k": k, "us_per_layer": round(us, 3)}
+
+
 def cpu_baseline(W, seconds: float):
     """The oracle on the decode workload's first sequences: score every key (fp64) and run
     the full-sort top-k, repeated until `seconds` of work; returns keys scored per second."""
@@ -323,6 +338,7 @@ def main():
     print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scorer {d['scorer_us']:.2f} us "
           f"({d['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
     pre = None
+    dcp = bench_dcp_merge(torch, ifp4, args)
     if not args.no_prefill:
         pre = bench_prefill(torch, ifp4, W, args)
         print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us",
@@ -366,6 +382,7 @@ def main():
                      "alg_bytes_per_launch": d["alg_bytes"]},
         "cpu_baseline": cpu,
         "prefill": pre,
+        "dcp_merge": dcp,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

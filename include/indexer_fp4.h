@@ -216,6 +216,23 @@ int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const i
                  int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld,
                  void *workspace, int64_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------------
+ * Candidate merge for context-parallel decode ([P2] DCP commit: each rank takes a local
+ * top-k over its share of a sequence's pages, the ranks exchange candidates, and a merge
+ * top-k reads the exchanged fp32 scores).
+ * For row r, among the candidates (cand_score[r][c], cand_index[r][c]), c < n_cand, whose
+ * index is >= 0 (an index < 0 is an empty slot), topk_idx[r][0 .. m) receives the indices
+ * of the m = min(k, #valid) candidates with the largest score, ties to the smaller index
+ * (as indexer_topk), in ascending index order; topk_idx[r][m .. k) is -1. Valid indices of
+ * a row must be distinct.
+ *   cand_score float [n_rows][cand_ld], cand_index int32 [n_rows][cand_ld]
+ * Errors: EINVAL (k outside 1..4096, n_cand outside 0..16384, cand_ld < n_cand,
+ * n_rows < 0, NULL pointers), ENOSPC (topk_ld < k), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int indexer_topk_merge(const float *cand_score, const int32_t *cand_index, int64_t cand_ld,
+                       int32_t n_rows, int32_t n_cand, int32_t k, int32_t *topk_idx,
+                       int64_t topk_ld, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

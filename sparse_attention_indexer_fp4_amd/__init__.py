@@ -34,6 +34,7 @@ EXPORTS = (
     "indexer_fp4_score_decode",
     "indexer_fp4_score_prefill",
     "indexer_topk_workspace_bytes",
+    "indexer_topk_merge",
     "indexer_topk",
 )
 
@@ -60,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P], ctypes.c_int),
         "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
         "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P], ctypes.c_int),
+        "indexer_topk_merge": ([P, P, I64, I32, I32, I32, P, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -209,6 +211,21 @@ def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None):
     _check(lib.indexer_topk(
         _ptr(logits), logits.stride(0), logits.shape[0], _ptr(row_len), max_len, k, _ptr(topk_idx),
         topk_idx.stride(0), _ptr(workspace), ws_bytes, _stream(logits)))
+
+
+def indexer_topk_merge(cand_score, cand_index, k, topk_idx):
+    """cand_score fp32 [rows, C], cand_index int32 [rows, C] (< 0: empty slot);
+    topk_idx int32 [rows, >=k] (output): the k best candidates' indices, ascending."""
+    _dev(cand_score, "cand_score", torch.float32)
+    _dev(cand_index, "cand_index", torch.int32)
+    _dev(topk_idx, "topk_idx", torch.int32, contiguous=False)
+    if cand_score.shape != cand_index.shape:
+        raise ValueError("cand_score and cand_index must have the same shape")
+    if topk_idx.stride(1) != 1:
+        raise ValueError("topk_idx rows must be contiguous")
+    rows, n = cand_score.shape
+    _check(lib.indexer_topk_merge(_ptr(cand_score), _ptr(cand_index), n, rows, n, k, _ptr(topk_idx),
+                                  topk_idx.stride(0), _stream(cand_score)))
 
 
 # ---- schedule-buffer inspection (host copies; for tests and diagnostics) -----------------

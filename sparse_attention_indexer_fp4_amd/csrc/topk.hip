@@ -737,6 +737,177 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   for (int j = max(total, 0) + tid; j < k; j += kFinishThreads) o[j] = -1;
 }
 
+// ---------------------------------------------------------------------------------------
+// Candidate merge for context-parallel decode ("Score a DSA sparse indexer in FP4", DCP
+// commit: every rank takes a local top-k over its share of a sequence's pages, the ranks
+// exchange (score, index) candidates and a merge top-k reads the exchanged fp32 scores).
+// One 1024-thread workgroup per row: the row's candidates are staged in LDS with the range
+// of their keys, a 1024-bin histogram spread over that range finds the bin of the k-th best,
+// the few candidates in it are ranked by counting (ties to the smaller index; radix select
+// when there are many), and the chosen indices are sorted ascending by a bitonic sort in LDS.
+constexpr int kMergeThreads = 1024;
+constexpr int kMergeWaves = kMergeThreads / 64;
+constexpr int kMergeMaxCand = 16384;
+constexpr int kMergeMaxK = 4096;
+constexpr int kMergeBins = 1024;
+
+__host__ __device__ inline int merge_sort_len(int k) {  // smallest power of two >= k
+  int p = 1;
+  while (p < k) p <<= 1;
+  return p;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *__restrict__ score,
+                                                                  const int32_t *__restrict__ index, int64_t ld,
+                                                                  int n_cand, int k, int32_t *__restrict__ out,
+                                                                  int64_t out_ld) {
+  extern __shared__ uint32_t lds[];  // keys[n_cand], indices[n_cand], sort buffer[merge_sort_len(k)]
+  __shared__ uint32_t hist[kMergeBins];
+  __shared__ uint32_t chosen[kMergeMaxCand / 32];  // chosen candidates of bin b, by position
+  __shared__ uint32_t ckey[kShortRank], cpos[kShortRank];
+  __shared__ int s_scan[3 * kMergeWaves], s_misc[8];
+  __shared__ uint32_t s_mm[2 * kMergeWaves];
+  __shared__ int s_gathered;  // indices gathered for the sort (block_select uses s_misc[4..6])
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t *keys = lds, *idx = lds + n_cand, *buf = lds + 2 * n_cand;
+  const int P2 = merge_sort_len(k);
+  // stage; an empty slot (index < 0) gets index 0xFFFFFFFF and never counts
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  int nv = 0;
+  for (int c = tid; c < n_cand; c += kMergeThreads) {
+    const int32_t ix = index[r * ld + c];
+    const bool ok = ix >= 0;
+    const uint32_t key = order_key(score[r * ld + c]);
+    keys[c] = key;
+    idx[c] = ok ? (uint32_t)ix : 0xFFFFFFFFu;
+    if (ok) {
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
+      nv++;
+    }
+  }
+  for (int i = tid; i < kMergeBins; i += kMergeThreads) hist[i] = 0u;
+  for (int i = tid; i < (n_cand + 31) / 32; i += kMergeThreads) chosen[i] = 0u;
+  if (tid == 0) {
+    s_misc[3] = 0;  // bin-b candidates listed
+    s_gathered = 0;
+  }
+  block_minmax<kMergeThreads>(kmin, kmax, s_mm);
+  nv = block_suffix_sum<kMergeThreads>(nv, s_scan);
+  if (tid == 0) s_misc[7] = nv;
+  __syncthreads();
+  nv = s_misc[7];
+  const int take_n = min(k, nv);
+  const int bl = 32 - __clz((int)(kmax - kmin));
+  const int sh = bl > 10 ? bl - 10 : 0;
+  auto digit = [&](uint32_t key) { return min((key - kmin) >> sh, (uint32_t)(kMergeBins - 1)); };
+  uint32_t b = 0;
+  if (nv > k) {
+    for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
+      const int c = c0 + tid;
+      const bool ok = c < n_cand && idx[c] != 0xFFFFFFFFu;
+      hist_put(hist, ok ? digit(keys[c]) : 0u, ok);
+    }
+    __syncthreads();
+    {
+      const uint32_t h = hist[tid];  // one bin per thread
+      const int acc = block_suffix_sum<kMergeThreads>((int)h, s_scan);
+      if (acc >= k && acc - (int)h < k) {
+        s_misc[0] = tid;
+        s_misc[1] = k - (acc - (int)h);
+        s_misc[2] = (int)h;
+      }
+      __syncthreads();
+    }
+    b = (uint32_t)s_misc[0];
+    const int need = s_misc[1], nb = s_misc[2];
+    if (nb <= kShortRank) {
+      for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
+        const int c = c0 + tid;
+        const bool in_b = c < n_cand && idx[c] != 0xFFFFFFFFu && digit(keys[c]) == b;
+        const uint64_t m = __ballot(in_b);
+        if (m) {
+          int at = 0;
+          if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
+          at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+          if (in_b && at < nb) {
+            ckey[at] = keys[c];
+            cpos[at] = (uint32_t)c;
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < nb) {
+        const uint32_t key = ckey[tid], ix = idx[cpos[tid]];
+        int rank = 0;
+        for (int g = 0; g < nb; g++) {
+          const uint32_t kg = ckey[g];
+          rank += (kg > key || (kg == key && idx[cpos[g]] < ix)) ? 1 : 0;
+        }
+        if (rank < need) atomicOr(&chosen[cpos[tid] >> 5], 1u << (cpos[tid] & 31));
+      }
+    } else {
+      const uint32_t other = b == 0 ? 0xFFFFFFFFu : 0u;
+      auto off_of = [&](int c) {
+        return (idx[c] != 0xFFFFFFFFu && digit(keys[c]) == b) ? keys[c] - kmin : other;
+      };
+      int rem = need, n_eq = 0;
+      const uint32_t T = kmin + block_select<kMergeThreads>(n_cand, off_of, b << sh, top_bits_mask(32 - sh), sh,
+                                                            &rem, &n_eq, hist, s_scan, s_misc + 4);
+      uint32_t cut = 0xFFFFFFFFu;  // keys equal to T with index <= cut are kept
+      if (rem < n_eq) {            // the rem smallest indices: the largest 2^31 - 1 - index
+        int rem2 = rem, n_eq2 = 0;
+        const uint32_t sel = block_select<kMergeThreads>(
+            n_cand,
+            [&](int c) { return (idx[c] != 0xFFFFFFFFu && keys[c] == T) ? (0x7FFFFFFFu - idx[c]) : 0xFFFFFFFFu; },
+            0u, 0x80000000u, 31, &rem2, &n_eq2, hist, s_scan, s_misc + 4);
+        cut = 0x7FFFFFFFu - sel;
+      }
+      for (int c = tid; c < n_cand; c += kMergeThreads) {
+        const uint32_t key = keys[c];
+        if (idx[c] != 0xFFFFFFFFu && digit(key) == b && (key > T || (key == T && idx[c] <= cut)))
+          atomicOr(&chosen[c >> 5], 1u << (c & 31));
+      }
+    }
+    __syncthreads();
+  }
+  // gather the chosen indices (any order), pad to a power of two, sort ascending
+  for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
+    const int c = c0 + tid;
+    bool t = c < n_cand && idx[c] != 0xFFFFFFFFu;
+    if (t && nv > k) t = digit(keys[c]) > b || ((chosen[c >> 5] >> (c & 31)) & 1u);
+    const uint64_t m = __ballot(t);
+    if (m) {
+      int at = 0;
+      if (lane == 0) at = atomicAdd(&s_gathered, __popcll(m));
+      at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
+      if (t && at < take_n) buf[at] = idx[c];
+    }
+  }
+  __syncthreads();
+  for (int i = take_n + tid; i < P2; i += kMergeThreads) buf[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  for (int size = 2; size <= P2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P2; i += kMergeThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint32_t a = buf[i], c = buf[j];
+          const bool up = (i & size) == 0;
+          if ((a > c) == up) {
+            buf[i] = c;
+            buf[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t *o = out + r * out_ld;
+  for (int j = tid; j < k; j += kMergeThreads) o[j] = j < take_n ? (int32_t)buf[j] : -1;
+}
+
 }  // namespace ifp4
 
 using namespace ifp4;
@@ -804,4 +975,33 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   hipLaunchKernelGGL(topk_finish_kernel, dim3(n_rows), dim3(kFinishThreads), lds, st, row_len, max_len, k, ws,
                      n_rows, topk_idx, topk_ld);
   return launch_status("topk");
+}
+
+extern "C" int indexer_topk_merge(const float *cand_score, const int32_t *cand_index, int64_t cand_ld,
+                                  int32_t n_rows, int32_t n_cand, int32_t k, int32_t *topk_idx, int64_t topk_ld,
+                                  void *stream) {
+  clear_error();
+  if (k <= 0 || k > kMergeMaxK || n_rows < 0 || n_cand < 0 || n_cand > kMergeMaxCand)
+    return fail(INDEXER_FP4_EINVAL, "topk_merge: k=%d in 1..%d, n_rows=%d >= 0, n_cand=%d in 0..%d", k, kMergeMaxK,
+                n_rows, n_cand, kMergeMaxCand);
+  if (cand_ld < n_cand)
+    return fail(INDEXER_FP4_EINVAL, "topk_merge: cand_ld=%lld < n_cand=%d", (long long)cand_ld, n_cand);
+  if (topk_ld < k) return fail(INDEXER_FP4_ENOSPC, "topk_merge: topk_ld=%lld < k=%d", (long long)topk_ld, k);
+  if (n_rows > 0 && (!topk_idx || (n_cand > 0 && (!cand_score || !cand_index))))
+    return fail(INDEXER_FP4_EINVAL, "topk_merge: NULL pointer");
+  int rc = check_device();
+  if (rc) return rc;
+  if (n_rows == 0) return INDEXER_FP4_OK;
+  static bool lds_set = false;
+  if (!lds_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)topk_merge_kernel,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             4 * (2 * kMergeMaxCand + merge_sort_len(kMergeMaxK)));
+    if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk_merge: hipFuncSetAttribute: %s", hipGetErrorString(e));
+    lds_set = true;
+  }
+  const size_t lds = 4 * ((size_t)2 * n_cand + (size_t)merge_sort_len(k));
+  hipLaunchKernelGGL(topk_merge_kernel, dim3(n_rows), dim3(kMergeThreads), lds, (hipStream_t)stream, cand_score,
+                     cand_index, cand_ld, n_cand, k, topk_idx, topk_ld);
+  return launch_status("topk_merge");
 }

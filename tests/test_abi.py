@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
@@ -91,6 +91,12 @@ def test_host_argument_errors(L):
     assert L.indexer_topk(None, 100, 4, None, 100, 32, None, 16, None, 0, None) == -2
     assert "topk_ld=16" in _err(L)
     assert L.indexer_topk(None, 100, 4, None, 200, 32, None, 32, None, 0, None) == -1
+    L.indexer_topk_merge.argtypes = [P, P, I64, I32, I32, I32, P, I64, P]
+    assert L.indexer_topk_merge(None, None, 16, 2, 16, 0, None, 16, None) == -1
+    assert L.indexer_topk_merge(None, None, 16, 2, 16, 8192, None, 8192, None) == -1
+    assert L.indexer_topk_merge(None, None, 8, 2, 16, 8, None, 8, None) == -1
+    assert "cand_ld=8" in _err(L)
+    assert L.indexer_topk_merge(P(16), P(16), 16, 2, 16, 8, P(16), 4, None) == -2
     L.indexer_fp4_quant_and_cache.argtypes = [P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P]
     assert L.indexer_fp4_quant_and_cache(None, 4, 128, None, None, None, 1, None, 0, 0, None, None, None) == -1
     assert L.indexer_fp4_quant_and_cache(P(16), 4, 100, P(16), P(16), P(16), 1, None, 0, 0, None, None, None) == -1

@@ -404,3 +404,72 @@ def test_graph_replay_bitwise_stable(ifp4):
             assert np.isnan(gl[r, n:]).all()
         assert np.array_equal(g_out["top"].cpu().numpy(), e_out["top"].cpu().numpy())
         assert np.array_equal(g_out["row_len"].cpu().numpy(), np.asarray(c, np.int32))
+
+
+# ---------------------------------------------------------------------------- context parallelism
+
+@pytest.mark.parametrize("rows,n_cand,k", [(8, 8192, 2048), (4, 16384, 2048), (6, 300, 64), (3, 100, 4096)])
+def test_topk_merge_matches_oracle(ifp4, rows, n_cand, k):
+    rng = np.random.default_rng(n_cand + k)
+    sc = rng.standard_normal((rows, n_cand)).astype(np.float32)
+    sc[1] = np.round(sc[1] * 4) / 4  # heavy ties
+    sc[2] = 1.5                      # one value
+    ix = rng.permutation(2 * rows * n_cand)[: rows * n_cand].reshape(rows, n_cand).astype(np.int32)
+    ix[0, ::3] = -1                  # empty slots
+    if rows > 3:
+        ix[3, :] = -1                # no candidate at all
+    _say(f"topk_merge rows={rows} n_cand={n_cand} k={k}")
+    top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk_merge(to_dev(sc), to_dev(ix), k, top)
+    got = top.cpu().numpy()
+    want = oracle.topk_merge(sc.astype(np.float64), ix, k)
+    for r in range(rows):
+        m = int((want[r] >= 0).sum())
+        assert list(got[r][:m]) == sorted(want[r][:m].tolist()), f"row {r}"
+        assert (got[r][m:] == -1).all()
+
+
+def test_context_parallel_decode_on_one_gpu(ifp4):
+    """Context parallelism on one GPU's share: W = 4 page-interleaved shards of every
+    sequence are scored by the scorer through their own block tables, each takes a local
+    top-k, the candidates are exchanged (stubbed as a device gather) and merged: the result
+    equals the unsharded decode top-k exactly."""
+    Wn, k, units = 4, 2048, 512
+    case = W.decode_case([20000, 9000, 131, 2049 + 64 * 9], heads=64, topk=k, seed=31)
+    B = case.batch
+    g = gpu_decode(case)  # unsharded: cache write, schedule, score, top-k
+    kp, ks, qp, qs = g["kp"], g["ks"], g["qp"], g["qs"]
+    wv = to_dev(case.w)
+    bt = case.block_table
+    pages = -(-case.ctx // 64)
+    lw = -(-bt.shape[1] // Wn)  # local table width
+    cand_s = torch.full((B, Wn * k), 0.0, dtype=torch.float32, device=dev())
+    cand_i = torch.full((B, Wn * k), -1, dtype=torch.int32, device=dev())
+    for s in range(Wn):
+        lbt = np.full((B, lw), -1, np.int32)
+        lctx = np.zeros(B, np.int32)
+        for b in range(B):
+            own = np.arange(s, pages[b], Wn)  # this shard's global pages of sequence b
+            lbt[b, : own.size] = bt[b, own]
+            lctx[b] = sum(min(64, int(case.ctx[b]) - 64 * int(p)) for p in own)
+        _say(f"shard {s}: local ctx {lctx.tolist()}")
+        lld = lw * 64
+        sched = torch.empty(ifp4.indexer_fp4_decode_sched_bytes(B, 1, units), dtype=torch.uint8, device=dev())
+        rl = torch.empty(B, dtype=torch.int32, device=dev())
+        ifp4.indexer_fp4_decode_schedule(to_dev(lctx), 1, units, sched, rl)
+        lg = torch.full((B, lld), float("nan"), dtype=torch.float32, device=dev())
+        ifp4.indexer_fp4_score_decode(qp, qs, wv, kp, ks, to_dev(lbt), 1, sched, units, rl, lg)
+        ltop = torch.full((B, k), -1, dtype=torch.int32, device=dev())
+        ws = torch.zeros(max(ifp4.indexer_topk_workspace_bytes(B, lld, k), 16), dtype=torch.uint8, device=dev())
+        ifp4.indexer_topk(lg, rl, lld, k, ltop, ws)
+        assert ifp4.sched_error(sched) == 0
+        # the exchange: scores and global columns of the local candidates
+        li = ltop.long()
+        ok = li >= 0
+        sc = torch.gather(lg, 1, li.clamp(min=0))
+        gi = ((li // 64) * Wn + s) * 64 + li % 64
+        cand_s[:, s * k:(s + 1) * k] = torch.where(ok, sc, torch.zeros_like(sc))
+        cand_i[:, s * k:(s + 1) * k] = torch.where(ok, gi, torch.full_like(gi, -1)).int()
+    merged = torch.full((B, k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk_merge(cand_s, cand_i, k, merged)
+    assert np.array_equal(merged.cpu().numpy(), g["top"].cpu().numpy())
