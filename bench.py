@@ -91,6 +91,9 @@ def build_decode(torch, ifp4, W, layers, units, seed):
         logits=torch.empty((B, ld), dtype=torch.float32, device=dev),
         top=torch.empty((B, k), dtype=torch.int32, device=dev),
         ws=torch.zeros(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 1), dtype=torch.uint8, device=dev),
+        # first-digit histograms: filled by each layer's scorer, consumed and re-zeroed by its top-k
+        hist=ifp4.row_histogram(B, dev),
+        hist_scorer=ifp4.row_histogram(B, dev),  # the scorer-only graph's (never read)
     )
     torch.cuda.synchronize()
     meta = dict(B=B, H=H, k=k, ctx=int(ctx[0]), n_keys=int(ctx.astype(np.int64).sum()), n_pages_read=need,
@@ -106,15 +109,15 @@ def decode_step(ifp4, L, S, meta):
         ifp4.indexer_fp4_quant_and_cache(lay["knew"], S["new_slots"], lay["kp"], lay["ks"], lay["q"], lay["qp"],
                                          lay["qs"])
         ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
-                                      units, S["row_len"], S["logits"])
-        ifp4.indexer_topk(S["logits"], S["row_len"], ld, k, S["top"], S["ws"])
+                                      units, S["row_len"], S["logits"], S["hist"])
+        ifp4.indexer_topk(S["logits"], S["row_len"], ld, k, S["top"], S["ws"], S["hist"])
 
 
 def decode_scorers(ifp4, L, S, meta):
-    """The step's 21 scorer launches alone (one per layer cache)."""
+    """The step's 21 scorer launches alone (one per layer cache), histogram included."""
     for lay in L:
         ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
-                                      meta["units"], S["row_len"], S["logits"])
+                                      meta["units"], S["row_len"], S["logits"], S["hist_scorer"])
 
 
 def capture(torch, fn):

@@ -161,9 +161,14 @@ int indexer_fp4_prefill_schedule(const int32_t *cu_rows, const int32_t *start_po
  * pages through block_table[b]. Columns >= row_len[r] are not written.
  *   sched, row_len  as written by indexer_fp4_decode_schedule for the same batch,
  *                   next_n and n_units (sched's error word may be updated)
+ *   row_hist        optional (NULL: none), uint32 [batch*next_n][4096], 16-byte aligned,
+ *                   zero-filled before its first use: the scorer adds the histogram of
+ *                   every written logit's top 12 order-key bits (layout private to the
+ *                   library), which indexer_topk takes instead of building its own and
+ *                   leaves zero-filled again.
  * Errors: EINVAL (n_heads not a multiple of 16 or above 128, batch/next_n/n_units that
- * are not those of the schedule's sizes, negative sizes), ENOSPC (logits_ld < 64*bt_ld
- * or bt_ld <= 0), EARCH, EHIP.
+ * are not those of the schedule's sizes, negative sizes, misaligned row_hist), ENOSPC
+ * (logits_ld < 64*bt_ld or bt_ld <= 0), EARCH, EHIP.
  * --------------------------------------------------------------------------------- */
 int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale,
                              const float *weights, int32_t n_heads, const uint8_t *kv_packed,
@@ -171,7 +176,7 @@ int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale,
                              const int32_t *block_table, int64_t bt_ld, int32_t batch,
                              int32_t next_n, void *sched, int32_t n_units,
                              const int32_t *row_len, float *logits, int64_t logits_ld,
-                             void *stream);
+                             uint32_t *row_hist, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Prefill scorer ([P2] commit message: the FP4 prefill variant; [P1] section 3: the
@@ -207,14 +212,19 @@ int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
  *              zero-filled again, so one buffer serves any number of calls on one
  *              stream. Calls that share it must not overlap; after an EHIP error zero
  *              it again.
- * Errors: EINVAL (k <= 0, n_rows < 0, max_len < 0, max_len > 2^20 with k < max_len),
- * ENOSPC (topk_ld < k, workspace too small), EARCH, EHIP. Rows longer than max_len
- * are clamped to max_len (device-side; max_len must not exceed logits_ld).
+ *   row_hist   optional (NULL: none): the histogram indexer_fp4_score_decode filled for
+ *              exactly these logits and rows; it replaces one pass of this call and is
+ *              left zero-filled. A histogram of other logits gives a meaningless (though
+ *              in-bounds, -1 padded) selection.
+ * Errors: EINVAL (k <= 0, n_rows < 0, max_len < 0, max_len > 2^20 with k < max_len,
+ * misaligned row_hist), ENOSPC (topk_ld < k, workspace too small), EARCH, EHIP. Rows
+ * longer than max_len are clamped to max_len (device-side; max_len must not exceed
+ * logits_ld).
  * --------------------------------------------------------------------------------- */
 int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len, int32_t k);
 int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
                  int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld,
-                 void *workspace, int64_t ws_bytes, void *stream);
+                 void *workspace, int64_t ws_bytes, uint32_t *row_hist, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Candidate merge for context-parallel decode ([P2] DCP commit: each rank takes a local

@@ -57,10 +57,10 @@ def _load() -> ctypes.CDLL:
         "indexer_fp4_decode_schedule": ([P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32], I64),
         "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
-        "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P], ctypes.c_int),
+        "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P], ctypes.c_int),
         "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
-        "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P], ctypes.c_int),
+        "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P, P], ctypes.c_int),
         "indexer_topk_merge": ([P, P, I64, I32, I32, I32, P, I64, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -150,9 +150,12 @@ def indexer_fp4_prefill_schedule(cu_rows, start_pos, n_rows_padded, n_units, sch
 
 
 def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched, n_units,
-                             row_len, logits):
+                             row_len, logits, row_hist=None):
     """q_packed [B*next_n, H, 64], q_scale [B*next_n, H, 4], weights fp32 [B*next_n, H],
-    block_table int32 [B, W], logits fp32 [B*next_n, LD] (row stride logits.stride(0))."""
+    block_table int32 [B, W], logits fp32 [B*next_n, LD] (row stride logits.stride(0)).
+
+    row_hist: optional int32 [B*next_n, 4096] (zero-filled before first use; see
+    row_histogram) that the scorer fills for indexer_topk."""
     _dev(q_packed, "q_packed", torch.uint8)
     _dev(q_scale, "q_scale", torch.uint8)
     _dev(weights, "weights", torch.float32)
@@ -165,10 +168,11 @@ def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, bl
     if logits.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
     batch, bt_ld = block_table.shape
+    _check_hist(row_hist, batch * next_n)
     _check(lib.indexer_fp4_score_decode(
         _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
         kv_packed.shape[0], _ptr(block_table), bt_ld, batch, next_n, _ptr(sched), n_units, _ptr(row_len),
-        _ptr(logits), logits.stride(0), _stream(logits)))
+        _ptr(logits), logits.stride(0), _ptr(row_hist), _stream(logits)))
 
 
 def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, sched, n_units,
@@ -193,24 +197,42 @@ def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, b
         _ptr(logits), logits.stride(0), _stream(logits)))
 
 
+HIST_BINS = 4096
+
+
+def row_histogram(n_rows: int, device="cuda"):
+    """A zeroed per-row histogram for indexer_fp4_score_decode / indexer_topk."""
+    return torch.zeros(n_rows, HIST_BINS, dtype=torch.int32, device=device)
+
+
+def _check_hist(row_hist, n_rows):
+    if row_hist is None:
+        return
+    _dev(row_hist, "row_hist", torch.int32)
+    if row_hist.numel() < n_rows * HIST_BINS:
+        raise ValueError(f"row_hist holds {row_hist.numel()} words, needs {n_rows} x {HIST_BINS}")
+
+
 def indexer_topk_workspace_bytes(n_rows: int, max_len: int, k: int) -> int:
     return int(lib.indexer_topk_workspace_bytes(n_rows, max_len, k))
 
 
-def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None):
+def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None, row_hist=None):
     """logits fp32 [rows, LD]; row_len int32 [rows]; topk_idx int32 [rows, >=k] (output).
 
     workspace: uint8 device buffer of indexer_topk_workspace_bytes(...) bytes, zero-filled
-    before its first use (each successful call leaves it zeroed again)."""
+    before its first use (each successful call leaves it zeroed again).
+    row_hist: the histogram indexer_fp4_score_decode filled for these logits (left zeroed)."""
     _dev(logits, "logits", torch.float32, contiguous=False)
     _dev(row_len, "row_len", torch.int32)
     _dev(topk_idx, "topk_idx", torch.int32, contiguous=False)
     if logits.stride(1) != 1 or topk_idx.stride(1) != 1:
         raise ValueError("logits and topk_idx rows must be contiguous")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check_hist(row_hist, logits.shape[0])
     _check(lib.indexer_topk(
         _ptr(logits), logits.stride(0), logits.shape[0], _ptr(row_len), max_len, k, _ptr(topk_idx),
-        topk_idx.stride(0), _ptr(workspace), ws_bytes, _stream(logits)))
+        topk_idx.stride(0), _ptr(workspace), ws_bytes, _ptr(row_hist), _stream(logits)))
 
 
 def indexer_topk_merge(cand_score, cand_index, k, topk_idx):

@@ -119,4 +119,35 @@ __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)byte_offset, 0, IFP4_STORE_POLICY);
 }
 
+// Order-preserving 32-bit key of a float (flip the sign bit of non-negative values, invert
+// negative ones; -0.0 is folded onto +0.0): a > b as floats iff key(a) > key(b).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Histograms of a row's logits on the top 12 key bits (the top-k's first digit), kept in
+// device memory by the decode scorer and the top-k: bin b lives at word hist_slot(b), so
+// neighbouring bins sit in different 256-byte blocks and device-wide atomics from many
+// workgroups on the few occupied bins of a row do not queue on one block.
+constexpr int kHistBins = 4096;
+__host__ __device__ constexpr uint32_t hist_slot(uint32_t b) { return ((b & 63u) << 6) | (b >> 6); }
+
+// Histogram increment of digit d for lanes with `ok`. A wave whose counted keys all share
+// one digit (ties, constant rows) adds them with one atomic instead of 64 conflicting ones.
+// Works on LDS and on global memory (through the pointer's address space).
+template <class Ptr>
+__device__ __forceinline__ void hist_put(Ptr h, uint32_t d, bool ok) {
+  const uint64_t act = __ballot(ok);
+  if (act == 0) return;
+  const int first = __ffsll((unsigned long long)act) - 1;
+  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
+  if (__ballot(ok && d != d0) == 0) {
+    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
+  } else if (ok) {
+    atomicAdd(&h[d], 1u);
+  }
+}
+
 }  // namespace ifp4

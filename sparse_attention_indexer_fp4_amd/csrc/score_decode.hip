@@ -22,6 +22,12 @@
 // Each wave keeps D pages in flight in a register ring. A unit with no work exits before
 // any other load (empty CTAs of a large grid must cost nothing: the pages measured 8.75
 // against 2.99 us per layer at 4096 against 512 units).
+//
+// With a row histogram the scorer also counts every logit it writes by its top 12 order-key
+// bits, the first digit of the top-k's selection, so the top-k does not read the logits an
+// extra time: rows of the unit's first sequence (nearly all its items) are counted in LDS and
+// added to the device histogram at the end, the rare pages of later sequences straight into
+// device memory.
 #include "score_common.h"
 
 // waves per unit and pages in flight per wave (tuned on MI355X at 8 x 131072, 64 heads)
@@ -34,12 +40,20 @@
 
 namespace ifp4 {
 
+// A device histogram addressed by bin (hist_slot places the bins).
+struct SlottedHist {
+  uint32_t *g;
+  __device__ __forceinline__ uint32_t &operator[](uint32_t b) const { return g[hist_slot(b)]; }
+};
+
 template <int NH16, int NN, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
     const int32_t *__restrict__ bt_g, int64_t bt_ld, int batch, int n_units, const int32_t *__restrict__ sched_g,
-    int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g, float *__restrict__ logits, int64_t ld) {
+    int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g, float *__restrict__ logits, int64_t ld,
+    uint32_t *__restrict__ row_hist) {
+  extern __shared__ uint32_t uh[];  // [NN][kHistBins] with a row histogram
   const DecodeSchedLayout L(batch, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
@@ -56,12 +70,23 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
     return;
   }
-  // this wave's contiguous share of the unit's items
+  const bool fuse = row_hist != nullptr;
+  const int qs0 = sched[L.unit_seq + u];  // the unit's first sequence: histogram in LDS
+  if (qs0 < 0 || qs0 >= batch) {
+    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
+    return;
+  }
+  if (fuse) {
+    for (int i = threadIdx.x; i < NN * kHistBins / 4; i += NW * 64)
+      reinterpret_cast<uint4 *>(uh)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+  }
+  // this wave's contiguous share of the unit's items (none for some waves of a short unit,
+  // which still meet the workgroup's barriers)
   const int per = (it1 - it0 + NW - 1) / NW;
   const int w0 = it0 + wv * per;
   const int w1 = min(it1, w0 + per);
-  if (w0 >= w1) return;
-  const int n_my = w1 - w0;
+  const int n_my = max(0, w1 - w0);
   const int32_t *cum = sched_g + L.cum;
 
   // Item table, one lane per item, for 64 items at a time: sequence, page index within
@@ -137,39 +162,65 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
       const uint32_t bytes = sok[K] ? 4u * (uint32_t)max(len, 0) : 0u;
       const float v = page_logit<NH16, NN, N>(P[K], R, lane);
       buffer_store_f32(v, buffer_view(logits + r * ld, bytes), 4u * col);
+      if (fuse) {  // exactly the logits stored above
+        const bool kept = 4u * col < bytes;
+        const uint32_t d = order_key(v) >> 20;
+        if (qb == qs0) hist_put(uh + N * kHistBins, d, kept);
+        else hist_put(SlottedHist{row_hist + r * kHistBins}, d, kept);
+      }
     });
   };
 
-  // the first pages are in flight before the query rows are fetched
-  static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
-  for (int i0 = 0; i0 < n_my; i0 += D) {
-    static_for<D>([&](auto kk) {
-      score(kk);
-      issue(kk, i0 + decltype(kk)::value + D);
-    });
+  if (n_my > 0) {
+    // the first pages are in flight before the query rows are fetched
+    static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
+    for (int i0 = 0; i0 < n_my; i0 += D) {
+      static_for<D>([&](auto kk) {
+        score(kk);
+        issue(kk, i0 + decltype(kk)::value + D);
+      });
+    }
+  }
+  if (fuse) {  // occupied bins only, one device atomic each
+    __syncthreads();
+    uint32_t *g = row_hist + (int64_t)qs0 * NN * kHistBins;
+    for (int i = threadIdx.x; i < NN * kHistBins; i += NW * 64) {
+      const uint32_t c = uh[i];
+      if (c) atomicAdd(&g[(i / kHistBins) * kHistBins + hist_slot(i % kHistBins)], c);
+    }
   }
 }
 
 template <int NH16, int NN>
-static void launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
+static int launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
                           int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                           int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len, float *logits,
-                          int64_t ld) {
+                          int64_t ld, uint32_t *row_hist) {
   constexpr int NW = IFP4_DECODE_WAVES, D = IFP4_DECODE_RING;
-  hipLaunchKernelGGL((score_decode_kernel<NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
-                     n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len, logits, ld);
+  constexpr size_t kHistLds = (size_t)NN * kHistBins * 4;
+  static bool lds_set = false;  // raise the dynamic LDS limit once per instantiation
+  if (row_hist && !lds_set) {
+    const hipError_t e = hipFuncSetAttribute((const void *)score_decode_kernel<NH16, NN, NW, D>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHistLds);
+    if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "score_decode: hipFuncSetAttribute: %s", hipGetErrorString(e));
+    lds_set = true;
+  }
+  hipLaunchKernelGGL((score_decode_kernel<NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), row_hist ? kHistLds : 0,
+                     st, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len,
+                     logits, ld, row_hist);
+  return INDEXER_FP4_OK;
 }
 
 template <int NH16>
-static void launch_decode_nn(int next_n, hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs,
-                             const float *w, int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages,
-                             const int32_t *bt, int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len,
-                             float *logits, int64_t ld) {
+static int launch_decode_nn(int next_n, hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs,
+                            const float *w, int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages,
+                            const int32_t *bt, int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len,
+                            float *logits, int64_t ld, uint32_t *row_hist) {
   switch (next_n) {
-    case 1: launch_decode<NH16, 1>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld); break;
-    case 2: launch_decode<NH16, 2>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld); break;
-    case 3: launch_decode<NH16, 3>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld); break;
-    default: launch_decode<NH16, 4>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld); break;
+    case 1: return launch_decode<NH16, 1>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    case 2: return launch_decode<NH16, 2>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    case 3: return launch_decode<NH16, 3>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    default: return launch_decode<NH16, 4>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
   }
 }
 
@@ -181,7 +232,7 @@ extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *
                                         int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
                                         int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
                                         int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
-                                        float *logits, int64_t logits_ld, void *stream) {
+                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
   clear_error();
   if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > INDEXER_FP4_MAX_HEADS)
     return fail(INDEXER_FP4_EINVAL, "n_heads=%d must be a positive multiple of %d and at most %d", n_heads,
@@ -198,6 +249,7 @@ extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *
   if (n_pages > 0 && (!kv_packed || !kv_scale)) return fail(INDEXER_FP4_EINVAL, "score_decode: NULL cache plane");
   if (((uintptr_t)q_packed | (uintptr_t)weights | (uintptr_t)kv_packed | (uintptr_t)kv_scale) % 16 != 0)
     return fail(INDEXER_FP4_EINVAL, "score_decode: q_packed, weights and both planes must be 16-byte aligned");
+  if ((uintptr_t)row_hist % 16 != 0) return fail(INDEXER_FP4_EINVAL, "score_decode: row_hist must be 16-byte aligned");
   int rc = check_device();
   if (rc) return rc;
   if (batch == 0) return INDEXER_FP4_OK;
@@ -205,9 +257,9 @@ extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *
   int32_t *sc = (int32_t *)sched;
   switch (n_heads / 16) {
 #define IFP4_CASE(X) \
-  case X: launch_decode_nn<X>(next_n, st, n_units, q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, batch, sc, row_len, logits, logits_ld); break;
+  case X: rc = launch_decode_nn<X>(next_n, st, n_units, q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, batch, sc, row_len, logits, logits_ld, row_hist); break;
     IFP4_CASE(1) IFP4_CASE(2) IFP4_CASE(3) IFP4_CASE(4) IFP4_CASE(5) IFP4_CASE(6) IFP4_CASE(7) IFP4_CASE(8)
 #undef IFP4_CASE
   }
-  return launch_status("score_decode");
+  return rc ? rc : launch_status("score_decode");
 }

@@ -19,12 +19,6 @@
 
 namespace ifp4 {
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 ranks with +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
@@ -137,20 +131,6 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
   __syncthreads();
 }
 
-// LDS histogram increment of digit d for lanes with `ok`. A wave whose counted keys all share
-// one digit (ties, constant rows) adds them with one atomic instead of 64 conflicting ones.
-__device__ __forceinline__ void hist_put(uint32_t *h, uint32_t d, bool ok) {
-  const uint64_t act = __ballot(ok);
-  if (act == 0) return;
-  const int first = __ffsll((unsigned long long)act) - 1;
-  const uint32_t d0 = __builtin_amdgcn_readlane(d, first);
-  if (__ballot(ok && d != d0) == 0) {
-    if ((int)(threadIdx.x & 63) == first) atomicAdd(&h[d0], (uint32_t)__popcll(act));
-  } else if (ok) {
-    atomicAdd(&h[d], 1u);
-  }
-}
-
 // ---------------------------------------------------------------------------------------
 // Rows up to kShortMax keys: one 256-thread workgroup per row (several rows share a CU). The
 // row's keys are staged in LDS with their smallest and largest value; a 1024-bin histogram
@@ -166,7 +146,8 @@ constexpr int kShortRank = 256;  // bin-b keys ranked by counting
 
 __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len, int64_t max_len,
-                                                                int k, int32_t *__restrict__ out, int64_t out_ld) {
+                                                                int k, uint32_t *__restrict__ row_hist,
+                                                                int32_t *__restrict__ out, int64_t out_ld) {
   extern __shared__ uint32_t keys[];  // max_len words
   __shared__ uint32_t hist[kShortBins];
   __shared__ uint32_t sel[kShortMax / 32];  // chosen bin-b keys, by column
@@ -180,6 +161,8 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
   len64 = len64 < 0 ? 0 : (len64 > max_len ? max_len : len64);
   const int n = (int)len64;
   int32_t *o = out + r * out_ld;
+  if (row_hist)  // not used for rows this short: left zero for the next scorer call
+    for (int i = tid; i < kHistBins; i += kShortThreads) row_hist[r * kHistBins + i] = 0u;
   if (n <= k) {  // short row: every key is kept
     for (int j = tid; j < k; j += kShortThreads) o[j] = j < n ? j : -1;
     return;
@@ -416,7 +399,7 @@ __device__ __forceinline__ void block_suffix_sum3(int &a, int &b, int &c, int *s
 
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len,
-                                                                int64_t max_len, int k, uint32_t *__restrict__ ws) {
+                                                                int64_t max_len, int k, uint32_t *__restrict__ h1) {
   __shared__ uint32_t h[kBins];
   const int r = blockIdx.y, tid = threadIdx.x;
   const int64_t len = clamped_len(row_len, r, max_len);
@@ -435,13 +418,17 @@ __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) hist_put(h, order_key(v[u]) >> 20, start + u * kLongThreads + tid < end);
   __syncthreads();
-  hist_flush<kLongThreads>(h, ws + (int64_t)r * kBins);  // hist1 leads the workspace
+  uint32_t *g = h1 + (int64_t)r * kHistBins;  // occupied bins only, one atomic each
+  for (int b = tid; b < kBins; b += kLongThreads) {
+    const uint32_t c = h[b];
+    if (c) atomicAdd(&g[hist_slot(b)], c);
+  }
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float *__restrict__ logits, int64_t ld,
                                                                    const int32_t *__restrict__ row_len,
                                                                    int64_t max_len, int k, uint32_t *__restrict__ ws,
-                                                                   int rows) {
+                                                                   int rows, const uint32_t *__restrict__ h1) {
   __shared__ uint32_t h2[kBins];
   __shared__ int s_scan[kLongWaves];
   __shared__ int s_bin;
@@ -466,13 +453,13 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   for (int i = tid; i < kBins; i += kLongThreads) h2[i] = 0u;
   // the bin of the row's k-th largest key, from the row's digit-1 histogram
   {
-    const uint32_t *gh = ws + L.hist1 + (int64_t)r * kBins;
+    const uint32_t *gh = h1 + (int64_t)r * kHistBins;
     constexpr int kPer = kBins / kLongThreads;
     uint32_t cnt[kPer];
     int sum = 0;
     if (tid == 0) s_bin = 0;  // published by the scan's barriers
 #pragma unroll
-    for (int i = 0; i < kPer; i++) cnt[i] = gh[kPer * tid + i];
+    for (int i = 0; i < kPer; i++) cnt[i] = gh[hist_slot(kPer * tid + i)];
 #pragma unroll
     for (int i = 0; i < kPer; i++) sum += (int)cnt[i];
     int acc = block_suffix_sum<kLongThreads>(sum, s_scan);  // keys in bins >= kPer*tid
@@ -534,8 +521,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
 
 __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32_t *__restrict__ row_len,
                                                                     int64_t max_len, int k, uint32_t *__restrict__ ws,
-                                                                    int rows, int32_t *__restrict__ out,
-                                                                    int64_t out_ld) {
+                                                                    int rows, uint32_t *__restrict__ h1,
+                                                                    int32_t *__restrict__ out, int64_t out_ld) {
   // dynamic LDS: bitmap of the row's columns, then the candidates of bin b2 (keys, columns)
   extern __shared__ uint32_t lds[];
   __shared__ uint32_t hist[4 * 256];
@@ -545,7 +532,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   const LongWs L(rows, max_len);
   const int chunks = (int)((max_len + kChunk - 1) / kChunk);
   const int64_t cap = (int64_t)chunks * kChunk;
-  uint32_t *g1 = ws + L.hist1 + (int64_t)r * kBins;
+  uint32_t *g1 = h1 + (int64_t)r * kHistBins;
   uint32_t *g2 = ws + L.hist2 + (int64_t)r * kBins;
   const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
   const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
@@ -577,10 +564,17 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   int32_t *o = out + r * out_ld;
   if (len <= k) {  // short row: every key is kept (the other kernels left it alone)
     for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
+#pragma unroll
+    for (int i = 0; i < 4; i++) g1[4 * tid + i] = 0u;  // a scorer-filled histogram counts it
     return;
   }
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
   const bool mine = c < used;
+  if (tid == 0) {  // defaults if no bin matches (a digit-1 histogram of other logits)
+    s_misc[0] = 0;
+    s_misc[1] = 0;
+    s_misc[2] = 0;
+  }
   const int ns = mine ? ns_raw : 0, nc = mine ? nc_raw : 0;
   const int nwords = (int)((len + 31) / 32);
   uint32_t *bitmap = lds;
@@ -924,7 +918,7 @@ extern "C" int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len,
 
 extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
                             int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, void *workspace,
-                            int64_t ws_bytes, void *stream) {
+                            int64_t ws_bytes, uint32_t *row_hist, void *stream) {
   clear_error();
   if (k <= 0 || n_rows < 0 || max_len < 0)
     return fail(INDEXER_FP4_EINVAL, "topk: k=%d must be > 0, n_rows=%d >= 0, max_len=%lld >= 0", k, n_rows,
@@ -940,6 +934,7 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   if (ws_bytes < need)
     return fail(INDEXER_FP4_ENOSPC, "topk: workspace needs %lld bytes, has %lld", (long long)need, (long long)ws_bytes);
   if (n_rows > 0 && (!logits || !row_len || !topk_idx)) return fail(INDEXER_FP4_EINVAL, "topk: NULL pointer");
+  if ((uintptr_t)row_hist % 16 != 0) return fail(INDEXER_FP4_EINVAL, "topk: row_hist must be 16-byte aligned");
   int rc = check_device();
   if (rc) return rc;
   if (n_rows == 0) return INDEXER_FP4_OK;
@@ -960,7 +955,7 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
     // the kernel returns before staging anything)
     const size_t lds = max_len <= kShortMax ? (size_t)(4 * max_len) : 0;
     hipLaunchKernelGGL(topk_row_kernel, dim3(n_rows), dim3(kShortThreads), lds, st, logits, logits_ld, row_len,
-                       max_len, k, topk_idx, topk_ld);
+                       max_len, k, row_hist, topk_idx, topk_ld);
     return launch_status("topk");
   }
   if (!workspace || (uintptr_t)workspace % 16 != 0)
@@ -968,12 +963,15 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   uint32_t *ws = (uint32_t *)workspace;
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
   const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_sub_cap(max_len));
-  hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
-                     max_len, k, ws);
+  // the digit-1 histograms: filled by the decode scorer, or built here in the workspace
+  uint32_t *h1 = row_hist ? row_hist : ws + LongWs(n_rows, max_len).hist1;
+  if (!row_hist)
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
+                       max_len, k, h1);
   hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld,
-                     row_len, max_len, k, ws, n_rows);
+                     row_len, max_len, k, ws, n_rows, h1);
   hipLaunchKernelGGL(topk_finish_kernel, dim3(n_rows), dim3(kFinishThreads), lds, st, row_len, max_len, k, ws,
-                     n_rows, topk_idx, topk_ld);
+                     n_rows, h1, topk_idx, topk_ld);
   return launch_status("topk");
 }
 

@@ -34,7 +34,9 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 # ---------------------------------------------------------------------------- decode
 
-def gpu_decode(case: W.DecodeCase, units=None, ld=None, fill=float("nan"), cache_fill=0, run_topk=True):
+def gpu_decode(case: W.DecodeCase, units=None, ld=None, fill=float("nan"), cache_fill=0, run_topk=True, fused=False):
+    """fused: the scorer fills the top-k's first histogram (out["hist"]: a copy taken between
+    the two calls; out["row_hist"]: the buffer after the top-k)."""
     import sparse_attention_indexer_fp4_amd as ifp4
 
     units = units or ifp4.DECODE_UNITS
@@ -49,14 +51,18 @@ def gpu_decode(case: W.DecodeCase, units=None, ld=None, fill=float("nan"), cache
     row_len = torch.empty(rows, dtype=torch.int32, device=dev())
     ifp4.indexer_fp4_decode_schedule(to_dev(case.ctx), nn, units, sched, row_len)
     logits = torch.full((rows, ld), fill, dtype=torch.float32, device=dev())
+    row_hist = ifp4.row_histogram(rows, dev()) if fused else None
     ifp4.indexer_fp4_score_decode(qp, qs, to_dev(case.w), kp, ks, to_dev(case.block_table), nn, sched, units,
-                                  row_len, logits)
+                                  row_len, logits, row_hist)
     out = dict(kp=kp, ks=ks, qp=qp, qs=qs, sched=sched, row_len=row_len, logits=logits, units=units, ld=ld)
+    if fused:
+        out["hist"] = row_hist.clone()
+        out["row_hist"] = row_hist
     if run_topk:
         top = torch.full((rows, case.topk), -7, dtype=torch.int32, device=dev())
         ws_bytes = ifp4.indexer_topk_workspace_bytes(rows, ld, case.topk)
         ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev())
-        ifp4.indexer_topk(logits, row_len, ld, case.topk, top, ws)
+        ifp4.indexer_topk(logits, row_len, ld, case.topk, top, ws, row_hist)
         out["top"] = top
     torch.cuda.synchronize()
     out["err"] = ifp4.sched_error(sched)

@@ -73,24 +73,30 @@ def test_host_argument_errors(L):
     L.indexer_fp4_prefill_schedule.argtypes = [P, P, I32, I32, I32, P, I64, P, P]
     assert L.indexer_fp4_prefill_schedule(None, None, 4, 1001, 4096, None, 0, None, None) == -1
     assert "multiple of 8" in _err(L)
-    L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P]
+    L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P]
     # head count not a multiple of 16 (the MFMA tile height)
     assert L.indexer_fp4_score_decode(None, None, None, 24, None, None, 0, None, 8, 1, 1, None, 512, None,
-                                      None, 512, None) == -1
+                                      None, 512, None, None) == -1
     assert "n_heads=24" in _err(L)
     # logits row too short for the block table
     assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 1, 1, None, 512, None,
-                                      None, 500, None) == -2
+                                      None, 500, None, None) == -2
     assert "logits_ld=500" in _err(L)
+    # a row histogram that is not 16-byte aligned
+    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 0, 1, P(16), 512, P(16),
+                                      None, 512, P(20), None) == -1
+    assert "row_hist" in _err(L)
     L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P]
     assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, None, 8, 0, None, 512, 8, None,
                                        None, 512, None) == -1
-    L.indexer_topk.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, I64, P]
-    assert L.indexer_topk(None, 100, 4, None, 100, 0, None, 16, None, 0, None) == -1
+    L.indexer_topk.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, I64, P, P]
+    assert L.indexer_topk(None, 100, 4, None, 100, 0, None, 16, None, 0, None, None) == -1
     assert "k=0" in _err(L)
-    assert L.indexer_topk(None, 100, 4, None, 100, 32, None, 16, None, 0, None) == -2
+    assert L.indexer_topk(None, 100, 4, None, 100, 32, None, 16, None, 0, None, None) == -2
     assert "topk_ld=16" in _err(L)
-    assert L.indexer_topk(None, 100, 4, None, 200, 32, None, 32, None, 0, None) == -1
+    assert L.indexer_topk(None, 100, 4, None, 200, 32, None, 32, None, 0, None, None) == -1
+    assert L.indexer_topk(None, 100, 0, None, 100, 32, None, 32, None, 0, P(20), None) == -1
+    assert "row_hist" in _err(L)
     L.indexer_topk_merge.argtypes = [P, P, I64, I32, I32, I32, P, I64, P]
     assert L.indexer_topk_merge(None, None, 16, 2, 16, 0, None, 16, None) == -1
     assert L.indexer_topk_merge(None, None, 16, 2, 16, 8192, None, 8192, None) == -1

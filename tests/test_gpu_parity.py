@@ -250,6 +250,63 @@ def test_full_size_decode(ifp4, name):
     check_topk(g["top"].cpu().numpy(), o["top"], o["s"], o["row_len"], case.topk)
 
 
+def _order_hist(lg, n):
+    """Per-row counts of the top 12 order-key bits of lg[r, :n[r]], in the device layout (bin b
+    at word (b % 64) * 64 + b // 64)."""
+    u = lg.view(np.uint32).copy()
+    u[u == 0x80000000] = 0
+    key = np.where(u >> 31 == 1, ~u, u | np.uint32(0x80000000))
+    out = np.zeros((lg.shape[0], 4096), np.int64)
+    b = np.arange(4096)
+    for r in range(lg.shape[0]):
+        h = np.bincount((key[r, : int(n[r])] >> 20).astype(np.int64), minlength=4096)
+        out[r, (b % 64) * 64 + b // 64] = h
+    return out
+
+
+FUSED_CASES = [
+    dict(name="long_ragged", ctx=[20000, 9000, 131, 2625], heads=64, topk=2048),
+    dict(name="long_next_n2", ctx=[17000, 30000], heads=32, topk=2048, next_n=2),
+    dict(name="long_next_n4", ctx=[40000, 16385], heads=16, topk=512, next_n=4),
+    dict(name="short_rows", ctx=[300, 191], heads=64, topk=64, next_n=2),
+    dict(name="h128_mixed", ctx=[64, 1, 20100, 640, 70000], heads=128, topk=2048),
+]
+
+
+@pytest.mark.parametrize("p", FUSED_CASES, ids=lambda p: p["name"])
+@pytest.mark.parametrize("units", [512, 5, 37])
+def test_fused_histogram(ifp4, p, units):
+    """The scorer's histogram is exactly that of the logits it wrote (every row, including rows
+    of sequences that start inside a unit), the top-k that takes it selects exactly what the
+    top-k that builds its own selects, and it is left zero-filled."""
+    p = dict(p)
+    name = p.pop("name")
+    case = W.decode_case(name=name, seed=units, **p)
+    _say(f"fused {name} ctx={list(case.ctx)} H={case.heads} next_n={case.next_n} units={units}")
+    a = gpu_decode(case, units=units)
+    b = gpu_decode(case, units=units, fused=True)
+    assert a["err"] == 0 and b["err"] == 0
+    la, lb = a["logits"].cpu().numpy(), b["logits"].cpu().numpy()
+    assert np.array_equal(la.view(np.uint32), lb.view(np.uint32))
+    rl = b["row_len"].cpu().numpy()
+    assert np.array_equal(b["hist"].cpu().numpy().astype(np.int64), _order_hist(lb, rl))
+    assert np.array_equal(a["top"].cpu().numpy(), b["top"].cpu().numpy())
+    assert not b["row_hist"].any().item()
+
+
+def test_fused_histogram_full_size(ifp4):
+    case = W.decode_config("decode_b8_128k")
+    _say(f"fused full-size: B={case.batch} ctx={int(case.ctx[0])}")
+    a = gpu_decode(case)
+    b = gpu_decode(case, fused=True)
+    assert a["err"] == 0 and b["err"] == 0
+    lb = b["logits"].cpu().numpy()
+    assert np.array_equal(a["logits"].cpu().numpy().view(np.uint32), lb.view(np.uint32))
+    assert np.array_equal(b["hist"].cpu().numpy().astype(np.int64), _order_hist(lb, b["row_len"].cpu().numpy()))
+    assert np.array_equal(a["top"].cpu().numpy(), b["top"].cpu().numpy())
+    assert not b["row_hist"].any().item()
+
+
 # ---------------------------------------------------------------------------- long-row top-k
 
 def _topk_exact(ifp4, lg, rl, k, max_len, ws=None, pad=0):
@@ -329,7 +386,8 @@ def test_topk_rows_sharing_leading_bits(ifp4, n, k):
 
 # ---------------------------------------------------------------------------- graph replay
 
-def test_graph_replay_bitwise_stable(ifp4):
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_bitwise_stable(ifp4, fused):
     """One decode step (schedule, key/query write, scorer, top-k) captured once at fixed
     addresses and replayed under four context-length vectors written in place: every replay
     equals an eager run of the same inputs bit for bit (the schedule is what lets a captured
@@ -362,14 +420,15 @@ def test_graph_replay_bitwise_stable(ifp4):
                     logits=torch.full((B, ld), float("nan"), dtype=torch.float32, device=dev()),
                     top=torch.full((B, k), -7, dtype=torch.int32, device=dev()),
                     ws=torch.zeros(max(ifp4.indexer_topk_workspace_bytes(B, ld, k), 16), dtype=torch.uint8,
-                                   device=dev()))
+                                   device=dev()),
+                    hist=ifp4.row_histogram(B, dev()) if fused else None)
 
     def step(o):
         ifp4.indexer_fp4_decode_schedule(ctx, 1, units, o["sched"], o["row_len"])
         ifp4.indexer_fp4_quant_and_cache(knew, slots, kp, ks, q, o["qp"], o["qs"])
         ifp4.indexer_fp4_score_decode(o["qp"], o["qs"], w, kp, ks, bt, 1, o["sched"], units, o["row_len"],
-                                      o["logits"])
-        ifp4.indexer_topk(o["logits"], o["row_len"], ld, k, o["top"], o["ws"])
+                                      o["logits"], o["hist"])
+        ifp4.indexer_topk(o["logits"], o["row_len"], ld, k, o["top"], o["ws"], o["hist"])
 
     def set_ctx(c):
         ctx.copy_(to_dev(np.asarray(c, np.int32)))
@@ -404,6 +463,8 @@ def test_graph_replay_bitwise_stable(ifp4):
             assert np.isnan(gl[r, n:]).all()
         assert np.array_equal(g_out["top"].cpu().numpy(), e_out["top"].cpu().numpy())
         assert np.array_equal(g_out["row_len"].cpu().numpy(), np.asarray(c, np.int32))
+        if fused:
+            assert not g_out["hist"].any().item() and not e_out["hist"].any().item()
 
 
 # ---------------------------------------------------------------------------- context parallelism
