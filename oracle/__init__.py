@@ -71,7 +71,13 @@ def _declare(L):
         "oracle_topk_merge": [P, P, I64, I64, I32, I32, P, I64],
         "oracle_decode_schedule": [P, I32, I32, P, P, P, P, P],
         "oracle_prefill_schedule": [P, P, I32, I32, I32, I32, I32, P, P, P, P, P],
+        "oracle_layer_norm": [P, I32, P, P, ctypes.c_float, P],
+        "oracle_rope": [P, I32, I32, P],
+        "oracle_norm_rope_quant_and_cache": [P, I64, I64, P, P, ctypes.c_float, P, P, I64, I32, I32, P, P, P, I64,
+                                             P, I32, P, P, P, ctypes.c_float, P, I32, P, P, P],
     }
+    L.oracle_bf16_round.argtypes = [ctypes.c_double]
+    L.oracle_bf16_round.restype = ctypes.c_uint16
     for name, args in sigs.items():
         fn = getattr(L, name)
         fn.argtypes = args
@@ -152,6 +158,70 @@ def dequant_q(q_packed, q_scale, row, h):
     out = np.zeros(128, np.float64)
     n_heads = q_packed.shape[1]
     _check(lib().oracle_dequant_q(_p(q_packed), _p(q_scale), int(row), n_heads, int(h), _p(out)), "dequant_q")
+    return out
+
+
+# ---- fused writer: k_norm, RoPE, bf16 rounding (readings R8-R11 in oracle.c) ----------
+
+def bf16_round(x) -> np.ndarray:
+    """fp64 values -> nearest bf16 bit patterns (ties to even), elementwise."""
+    x = np.asarray(x, np.float64)
+    f = np.vectorize(lambda v: lib().oracle_bf16_round(float(v)), otypes=[np.uint16])
+    return f(x) if x.size else np.zeros(x.shape, np.uint16)
+
+
+def layer_norm(x, gamma, beta, eps):
+    x = _c(x, np.float64)
+    y = np.zeros_like(x)
+    g = _c(gamma, np.float32)
+    b = None if beta is None else _c(beta, np.float32)
+    _check(lib().oracle_layer_norm(_p(x), x.size, _p(g), None if b is None else _p(b), float(eps), _p(y)),
+           "layer_norm")
+    return y
+
+
+def rope(x, cs_row, rope_dim, interleaved=False):
+    """x: fp64 [128] (copied), cs_row: fp32 [rope_dim] = cos[half] then sin[half]."""
+    y = np.array(x, np.float64, copy=True)
+    c = _c(cs_row, np.float32)
+    _check(lib().oracle_rope(_p(y), int(rope_dim), int(interleaved), _p(c)), "rope")
+    return y
+
+
+def norm_rope_quant_and_cache(k_bf16, positions, cos_sin, rope_dim, interleaved, gamma, beta, eps, slot_mapping,
+                              kv_packed, kv_scale, q_bf16=None, weights=None, weight_scale=1.0, all_q=False):
+    """The fused writer. Writes keys into (kv_packed, kv_scale) in place and returns dict(qp, qs,
+    w_mqa, err, k_pre, q_pre): the fp64 vectors just before bf16 rounding (NaN where not computed)."""
+    k = _c(k_bf16, np.uint16)
+    n_tok, k_ld = k.shape
+    pos = _c(positions, np.int64)
+    cs = _c(cos_sin if cos_sin is not None else np.zeros((1, 2), np.float32), np.float32)
+    max_pos = cs.shape[0] if cos_sin is not None else 0
+    slots = _c(slot_mapping, np.int64)
+    g = None if gamma is None else _c(gamma, np.float32)
+    b = None if beta is None else _c(beta, np.float32)
+    k_pre = np.zeros((n_tok, 128), np.float64)
+    out = dict(k_pre=k_pre)
+    if q_bf16 is not None:
+        q = _c(q_bf16, np.uint16)
+        H = q.shape[1]
+        w = _c(weights, np.float32)
+        qp = np.zeros((n_tok, H, 64), np.uint8)
+        qs = np.zeros((n_tok, H, 4), np.uint8)
+        wm = np.zeros((n_tok, H), np.float32)
+        q_pre = np.zeros((n_tok, H, 128), np.float64)
+        out.update(qp=qp, qs=qs, w_mqa=wm, q_pre=q_pre)
+    else:
+        q = w = qp = qs = wm = q_pre = None
+        H = 0
+    err = np.zeros(1, np.int32)
+    _check(lib().oracle_norm_rope_quant_and_cache(
+        _p(k), n_tok, k_ld, None if g is None else _p(g), None if b is None else _p(b), float(eps), _p(pos), _p(cs),
+        max_pos, int(rope_dim), int(interleaved), _p(slots), _p(kv_packed), _p(kv_scale), kv_packed.shape[0],
+        None if q is None else _p(q), H, None if qp is None else _p(qp), None if qs is None else _p(qs),
+        None if w is None else _p(w), float(weight_scale), None if wm is None else _p(wm), int(bool(all_q)),
+        _p(k_pre), None if q_pre is None else _p(q_pre), _p(err)), "norm_rope_quant_and_cache")
+    out["err"] = int(err[0])
     return out
 
 

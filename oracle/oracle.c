@@ -16,6 +16,19 @@
  *   R5 padding rows see an empty key range (they "read no key").
  *   R6 score: sum over heads of w * max(0, q.k); no other factor.
  *   R7 top-k ties: the lower column wins.
+ * and, for the fused writer (the pages name k_norm, RoPE on q and k and the
+ * weights_mqa output of the widened writer, but print none of their formulas):
+ *   R8  k_norm is a LayerNorm over the key's 128 elements with the biased
+ *       variance, (x - mean) / sqrt(var + eps) * gamma + beta; keys only, before RoPE.
+ *   R9  RoPE rotates pairs of the first rope_dim elements of each key and query
+ *       head; the angle table row of the token's position holds cos[0, half) then
+ *       sin[0, half); pair i is (i, i + half) (half-split) or (2i, 2i + 1)
+ *       (interleaved) and turns (a, b) into (a cos - b sin, b cos + a sin).
+ *   R10 the normalized, rotated vectors are rounded to bf16 (nearest, ties to
+ *       even) and then quantized exactly like plain bf16 writer input.
+ *   R11 weights_mqa = weight_scale * weights; a row the writer skips (slot < 0
+ *       unless all_q, or a position outside the table) gets zero weights and
+ *       the quantization of a zero query.
  */
 #include "oracle.h"
 
@@ -413,6 +426,123 @@ int oracle_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, in
     int32_t t = 0;
     while (t < nt && cum_items[t + 1] <= unit_begin[u]) t++;
     unit_tile[u] = t;
+  }
+  return 0;
+}
+
+/* ---- fused writer ([P2] commit message and review fixes: the widened writer
+ * normalizes keys with k_norm before the quantizer, applies RoPE to q and k,
+ * skips slot < 0 rows and must zero weights_mqa for the rows it skips) ------- */
+
+/* Nearest bf16 to x, ties to even (R10): bf16 keeps fp32's exponent range and 8
+ * significant bits; below 2^-126 its step is 2^-133. Returns the bit pattern. */
+uint16_t oracle_bf16_round(double x) {
+  if (isnan(x)) return 0x7FC0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  int ex;
+  frexp(a, &ex); /* a in [2^(ex-1), 2^ex) */
+  int q = (ex - 1 >= -126) ? (ex - 1) - 7 : -133;
+  double v = ldexp(rint(ldexp(a, -q)), q); /* rint: nearest, ties to even */
+  if (v >= ldexp(1.0, 128)) return sign | 0x7F80;
+  float f = (float)v; /* exact */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return sign | (uint16_t)(u >> 16);
+}
+
+/* R8 */
+int oracle_layer_norm(const double *x, int32_t n, const float *gamma, const float *beta, float eps, double *y) {
+  if (n <= 0) return -1;
+  double mean = 0.0, var = 0.0;
+  for (int i = 0; i < n; i++) mean += x[i];
+  mean /= n;
+  for (int i = 0; i < n; i++) var += (x[i] - mean) * (x[i] - mean);
+  var /= n;
+  double inv = 1.0 / sqrt(var + (double)eps);
+  for (int i = 0; i < n; i++) y[i] = (x[i] - mean) * inv * (double)gamma[i] + (beta ? (double)beta[i] : 0.0);
+  return 0;
+}
+
+/* R9, in place on x[0, rope_dim); cs is the table row {cos[half], sin[half]}. */
+int oracle_rope(double *x, int32_t rope_dim, int32_t interleaved, const float *cs) {
+  if (rope_dim < 0 || rope_dim % 2) return -1;
+  int half = rope_dim / 2;
+  for (int i = 0; i < half; i++) {
+    int ia = interleaved ? 2 * i : i, ib = interleaved ? 2 * i + 1 : i + half;
+    double c = cs[i], s = cs[half + i], a = x[ia], b = x[ib];
+    x[ia] = a * c - b * s;
+    x[ib] = b * c + a * s;
+  }
+  return 0;
+}
+
+static void zero_vector(uint8_t *packed, uint8_t *scales) {
+  uint16_t z[KEY_DIM] = {0};
+  encode_vector(z, packed, scales);
+}
+
+/* The fused writer, token by token (R8-R11). k_pre / q_pre (optional) receive
+ * the fp64 vectors just before bf16 rounding (NaN for rows not computed). err
+ * gets 16 for a position outside [0, max_pos) with rope_dim > 0 and 32 for a
+ * slot past the pool (key skipped). */
+int oracle_norm_rope_quant_and_cache(const uint16_t *k, int64_t n_tok, int64_t k_ld, const float *gamma,
+                                     const float *beta, float eps, const int64_t *pos, const float *cos_sin,
+                                     int64_t max_pos, int32_t rope_dim, int32_t interleaved, const int64_t *slot,
+                                     uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const uint16_t *q,
+                                     int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale, const float *weights,
+                                     float weight_scale, float *weights_mqa, int32_t all_q, double *k_pre,
+                                     double *q_pre, int32_t *err) {
+  if (n_tok < 0 || k_ld < KEY_DIM || n_pages < 0 || rope_dim < 0 || rope_dim > KEY_DIM || rope_dim % 2) return -1;
+  *err = 0;
+  for (int64_t t = 0; t < n_tok; t++) {
+    int bad_pos = rope_dim > 0 && (pos[t] < 0 || pos[t] >= max_pos);
+    if (bad_pos) *err |= 16;
+    const float *cs = bad_pos || rope_dim == 0 ? NULL : &cos_sin[pos[t] * rope_dim];
+    double v[KEY_DIM];
+    uint16_t bits[KEY_DIM];
+    /* key */
+    if (k_pre)
+      for (int i = 0; i < KEY_DIM; i++) k_pre[t * KEY_DIM + i] = NAN;
+    int in_pool = slot[t] >= 0 && slot[t] / PAGE_KEYS < n_pages;
+    if (slot[t] >= 0 && !in_pool) *err |= 32;
+    if (!bad_pos && in_pool) {
+      for (int i = 0; i < KEY_DIM; i++) v[i] = bf16_to_double(k[t * k_ld + i]);
+      if (gamma) oracle_layer_norm(v, KEY_DIM, gamma, beta, eps, v);
+      if (cs) oracle_rope(v, rope_dim, interleaved, cs);
+      for (int i = 0; i < KEY_DIM; i++) {
+        if (k_pre) k_pre[t * KEY_DIM + i] = v[i];
+        bits[i] = oracle_bf16_round(v[i]);
+      }
+      int64_t page = slot[t] / PAGE_KEYS;
+      int p = (int)(slot[t] % PAGE_KEYS);
+      uint8_t packed[64], scales[4];
+      encode_vector(bits, packed, scales);
+      memcpy(&kv_packed[(page * PAGE_KEYS + p) * 64], packed, 64);
+      for (int g = 0; g < 4; g++) kv_scale[(page * 4 + g) * PAGE_KEYS + oracle_scale_slot(p)] = scales[g];
+    }
+    /* query heads and weights */
+    if (!q) continue;
+    int live = !bad_pos && (slot[t] >= 0 || all_q);
+    for (int32_t h = 0; h < n_heads; h++) {
+      int64_t vh = t * n_heads + h;
+      if (q_pre)
+        for (int i = 0; i < KEY_DIM; i++) q_pre[vh * KEY_DIM + i] = NAN;
+      if (!live) {
+        zero_vector(&q_packed[vh * 64], &q_scale[vh * 4]);
+        weights_mqa[vh] = 0.0f;
+        continue;
+      }
+      for (int i = 0; i < KEY_DIM; i++) v[i] = bf16_to_double(q[vh * KEY_DIM + i]);
+      if (cs) oracle_rope(v, rope_dim, interleaved, cs);
+      for (int i = 0; i < KEY_DIM; i++) {
+        if (q_pre) q_pre[vh * KEY_DIM + i] = v[i];
+        bits[i] = oracle_bf16_round(v[i]);
+      }
+      encode_vector(bits, &q_packed[vh * 64], &q_scale[vh * 4]);
+      weights_mqa[vh] = (float)((double)weight_scale * (double)weights[vh]);
+    }
   }
   return 0;
 }

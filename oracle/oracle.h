@@ -112,6 +112,18 @@ int oracle_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, in
                             int32_t max_tiles, int32_t *n_tiles, int32_t *tiles, int32_t *cum_items,
                             int32_t *unit_begin, int32_t *unit_tile);
 
+/* Fused writer pieces and composition (readings R8-R11 in oracle.c). */
+uint16_t oracle_bf16_round(double x);
+int oracle_layer_norm(const double *x, int32_t n, const float *gamma, const float *beta, float eps, double *y);
+int oracle_rope(double *x, int32_t rope_dim, int32_t interleaved, const float *cs);
+int oracle_norm_rope_quant_and_cache(const uint16_t *k, int64_t n_tok, int64_t k_ld, const float *gamma,
+                                     const float *beta, float eps, const int64_t *pos, const float *cos_sin,
+                                     int64_t max_pos, int32_t rope_dim, int32_t interleaved, const int64_t *slot,
+                                     uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const uint16_t *q,
+                                     int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale, const float *weights,
+                                     float weight_scale, float *weights_mqa, int32_t all_q, double *k_pre,
+                                     double *q_pre, int32_t *err);
+
 #ifdef __cplusplus
 }
 #endif

@@ -571,3 +571,161 @@ def test_topk_merge_skips_empty_slots_and_pads():
     # equal scores: the smaller index first
     got = oracle.topk_merge(np.array([[1.0, 1.0, 1.0]]), np.array([[8, 3, 5]], np.int32), 2)
     assert got[0].tolist() == [3, 5]
+
+
+# ---------------------------------------------------------------------------- fused writer (R8-R11)
+
+def test_bf16_round_matches_torch_on_fp32_values():
+    """On values that are exactly fp32, rounding to bf16 is torch's own fp32 -> bf16 conversion
+    (nearest, ties to even), subnormals and ties included."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[(bits & 0x7F800000) != 0x7F800000]                 # finite
+    ties = (rng.integers(0, 2**16, 5000, dtype=np.uint32) << 16) | 0x8000
+    ties = ties[(ties & 0x7F800000) != 0x7F800000]
+    sub = rng.integers(0, 2**23, 5000, dtype=np.uint32)             # subnormal fp32
+    allb = np.concatenate([bits, ties, sub, [0, 0x80000000, 0x7F7FFFFF]]).astype(np.uint32)
+    f = allb.view(np.float32)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_round(f.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_round_is_a_single_rounding():
+    """A double just above a bf16 tie rounds up; rounding through fp32 first would see the tie and
+    go to even."""
+    assert int(oracle.bf16_round(1.0 + 2.0**-8 + 2.0**-30)) == 0x3F81
+    assert int(oracle.bf16_round(1.0 + 2.0**-8)) == 0x3F80             # the tie itself: even
+    assert int(oracle.bf16_round(-(1.0 + 3 * 2.0**-8))) == 0xBF82
+    assert int(oracle.bf16_round(2.0**-133 * 0.5)) == 0                 # half the least step: even (zero)
+    assert int(oracle.bf16_round(2.0**-133 * 0.75)) == 1
+    assert int(oracle.bf16_round(3.4e38)) == 0x7F80                     # past the largest finite: inf
+
+
+def test_layer_norm_closed_form():
+    x = np.arange(128, dtype=np.float64)
+    mean, var = 63.5, (128**2 - 1) / 12.0                               # of 0..n-1
+    eps = np.float32(1e-6)
+    ones, zeros = np.ones(128, np.float32), np.zeros(128, np.float32)
+    y = oracle.layer_norm(x, ones, zeros, eps)
+    want = (x - mean) / np.sqrt(var + float(eps))
+    assert np.allclose(y, want, rtol=1e-14, atol=1e-14)
+    g = np.linspace(-2, 2, 128).astype(np.float32)
+    b = np.linspace(1, -1, 128).astype(np.float32)
+    y2 = oracle.layer_norm(x, g, b, eps)
+    assert np.allclose(y2, want * g.astype(np.float64) + b.astype(np.float64), rtol=1e-13, atol=1e-13)
+    # invariants for random input: zero mean, variance var / (var + eps)
+    r = np.random.default_rng(2).standard_normal(128) * 3 + 5
+    y3 = oracle.layer_norm(r, ones, zeros, np.float32(0.5))
+    v = r.var()
+    assert abs(y3.mean()) < 1e-13 and abs(y3.var() - v / (v + 0.5)) < 1e-12
+
+
+@pytest.mark.parametrize("rope_dim", [64, 32, 128])
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_rope_is_complex_multiplication(rope_dim, interleaved):
+    """Each rotated pair (a, b) is (a + ib) * exp(i theta); elements past rope_dim are untouched."""
+    rng = np.random.default_rng(rope_dim + interleaved)
+    half = rope_dim // 2
+    theta = rng.uniform(-np.pi, np.pi, half)
+    cs = np.concatenate([np.cos(theta), np.sin(theta)]).astype(np.float32)
+    x = rng.standard_normal(128)
+    y = oracle.rope(x, cs, rope_dim, interleaved)
+    ia = np.arange(half) * 2 if interleaved else np.arange(half)
+    ib = ia + 1 if interleaved else ia + half
+    z = (x[ia] + 1j * x[ib]) * (cs[:half].astype(np.float64) + 1j * cs[half:].astype(np.float64))
+    assert np.allclose(y[ia], z.real, rtol=0, atol=1e-14) and np.allclose(y[ib], z.imag, rtol=0, atol=1e-14)
+    assert np.array_equal(y[rope_dim:], x[rope_dim:])
+    # angle 0 is the identity; a quarter turn maps (a, b) to (-b, a)
+    ident = np.concatenate([np.ones(half), np.zeros(half)]).astype(np.float32)
+    assert np.array_equal(oracle.rope(x, ident, rope_dim, interleaved), x)
+    quarter = np.concatenate([np.zeros(half), np.ones(half)]).astype(np.float32)
+    yq = oracle.rope(x, quarter, rope_dim, interleaved)
+    assert np.array_equal(yq[ia], -x[ib]) and np.array_equal(yq[ib], x[ia])
+
+
+def _writer_inputs(n_tok, H, seed, rope_dim=64):
+    rng = np.random.default_rng(seed)
+    k = W.normal_bf16(rng, (n_tok, 128))
+    q = W.normal_bf16(rng, (n_tok, H, 128))
+    w = rng.standard_normal((n_tok, H)).astype(np.float32)
+    max_pos = 4096
+    inv = 10000.0 ** (-np.arange(rope_dim // 2) * 2.0 / max(rope_dim, 1))
+    ang = np.arange(max_pos)[:, None] * inv[None, :]
+    cs = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    pos = rng.integers(0, max_pos, n_tok).astype(np.int64)
+    return k, q, w, cs, pos
+
+
+def test_fused_writer_without_norm_and_rope_is_the_plain_writer():
+    n_tok, H = 40, 16
+    k, q, w, cs, pos = _writer_inputs(n_tok, H, 1)
+    slots = np.arange(n_tok, dtype=np.int64) * 3
+    slots[5] = -1
+    kp0, ks0 = np.zeros((4, 64, 64), np.uint8), np.zeros((4, 4, 64), np.uint8)
+    kp1, ks1 = kp0.copy(), ks0.copy()
+    oracle.quant_and_cache(k, slots, kp0, ks0)
+    qp0, qs0 = oracle.quant_q(q)
+    o = oracle.norm_rope_quant_and_cache(k, pos, None, 0, False, None, None, 0.0, slots, kp1, ks1, q, w, 0.25,
+                                         all_q=True)
+    assert o["err"] == 0
+    assert np.array_equal(kp0, kp1) and np.array_equal(ks0, ks1)
+    assert np.array_equal(o["qp"], qp0) and np.array_equal(o["qs"], qs0)
+    assert np.array_equal(o["w_mqa"], (w.astype(np.float64) * 0.25).astype(np.float32))
+
+
+def test_fused_writer_skips_and_flags_rows():
+    """slot < 0: no key, and (unless all_q) the zero query and zero weights; a position outside the
+    table: the whole row is skipped and flagged 16; a slot past the pool: the key is skipped and
+    flagged 32, the query is written."""
+    n_tok, H = 6, 16
+    k, q, w, cs, pos = _writer_inputs(n_tok, H, 2)
+    slots = np.array([0, -1, 5, 7, 64 * 4 + 3, 9], np.int64)
+    pos[3] = 4096                                                       # one past the table
+    g = np.ones(128, np.float32)
+    kp, ks = np.zeros((4, 64, 64), np.uint8), np.zeros((4, 4, 64), np.uint8)
+    o = oracle.norm_rope_quant_and_cache(k, pos, cs, 64, False, g, None, 1e-6, slots, kp, ks, q, w, 1.0)
+    assert o["err"] == 16 | 32
+    zq, zs = oracle.quant_q(np.zeros((1, H, 128), np.uint16))
+    for t in (1, 3):
+        assert np.array_equal(o["qp"][t], zq[0]) and np.array_equal(o["qs"][t], zs[0])
+        assert not o["w_mqa"][t].any() and np.isnan(o["q_pre"][t]).all() and np.isnan(o["k_pre"][t]).all()
+    assert np.isnan(o["k_pre"][4]).all() and not np.isnan(o["q_pre"][4]).any() and o["w_mqa"][4].any()
+    assert not kp[0, 7].any()                                           # row 3's slot stayed empty
+    o2 = oracle.norm_rope_quant_and_cache(k, pos, cs, 64, False, g, None, 1e-6, slots, kp.copy(), ks.copy(), q, w,
+                                          1.0, all_q=True)
+    assert not np.isnan(o2["q_pre"][1]).any() and o2["w_mqa"][1].any()  # all_q computes slot < 0 rows
+    assert np.isnan(o2["q_pre"][3]).all()                               # but not a bad position
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_fused_writer_dequantizes_to_the_normalized_rotated_vector(interleaved):
+    """Decoding what the fused writer stored gives the normalized, rotated vector within the MXFP4
+    error bound (half a grid step of each block's scale, plus bf16 rounding)."""
+    n_tok, H = 24, 16
+    k, q, w, cs, pos = _writer_inputs(n_tok, H, 3)
+    rng = np.random.default_rng(4)
+    g = rng.uniform(0.5, 1.5, 128).astype(np.float32)
+    b = rng.uniform(-0.2, 0.2, 128).astype(np.float32)
+    slots = np.arange(n_tok, dtype=np.int64)
+    kp, ks = np.zeros((1, 64, 64), np.uint8), np.zeros((1, 4, 64), np.uint8)
+    o = oracle.norm_rope_quant_and_cache(k, pos, cs, 64, interleaved, g, b, 1e-6, slots, kp, ks, q, w, 1.0)
+    kf = k.astype(np.uint32) << 16
+    for t in range(n_tok):
+        x = kf[t].view(np.float32).astype(np.float64)
+        xn = (x - x.mean()) / np.sqrt(x.var() + np.float64(np.float32(1e-6))) * g + b
+        c, sn = cs[pos[t], :32].astype(np.float64), cs[pos[t], 32:].astype(np.float64)
+        ia = np.arange(32) * 2 if interleaved else np.arange(32)
+        ib = ia + 1 if interleaved else ia + 32
+        z = (xn[ia] + 1j * xn[ib]) * (c + 1j * sn)
+        want = xn.copy()
+        want[ia], want[ib] = z.real, z.imag
+        assert np.allclose(o["k_pre"][t], want, rtol=1e-9, atol=1e-9)
+        got = oracle.dequant_key(kp, ks, 0, t)
+        for blk in range(4):
+            sl = slice(32 * blk, 32 * blk + 32)
+            step = 2.0 ** (int(ks[0, blk, oracle.scale_slot(t)]) - 127)   # E2M1 grid step at 1 is 0.5 * scale
+            bound = np.maximum(0.25 * step, 1.0 * step) + np.abs(want[sl]) * 2.0**-8
+            assert (np.abs(got[sl] - np.clip(want[sl], -6 * step, 6 * step)) <= bound).all()
