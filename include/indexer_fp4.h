@@ -70,12 +70,15 @@ enum {
   INDEXER_FP4_EHIP = -4    /* the HIP runtime reported an error */
 };
 
-/* Flags the kernels OR into the schedule buffer's error word (device-side problems). */
+/* Flags the kernels OR into the schedule buffer's error word (device-side problems),
+ * and (the last two) the fused writer into its caller's error word. */
 enum {
   INDEXER_FP4_DEV_BAD_PAGE = 1,      /* block-table entry outside [0, n_pages): page skipped */
   INDEXER_FP4_DEV_TABLE_SHORT = 2,   /* a row needs more pages than bt_ld: rest skipped */
   INDEXER_FP4_DEV_BAD_SCHEDULE = 4,  /* schedule built for other sizes than the call's */
-  INDEXER_FP4_DEV_BAD_LENGTH = 8     /* negative length or cu_rows not ascending */
+  INDEXER_FP4_DEV_BAD_LENGTH = 8,    /* negative length or cu_rows not ascending */
+  INDEXER_FP4_DEV_BAD_POSITION = 16, /* a rotary position outside the cos/sin table: row skipped */
+  INDEXER_FP4_DEV_SLOT_OUT_OF_POOL = 32 /* a slot at or past n_pages*64: key skipped */
 };
 
 #define INDEXER_FP4_PAGE 64       /* tokens per page ([P2] review fixes: block size 64) */
@@ -151,6 +154,50 @@ int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, in
 int indexer_fp4_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
                                  int32_t n_rows_padded, int32_t n_units, void *sched,
                                  int64_t sched_bytes, int32_t *row_len, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Fused writer: key LayerNorm and RoPE, then the cache write and query quantization
+ * above, and the scorer's weights ([P2] commit message: the widened writer emits the
+ * quantized query and weights_mqa, k_norm runs before the quantizer; review fixes:
+ * slot < 0 rows are skipped and their weights_mqa must be zero). The pages give no
+ * formulas; these are the readings:
+ *   key   LayerNorm over its 128 elements (biased variance): (x - mean) /
+ *         sqrt(var + eps) * k_norm_weight + k_norm_bias (skipped if k_norm_weight is
+ *         NULL; a NULL bias is zero), then RoPE;
+ *   query RoPE only, per head;
+ *   RoPE  rotates pairs of the first rope_dim elements: pair i is (i, i + rope_dim/2),
+ *         or (2i, 2i+1) when rope_interleaved, and (a, b) becomes (a cos - b sin,
+ *         b cos + a sin) with cos = cos_sin[pos][i], sin = cos_sin[pos][rope_dim/2 + i];
+ *   the fp32 result is rounded once to bf16 (nearest, ties to even) and quantized as
+ *   indexer_fp4_quant_and_cache quantizes bf16 input;
+ *   weights_mqa[t][h] = weight_scale * weights[t][h].
+ *
+ *   k_bf16        bf16 [n_tok][k_ld] (first 128 used); token t's key
+ *   k_norm_weight, k_norm_bias  fp32 [128] or NULL; eps >= 0
+ *   positions     int64 [n_tok] (needed when rope_dim > 0)
+ *   cos_sin       fp32 [max_pos][rope_dim]; rope_dim a multiple of 16 in 0..128
+ *   slot_mapping, kv_packed, kv_scale, n_pages  as for indexer_fp4_quant_and_cache
+ *   q_bf16        bf16 [n_tok][n_heads][128] or NULL (no query arm); token t's heads
+ *   q_packed, q_scale  outputs [n_tok][n_heads][64] / [n_tok][n_heads][4]
+ *   weights       fp32 [n_tok][n_heads]; weights_mqa output of the same shape
+ *   all_q         0: a token with slot < 0 gets the zero query (codes 0, scale byte 0)
+ *                 and weights_mqa 0; nonzero: its query and weights are computed
+ *   err           int32 word or NULL: INDEXER_FP4_DEV_BAD_POSITION (position outside
+ *                 [0, max_pos) with rope_dim > 0: key skipped, zero query and weights),
+ *                 INDEXER_FP4_DEV_SLOT_OUT_OF_POOL (key skipped, query written)
+ * Errors: EINVAL (negative sizes, rope_dim not a multiple of 16 or above 128, a bias
+ * without a weight, eps < 0, k_ld < 128 or not a multiple of 8, missing or misaligned
+ * pointers an arm needs), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int indexer_fp4_norm_rope_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
+                                          const float *k_norm_weight, const float *k_norm_bias, float eps,
+                                          const int64_t *positions, const float *cos_sin, int64_t max_pos,
+                                          int32_t rope_dim, int32_t rope_interleaved,
+                                          const int64_t *slot_mapping, uint8_t *kv_packed, uint8_t *kv_scale,
+                                          int64_t n_pages, const void *q_bf16, int32_t n_heads,
+                                          uint8_t *q_packed, uint8_t *q_scale, const float *weights,
+                                          float weight_scale, float *weights_mqa, int32_t all_q, int32_t *err,
+                                          void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Decode scorer ([P2] commit message and PR description: the FP4 mqa-logits kernel

@@ -27,6 +27,7 @@ PREFILL_UNITS = 512
 EXPORTS = (
     "indexer_fp4_last_error",
     "indexer_fp4_quant_and_cache",
+    "indexer_fp4_norm_rope_quant_and_cache",
     "indexer_fp4_decode_sched_bytes",
     "indexer_fp4_decode_schedule",
     "indexer_fp4_prefill_sched_bytes",
@@ -49,10 +50,12 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950) first")
     L = ctypes.CDLL(LIB_PATH)
-    P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    P, I32, I64, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
     sig = {
         "indexer_fp4_last_error": ([], ctypes.c_char_p),
         "indexer_fp4_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
+        "indexer_fp4_norm_rope_quant_and_cache": ([P, I64, I64, P, P, F32, P, P, I64, I32, I32, P, P, P, I64, P, I32,
+                                                   P, P, P, F32, P, I32, P, P], ctypes.c_int),
         "indexer_fp4_decode_sched_bytes": ([I32, I32, I32], I64),
         "indexer_fp4_decode_schedule": ([P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32], I64),
@@ -119,6 +122,50 @@ def indexer_fp4_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, q=None, q_
     _check(lib.indexer_fp4_quant_and_cache(
         _ptr(k), n_tok, 0 if k is None else k.stride(0), _ptr(slot_mapping), _ptr(kv_packed), _ptr(kv_scale),
         kv_packed.shape[0], _ptr(q), rows, heads, _ptr(q_packed), _ptr(q_scale), _stream(kv_packed)))
+
+
+def indexer_fp4_norm_rope_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, positions=None, cos_sin=None,
+                                          rope_dim=0, interleaved=False, k_norm_weight=None, k_norm_bias=None,
+                                          eps=1e-6, q=None, q_packed=None, q_scale=None, weights=None,
+                                          weight_scale=1.0, weights_mqa=None, all_q=False, err=None):
+    """Fused writer: k [n_tok, >=128] bf16 -> LayerNorm (if k_norm_weight) -> RoPE (first rope_dim
+    elements, cos_sin fp32 [max_pos, rope_dim]) -> MXFP4 cache write; q [n_tok, H, 128] bf16 ->
+    RoPE -> q_packed/q_scale; weights_mqa = weight_scale * weights (fp32 [n_tok, H]).
+    err: optional int32 [1] device word for the INDEXER_FP4_DEV_* flags."""
+    _dev(k, "k", torch.bfloat16, contiguous=False)
+    if k.dim() != 2 or k.stride(1) != 1:
+        raise ValueError("k must be 2-D with unit stride along the head dimension")
+    n_tok = k.shape[0]
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(kv_packed, "kv_packed", torch.uint8)
+    _dev(kv_scale, "kv_scale", torch.uint8)
+    max_pos = 0
+    if rope_dim:
+        _dev(positions, "positions", torch.int64)
+        _dev(cos_sin, "cos_sin", torch.float32)
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != rope_dim:
+            raise ValueError("cos_sin must be [max_pos, rope_dim]")
+        max_pos = cos_sin.shape[0]
+    for t, name in ((k_norm_weight, "k_norm_weight"), (k_norm_bias, "k_norm_bias")):
+        if t is not None:
+            _dev(t, name, torch.float32)
+    heads = 0
+    if q is not None:
+        _dev(q, "q", torch.bfloat16)
+        if q.dim() != 3 or q.shape[0] != n_tok or q.shape[2] != HEAD_DIM:
+            raise ValueError("q must be [n_tok, heads, 128]")
+        heads = q.shape[1]
+        _dev(q_packed, "q_packed", torch.uint8)
+        _dev(q_scale, "q_scale", torch.uint8)
+        _dev(weights, "weights", torch.float32)
+        _dev(weights_mqa, "weights_mqa", torch.float32)
+    if err is not None:
+        _dev(err, "err", torch.int32)
+    _check(lib.indexer_fp4_norm_rope_quant_and_cache(
+        _ptr(k), n_tok, k.stride(0), _ptr(k_norm_weight), _ptr(k_norm_bias), float(eps), _ptr(positions),
+        _ptr(cos_sin), max_pos, int(rope_dim), int(bool(interleaved)), _ptr(slot_mapping), _ptr(kv_packed),
+        _ptr(kv_scale), kv_packed.shape[0], _ptr(q), heads, _ptr(q_packed), _ptr(q_scale), _ptr(weights),
+        float(weight_scale), _ptr(weights_mqa), int(bool(all_q)), _ptr(err), _stream(kv_packed)))
 
 
 def indexer_fp4_decode_sched_bytes(batch: int, next_n: int, n_units: int) -> int:

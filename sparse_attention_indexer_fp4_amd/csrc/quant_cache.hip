@@ -113,6 +113,159 @@ __global__ __launch_bounds__(256) void quant_cache_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Fused writer: key LayerNorm (k_norm), RoPE on keys and query heads, then the MXFP4 write
+// above, plus the scorer's per-head weights ("Score a DSA sparse indexer in FP4", commit
+// message: the widened writer emits the quantized query and weights_mqa, and k_norm runs
+// before the quantizer; review fixes: slot < 0 rows are skipped and their weights_mqa must
+// be zero). The pages give no formulas; the kernel takes these readings: LayerNorm over the
+// key's 128 elements with the biased variance, (x - mean) / sqrt(var + eps) * gamma + beta;
+// RoPE pairs (i, i + rope_dim/2) or (2i, 2i + 1) of the first rope_dim elements, pair i
+// turned by the angle whose cos and sin are entries i and rope_dim/2 + i of the position's
+// table row; the result rounded once to bf16 (nearest, ties to even) and quantized like
+// plain bf16 input; weights_mqa = weight_scale * weights.
+//
+// Same lane split as the plain writer: 16 lanes per 128-element vector, 8 elements per
+// lane, so the LayerNorm sums are 4-step butterflies inside the 16-lane group and a
+// half-split rotation partner sits rope_dim/16 lanes away (rope_dim is a multiple of 16).
+
+__device__ __forceinline__ float bf16_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, nearest, ties to even (finite input).
+__device__ __forceinline__ uint32_t float_to_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float group16_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+__device__ __forceinline__ void unpack8(uint4 in, float x[8]) {
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+#pragma unroll
+  for (int h = 0; h < 4; h++) {
+    x[2 * h] = bf16_to_float(w[h] & 0xFFFFu);
+    x[2 * h + 1] = bf16_to_float(w[h] >> 16);
+  }
+}
+
+__device__ __forceinline__ uint4 pack8(const float x[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int h = 0; h < 4; h++) w[h] = float_to_bf16(x[2 * h]) | (float_to_bf16(x[2 * h + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Rotates this lane's elements 8l .. 8l+7 in place. All 16 lanes of the group call it.
+__device__ __forceinline__ void rope8(float x[8], int l, const float *__restrict__ cs, int rope_dim,
+                                      bool interleaved) {
+  const int half = rope_dim >> 1;
+  float part[8];
+  if (!interleaved) {  // partner lane: l +- half/8 inside the group
+    const int hl = half >> 3;
+    const int src = (threadIdx.x & 63 & ~15) + (l < hl ? l + hl : l - hl);
+#pragma unroll
+    for (int j = 0; j < 8; j++) part[j] = __shfl(x[j], src, 64);
+  }
+  if (8 * l >= rope_dim) return;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int i = 8 * l + j;
+    float a, b;
+    int m;
+    bool first;
+    if (interleaved) {
+      m = i >> 1;
+      first = (j & 1) == 0;
+      a = x[j];
+      b = x[j ^ 1];
+    } else {
+      first = i < half;
+      m = first ? i : i - half;
+      a = x[j];
+      b = part[j];
+    }
+    const float c = cs[m], sn = cs[half + m];
+    part[j] = first ? a * c - b * sn : a * c + b * sn;  // a is this element, b its partner
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) x[j] = part[j];
+}
+
+__global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
+    const uint16_t *__restrict__ k, int64_t n_tok, int64_t k_ld, const float *__restrict__ gamma,
+    const float *__restrict__ beta, float eps, const int64_t *__restrict__ positions, const float *__restrict__ cos_sin,
+    int64_t max_pos, int rope_dim, bool interleaved, const int64_t *__restrict__ slots, uint8_t *__restrict__ kv_packed,
+    uint8_t *__restrict__ kv_scale, int64_t n_pages, const uint16_t *__restrict__ q, int n_heads,
+    uint8_t *__restrict__ q_packed, uint8_t *__restrict__ q_scale, const float *__restrict__ weights,
+    float weight_scale, float *__restrict__ weights_mqa, bool all_q, int32_t *__restrict__ err) {
+  const int64_t n_q_vec = q ? n_tok * (int64_t)n_heads : 0;
+  const int64_t total = (n_tok + n_q_vec) * kLanesPerVec;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t v = i / kLanesPerVec;
+    const int l = (int)(i % kLanesPerVec);
+    const int g = l >> 2;
+    const bool is_key = v < n_tok;
+    const int64_t t = is_key ? v : (v - n_tok) / n_heads;  // token
+    // every decision below is uniform over the vector's 16 lanes
+    const int64_t pos = rope_dim > 0 ? positions[t] : 0;
+    const bool bad_pos = rope_dim > 0 && (pos < 0 || pos >= max_pos);
+    const int64_t slot = slots[t];
+    const float *cs = cos_sin + (bad_pos ? 0 : pos) * rope_dim;
+    uint32_t sc;
+    if (is_key) {
+      const bool in_pool = slot >= 0 && slot < n_pages * kPage;
+      if (err && l == 0 && (bad_pos || (slot >= 0 && !in_pool)))
+        atomicOr(err, (bad_pos ? INDEXER_FP4_DEV_BAD_POSITION : 0) |
+                          (slot >= 0 && !in_pool ? INDEXER_FP4_DEV_SLOT_OUT_OF_POOL : 0));
+      if (bad_pos || !in_pool) continue;
+      float x[8];
+      unpack8(*reinterpret_cast<const uint4 *>(k + t * k_ld + 8 * l), x);
+      if (gamma) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) s += x[j];
+        const float mean = group16_sum(s) * (1.0f / kHeadDim);
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          x[j] -= mean;
+          ss += x[j] * x[j];
+        }
+        const float inv = 1.0f / sqrtf(group16_sum(ss) * (1.0f / kHeadDim) + eps);
+#pragma unroll
+        for (int j = 0; j < 8; j++) x[j] = x[j] * inv * gamma[8 * l + j] + (beta ? beta[8 * l + j] : 0.f);
+      }
+      if (rope_dim > 0) rope8(x, l, cs, rope_dim, interleaved);
+      const uint32_t d = encode_lane8(pack8(x), sc);
+      const int64_t page = slot / kPage;
+      const int p = (int)(slot % kPage);
+      *reinterpret_cast<uint32_t *>(kv_packed + (page * kPage + p) * kKeyBytes + 4 * l) = d;
+      if ((l & 3) == 0) kv_scale[(page * kGroups + g) * kPage + (p % 16) * 4 + p / 16] = (uint8_t)sc;
+    } else {
+      const int64_t vq = v - n_tok;
+      const bool live = !bad_pos && (slot >= 0 || all_q);
+      uint32_t d = 0;
+      sc = 0;  // a skipped row stores the quantization of a zero vector and weight 0
+      if (live) {
+        float x[8];
+        unpack8(*reinterpret_cast<const uint4 *>(q + vq * kHeadDim + 8 * l), x);
+        if (rope_dim > 0) rope8(x, l, cs, rope_dim, interleaved);
+        d = encode_lane8(pack8(x), sc);
+      }
+      *reinterpret_cast<uint32_t *>(q_packed + vq * kKeyBytes + 4 * l) = d;
+      if ((l & 3) == 0) q_scale[vq * kGroups + g] = (uint8_t)sc;
+      if (l == 0) weights_mqa[vq] = live ? weight_scale * weights[vq] : 0.f;
+    }
+  }
+}
+
 }  // namespace ifp4
 
 using namespace ifp4;
@@ -154,4 +307,55 @@ extern "C" int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, in
                      (const uint16_t *)k_bf16, n_tok, k_ld, slot_mapping, kv_packed, kv_scale, n_pages,
                      (const uint16_t *)q_bf16, n_q_vec, q_packed, q_scale);
   return launch_status("quant_and_cache");
+}
+
+extern "C" int indexer_fp4_norm_rope_quant_and_cache(
+    const void *k_bf16, int64_t n_tok, int64_t k_ld, const float *k_norm_weight, const float *k_norm_bias, float eps,
+    const int64_t *positions, const float *cos_sin, int64_t max_pos, int32_t rope_dim, int32_t rope_interleaved,
+    const int64_t *slot_mapping, uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
+    int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale, const float *weights, float weight_scale,
+    float *weights_mqa, int32_t all_q, int32_t *err, void *stream) {
+  clear_error();
+  if (n_tok < 0 || n_pages < 0)
+    return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: negative size: n_tok=%lld n_pages=%lld", (long long)n_tok,
+                (long long)n_pages);
+  if (rope_dim < 0 || rope_dim > kHeadDim || rope_dim % 16 != 0)
+    return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: rope_dim=%d must be a multiple of 16 in 0..%d", rope_dim,
+                kHeadDim);
+  if (!k_norm_weight && k_norm_bias)
+    return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: k_norm_bias without k_norm_weight");
+  if (!(eps >= 0.f)) return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: eps must be >= 0");
+  if (n_tok > 0) {
+    if (!k_bf16 || !slot_mapping || !kv_packed || !kv_scale)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: n_tok=%lld needs k, slot_mapping and both planes",
+                  (long long)n_tok);
+    if (k_ld < kHeadDim || k_ld % 8 != 0)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: k_ld=%lld must be >= %d and a multiple of 8",
+                  (long long)k_ld, kHeadDim);
+    if (((uintptr_t)k_bf16 | (uintptr_t)kv_packed) % 16 != 0)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: k and kv_packed must be 16-byte aligned");
+    if (rope_dim > 0 && (!positions || !cos_sin || max_pos <= 0))
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: rope_dim=%d needs positions and a cos/sin table", rope_dim);
+  }
+  const bool q_arm = q_bf16 != nullptr && n_tok > 0;
+  if (q_arm) {
+    if (n_heads <= 0) return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: n_heads=%d must be positive", n_heads);
+    if (!q_packed || !q_scale || !weights || !weights_mqa)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: the query arm needs q_packed, q_scale, weights and weights_mqa");
+    if (((uintptr_t)q_bf16 | (uintptr_t)q_packed) % 16 != 0)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: q and q_packed must be 16-byte aligned");
+  }
+  int rc = check_device();
+  if (rc) return rc;
+  const int64_t total = (n_tok + (q_arm ? n_tok * (int64_t)n_heads : 0)) * kLanesPerVec;
+  if (total == 0) return INDEXER_FP4_OK;
+  const int threads = 256;
+  int64_t blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(norm_rope_quant_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
+                     (const uint16_t *)k_bf16, n_tok, k_ld, k_norm_weight, k_norm_bias, eps, positions, cos_sin,
+                     max_pos, rope_dim, rope_interleaved != 0, slot_mapping, kv_packed, kv_scale, n_pages,
+                     q_arm ? (const uint16_t *)q_bf16 : nullptr, n_heads, q_packed, q_scale, weights, weight_scale,
+                     weights_mqa, all_q != 0, err);
+  return launch_status("norm_rope_quant_and_cache");
 }

@@ -14,9 +14,13 @@ LIB = os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "libindexer_fp4.so"
 
 @pytest.fixture(scope="module")
 def L():
-    if not os.path.exists(LIB):
-        from sparse_attention_indexer_fp4_amd import build
+    if not os.path.exists(LIB):  # build without importing the package (it loads the library)
+        import importlib.util
 
+        spec = importlib.util.spec_from_file_location(
+            "_ifp4_build", os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "build.py"))
+        build = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(build)
         build.build()
     lib = ctypes.CDLL(LIB)
     lib.indexer_fp4_last_error.restype = ctypes.c_char_p
@@ -36,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
@@ -107,3 +111,20 @@ def test_host_argument_errors(L):
     assert L.indexer_fp4_quant_and_cache(None, 4, 128, None, None, None, 1, None, 0, 0, None, None, None) == -1
     assert L.indexer_fp4_quant_and_cache(P(16), 4, 100, P(16), P(16), P(16), 1, None, 0, 0, None, None, None) == -1
     assert "k_ld=100" in _err(L)
+    F32 = ctypes.c_float
+    L.indexer_fp4_norm_rope_quant_and_cache.argtypes = [P, I64, I64, P, P, F32, P, P, I64, I32, I32, P, P, P, I64,
+                                                        P, I32, P, P, P, F32, P, I32, P, P]
+    fused = L.indexer_fp4_norm_rope_quant_and_cache
+
+    def call(rope_dim=0, bias=None, weight=None, eps=1e-6, positions=None, cs=None, max_pos=0, q=None, heads=0,
+             n_tok=4, k_ld=128):
+        return fused(P(16), n_tok, k_ld, weight, bias, eps, positions, cs, max_pos, rope_dim, 0, P(16), P(16),
+                     P(16), 1, q, heads, P(16), P(16), P(16), 1.0, P(16), 0, None, None)
+    assert call(rope_dim=24) == -1 and "rope_dim=24" in _err(L)
+    assert call(rope_dim=144) == -1
+    assert call(bias=P(16)) == -1 and "bias" in _err(L)
+    assert call(weight=P(16), eps=-1.0) == -1 and "eps" in _err(L)
+    assert call(rope_dim=64) == -1 and "cos/sin" in _err(L)
+    assert call(k_ld=120) == -1 and "k_ld=120" in _err(L)
+    assert call(q=P(16), heads=0) == -1 and "n_heads=0" in _err(L)
+    assert call(n_tok=-1) == -1

@@ -232,3 +232,49 @@ def step_keys(case: PrefillCase, step: PrefillStep):
         ks.append(case.keys[r][a:b])
         ss.append(case.slots[r][a:b])
     return np.concatenate(ks), np.concatenate(ss)
+
+
+# ---------------------------------------------------------------------------- fused writer inputs
+
+@dataclass
+class WriterCase:
+    """Inputs of the fused writer: per token a bf16 key, H bf16 query heads, fp32 head weights,
+    a rotary position and a cache slot, plus the LayerNorm parameters and the cos/sin table."""
+    k: np.ndarray          # uint16 [n_tok, 128] (bf16 bits)
+    q: np.ndarray          # uint16 [n_tok, H, 128]
+    w: np.ndarray          # float32 [n_tok, H]
+    gamma: np.ndarray      # float32 [128]
+    beta: np.ndarray       # float32 [128]
+    cos_sin: np.ndarray    # float32 [max_pos, rope_dim]: cos of the angles, then their sin
+    positions: np.ndarray  # int64 [n_tok]
+    slots: np.ndarray      # int64 [n_tok]
+    n_pages: int
+    rope_dim: int
+
+
+def rope_table(max_pos: int, rope_dim: int, base: float = 10000.0) -> np.ndarray:
+    """The usual rotary angle table: angle (p, i) = p * base^(-2i / rope_dim), stored as fp32
+    cos values for i < rope_dim/2 followed by the sin values."""
+    if rope_dim == 0:
+        return np.zeros((max_pos, 0), np.float32)
+    inv = base ** (-np.arange(rope_dim // 2, dtype=np.float64) * 2.0 / rope_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+def writer_case(n_tok, heads, rope_dim=64, max_pos=8192, seed=0, pad_every=0, key_scale=1.0) -> WriterCase:
+    """Keys ~ N(key_scale, 1)-ish activations (an offset so LayerNorm has a mean to remove), q ~
+    N(0, 1), weights ~ N(0, 1), gamma ~ U(0.5, 1.5), beta ~ U(-0.2, 0.2), positions uniform in the
+    table, every token on its own slot of a shuffled pool; every pad_every-th token has slot -1."""
+    rk, rq, rw, rg, rp, rs = _streams(seed, 6)
+    k = bf16_bits(rk.standard_normal((n_tok, HEAD_DIM)).astype(np.float32) + np.float32(key_scale))
+    q = normal_bf16(rq, (n_tok, heads, HEAD_DIM))
+    w = rw.standard_normal((n_tok, heads)).astype(np.float32)
+    gamma = rg.uniform(0.5, 1.5, HEAD_DIM).astype(np.float32)
+    beta = rg.uniform(-0.2, 0.2, HEAD_DIM).astype(np.float32)
+    positions = rp.integers(0, max_pos, n_tok).astype(np.int64)
+    n_pages = -(-n_tok // PAGE) + 1
+    slots = rs.permutation(n_pages * PAGE)[:n_tok].astype(np.int64)
+    if pad_every:
+        slots[::pad_every] = -1
+    return WriterCase(k, q, w, gamma, beta, rope_table(max_pos, rope_dim), positions, slots, n_pages, rope_dim)
