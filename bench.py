@@ -3,7 +3,8 @@
 
 A step is one decode step of the indexer over 21 layers at batch 8 x context 131072 (64
 index heads x 128, index_topk 2048): the decode schedule is published once, then every
-layer writes its 8 new keys and quantizes its queries (indexer_fp4_quant_and_cache),
+layer writes its 8 new keys and quantizes its queries with the fused writer (key LayerNorm,
+RoPE on keys and query heads, MXFP4 write, weights_mqa: indexer_fp4_norm_rope_quant_and_cache),
 scores all keys (indexer_fp4_score_decode) and selects the top-k (indexer_topk). Each layer
 has its own key cache (21 x 78 MB), so the scan streams from HBM instead of the 256 MB
 last-level cache. The pages' indexer has 21 layers ("Score a DSA sparse indexer in FP4",
@@ -33,6 +34,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4
+ROPE_DIM = 64                  # rotated leading elements of each 128-element key / query head
+WEIGHT_SCALE = (128 * 64) ** -0.5  # softmax scale 128^-1/2 times heads^-1/2
 METRIC = "indexer keys scored/sec + µs/layer decode & prefill; % HBM / MFMA roofline"
 
 
@@ -80,12 +83,18 @@ def build_decode(torch, ifp4, W, layers, units, seed):
         q = torch.randn((B, H, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
         w = torch.rand((B, H), generator=gen, device=dev, dtype=torch.float32)
         knew = torch.randn((B, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-        L.append(dict(kp=kp, ks=ks, q=q, w=w, knew=knew,
+        gamma = torch.rand(128, generator=gen, device=dev, dtype=torch.float32) + 0.5
+        beta = (torch.rand(128, generator=gen, device=dev, dtype=torch.float32) - 0.5) * 0.4
+        L.append(dict(kp=kp, ks=ks, q=q, w=w, knew=knew, gamma=gamma, beta=beta,
+                      wm=torch.empty((B, H), dtype=torch.float32, device=dev),
                       qp=torch.empty((B, H, 64), dtype=torch.uint8, device=dev),
                       qs=torch.empty((B, H, 4), dtype=torch.uint8, device=dev)))
     ld = bt.shape[1] * 64
     shared = dict(
         ctx=torch.from_numpy(ctx).to(dev), bt=bt_t, new_slots=new_slots,
+        # rotary table over the context and the new tokens' positions
+        cos_sin=torch.from_numpy(W.rope_table(int(ctx.max()), ROPE_DIM)).to(dev),
+        positions=torch.from_numpy((ctx - 1).astype(np.int64)).to(dev),
         sched=torch.empty(ifp4.indexer_fp4_decode_sched_bytes(B, 1, units), dtype=torch.uint8, device=dev),
         row_len=torch.empty(B, dtype=torch.int32, device=dev),
         logits=torch.empty((B, ld), dtype=torch.float32, device=dev),
@@ -106,17 +115,25 @@ def decode_step(ifp4, L, S, meta):
     units, ld, k = meta["units"], meta["ld"], meta["k"]
     ifp4.indexer_fp4_decode_schedule(S["ctx"], 1, units, S["sched"], S["row_len"])
     for lay in L:
-        ifp4.indexer_fp4_quant_and_cache(lay["knew"], S["new_slots"], lay["kp"], lay["ks"], lay["q"], lay["qp"],
-                                         lay["qs"])
-        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
+        write_decode(ifp4, lay, S)
+        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
                                       units, S["row_len"], S["logits"], S["hist"])
         ifp4.indexer_topk(S["logits"], S["row_len"], ld, k, S["top"], S["ws"], S["hist"])
+
+
+def write_decode(ifp4, lay, S):
+    """The layer's fused write: the new keys normalized, rotated and cached, the query heads
+    rotated and quantized, the head weights scaled (softmax scale times heads^-1/2)."""
+    ifp4.indexer_fp4_norm_rope_quant_and_cache(
+        lay["knew"], S["new_slots"], lay["kp"], lay["ks"], positions=S["positions"], cos_sin=S["cos_sin"],
+        rope_dim=ROPE_DIM, k_norm_weight=lay["gamma"], k_norm_bias=lay["beta"], eps=1e-6, q=lay["q"],
+        q_packed=lay["qp"], q_scale=lay["qs"], weights=lay["w"], weight_scale=WEIGHT_SCALE, weights_mqa=lay["wm"])
 
 
 def decode_scorers(ifp4, L, S, meta):
     """The step's 21 scorer launches alone (one per layer cache), histogram included."""
     for lay in L:
-        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["w"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
+        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
                                       meta["units"], S["row_len"], S["logits"], S["hist_scorer"])
 
 
@@ -165,11 +182,21 @@ def bench_decode(torch, ifp4, W, args):
     scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
     scorer_graph.replay()
     scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / args.layers
+    # the step's other per-layer kernel: the fused writer (and the plain writer beside it)
+    writer_graph = capture(torch, lambda: [write_decode(ifp4, lay, S) for lay in L])
+    writer_us = 1e3 * timed_replays(torch, writer_graph, args.steps) / args.layers
+    plain_graph = capture(torch, lambda: [ifp4.indexer_fp4_quant_and_cache(
+        lay["knew"], S["new_slots"], lay["kp"], lay["ks"], lay["q"], lay["qp"], lay["qs"]) for lay in L])
+    plain_us = 1e3 * timed_replays(torch, plain_graph, args.steps) / args.layers
+    for lay in L:  # leave the fused write's outputs in place
+        write_decode(ifp4, lay, S)
     keys_per_step = meta["n_keys"] * args.layers
     alg_bytes = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
     achieved = alg_bytes / (scorer_us * 1e-6) / 1e9
     return dict(meta=meta, ms_per_step=ms_per_step, wall_s=wall, keys_per_s=keys_per_step / (ms_per_step * 1e-3),
-                scorer_us=scorer_us, alg_bytes=alg_bytes, achieved_gbs=achieved)
+                scorer_us=scorer_us, alg_bytes=alg_bytes, achieved_gbs=achieved,
+                writer={"fused_us_per_layer": round(writer_us, 3), "plain_us_per_layer": round(plain_us, 3),
+                        "tokens": meta["B"], "heads": meta["H"], "rope_dim": ROPE_DIM})
 
 
 def bench_prefill(torch, ifp4, W, args):
@@ -384,6 +411,7 @@ def main():
                      "kernel": "score_decode", "launch_us_mean": round(d["scorer_us"], 3),
                      "alg_bytes_per_launch": d["alg_bytes"]},
         "cpu_baseline": cpu,
+        "writer": d["writer"],
         "prefill": pre,
         "dcp_merge": dcp,
     }

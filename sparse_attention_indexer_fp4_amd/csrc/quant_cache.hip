@@ -161,12 +161,45 @@ __device__ __forceinline__ uint4 pack8(const float x[8]) {
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// This lane's angle-table entries: element 8l + j of a rotated vector uses cos c[j] and sin
+// sn[j] (entries m and rope_dim/2 + m of the row, m its pair index). All 16 B loads: rope_dim
+// is a multiple of 16 and the table 16-byte aligned.
+__device__ __forceinline__ void rope_angles(const float *__restrict__ row, int l, int rope_dim, bool interleaved,
+                                            float c[8], float sn[8]) {
+  const int half = rope_dim >> 1;
+  if (interleaved) {  // pairs (2m, 2m+1): m = 4l .. 4l+3, each used twice
+    const float4 c4 = *reinterpret_cast<const float4 *>(row + 4 * l);
+    const float4 s4 = *reinterpret_cast<const float4 *>(row + half + 4 * l);
+    const float cc[4] = {c4.x, c4.y, c4.z, c4.w}, ss[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      c[j] = cc[j >> 1];
+      sn[j] = ss[j >> 1];
+    }
+  } else {  // pairs (m, m + half): m = (8l mod half) .. +7
+    const int m0 = (8 * l) % half;
+    const float4 c0 = *reinterpret_cast<const float4 *>(row + m0), c1 = *reinterpret_cast<const float4 *>(row + m0 + 4);
+    const float4 s0 = *reinterpret_cast<const float4 *>(row + half + m0);
+    const float4 s1 = *reinterpret_cast<const float4 *>(row + half + m0 + 4);
+    const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      c[j] = cc[j];
+      sn[j] = ss[j];
+    }
+  }
+}
+
 // Rotates this lane's elements 8l .. 8l+7 in place. All 16 lanes of the group call it.
-__device__ __forceinline__ void rope8(float x[8], int l, const float *__restrict__ cs, int rope_dim,
-                                      bool interleaved) {
+__device__ __forceinline__ void rope8(float x[8], int l, int rope_dim, bool interleaved, const float c[8],
+                                      const float sn[8]) {
   const int half = rope_dim >> 1;
   float part[8];
-  if (!interleaved) {  // partner lane: l +- half/8 inside the group
+  if (interleaved) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) part[j] = x[j ^ 1];
+  } else {  // partner lane: l +- half/8 inside the group
     const int hl = half >> 3;
     const int src = (threadIdx.x & 63 & ~15) + (l < hl ? l + hl : l - hl);
 #pragma unroll
@@ -175,26 +208,10 @@ __device__ __forceinline__ void rope8(float x[8], int l, const float *__restrict
   if (8 * l >= rope_dim) return;
 #pragma unroll
   for (int j = 0; j < 8; j++) {
-    const int i = 8 * l + j;
-    float a, b;
-    int m;
-    bool first;
-    if (interleaved) {
-      m = i >> 1;
-      first = (j & 1) == 0;
-      a = x[j];
-      b = x[j ^ 1];
-    } else {
-      first = i < half;
-      m = first ? i : i - half;
-      a = x[j];
-      b = part[j];
-    }
-    const float c = cs[m], sn = cs[half + m];
-    part[j] = first ? a * c - b * sn : a * c + b * sn;  // a is this element, b its partner
+    const bool first = interleaved ? (j & 1) == 0 : 8 * l < half;
+    // this element a, its partner b: the first of a pair becomes a cos - b sin, the second a cos + b sin
+    x[j] = first ? x[j] * c[j] - part[j] * sn[j] : x[j] * c[j] + part[j] * sn[j];
   }
-#pragma unroll
-  for (int j = 0; j < 8; j++) x[j] = part[j];
 }
 
 __global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
@@ -212,12 +229,31 @@ __global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
     const int l = (int)(i % kLanesPerVec);
     const int g = l >> 2;
     const bool is_key = v < n_tok;
-    const int64_t t = is_key ? v : (v - n_tok) / n_heads;  // token
-    // every decision below is uniform over the vector's 16 lanes
-    const int64_t pos = rope_dim > 0 ? positions[t] : 0;
-    const bool bad_pos = rope_dim > 0 && (pos < 0 || pos >= max_pos);
+    const int64_t vq = v - n_tok;
+    const int64_t t = is_key ? v : vq / n_heads;  // token
+    // Every load that needs only (token, lane) goes out first, in one round; only the angle
+    // table row waits for the position. Decisions are uniform over the vector's 16 lanes.
+    const int64_t pos_raw = rope_dim > 0 ? positions[t] : 0;
     const int64_t slot = slots[t];
-    const float *cs = cos_sin + (bad_pos ? 0 : pos) * rope_dim;
+    const uint4 raw = *reinterpret_cast<const uint4 *>(is_key ? k + t * k_ld + 8 * l : q + vq * kHeadDim + 8 * l);
+    float gm[8], bt[8];
+    const bool norm = is_key && gamma;
+    if (norm) {
+      const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * l), g1 = *reinterpret_cast<const float4 *>(gamma + 8 * l + 4);
+      gm[0] = g0.x, gm[1] = g0.y, gm[2] = g0.z, gm[3] = g0.w, gm[4] = g1.x, gm[5] = g1.y, gm[6] = g1.z, gm[7] = g1.w;
+      if (beta) {
+        const float4 b0 = *reinterpret_cast<const float4 *>(beta + 8 * l), b1 = *reinterpret_cast<const float4 *>(beta + 8 * l + 4);
+        bt[0] = b0.x, bt[1] = b0.y, bt[2] = b0.z, bt[3] = b0.w, bt[4] = b1.x, bt[5] = b1.y, bt[6] = b1.z, bt[7] = b1.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) bt[j] = 0.f;
+      }
+    }
+    const float wv = !is_key && l == 0 ? weights[vq] : 0.f;
+    const bool bad_pos = rope_dim > 0 && (pos_raw < 0 || pos_raw >= max_pos);
+    float c[8], sn[8];
+    if (rope_dim > 0 && 8 * l < rope_dim)
+      rope_angles(cos_sin + (bad_pos ? 0 : pos_raw) * rope_dim, l, rope_dim, interleaved, c, sn);
     uint32_t sc;
     if (is_key) {
       const bool in_pool = slot >= 0 && slot < n_pages * kPage;
@@ -226,8 +262,8 @@ __global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
                           (slot >= 0 && !in_pool ? INDEXER_FP4_DEV_SLOT_OUT_OF_POOL : 0));
       if (bad_pos || !in_pool) continue;
       float x[8];
-      unpack8(*reinterpret_cast<const uint4 *>(k + t * k_ld + 8 * l), x);
-      if (gamma) {
+      unpack8(raw, x);
+      if (norm) {
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; j++) s += x[j];
@@ -240,28 +276,27 @@ __global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
         }
         const float inv = 1.0f / sqrtf(group16_sum(ss) * (1.0f / kHeadDim) + eps);
 #pragma unroll
-        for (int j = 0; j < 8; j++) x[j] = x[j] * inv * gamma[8 * l + j] + (beta ? beta[8 * l + j] : 0.f);
+        for (int j = 0; j < 8; j++) x[j] = x[j] * inv * gm[j] + bt[j];
       }
-      if (rope_dim > 0) rope8(x, l, cs, rope_dim, interleaved);
+      if (rope_dim > 0) rope8(x, l, rope_dim, interleaved, c, sn);
       const uint32_t d = encode_lane8(pack8(x), sc);
       const int64_t page = slot / kPage;
       const int p = (int)(slot % kPage);
       *reinterpret_cast<uint32_t *>(kv_packed + (page * kPage + p) * kKeyBytes + 4 * l) = d;
       if ((l & 3) == 0) kv_scale[(page * kGroups + g) * kPage + (p % 16) * 4 + p / 16] = (uint8_t)sc;
     } else {
-      const int64_t vq = v - n_tok;
       const bool live = !bad_pos && (slot >= 0 || all_q);
       uint32_t d = 0;
       sc = 0;  // a skipped row stores the quantization of a zero vector and weight 0
       if (live) {
         float x[8];
-        unpack8(*reinterpret_cast<const uint4 *>(q + vq * kHeadDim + 8 * l), x);
-        if (rope_dim > 0) rope8(x, l, cs, rope_dim, interleaved);
+        unpack8(raw, x);
+        if (rope_dim > 0) rope8(x, l, rope_dim, interleaved, c, sn);
         d = encode_lane8(pack8(x), sc);
       }
       *reinterpret_cast<uint32_t *>(q_packed + vq * kKeyBytes + 4 * l) = d;
       if ((l & 3) == 0) q_scale[vq * kGroups + g] = (uint8_t)sc;
-      if (l == 0) weights_mqa[vq] = live ? weight_scale * weights[vq] : 0.f;
+      if (l == 0) weights_mqa[vq] = live ? weight_scale * wv : 0.f;
     }
   }
 }
@@ -336,6 +371,8 @@ extern "C" int indexer_fp4_norm_rope_quant_and_cache(
       return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: k and kv_packed must be 16-byte aligned");
     if (rope_dim > 0 && (!positions || !cos_sin || max_pos <= 0))
       return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: rope_dim=%d needs positions and a cos/sin table", rope_dim);
+    if (((uintptr_t)cos_sin | (uintptr_t)k_norm_weight | (uintptr_t)k_norm_bias) % 16 != 0)
+      return fail(INDEXER_FP4_EINVAL, "norm_rope_quant: cos_sin, k_norm_weight and k_norm_bias must be 16-byte aligned");
   }
   const bool q_arm = q_bf16 != nullptr && n_tok > 0;
   if (q_arm) {
