@@ -72,10 +72,17 @@ def _declare(L):
         "oracle_decode_schedule": [P, I32, I32, P, P, P, P, P],
         "oracle_prefill_schedule": [P, P, I32, I32, I32, I32, I32, P, P, P, P, P],
         "oracle_layer_norm": [P, I32, P, P, ctypes.c_float, P],
+        "oracle_mx8_encode_blocks": [P, I64, P, P],
+        "oracle_quant8_and_cache": [P, I64, I64, P, P, P, I64],
+        "oracle_quant8_q": [P, I64, I32, P, P],
+        "oracle_dequant8_key": [P, P, I64, I64, ctypes.c_int, P],
+        "oracle_score8": [P, P, P, I32, I64, P, P, P, P, I64, P, I64, P, I64, P],
         "oracle_rope": [P, I32, I32, P],
         "oracle_norm_rope_quant_and_cache": [P, I64, I64, P, P, ctypes.c_float, P, P, I64, I32, I32, P, P, P, I64,
                                              P, I32, P, P, P, ctypes.c_float, P, I32, P, P, P],
     }
+    L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+    L.oracle_e4m3_value.restype = ctypes.c_double
     L.oracle_bf16_round.argtypes = [ctypes.c_double]
     L.oracle_bf16_round.restype = ctypes.c_uint16
     for name, args in sigs.items():
@@ -159,6 +166,54 @@ def dequant_q(q_packed, q_scale, row, h):
     n_heads = q_packed.shape[1]
     _check(lib().oracle_dequant_q(_p(q_packed), _p(q_scale), int(row), n_heads, int(h), _p(out)), "dequant_q")
     return out
+
+
+# ---- MXFP8 comparator (reading R12 in oracle.c) ---------------------------------------
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(int(code))
+
+
+def mx8_encode_blocks(vals_bf16: np.ndarray):
+    """uint16 [n_blocks, 32] -> (scale uint8 [n_blocks], codes uint8 [n_blocks, 32])."""
+    v = _c(vals_bf16, np.uint16).reshape(-1, 32)
+    n = v.shape[0]
+    scale = np.zeros(n, np.uint8)
+    codes = np.zeros((n, 32), np.uint8)
+    _check(lib().oracle_mx8_encode_blocks(_p(v), n, _p(scale), _p(codes)), "mx8_encode_blocks")
+    return scale, codes
+
+
+def quant8_and_cache(k_bf16, slot_mapping, kv_packed, kv_scale):
+    """kv_packed uint8 [n_pages, 64, 128], kv_scale uint8 [n_pages, 4, 64], written in place."""
+    k = _c(k_bf16, np.uint16)
+    slots = _c(slot_mapping, np.int64)
+    n_pages = kv_packed.shape[0]
+    assert kv_packed.shape == (n_pages, 64, 128) and kv_scale.shape == (n_pages, 4, 64)
+    _check(lib().oracle_quant8_and_cache(_p(k), k.shape[0], k.shape[1], _p(slots), _p(kv_packed), _p(kv_scale),
+                                         n_pages), "quant8_and_cache")
+
+
+def quant8_q(q_bf16):
+    q = _c(q_bf16, np.uint16)
+    rows, h, d = q.shape
+    qp = np.zeros((rows, h, 128), np.uint8)
+    qs = np.zeros((rows, h, 4), np.uint8)
+    _check(lib().oracle_quant8_q(_p(q), rows, h, _p(qp), _p(qs)), "quant8_q")
+    return qp, qs
+
+
+def dequant8_key(kv_packed, kv_scale, page, pos):
+    out = np.zeros(128, np.float64)
+    _check(lib().oracle_dequant8_key(_p(kv_packed), _p(kv_scale), kv_packed.shape[0], int(page), int(pos), _p(out)),
+           "dequant8_key")
+    return out
+
+
+def score8(q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_table, ld=None, fill=np.nan):
+    """score() over MXFP8 planes."""
+    return _score_impl(lib().oracle_score8, q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale,
+                       block_table, ld, fill)
 
 
 # ---- fused writer: k_norm, RoPE, bf16 rounding (readings R8-R11 in oracle.c) ----------
@@ -251,6 +306,11 @@ def prefill_geometry(cu_rows, start_pos, n_rows_padded):
 
 def score(q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_table, ld=None, fill=np.nan):
     """fp64 logits [rows, ld]; entries at j >= row_len keep `fill`. Returns (logits, reads)."""
+    return _score_impl(lib().oracle_score, q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale,
+                       block_table, ld, fill)
+
+
+def _score_impl(fn, q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_table, ld, fill):
     qp = _c(q_packed, np.uint8)
     qs = _c(q_scale, np.uint8)
     w = _c(w, np.float32)
@@ -262,8 +322,8 @@ def score(q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_tab
         ld = max(int(rl.max()) if rl.size else 1, 1)
     out = np.full((rows, ld), fill, np.float64)
     reads = np.zeros(rows, np.int64)
-    _check(lib().oracle_score(_p(qp), _p(qs), _p(w), h, rows, _p(rs), _p(rl), _p(kv_packed), _p(kv_scale),
-                              kv_packed.shape[0], _p(bt), bt.shape[1], _p(out), ld, _p(reads)), "score")
+    _check(fn(_p(qp), _p(qs), _p(w), h, rows, _p(rs), _p(rl), _p(kv_packed), _p(kv_scale), kv_packed.shape[0],
+              _p(bt), bt.shape[1], _p(out), ld, _p(reads)), "score")
     return out, reads
 
 

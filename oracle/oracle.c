@@ -29,6 +29,13 @@
  *   R11 weights_mqa = weight_scale * weights; a row the writer skips (slot < 0
  *       unless all_q, or a position outside the table) gets zero weights and
  *       the quantization of a zero query.
+ * and, for the FP8 comparator (the pages compare against an FP8 indexer but do not
+ * give its format):
+ *   R12 FP8 is MXFP8 [OCP MX v1.0]: E4M3 elements (bias 7, largest 448, no
+ *       infinities) with one e8m0 scale per 32; scale exponent floor(log2 amax) - 8
+ *       clamped to [-127, 127]; elements nearest on the E4M3 grid, ties to the even
+ *       code, saturating at 448. The key cache is 128 code bytes per key in a plane
+ *       like the FP4 one, and the scale plane is the FP4 scale plane.
  */
 #include "oracle.h"
 
@@ -156,11 +163,133 @@ int oracle_quant_q(const uint16_t *q, int64_t n_rows, int32_t n_heads, uint8_t *
   return 0;
 }
 
+/* ---- MXFP8 (R12) ---------------------------------------------------------------- */
+
+/* E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+ * subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN [OCP 8-bit floating point]. */
+double oracle_e4m3_value(int code) {
+  int e = (code >> 3) & 15, m = code & 7;
+  double mag = e ? ldexp(1.0 + m / 8.0, e - 7) : ldexp(m / 8.0, -6);
+  if ((code & 0x7F) == 0x7F) mag = NAN;
+  return (code & 0x80) ? -mag : mag;
+}
+
+/* Nearest finite E4M3 magnitude code (0..0x7E) for x >= 0, ties to the even code;
+ * past 448 the nearest point is 448, the saturation. */
+static int e4m3_nearest_code(double x) {
+  int best = 0;
+  double best_d = fabs(x);
+  for (int c = 1; c <= 0x7E; c++) {
+    double d = fabs(x - oracle_e4m3_value(c));
+    if (d < best_d || (d == best_d && (c % 2) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return best;
+}
+
+static void encode_block8(const double *v, uint8_t *scale, uint8_t *codes) {
+  double amax = 0.0;
+  for (int i = 0; i < BLOCK_ELEMS; i++)
+    if (fabs(v[i]) > amax) amax = fabs(v[i]);
+  int e = -127;
+  if (amax > 0.0) {
+    int ex;
+    frexp(amax, &ex);
+    e = (ex - 1) - 8; /* E4M3's largest exponent is 8 */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+  }
+  *scale = (uint8_t)(e + 127);
+  for (int i = 0; i < BLOCK_ELEMS; i++) {
+    int code = e4m3_nearest_code(ldexp(fabs(v[i]), -e));
+    if (signbit(v[i])) code |= 0x80;
+    codes[i] = (uint8_t)code;
+  }
+}
+
+/* One 128-dim vector -> 128 code bytes (element d at byte d) + 4 scale bytes. */
+static void encode_vector8(const uint16_t *src, uint8_t *packed, uint8_t *scales) {
+  for (int g = 0; g < KEY_DIM / BLOCK_ELEMS; g++) {
+    double v[BLOCK_ELEMS];
+    for (int i = 0; i < BLOCK_ELEMS; i++) v[i] = bf16_to_double(src[g * BLOCK_ELEMS + i]);
+    encode_block8(v, &scales[g], &packed[g * BLOCK_ELEMS]);
+  }
+}
+
+int oracle_mx8_encode_blocks(const uint16_t *vals, int64_t n_blocks, uint8_t *scale, uint8_t *codes) {
+  if (n_blocks < 0) return -1;
+  for (int64_t b = 0; b < n_blocks; b++) {
+    double v[BLOCK_ELEMS];
+    for (int i = 0; i < BLOCK_ELEMS; i++) v[i] = bf16_to_double(vals[b * BLOCK_ELEMS + i]);
+    encode_block8(v, &scale[b], &codes[b * BLOCK_ELEMS]);
+  }
+  return 0;
+}
+
+int oracle_quant8_and_cache(const uint16_t *k, int64_t n_tok, int64_t k_ld, const int64_t *slot,
+                            uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages) {
+  if (n_tok < 0 || k_ld < KEY_DIM || n_pages < 0) return -1;
+  for (int64_t t = 0; t < n_tok; t++) {
+    if (slot[t] < 0) continue;
+    int64_t page = slot[t] / PAGE_KEYS;
+    int pos = (int)(slot[t] % PAGE_KEYS);
+    if (page >= n_pages) return -2;
+    uint8_t scales[4];
+    encode_vector8(&k[t * k_ld], &kv_packed[(page * PAGE_KEYS + pos) * KEY_DIM], scales);
+    for (int g = 0; g < 4; g++) kv_scale[(page * 4 + g) * PAGE_KEYS + oracle_scale_slot(pos)] = scales[g];
+  }
+  return 0;
+}
+
+int oracle_quant8_q(const uint16_t *q, int64_t n_rows, int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale) {
+  if (n_rows < 0 || n_heads <= 0) return -1;
+  for (int64_t v = 0; v < n_rows * n_heads; v++)
+    encode_vector8(&q[v * KEY_DIM], &q_packed[v * KEY_DIM], &q_scale[v * 4]);
+  return 0;
+}
+
+/* Element formats of the packed planes: 4 = MXFP4 (64 bytes a vector), 8 = MXFP8 (128). */
+static int vec_bytes(int fmt) { return fmt == 8 ? KEY_DIM : KEY_DIM / 2; }
+
 /* value of element d of a packed 128-dim vector with its 4 scale bytes */
+static double element_fmt(int fmt, const uint8_t *packed, const uint8_t scales[4], int d) {
+  double v;
+  if (fmt == 8) {
+    v = oracle_e4m3_value(packed[d]);
+  } else {
+    uint8_t byte = packed[d / 2];
+    v = oracle_e2m1_value((d % 2 == 0) ? (byte & 0xF) : (byte >> 4));
+  }
+  return v * oracle_e8m0_value(scales[d / BLOCK_ELEMS]);
+}
+
+static int dequant_key_fmt(int fmt, const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
+                           int64_t page, int pos, double *out) {
+  if (page < 0 || page >= n_pages || pos < 0 || pos >= PAGE_KEYS) return -1;
+  uint8_t scales[4];
+  for (int g = 0; g < 4; g++) scales[g] = kv_scale[(page * 4 + g) * PAGE_KEYS + oracle_scale_slot(pos)];
+  const uint8_t *packed = &kv_packed[(page * PAGE_KEYS + pos) * vec_bytes(fmt)];
+  for (int d = 0; d < KEY_DIM; d++) out[d] = element_fmt(fmt, packed, scales, d);
+  return 0;
+}
+
+static int dequant_q_fmt(int fmt, const uint8_t *q_packed, const uint8_t *q_scale, int64_t row, int32_t n_heads,
+                         int32_t h, double *out) {
+  if (row < 0 || h < 0 || h >= n_heads) return -1;
+  int64_t v = row * n_heads + h;
+  for (int d = 0; d < KEY_DIM; d++) out[d] = element_fmt(fmt, &q_packed[v * vec_bytes(fmt)], &q_scale[v * 4], d);
+  return 0;
+}
+
+int oracle_dequant8_key(const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages, int64_t page, int pos,
+                        double *out) {
+  return dequant_key_fmt(8, kv_packed, kv_scale, n_pages, page, pos, out);
+}
+
 static double element(const uint8_t *packed, const uint8_t scales[4], int d) {
-  uint8_t byte = packed[d / 2];
-  int code = (d % 2 == 0) ? (byte & 0xF) : (byte >> 4);
-  return oracle_e2m1_value(code) * oracle_e8m0_value(scales[d / BLOCK_ELEMS]);
+  return element_fmt(4, packed, scales, d);
 }
 
 int oracle_dequant_key(const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
@@ -228,12 +357,17 @@ static double score_one(const double *qd, const float *w, int32_t n_heads, const
   return s;
 }
 
-static int dequant_row_q(const uint8_t *q_packed, const uint8_t *q_scale, int64_t r, int32_t n_heads,
+static int dequant_row_q(int fmt, const uint8_t *q_packed, const uint8_t *q_scale, int64_t r, int32_t n_heads,
                          double *qd) {
   for (int32_t h = 0; h < n_heads; h++)
-    if (oracle_dequant_q(q_packed, q_scale, r, n_heads, h, &qd[h * KEY_DIM])) return -1;
+    if (dequant_q_fmt(fmt, q_packed, q_scale, r, n_heads, h, &qd[h * KEY_DIM])) return -1;
   return 0;
 }
+
+static int score_fmt(int fmt, const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
+                     int64_t n_rows, const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
+                     const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+                     double *logits, int64_t ld, int64_t *reads);
 
 /* Paged DSA index score ([P2] PR description: logits straight from the
  * paged FP4 cache; the page table maps a row's keys to pages). */
@@ -242,6 +376,23 @@ int oracle_score(const uint8_t *q_packed, const uint8_t *q_scale, const float *w
                  const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
                  const int32_t *block_table, int64_t bt_ld, double *logits, int64_t ld,
                  int64_t *reads) {
+  return score_fmt(4, q_packed, q_scale, w, n_heads, n_rows, row_seq, row_len, kv_packed, kv_scale, n_pages,
+                   block_table, bt_ld, logits, ld, reads);
+}
+
+/* The same score over MXFP8 queries and keys (R12). */
+int oracle_score8(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
+                  int64_t n_rows, const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
+                  const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+                  double *logits, int64_t ld, int64_t *reads) {
+  return score_fmt(8, q_packed, q_scale, w, n_heads, n_rows, row_seq, row_len, kv_packed, kv_scale, n_pages,
+                   block_table, bt_ld, logits, ld, reads);
+}
+
+static int score_fmt(int fmt, const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
+                     int64_t n_rows, const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
+                     const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+                     double *logits, int64_t ld, int64_t *reads) {
   if (n_heads <= 0 || n_rows < 0) return -1;
   double *qd = (double *)malloc(sizeof(double) * n_heads * KEY_DIM);
   if (!qd) return -3;
@@ -249,14 +400,14 @@ int oracle_score(const uint8_t *q_packed, const uint8_t *q_scale, const float *w
   for (int64_t r = 0; r < n_rows && !err; r++) {
     int64_t len = row_len[r];
     if (len > ld || (len + PAGE_KEYS - 1) / PAGE_KEYS > bt_ld) { err = -1; break; }
-    if (dequant_row_q(q_packed, q_scale, r, n_heads, qd)) { err = -1; break; }
+    if (dequant_row_q(fmt, q_packed, q_scale, r, n_heads, qd)) { err = -1; break; }
     const int32_t *bt = &block_table[(int64_t)row_seq[r] * bt_ld];
     int64_t nread = 0;
     int bad = 0;
 #pragma omp parallel for schedule(static) reduction(+ : nread) reduction(| : bad)
     for (int64_t j = 0; j < len; j++) {
       double kd[KEY_DIM];
-      if (oracle_dequant_key(kv_packed, kv_scale, n_pages, bt[j / PAGE_KEYS], (int)(j % PAGE_KEYS), kd)) {
+      if (dequant_key_fmt(fmt, kv_packed, kv_scale, n_pages, bt[j / PAGE_KEYS], (int)(j % PAGE_KEYS), kd)) {
         bad = 1;
         continue;
       }
@@ -284,7 +435,7 @@ int oracle_score_pairs(const uint8_t *q_packed, const uint8_t *q_scale, const fl
     double *qd = (double *)malloc(sizeof(double) * n_heads * KEY_DIM);
     double kd[KEY_DIM];
     if (!qd) { bad = 1; continue; }
-    if (dequant_row_q(q_packed, q_scale, r, n_heads, qd) ||
+    if (dequant_row_q(4, q_packed, q_scale, r, n_heads, qd) ||
         oracle_dequant_key(kv_packed, kv_scale, n_pages, block_table[(int64_t)row_seq[r] * bt_ld + j / PAGE_KEYS],
                            (int)(j % PAGE_KEYS), kd)) {
       bad = 1;

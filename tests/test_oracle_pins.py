@@ -729,3 +729,83 @@ def test_fused_writer_dequantizes_to_the_normalized_rotated_vector(interleaved):
             step = 2.0 ** (int(ks[0, blk, oracle.scale_slot(t)]) - 127)   # E2M1 grid step at 1 is 0.5 * scale
             bound = np.maximum(0.25 * step, 1.0 * step) + np.abs(want[sl]) * 2.0**-8
             assert (np.abs(got[sl] - np.clip(want[sl], -6 * step, 6 * step)) <= bound).all()
+
+
+# ---------------------------------------------------------------------------- MXFP8 comparator (R12)
+
+def test_e4m3_values_match_torch():
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = np.array([oracle.e4m3_value(int(c)) for c in codes])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    assert np.array_equal(got[~np.isnan(got)], want[~np.isnan(want)])
+
+
+def test_mx8_element_rounding_matches_torch_at_unit_scale():
+    """Every bf16 value of magnitude in [2^-12, 448], in blocks anchored by 256 (scale 2^0): the
+    codes are torch's fp32 -> float8_e4m3fn conversion (nearest, ties to even)."""
+    import torch
+
+    mags = []
+    for e in range(-12, 9):
+        for m in range(128):
+            v = (1 + m / 128) * 2.0**e
+            if v <= 448:
+                mags.append(v)
+    vals = np.array(mags + [-v for v in mags], np.float32)
+    vals = np.concatenate([vals, np.zeros((-len(vals)) % 31, np.float32)])
+    blocks = vals.reshape(-1, 31)
+    blocks = np.concatenate([np.full((blocks.shape[0], 1), 256.0, np.float32), blocks], axis=1)
+    bits = W.bf16_bits(blocks)
+    assert np.array_equal(W.bf16_to_f32(bits), blocks)  # all exact in bf16
+    scale, codes = oracle.mx8_encode_blocks(bits)
+    assert (scale == 127).all()
+    want = torch.from_numpy(blocks.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want)
+
+
+def test_mx8_scale_rule_and_saturation():
+    def enc(vals):
+        b = W.bf16_bits(np.asarray(vals, np.float32).reshape(1, 32))
+        return oracle.mx8_encode_blocks(b)
+
+    s, c = enc([1.0] + [0.0] * 31)           # amax 1: 2^(0 - 8), 1.0 -> 256 = 0x78
+    assert s[0] == 127 - 8 and c[0, 0] == 0x78
+    s, c = enc([448.0, 500.0] + [0.0] * 30)  # amax 500: scale 2^0, 500 saturates to 448
+    assert s[0] == 127 and c[0, 0] == 0x7E and c[0, 1] == 0x7E
+    s, c = enc([0.0] * 32)
+    assert s[0] == 0 and not c.any()
+    s, c = enc([-3.0e-39] + [0.0] * 31)      # the smallest scales clamp at 2^-127
+    assert s[0] == 0
+
+
+def test_fp8_scores_equal_fp4_scores_on_fp4_representable_data():
+    """E4M3 holds every E2M1 value, so data already on an MXFP4 grid passes through MXFP8
+    unchanged: the FP8 score equals the FP4 score exactly (an FP4-pinned quantity)."""
+    case = W.decode_case([300, 130], heads=16, topk=32, seed=12)
+    kp4 = np.zeros((case.n_pages, 64, 64), np.uint8)
+    ks4 = np.zeros((case.n_pages, 4, 64), np.uint8)
+    oracle.quant_and_cache(case.keys, case.slots, kp4, ks4)
+    qp4, qs4 = oracle.quant_q(case.q)
+    # bf16 images of the FP4-quantized vectors (exact: FP4 values times powers of two)
+    keys_q = np.zeros_like(case.keys)
+    for t, s in enumerate(case.slots):
+        keys_q[t] = W.bf16_bits(oracle.dequant_key(kp4, ks4, s // 64, s % 64).astype(np.float32))
+    q_q = np.zeros_like(case.q)
+    for r in range(case.rows):
+        for h in range(case.heads):
+            q_q[r, h] = W.bf16_bits(oracle.dequant_q(qp4, qs4, r, h).astype(np.float32))
+    kp8 = np.zeros((case.n_pages, 64, 128), np.uint8)
+    ks8 = np.zeros((case.n_pages, 4, 64), np.uint8)
+    oracle.quant8_and_cache(keys_q, case.slots, kp8, ks8)
+    qp8, qs8 = oracle.quant8_q(q_q)
+    rs, rl = oracle.decode_geometry(case.ctx)
+    s4, _ = oracle.score(qp4, qs4, case.w, rs, rl, kp4, ks4, case.block_table)
+    s8, _ = oracle.score8(qp8, qs8, case.w, rs, rl, kp8, ks8, case.block_table)
+    assert np.array_equal(np.isnan(s4), np.isnan(s8))
+    assert np.array_equal(s4[~np.isnan(s4)], s8[~np.isnan(s8)])
+    for t, s in enumerate(case.slots[:50]):  # and the keys decode to the same values
+        assert np.array_equal(oracle.dequant8_key(kp8, ks8, s // 64, s % 64),
+                              oracle.dequant_key(kp4, ks4, s // 64, s % 64))
