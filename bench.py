@@ -54,7 +54,9 @@ def decode_scorer_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -> int
     return n_keys * (64 + 4 + 4) + n_pages * 4 + rows * (heads * (64 + 4) + heads * 4 + 4)
 
 
-def build_decode(torch, ifp4, W, layers, units, seed):
+def build_decode(torch, ifp4, W, layers, units, seed, fp8=False):
+    """The decode workload's layers; with fp8, every layer also gets MXFP8 planes of the same
+    keys and queries (the FP8 comparator)."""
     dev = torch.device("cuda:0")
     case_ctx = W.DECODE_CONFIGS["decode_b8_128k"]
     ctx = np.array(case_ctx["ctx"], np.int32)
@@ -79,13 +81,22 @@ def build_decode(torch, ifp4, W, layers, units, seed):
         ks = torch.empty((n_pages, 4, 64), dtype=torch.uint8, device=dev)
         keys = torch.randn((B * int(ctx[0]), 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
         ifp4.indexer_fp4_quant_and_cache(keys, slots_all_t, kp, ks)
+        extra = {}
+        if fp8:
+            extra["kp8"] = torch.empty((n_pages, 64, 128), dtype=torch.uint8, device=dev)
+            extra["ks8"] = torch.empty((n_pages, 4, 64), dtype=torch.uint8, device=dev)
+            ifp4.indexer_fp8_quant_and_cache(keys, slots_all_t, extra["kp8"], extra["ks8"])
         del keys
         q = torch.randn((B, H, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        if fp8:
+            extra["qp8"] = torch.empty((B, H, 128), dtype=torch.uint8, device=dev)
+            extra["qs8"] = torch.empty((B, H, 4), dtype=torch.uint8, device=dev)
+            ifp4.indexer_fp8_quant_and_cache(None, None, extra["kp8"], extra["ks8"], q, extra["qp8"], extra["qs8"])
         w = torch.rand((B, H), generator=gen, device=dev, dtype=torch.float32)
         knew = torch.randn((B, 128), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
         gamma = torch.rand(128, generator=gen, device=dev, dtype=torch.float32) + 0.5
         beta = (torch.rand(128, generator=gen, device=dev, dtype=torch.float32) - 0.5) * 0.4
-        L.append(dict(kp=kp, ks=ks, q=q, w=w, knew=knew, gamma=gamma, beta=beta,
+        L.append(dict(kp=kp, ks=ks, q=q, w=w, knew=knew, gamma=gamma, beta=beta, **extra,
                       wm=torch.empty((B, H), dtype=torch.float32, device=dev),
                       qp=torch.empty((B, H, 64), dtype=torch.uint8, device=dev),
                       qs=torch.empty((B, H, 4), dtype=torch.uint8, device=dev)))
@@ -273,6 +284,46 @@ def bench_prefill(torch, ifp4, W, args):
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)})
 
 
+def bench_fp8_comparator(torch, ifp4, W, args):
+    """The pages' FP4-vs-FP8 scorer comparison on this hardware: the same decode workload's
+    keys and queries in MXFP8 planes, scored by the same scorer template; the step's 21 scorer
+    launches per replay for each format (no histogram, so only the scan differs)."""
+    L, S, meta = build_decode(torch, ifp4, W, args.layers, args.units, args.seed, fp8=True)
+    for lay in L:  # the FP4 queries and the scaled weights (the FP8 query planes hold the same queries unrotated)
+        write_decode(ifp4, lay, S)
+    ifp4.indexer_fp4_decode_schedule(S["ctx"], 1, meta["units"], S["sched"], S["row_len"])
+
+    def scorers(fp8):
+        fn = ifp4.indexer_fp8_score_decode if fp8 else ifp4.indexer_fp4_score_decode
+        for lay in L:
+            fn(lay["qp8"] if fp8 else lay["qp"], lay["qs8"] if fp8 else lay["qs"], lay["wm"],
+               lay["kp8"] if fp8 else lay["kp"], lay["ks8"] if fp8 else lay["ks"], S["bt"], 1, S["sched"],
+               meta["units"], S["row_len"], S["logits"])
+
+    us = {}
+    for name, fp8 in (("fp4", False), ("fp8", True)):
+        scorers(fp8)
+        g = capture(torch, lambda: scorers(fp8))
+        g.replay()
+        us[name] = 1e3 * timed_replays(torch, g, args.steps) / args.layers
+        del g
+    torch.cuda.synchronize()
+    if ifp4.sched_error(S["sched"]) != 0:
+        raise RuntimeError("fp8 comparator: device error flags")
+    n_keys, pages, B, H = meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"]
+    b4 = decode_scorer_bytes(n_keys, pages, B, H)
+    b8 = b4 + n_keys * 64 + B * H * 64  # 64 more code bytes per key and per query head
+    del L, S
+    torch.cuda.empty_cache()
+    return {"format": "MXFP8 (E4M3, e8m0 per 32)", "workload": "decode_b8_128k",
+            "fp4_scorer_us": round(us["fp4"], 3), "fp8_scorer_us": round(us["fp8"], 3),
+            "fp4_minus_fp8_us": round(us["fp4"] - us["fp8"], 3),
+            "time_ratio_fp4_over_fp8": round(us["fp4"] / us["fp8"], 4),
+            "cache_bytes_per_key": {"fp4": 68, "fp8": 132}, "byte_ratio_alg": round(b4 / b8, 4),
+            "fp8_achieved_gbs": round(b8 / (us["fp8"] * 1e-6) / 1e9, 1),
+            "fp8_frac": round(b8 / (us["fp8"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def bench_dcp_merge(torch, ifp4, args, shards=4, rows=8, k=2048):
     """Merge of `shards` local top-k candidate lists per row (context-parallel decode on one
     GPU's share; the exchange itself is not timed): one launch per layer."""
@@ -338,6 +389,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, a kernel of known traffic "
                          "for scaling hardware byte counters")
@@ -369,6 +421,11 @@ def main():
           f"({d['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
     pre = None
     dcp = bench_dcp_merge(torch, ifp4, args)
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = bench_fp8_comparator(torch, ifp4, W, args)
+        print(f"bench: fp8 comparator {fp8['fp4_scorer_us']:.2f} vs {fp8['fp8_scorer_us']:.2f} us", file=sys.stderr,
+              flush=True)
     if not args.no_prefill:
         pre = bench_prefill(torch, ifp4, W, args)
         print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us",
@@ -414,6 +471,7 @@ def main():
         "writer": d["writer"],
         "prefill": pre,
         "dcp_merge": dcp,
+        "fp8_comparator": fp8,
     }
     if rank == 0:
         print(json.dumps(line), flush=True)

@@ -226,6 +226,30 @@ int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale,
                              uint32_t *row_hist, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * FP8 comparator ([P2] PR description, Performance: the FP4 scorer is measured against
+ * the FP8 indexer's scorer, +2.3 us, and the scan's FP4/FP8 time ratio against the byte
+ * ratio). The pages give no FP8 format; these calls use OCP MXFP8: E4M3 elements (bias 7,
+ * largest 448, nearest with ties to even, saturating) with one e8m0 scale per 32 elements,
+ * scale exponent floor(log2 amax) - 8 clamped to [-127, 127].
+ *
+ * indexer_fp8_quant_and_cache: as indexer_fp4_quant_and_cache, but kv_packed is
+ *   [n_pages][64][128] (element d of a key at byte d) and q_packed [n_q_rows][n_heads][128];
+ *   the scale planes are laid out exactly as the FP4 ones.
+ * indexer_fp8_score_decode: as indexer_fp4_score_decode over those planes (same schedule,
+ *   lengths, logits, optional row histogram, errors).
+ * --------------------------------------------------------------------------------- */
+int indexer_fp8_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
+                                const int64_t *slot_mapping, uint8_t *kv_packed, uint8_t *kv_scale,
+                                int64_t n_pages, const void *q_bf16, int64_t n_q_rows, int32_t n_heads,
+                                uint8_t *q_packed, uint8_t *q_scale, void *stream);
+int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
+                             int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
+                             int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+                             int32_t batch, int32_t next_n, void *sched, int32_t n_units,
+                             const int32_t *row_len, float *logits, int64_t logits_ld,
+                             uint32_t *row_hist, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Prefill scorer ([P2] commit message: the FP4 prefill variant; [P1] section 3: the
  * row-group kernel finds a group's page table as group b -> block_tables[b]).
  * Same logit as decode for every valid row of the step; row r of request i reads its

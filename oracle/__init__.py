@@ -168,7 +168,7 @@ def dequant_q(q_packed, q_scale, row, h):
     return out
 
 
-# ---- MXFP8 comparator (reading R12 in oracle.c) ---------------------------------------
+# ---- MXFP8 comparator (reading R16 in oracle.c) ---------------------------------------
 
 def e4m3_value(code: int) -> float:
     return lib().oracle_e4m3_value(int(code))
@@ -216,7 +216,7 @@ def score8(q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_ta
                        block_table, ld, fill)
 
 
-# ---- fused writer: k_norm, RoPE, bf16 rounding (readings R8-R11 in oracle.c) ----------
+# ---- fused writer: k_norm, RoPE, bf16 rounding (readings R12-R15 in oracle.c) ----------
 
 def bf16_round(x) -> np.ndarray:
     """fp64 values -> nearest bf16 bit patterns (ties to even), elementwise."""

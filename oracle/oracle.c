@@ -18,20 +18,20 @@
  *   R7 top-k ties: the lower column wins.
  * and, for the fused writer (the pages name k_norm, RoPE on q and k and the
  * weights_mqa output of the widened writer, but print none of their formulas):
- *   R8  k_norm is a LayerNorm over the key's 128 elements with the biased
+ *   R12  k_norm is a LayerNorm over the key's 128 elements with the biased
  *       variance, (x - mean) / sqrt(var + eps) * gamma + beta; keys only, before RoPE.
- *   R9  RoPE rotates pairs of the first rope_dim elements of each key and query
+ *   R13  RoPE rotates pairs of the first rope_dim elements of each key and query
  *       head; the angle table row of the token's position holds cos[0, half) then
  *       sin[0, half); pair i is (i, i + half) (half-split) or (2i, 2i + 1)
  *       (interleaved) and turns (a, b) into (a cos - b sin, b cos + a sin).
- *   R10 the normalized, rotated vectors are rounded to bf16 (nearest, ties to
+ *   R14 the normalized, rotated vectors are rounded to bf16 (nearest, ties to
  *       even) and then quantized exactly like plain bf16 writer input.
- *   R11 weights_mqa = weight_scale * weights; a row the writer skips (slot < 0
+ *   R15 weights_mqa = weight_scale * weights; a row the writer skips (slot < 0
  *       unless all_q, or a position outside the table) gets zero weights and
  *       the quantization of a zero query.
  * and, for the FP8 comparator (the pages compare against an FP8 indexer but do not
  * give its format):
- *   R12 FP8 is MXFP8 [OCP MX v1.0]: E4M3 elements (bias 7, largest 448, no
+ *   R16 FP8 is MXFP8 [OCP MX v1.0]: E4M3 elements (bias 7, largest 448, no
  *       infinities) with one e8m0 scale per 32; scale exponent floor(log2 amax) - 8
  *       clamped to [-127, 127]; elements nearest on the E4M3 grid, ties to the even
  *       code, saturating at 448. The key cache is 128 code bytes per key in a plane
@@ -163,7 +163,7 @@ int oracle_quant_q(const uint16_t *q, int64_t n_rows, int32_t n_heads, uint8_t *
   return 0;
 }
 
-/* ---- MXFP8 (R12) ---------------------------------------------------------------- */
+/* ---- MXFP8 (R16) ---------------------------------------------------------------- */
 
 /* E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
  * subnormal (m/8 * 2^-6); 0x7F / 0xFF are NaN [OCP 8-bit floating point]. */
@@ -380,7 +380,7 @@ int oracle_score(const uint8_t *q_packed, const uint8_t *q_scale, const float *w
                    block_table, bt_ld, logits, ld, reads);
 }
 
-/* The same score over MXFP8 queries and keys (R12). */
+/* The same score over MXFP8 queries and keys (R16). */
 int oracle_score8(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
                   int64_t n_rows, const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
                   const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
@@ -585,7 +585,7 @@ int oracle_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, in
  * normalizes keys with k_norm before the quantizer, applies RoPE to q and k,
  * skips slot < 0 rows and must zero weights_mqa for the rows it skips) ------- */
 
-/* Nearest bf16 to x, ties to even (R10): bf16 keeps fp32's exponent range and 8
+/* Nearest bf16 to x, ties to even (R14): bf16 keeps fp32's exponent range and 8
  * significant bits; below 2^-126 its step is 2^-133. Returns the bit pattern. */
 uint16_t oracle_bf16_round(double x) {
   if (isnan(x)) return 0x7FC0;
@@ -603,7 +603,7 @@ uint16_t oracle_bf16_round(double x) {
   return sign | (uint16_t)(u >> 16);
 }
 
-/* R8 */
+/* R12 */
 int oracle_layer_norm(const double *x, int32_t n, const float *gamma, const float *beta, float eps, double *y) {
   if (n <= 0) return -1;
   double mean = 0.0, var = 0.0;
@@ -616,7 +616,7 @@ int oracle_layer_norm(const double *x, int32_t n, const float *gamma, const floa
   return 0;
 }
 
-/* R9, in place on x[0, rope_dim); cs is the table row {cos[half], sin[half]}. */
+/* R13, in place on x[0, rope_dim); cs is the table row {cos[half], sin[half]}. */
 int oracle_rope(double *x, int32_t rope_dim, int32_t interleaved, const float *cs) {
   if (rope_dim < 0 || rope_dim % 2) return -1;
   int half = rope_dim / 2;
@@ -634,7 +634,7 @@ static void zero_vector(uint8_t *packed, uint8_t *scales) {
   encode_vector(z, packed, scales);
 }
 
-/* The fused writer, token by token (R8-R11). k_pre / q_pre (optional) receive
+/* The fused writer, token by token (R12-R15). k_pre / q_pre (optional) receive
  * the fp64 vectors just before bf16 rounding (NaN for rows not computed). err
  * gets 16 for a position outside [0, max_pos) with rope_dim > 0 and 32 for a
  * slot past the pool (key skipped). */

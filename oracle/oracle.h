@@ -112,7 +112,7 @@ int oracle_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, in
                             int32_t max_tiles, int32_t *n_tiles, int32_t *tiles, int32_t *cum_items,
                             int32_t *unit_begin, int32_t *unit_tile);
 
-/* MXFP8 comparator (reading R12 in oracle.c): E4M3 value of a code; blocks of 32
+/* MXFP8 comparator (reading R16 in oracle.c): E4M3 value of a code; blocks of 32
  * bf16 values -> e8m0 byte + 32 codes; cache write (kv_packed [n_pages][64][128]) and
  * query quantization (q_packed [n_rows][n_heads][128]) with the FP4 scale layout;
  * one dequantized key; the paged score as oracle_score. */
@@ -128,7 +128,7 @@ int oracle_score8(const uint8_t *q_packed, const uint8_t *q_scale, const float *
                   const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
                   double *logits, int64_t ld, int64_t *reads);
 
-/* Fused writer pieces and composition (readings R8-R11 in oracle.c). */
+/* Fused writer pieces and composition (readings R12-R15 in oracle.c). */
 uint16_t oracle_bf16_round(double x);
 int oracle_layer_norm(const double *x, int32_t n, const float *gamma, const float *beta, float eps, double *y);
 int oracle_rope(double *x, int32_t rope_dim, int32_t interleaved, const float *cs);

@@ -34,6 +34,8 @@ EXPORTS = (
     "indexer_fp4_prefill_schedule",
     "indexer_fp4_score_decode",
     "indexer_fp4_score_prefill",
+    "indexer_fp8_quant_and_cache",
+    "indexer_fp8_score_decode",
     "indexer_topk_workspace_bytes",
     "indexer_topk_merge",
     "indexer_topk",
@@ -62,6 +64,8 @@ def _load() -> ctypes.CDLL:
         "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P], ctypes.c_int),
+        "indexer_fp8_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
+        "indexer_fp8_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P], ctypes.c_int),
         "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
         "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P, P], ctypes.c_int),
         "indexer_topk_merge": ([P, P, I64, I32, I32, I32, P, I64, P], ctypes.c_int),
@@ -103,6 +107,20 @@ def indexer_fp4_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, q=None, q_
     """k: bf16 [n_tok, >=128] (row stride k.stride(0)); slot_mapping int64 [n_tok];
     kv_packed uint8 [n_pages, 64, 64]; kv_scale uint8 [n_pages, 4, 64];
     q: bf16 [rows, H, 128] or None -> q_packed uint8 [rows, H, 64], q_scale uint8 [rows, H, 4]."""
+    _quant(lib.indexer_fp4_quant_and_cache, 64, k, slot_mapping, kv_packed, kv_scale, q, q_packed, q_scale)
+
+
+def indexer_fp8_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, q=None, q_packed=None, q_scale=None):
+    """MXFP8 comparator writer: as indexer_fp4_quant_and_cache with kv_packed uint8
+    [n_pages, 64, 128] and q_packed uint8 [rows, H, 128]."""
+    _quant(lib.indexer_fp8_quant_and_cache, 128, k, slot_mapping, kv_packed, kv_scale, q, q_packed, q_scale)
+
+
+def _quant(fn, vec_bytes, k, slot_mapping, kv_packed, kv_scale, q, q_packed, q_scale):
+    if kv_packed.dim() != 3 or kv_packed.shape[1:] != (64, vec_bytes):
+        raise ValueError(f"kv_packed must be [n_pages, 64, {vec_bytes}]")
+    if q_packed is not None and q_packed.shape[-1] != vec_bytes:
+        raise ValueError(f"q_packed rows must hold {vec_bytes} bytes")
     _dev(kv_packed, "kv_packed", torch.uint8)
     _dev(kv_scale, "kv_scale", torch.uint8)
     n_tok = 0 if k is None else k.shape[0]
@@ -119,7 +137,7 @@ def indexer_fp4_quant_and_cache(k, slot_mapping, kv_packed, kv_scale, q=None, q_
             raise ValueError("q must be [rows, heads, 128]")
         _dev(q_packed, "q_packed", torch.uint8)
         _dev(q_scale, "q_scale", torch.uint8)
-    _check(lib.indexer_fp4_quant_and_cache(
+    _check(fn(
         _ptr(k), n_tok, 0 if k is None else k.stride(0), _ptr(slot_mapping), _ptr(kv_packed), _ptr(kv_scale),
         kv_packed.shape[0], _ptr(q), rows, heads, _ptr(q_packed), _ptr(q_scale), _stream(kv_packed)))
 
@@ -203,6 +221,21 @@ def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, bl
 
     row_hist: optional int32 [B*next_n, 4096] (zero-filled before first use; see
     row_histogram) that the scorer fills for indexer_topk."""
+    _score_decode(lib.indexer_fp4_score_decode, 64, q_packed, q_scale, weights, kv_packed, kv_scale, block_table,
+                  next_n, sched, n_units, row_len, logits, row_hist)
+
+
+def indexer_fp8_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched, n_units,
+                             row_len, logits, row_hist=None):
+    """MXFP8 comparator scorer: as indexer_fp4_score_decode over 128-byte vectors."""
+    _score_decode(lib.indexer_fp8_score_decode, 128, q_packed, q_scale, weights, kv_packed, kv_scale, block_table,
+                  next_n, sched, n_units, row_len, logits, row_hist)
+
+
+def _score_decode(fn, vec_bytes, q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched,
+                  n_units, row_len, logits, row_hist):
+    if kv_packed.dim() != 3 or kv_packed.shape[1:] != (64, vec_bytes) or q_packed.shape[-1] != vec_bytes:
+        raise ValueError(f"planes must hold {vec_bytes}-byte vectors")
     _dev(q_packed, "q_packed", torch.uint8)
     _dev(q_scale, "q_scale", torch.uint8)
     _dev(weights, "weights", torch.float32)
@@ -216,7 +249,7 @@ def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, bl
         raise ValueError("logits rows must be contiguous")
     batch, bt_ld = block_table.shape
     _check_hist(row_hist, batch * next_n)
-    _check(lib.indexer_fp4_score_decode(
+    _check(fn(
         _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
         kv_packed.shape[0], _ptr(block_table), bt_ld, batch, next_n, _ptr(sched), n_units, _ptr(row_len),
         _ptr(logits), logits.stride(0), _ptr(row_hist), _stream(logits)))

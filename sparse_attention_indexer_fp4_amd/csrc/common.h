@@ -18,6 +18,8 @@ constexpr int kKeyBytes = kHeadDim / 2;          // packed E2M1 bytes per key (6
 constexpr int kGroups = kHeadDim / 32;           // e8m0 scales per key (4)
 constexpr int kPageBytes = kPage * kKeyBytes;    // packed plane bytes per page (4096)
 constexpr int kPageScaleBytes = kPage * kGroups; // scale plane bytes per page (256)
+constexpr int kKeyBytes8 = kHeadDim;             // MXFP8 (comparator): E4M3 bytes per key (128)
+constexpr int kPageBytes8 = kPage * kKeyBytes8;  // its packed plane bytes per page (8192)
 constexpr int kTileRows = INDEXER_FP4_TILE_ROWS; // prefill rows per tile
 
 // ---- errors (thread-local message, see indexer_fp4_last_error) -------------------------

@@ -114,6 +114,98 @@ __global__ __launch_bounds__(256) void quant_cache_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP8 writer for the FP8 comparator (the pages compare the FP4 indexer with an FP8 one
+// but give no FP8 format; this is OCP MXFP8): E4M3 elements (bias 7, largest 448, no
+// infinities) with one e8m0 scale per 32, scale exponent floor(log2 amax) - 8 clamped to
+// [-127, 127], elements rounded to nearest with ties to even and saturated at 448. Same
+// lanes as the FP4 writer; element d of a vector is byte d, scales in the FP4 scale plane.
+
+// floor(log2 amax) - 8, clamped; -127 for an all-zero block.
+__device__ __forceinline__ int block_exponent8(uint32_t amag) {
+  if (amag == 0) return -127;
+  const uint32_t ex = amag >> 7;
+  const uint32_t sig = ex ? (0x80u | (amag & 0x7Fu)) : (amag & 0x7Fu);
+  const int ep = ex ? (int)ex : 1;
+  const int e = (31 - __builtin_clz(sig)) + ep - 134 - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E4M3 code of bf16 bits b divided by 2^e. The magnitude is M * 2^(E - 7) with M the 8-bit
+// significand (no hidden bit for bf16 subnormals); its E4M3 step is 2^(max(L, -6) - 3) for
+// leading exponent L, so the code's significand is M shifted right by the difference,
+// rounded to nearest even; a carry into the exponent field is the correct next code.
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t b, int e) {
+  const uint32_t sign = (b >> 8) & 0x80u;
+  const uint32_t mag = b & 0x7FFFu;
+  if (mag == 0) return sign;
+  const uint32_t ex = mag >> 7;
+  const int M = (int)(ex ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu));
+  const int Ep = (ex ? (int)ex - 127 : -126) - e;          // value = M * 2^(Ep - 7)
+  const int L = Ep - 7 + (31 - __builtin_clz((uint32_t)M));  // floor(log2 value)
+  const int qe = (L > -6 ? L : -6) - 3;                     // log2 of the E4M3 step there
+  const int sh = qe - (Ep - 7);
+  int n;
+  if (sh <= 0) {
+    n = M << (-sh);  // exact (fewer significant bits than the step allows)
+  } else if (sh > 9) {
+    n = 0;           // below half the smallest step
+  } else {
+    n = M >> sh;
+    const int rem = M & ((1 << sh) - 1), half = 1 << (sh - 1);
+    n += (rem > half || (rem == half && (n & 1))) ? 1 : 0;
+  }
+  uint32_t code = qe == -9 ? (uint32_t)n : (uint32_t)(((qe + 10) << 3) + (n - 8));
+  if (code > 0x7Eu) code = 0x7Eu;  // saturate at 448 (0x7F is NaN)
+  return code | sign;
+}
+
+// This lane's eight bf16 -> eight E4M3 bytes (element i in byte i) and the block's scale.
+__device__ __forceinline__ uint2 encode8_lane8(uint4 in, uint32_t &scale) {
+  const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+  uint32_t amag = 0;
+#pragma unroll
+  for (int h = 0; h < 4; h++) amag = max(amag, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
+  amag = max(amag, (uint32_t)__shfl_xor((int)amag, 1, 64));
+  amag = max(amag, (uint32_t)__shfl_xor((int)amag, 2, 64));
+  const int e = block_exponent8(amag);
+  scale = (uint32_t)(e + 127);
+  uint32_t o[2] = {0u, 0u};
+#pragma unroll
+  for (int h = 0; h < 4; h++)
+    o[h >> 1] |= (e4m3_code(w[h] & 0xFFFFu, e) | (e4m3_code(w[h] >> 16, e) << 8)) << (16 * (h & 1));
+  return make_uint2(o[0], o[1]);
+}
+
+__global__ __launch_bounds__(256) void quant8_cache_kernel(
+    const uint16_t *__restrict__ k, int64_t n_tok, int64_t k_ld, const int64_t *__restrict__ slots,
+    uint8_t *__restrict__ kv_packed, uint8_t *__restrict__ kv_scale, int64_t n_pages,
+    const uint16_t *__restrict__ q, int64_t n_q_vec, uint8_t *__restrict__ q_packed,
+    uint8_t *__restrict__ q_scale) {
+  const int64_t total = (n_tok + n_q_vec) * kLanesPerVec;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int64_t v = i / kLanesPerVec;
+    const int l = (int)(i % kLanesPerVec);
+    const int g = l >> 2;
+    uint32_t sc;
+    if (v < n_tok) {
+      const int64_t slot = slots[v];
+      if (slot < 0 || slot >= n_pages * kPage) continue;
+      const uint2 d = encode8_lane8(*reinterpret_cast<const uint4 *>(k + v * k_ld + 8 * l), sc);
+      const int64_t page = slot / kPage;
+      const int pos = (int)(slot % kPage);
+      *reinterpret_cast<uint2 *>(kv_packed + (page * kPage + pos) * kKeyBytes8 + 8 * l) = d;
+      if ((l & 3) == 0) kv_scale[(page * kGroups + g) * kPage + (pos % 16) * 4 + pos / 16] = (uint8_t)sc;
+    } else {
+      const int64_t vq = v - n_tok;
+      const uint2 d = encode8_lane8(*reinterpret_cast<const uint4 *>(q + vq * kHeadDim + 8 * l), sc);
+      *reinterpret_cast<uint2 *>(q_packed + vq * kKeyBytes8 + 8 * l) = d;
+      if ((l & 3) == 0) q_scale[vq * kGroups + g] = (uint8_t)sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // Fused writer: key LayerNorm (k_norm), RoPE on keys and query heads, then the MXFP4 write
 // above, plus the scorer's per-head weights ("Score a DSA sparse indexer in FP4", commit
 // message: the widened writer emits the quantized query and weights_mqa, and k_norm runs
@@ -305,11 +397,9 @@ __global__ __launch_bounds__(256) void norm_rope_quant_cache_kernel(
 
 using namespace ifp4;
 
-extern "C" int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
-                                           const int64_t *slot_mapping, uint8_t *kv_packed,
-                                           uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
-                                           int64_t n_q_rows, int32_t n_heads, uint8_t *q_packed,
-                                           uint8_t *q_scale, void *stream) {
+static int quant_and_cache(bool fp8, const void *k_bf16, int64_t n_tok, int64_t k_ld, const int64_t *slot_mapping,
+                           uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
+                           int64_t n_q_rows, int32_t n_heads, uint8_t *q_packed, uint8_t *q_scale, void *stream) {
   clear_error();
   if (n_tok < 0 || n_pages < 0 || n_q_rows < 0)
     return fail(INDEXER_FP4_EINVAL, "negative size: n_tok=%lld n_pages=%lld n_q_rows=%lld",
@@ -338,10 +428,28 @@ extern "C" int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, in
   const int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(quant_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0, (hipStream_t)stream,
-                     (const uint16_t *)k_bf16, n_tok, k_ld, slot_mapping, kv_packed, kv_scale, n_pages,
-                     (const uint16_t *)q_bf16, n_q_vec, q_packed, q_scale);
-  return launch_status("quant_and_cache");
+  hipLaunchKernelGGL(fp8 ? quant8_cache_kernel : quant_cache_kernel, dim3((unsigned)blocks), dim3(threads), 0,
+                     (hipStream_t)stream, (const uint16_t *)k_bf16, n_tok, k_ld, slot_mapping, kv_packed, kv_scale,
+                     n_pages, (const uint16_t *)q_bf16, n_q_vec, q_packed, q_scale);
+  return launch_status(fp8 ? "fp8_quant_and_cache" : "quant_and_cache");
+}
+
+extern "C" int indexer_fp4_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
+                                           const int64_t *slot_mapping, uint8_t *kv_packed,
+                                           uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
+                                           int64_t n_q_rows, int32_t n_heads, uint8_t *q_packed,
+                                           uint8_t *q_scale, void *stream) {
+  return quant_and_cache(false, k_bf16, n_tok, k_ld, slot_mapping, kv_packed, kv_scale, n_pages, q_bf16, n_q_rows,
+                         n_heads, q_packed, q_scale, stream);
+}
+
+extern "C" int indexer_fp8_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
+                                           const int64_t *slot_mapping, uint8_t *kv_packed,
+                                           uint8_t *kv_scale, int64_t n_pages, const void *q_bf16,
+                                           int64_t n_q_rows, int32_t n_heads, uint8_t *q_packed,
+                                           uint8_t *q_scale, void *stream) {
+  return quant_and_cache(true, k_bf16, n_tok, k_ld, slot_mapping, kv_packed, kv_scale, n_pages, q_bf16, n_q_rows,
+                         n_heads, q_packed, q_scale, stream);
 }
 
 extern "C" int indexer_fp4_norm_rope_quant_and_cache(

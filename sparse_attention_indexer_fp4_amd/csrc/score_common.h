@@ -114,4 +114,148 @@ __device__ __forceinline__ float page_logit(const PageRegs &P, const RowRegs<NH1
   return keep + __shfl_xor(odd ? kx : ky, 16, 64);
 }
 
+// ---------------------------------------------------------------------------------------
+// The same building blocks over MXFP8 (E4M3) queries and keys, for the FP8 comparator. The
+// 16x16x128 scaled MFMA takes 32 FP8 bytes per lane; probed on the device, lane group g
+// (lanes 16g .. 16g+15) carries K elements [16g, 16g+16) in its first 16 bytes and
+// [64+16g, 64+16g+16) in its last 16, while its scale operand applies to the 32-element
+// block g, exactly as for FP4. So a lane loads its key's bytes 16g and 64+16g (16 each),
+// and the scale plane and its dword per lane are the FP4 ones.
+
+template <int SA, int SB>
+__device__ __forceinline__ floatx4 mfma_fp8(const uint4 (&a)[2], const uint4 (&b)[2], floatx4 c, uint32_t sa,
+                                            uint32_t sb) {
+  intx8 av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w, (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+  intx8 bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w, (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, SA, (int)sa, SB, (int)sb);
+}
+
+struct PageRegs8 {
+  uint4 k[4][2];  // 4 key tiles x (bytes 16g.., bytes 64+16g..)
+  uint32_t s;
+};
+
+template <int NH16, int NN>
+struct RowRegs8 {
+  uint4 qa[NN][NH16][2];
+  uint32_t qs[NN][(NH16 + 3) / 4];
+  float4 w[NN][NH16];
+};
+
+template <int NH16, int NN>
+__device__ __forceinline__ void load_rows8(RowRegs8<NH16, NN> &R, const uint8_t *__restrict__ qp,
+                                           const uint8_t *__restrict__ qs, const float *__restrict__ w,
+                                           int64_t row0, int n_valid, int n_heads, int lane) {
+  const int hl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int n = 0; n < NN; n++) {
+    if (n >= n_valid) break;
+    const int64_t r = row0 + n;
+#pragma unroll
+    for (int j = 0; j < (NH16 + 3) / 4; j++) R.qs[n][j] = 0;
+#pragma unroll
+    for (int m = 0; m < NH16; m++) {
+      const int64_t v = r * n_heads + 16 * m + hl;
+      R.qa[n][m][0] = *reinterpret_cast<const uint4 *>(qp + v * kKeyBytes8 + 16 * g);
+      R.qa[n][m][1] = *reinterpret_cast<const uint4 *>(qp + v * kKeyBytes8 + 64 + 16 * g);
+      R.qs[n][m / 4] |= (uint32_t)qs[v * kGroups + g] << (8 * (m % 4));
+      R.w[n][m] = *reinterpret_cast<const float4 *>(w + r * n_heads + 16 * m + 4 * g);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the query loads, as in load_rows
+}
+
+__device__ __forceinline__ void load_page8(PageRegs8 &P, const uint8_t *__restrict__ kvp,
+                                           const uint8_t *__restrict__ kvs, int64_t phys, int lane) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const uint8_t *base = kvp + phys * kPageBytes8 + (lane & 15) * kKeyBytes8 + (lane >> 4) * 16;
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(base + 2048 * t + 64 * h));
+      P.k[t][h] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  }
+  P.s = *reinterpret_cast<const uint32_t *>(kvs + phys * kPageScaleBytes + 4 * lane);
+}
+
+template <int NH16, int NN, int N>
+__device__ __forceinline__ float page_logit8(const PageRegs8 &P, const RowRegs8<NH16, NN> &R, int lane) {
+  float acc[4];
+  floatx4 c[2][NH16];
+  auto mfmas = [&](auto tt) {
+    constexpr int T = decltype(tt)::value;
+    static_for<NH16>([&](auto mm) {
+      constexpr int M = decltype(mm)::value;
+      const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+      c[T & 1][M] = mfma_fp8<M % 4, T>(R.qa[N][M], P.k[T], zero, R.qs[N][M / 4], P.s);
+    });
+  };
+  auto epilogue = [&](auto tt) {
+    constexpr int T = decltype(tt)::value;
+    float a = 0.f;
+    static_for<NH16>([&](auto mm) {
+      constexpr int M = decltype(mm)::value;
+      a += R.w[N][M].x * relu(c[T & 1][M][0]);
+      a += R.w[N][M].y * relu(c[T & 1][M][1]);
+      a += R.w[N][M].z * relu(c[T & 1][M][2]);
+      a += R.w[N][M].w * relu(c[T & 1][M][3]);
+    });
+    acc[T] = a;
+  };
+  mfmas(std::integral_constant<int, 0>{});
+  static_for<4>([&](auto tt) {
+    constexpr int T = decltype(tt)::value;
+    if constexpr (T + 1 < 4) mfmas(std::integral_constant<int, T + 1>{});
+    epilogue(tt);
+  });
+  const int G = lane >> 4;
+  const bool lo = G < 2;
+  float kx = lo ? acc[0] : acc[2];
+  float ky = lo ? acc[1] : acc[3];
+  kx += __shfl_xor(lo ? acc[2] : acc[0], 32, 64);
+  ky += __shfl_xor(lo ? acc[3] : acc[1], 32, 64);
+  const bool odd = G & 1;
+  const float keep = odd ? ky : kx;
+  return keep + __shfl_xor(odd ? kx : ky, 16, 64);
+}
+
+// Element-format policies of the decode scorer.
+struct FmtFp4 {
+  using Page = PageRegs;
+  template <int NH16, int NN>
+  using Rows = RowRegs<NH16, NN>;
+  static __device__ __forceinline__ void page(Page &P, const uint8_t *kvp, const uint8_t *kvs, int64_t phys, int lane) {
+    load_page(P, kvp, kvs, phys, lane);
+  }
+  template <int NH16, int NN>
+  static __device__ __forceinline__ void rows(Rows<NH16, NN> &R, const uint8_t *qp, const uint8_t *qs, const float *w,
+                                              int64_t row0, int n_valid, int n_heads, int lane) {
+    load_rows<NH16, NN>(R, qp, qs, w, row0, n_valid, n_heads, lane);
+  }
+  template <int NH16, int NN, int N>
+  static __device__ __forceinline__ float logit(const Page &P, const Rows<NH16, NN> &R, int lane) {
+    return page_logit<NH16, NN, N>(P, R, lane);
+  }
+};
+
+struct FmtFp8 {
+  using Page = PageRegs8;
+  template <int NH16, int NN>
+  using Rows = RowRegs8<NH16, NN>;
+  static __device__ __forceinline__ void page(Page &P, const uint8_t *kvp, const uint8_t *kvs, int64_t phys, int lane) {
+    load_page8(P, kvp, kvs, phys, lane);
+  }
+  template <int NH16, int NN>
+  static __device__ __forceinline__ void rows(Rows<NH16, NN> &R, const uint8_t *qp, const uint8_t *qs, const float *w,
+                                              int64_t row0, int n_valid, int n_heads, int lane) {
+    load_rows8<NH16, NN>(R, qp, qs, w, row0, n_valid, n_heads, lane);
+  }
+  template <int NH16, int NN, int N>
+  static __device__ __forceinline__ float logit(const Page &P, const Rows<NH16, NN> &R, int lane) {
+    return page_logit8<NH16, NN, N>(P, R, lane);
+  }
+};
+
 }  // namespace ifp4

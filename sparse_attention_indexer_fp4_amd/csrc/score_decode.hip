@@ -46,7 +46,7 @@ struct SlottedHist {
   __device__ __forceinline__ uint32_t &operator[](uint32_t b) const { return g[hist_slot(b)]; }
 };
 
-template <int NH16, int NN, int NW, int D>
+template <class F, int NH16, int NN, int NW, int D>
 __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   // other D-1 slots. Every slot refill is unconditional -- past the wave's last item it
   // reloads that item (a cache hit) and its logits are dropped -- so the compiler waits
   // only for the slot being scored.
-  PageRegs P[D];
+  typename F::Page P[D];
   int sb[D], sp[D];
   bool sok[D];
   auto issue = [&](auto kk, int i) {
@@ -143,15 +143,15 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     sb[K] = __builtin_amdgcn_readlane(v_seq, l);
     sp[K] = __builtin_amdgcn_readlane(v_page, l);
     sok[K] = live && phys >= 0;
-    load_page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);
+    F::page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);
   };
-  RowRegs<NH16, NN> R;
+  typename F::template Rows<NH16, NN> R;
   int qb = -1;
   auto score = [&](auto kk) {
     constexpr int K = decltype(kk)::value;
     if (sb[K] != qb) {  // a new sequence: its query rows (waits for everything in flight)
       qb = sb[K];
-      load_rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
+      F::template rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
     }
     const uint32_t col = (uint32_t)(sp[K] * kPage + lane);
     static_for<NN>([&](auto nn) {
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
       const int len = row_len[r];
       // logits past the row's length (or of a dropped slot) fall outside the view
       const uint32_t bytes = sok[K] ? 4u * (uint32_t)max(len, 0) : 0u;
-      const float v = page_logit<NH16, NN, N>(P[K], R, lane);
+      const float v = F::template logit<NH16, NN, N>(P[K], R, lane);
       buffer_store_f32(v, buffer_view(logits + r * ld, bytes), 4u * col);
       if (fuse) {  // exactly the logits stored above
         const bool kept = 4u * col < bytes;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   }
 }
 
-template <int NH16, int NN>
+template <class F, int NH16, int NN>
 static int launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
                           int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                           int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len, float *logits,
@@ -200,27 +200,27 @@ static int launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const u
   constexpr size_t kHistLds = (size_t)NN * kHistBins * 4;
   static bool lds_set = false;  // raise the dynamic LDS limit once per instantiation
   if (row_hist && !lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void *)score_decode_kernel<NH16, NN, NW, D>,
+    const hipError_t e = hipFuncSetAttribute((const void *)score_decode_kernel<F, NH16, NN, NW, D>,
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHistLds);
     if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "score_decode: hipFuncSetAttribute: %s", hipGetErrorString(e));
     lds_set = true;
   }
-  hipLaunchKernelGGL((score_decode_kernel<NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), row_hist ? kHistLds : 0,
+  hipLaunchKernelGGL((score_decode_kernel<F, NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), row_hist ? kHistLds : 0,
                      st, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len,
                      logits, ld, row_hist);
   return INDEXER_FP4_OK;
 }
 
-template <int NH16>
+template <class F, int NH16>
 static int launch_decode_nn(int next_n, hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs,
                             const float *w, int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages,
                             const int32_t *bt, int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len,
                             float *logits, int64_t ld, uint32_t *row_hist) {
   switch (next_n) {
-    case 1: return launch_decode<NH16, 1>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
-    case 2: return launch_decode<NH16, 2>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
-    case 3: return launch_decode<NH16, 3>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
-    default: return launch_decode<NH16, 4>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    case 1: return launch_decode<F, NH16, 1>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    case 2: return launch_decode<F, NH16, 2>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    case 3: return launch_decode<F, NH16, 3>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
+    default: return launch_decode<F, NH16, 4>(st, n_units, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, sched, row_len, logits, ld, row_hist);
   }
 }
 
@@ -228,11 +228,12 @@ static int launch_decode_nn(int next_n, hipStream_t st, int n_units, const uint8
 
 using namespace ifp4;
 
-extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
-                                        int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
-                                        int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
-                                        int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
-                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
+template <class F>
+static int score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights, int32_t n_heads,
+                        const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
+                        const int32_t *block_table, int64_t bt_ld, int32_t batch, int32_t next_n, void *sched,
+                        int32_t n_units, const int32_t *row_len, float *logits, int64_t logits_ld,
+                        uint32_t *row_hist, void *stream) {
   clear_error();
   if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > INDEXER_FP4_MAX_HEADS)
     return fail(INDEXER_FP4_EINVAL, "n_heads=%d must be a positive multiple of %d and at most %d", n_heads,
@@ -257,9 +258,28 @@ extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *
   int32_t *sc = (int32_t *)sched;
   switch (n_heads / 16) {
 #define IFP4_CASE(X) \
-  case X: rc = launch_decode_nn<X>(next_n, st, n_units, q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, batch, sc, row_len, logits, logits_ld, row_hist); break;
+  case X: rc = launch_decode_nn<F, X>(next_n, st, n_units, q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, batch, sc, row_len, logits, logits_ld, row_hist); break;
     IFP4_CASE(1) IFP4_CASE(2) IFP4_CASE(3) IFP4_CASE(4) IFP4_CASE(5) IFP4_CASE(6) IFP4_CASE(7) IFP4_CASE(8)
 #undef IFP4_CASE
   }
   return rc ? rc : launch_status("score_decode");
+}
+
+extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
+                                        int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
+                                        int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
+                                        int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
+                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
+  return score_decode<FmtFp4>(q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld,
+                              batch, next_n, sched, n_units, row_len, logits, logits_ld, row_hist, stream);
+}
+
+// The FP8 comparator: the same scorer over MXFP8 queries and keys (128 bytes a vector).
+extern "C" int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
+                                        int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
+                                        int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
+                                        int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
+                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
+  return score_decode<FmtFp8>(q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld,
+                              batch, next_n, sched, n_units, row_len, logits, logits_ld, row_hist, stream);
 }

@@ -573,7 +573,7 @@ def test_topk_merge_skips_empty_slots_and_pads():
     assert got[0].tolist() == [3, 5]
 
 
-# ---------------------------------------------------------------------------- fused writer (R8-R11)
+# ---------------------------------------------------------------------------- fused writer (R12-R15)
 
 def test_bf16_round_matches_torch_on_fp32_values():
     """On values that are exactly fp32, rounding to bf16 is torch's own fp32 -> bf16 conversion
@@ -731,7 +731,7 @@ def test_fused_writer_dequantizes_to_the_normalized_rotated_vector(interleaved):
             assert (np.abs(got[sl] - np.clip(want[sl], -6 * step, 6 * step)) <= bound).all()
 
 
-# ---------------------------------------------------------------------------- MXFP8 comparator (R12)
+# ---------------------------------------------------------------------------- MXFP8 comparator (R16)
 
 def test_e4m3_values_match_torch():
     import torch
