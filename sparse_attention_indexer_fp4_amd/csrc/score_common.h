@@ -19,7 +19,7 @@ struct RowRegs {
   float4 w[NN][NH16];                // weights of heads 16m + 4(l/16) + i
 };
 
-template <int NH16, int NN>
+template <int NH16, int NN, bool Wait = true>
 __device__ __forceinline__ void load_rows(RowRegs<NH16, NN> &R, const uint8_t *__restrict__ qp,
                                           const uint8_t *__restrict__ qs, const float *__restrict__ w,
                                           int64_t row0, int n_valid, int n_heads, int lane) {
@@ -41,8 +41,9 @@ __device__ __forceinline__ void load_rows(RowRegs<NH16, NN> &R, const uint8_t *_
   // Wait for the query loads here (vmcnt 0; expcnt and lgkmcnt left free). Rows are
   // reloaded only when a wave moves to another sequence or tile; without this wait the
   // compiler would have to assume at every page that the query loads are the youngest in
-  // flight and drain the whole page prefetch ring before each page's MFMAs.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // flight and drain the whole page prefetch ring before each page's MFMAs. (Without Wait
+  // the caller lets the compiler wait where the registers are first used.)
+  if constexpr (Wait) __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // One page as B operands. Key bytes are read with the non-temporal hint: each is used once

@@ -19,8 +19,14 @@
 // previous group are refilled P-B items ahead, and every wave scores its row for the whole
 // group from LDS without further synchronisation. Each wave keeps a table of 64 items at a
 // time (tile, page, physical page, whether its row reaches the page), built with one round
-// of per-lane loads. Logits past a row's length fall outside the store's range; the query
-// row stays in registers while the wave stays on a tile.
+// of per-lane loads. Logits past a row's length fall outside the store's range.
+//
+// Each wave keeps its row's query operands in LDS, in operand order, and refills its
+// registers from there at every group (per item in the rare group that crosses into a new
+// tile, which first stages the new row from global memory). Holding them in registers
+// across groups would put a join after every conditional reload, and the compiler resolves
+// such joins with dozens of register copies per item, a third of the VALU work. The first
+// tile's row is fetched at entry, while the item table is being built.
 #include "score_common.h"
 
 // pages in the LDS ring of a unit, and items between the unit's barriers (divides the ring)
@@ -160,20 +166,70 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
   // a store that writes nothing (empty range): keeps every wave at one store per item
   auto idle_store = [&]() { buffer_store_f32(0.f, buffer_view(logits, 0u), 0u); };
 
-  RowRegs<NH16, 1> R;
-  int qt = -1, row = 0, row_bytes = 0;
-  auto score = [&](auto ss) {
+  // This wave's query row in LDS: operands per M-tile and lane, weights per M-tile and lane
+  // group (16 lanes read one address), scale words per lane. The helpers below are called
+  // from every unrolled item and are forced inline: out of line, the row would be passed
+  // through private (scratch) memory.
+  constexpr int NQS = (NH16 + 3) / 4;
+  __shared__ uint4 q_lds[NW * NH16 * 64];
+  __shared__ float4 w_lds[NW * NH16 * 4];
+  __shared__ uint32_t qs_lds[NW * NQS * 64];
+  uint4 *my_qa = q_lds + wv * NH16 * 64;
+  float4 *my_w = w_lds + wv * NH16 * 4;
+  uint32_t *my_qs = qs_lds + wv * NQS * 64;
+  // (LDS traffic goes through native vector types: copies of the HIP vector structs become
+  // memcpys that keep the row in private memory)
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  auto stage_row = [&](const RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NH16; m++) {
+      const uint4 a = Q.qa[0][m];
+      *reinterpret_cast<u32x4 *>(my_qa + m * 64 + lane) = u32x4{a.x, a.y, a.z, a.w};
+      // all 16 lanes of a group store the same four weights to the same address (a
+      // conditional store here would also keep the row in private memory)
+      const float4 x = Q.w[0][m];
+      *reinterpret_cast<f32x4 *>(my_w + m * 4 + (lane >> 4)) = f32x4{x.x, x.y, x.z, x.w};
+    }
+#pragma unroll
+    for (int j = 0; j < NQS; j++) my_qs[j * 64 + lane] = Q.qs[0][j];
+  };
+  auto read_row = [&](RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < NH16; m++) {
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(my_qa + m * 64 + lane);
+      Q.qa[0][m] = make_uint4(a.x, a.y, a.z, a.w);
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(my_w + m * 4 + (lane >> 4));
+      Q.w[0][m] = make_float4(x.x, x.y, x.z, x.w);
+    }
+#pragma unroll
+    for (int j = 0; j < NQS; j++) Q.qs[0][j] = my_qs[j * 64 + lane];
+  };
+  // The first tile's row is requested before the item table is built and staged after the
+  // prologue's copies are issued, so its loads overlap the table's and the first pages'.
+  int qt = tcur, row = 0, row_bytes = 0;
+  RowRegs<NH16, 1> Q0;
+  const bool first_row = wv < tiles[4 * qt + 1];
+  if (first_row) {
+    row = tiles[4 * qt] + wv;
+    row_bytes = 4 * max(row_len[row], 0);
+    load_rows<NH16, 1, false>(Q0, qp, qs, w, row, 1, n_heads, lane);
+  }
+  // a new tile for this wave: stage its row (waits for everything in flight; once per tile)
+  auto enter_tile = [&](int t) __attribute__((always_inline)) {
+    qt = t;
+    const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * qt);
+    row = T.x + wv;  // only called for items this wave scores, so wv < T.y
+    row_bytes = 4 * max(row_len[row], 0);
+    RowRegs<NH16, 1> Q;
+    load_rows<NH16, 1>(Q, qp, qs, w, row, 1, n_heads, lane);
+    stage_row(Q);
+  };
+  auto score = [&](auto ss, const RowRegs<NH16, 1> &R) __attribute__((always_inline)) {
     constexpr int S = decltype(ss)::value;
     if (!sok[S]) {
       idle_store();
       return;
-    }
-    if (st[S] != qt) {  // a new tile: this wave's query row (waits for everything in flight)
-      qt = st[S];
-      const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * qt);
-      row = T.x + wv;  // sok implies wv < T.y
-      row_bytes = 4 * max(row_len[row], 0);
-      load_rows<NH16, 1>(R, qp, qs, w, row, 1, n_heads, lane);
     }
     PageRegs pg;
 #pragma unroll
@@ -182,6 +238,29 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const uint32_t col = (uint32_t)(sp[S] * kPage + lane);
     const float v = page_logit<NH16, 1, 0>(pg, R, lane);
     buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
+  };
+  // score the B items of group GG: one refill of the query registers from LDS when every
+  // item stays on the current tile, else per item after staging each new tile
+  auto score_group = [&](auto gg) __attribute__((always_inline)) {
+    constexpr int GG = decltype(gg)::value;
+    bool same = true;
+    static_for<B>([&](auto bb) {
+      constexpr int S = GG * B + decltype(bb)::value;
+      same = same && (!sok[S] || st[S] == qt);
+    });
+    if (same) {
+      RowRegs<NH16, 1> R;
+      read_row(R);
+      static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}, R); });
+    } else {
+      static_for<B>([&](auto bb) {
+        constexpr int S = GG * B + decltype(bb)::value;
+        if (sok[S] && st[S] != qt) enter_tile(st[S]);
+        RowRegs<NH16, 1> R;
+        read_row(R);
+        score(std::integral_constant<int, S>{}, R);
+      });
+    }
   };
 
   // Items go in groups of B; the ring holds G = P / B groups. At the start of group k the
@@ -196,6 +275,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     static_for<B>([&](auto bb) { issue(std::integral_constant<int, GG * B + decltype(bb)::value>{}, GG * B + decltype(bb)::value); });
     if (loader) static_for<B>([&](auto) { idle_store(); });
   });
+  if (first_row) stage_row(Q0);
   for (int i0 = 0; i0 < n_my; i0 += P) {
     static_for<G>([&](auto gg) {
       constexpr int GG = decltype(gg)::value;
@@ -210,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
         constexpr int BB = decltype(bb)::value;
         issue(std::integral_constant<int, GR * B + BB>{}, i0 + (GG + G - 1) * B + BB);
       });
-      static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}); });
+      score_group(gg);
     });
   }
 }

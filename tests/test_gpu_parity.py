@@ -213,7 +213,8 @@ def test_device_side_errors_flag_and_skip(ifp4):
 # ---------------------------------------------------------------------------- prefill scores
 
 @pytest.mark.parametrize("which,heads,units", [("prefill_tiny", 16, 512), ("prefill_tiny", 64, 7),
-                                               ("prefill_tiny", 64, 4096),
+                                               ("prefill_tiny", 64, 4096), ("prefill_tiny", 32, 13),
+                                               ("prefill_tiny", 128, 512),
                                                ("prefill_4req", 64, 512)])  # full size, as benched
 def test_prefill_scores_and_topk(ifp4, which, heads, units):
     case = W.prefill_config(which, heads=heads)

@@ -1,8 +1,15 @@
-"""Compile each kernel source to gfx950 assembly and check a codegen hazard seen with this
-toolchain: a scalar conditional select (s_cselect) whose condition code was last written by
-a non-compare instruction while the actual comparison went to VCC (v_cmp) in between. That
-pattern silently returned a wrong mask in the top-k kernel; the source now avoids the form
-that produced it, and this test keeps any kernel from reintroducing it."""
+"""Compile each kernel source to gfx950 assembly and check two codegen hazards seen with this
+toolchain:
+
+- a scalar conditional select (s_cselect) whose condition code was last written by a
+  non-compare instruction while the actual comparison went to VCC (v_cmp) in between. That
+  pattern silently returned a wrong mask in the top-k kernel; the source now avoids the form
+  that produced it;
+- private (scratch) memory. Register blocks copied through HIP's vector structs can stay in
+  private memory instead of registers; every scratch access is then a vector-memory
+  operation that the kernels' counted waits also wait for (the prefill scorer lost about
+  a fifth of its time to this). No kernel here needs private memory.
+"""
 import concurrent.futures
 import os
 import re
@@ -57,12 +64,40 @@ def test_lint_flags_the_known_bad_pattern():
     assert suspicious_selects(bad) and not suspicious_selects(good) and not suspicious_selects(mask)
 
 
-def test_kernels_have_no_stale_condition_selects():
+@pytest.fixture(scope="module")
+def kernel_asm():
     from sparse_attention_indexer_fp4_amd import build as B
 
     srcs = [os.path.join(B.CSRC, s) for s in B.SOURCES if s != "errors.hip"]
     with tempfile.TemporaryDirectory() as d, concurrent.futures.ThreadPoolExecutor(len(srcs)) as ex:
         outs = list(ex.map(lambda s: _asm(s, d), srcs))
-        for src, out in zip(srcs, outs):
-            hits = suspicious_selects(open(out).read())
-            assert not hits, f"{os.path.basename(src)}: {hits[:3]}"
+        return {os.path.basename(src): open(out).read() for src, out in zip(srcs, outs)}
+
+
+def test_kernels_have_no_stale_condition_selects(kernel_asm):
+    for name, text in kernel_asm.items():
+        hits = suspicious_selects(text)
+        assert not hits, f"{name}: {hits[:3]}"
+
+
+def scratch_users(asm_text):
+    """Kernels whose private segment is not empty: (name, bytes) from the kernel descriptors."""
+    out = []
+    for m in re.finditer(r"^\s*\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", asm_text, re.M | re.S):
+        size = re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", m.group(2))
+        if size and int(size.group(1)) != 0:
+            out.append((m.group(1), int(size.group(1))))
+    return out
+
+
+def test_lint_finds_private_segments():
+    text = "\n".join(["\t.amdhsa_kernel k0", "\t\t.amdhsa_private_segment_fixed_size 0", "\t.end_amdhsa_kernel",
+                      "\t.amdhsa_kernel k1", "\t\t.amdhsa_private_segment_fixed_size 192", "\t.end_amdhsa_kernel"])
+    assert scratch_users(text) == [("k1", 192)]
+
+
+def test_kernels_use_no_scratch(kernel_asm):
+    for name, text in kernel_asm.items():
+        assert ".amdhsa_kernel" in text, name
+        users = scratch_users(text)
+        assert not users, f"{name}: {users[:3]}"
