@@ -136,8 +136,10 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
 // row's keys are staged in LDS with their smallest and largest value; a 1024-bin histogram
 // spread linearly over that range (d = min((key - kmin) >> s, 1023)) finds the bin b that
 // holds the k-th largest key; keys in higher bins are kept and the few keys in b are ranked
-// by counting (radix select when there are many), ties to the lowest columns. The kept
-// columns are then gathered in ascending order, one contiguous column range per wave.
+// by counting (radix select when there are many), ties to the lowest columns. Each wave owns
+// one contiguous column range: one walk over it counts the keys above b and lists the keys
+// of b in the wave's own part of the list (no shared counter), and after the selection a
+// second walk writes the kept columns in ascending order.
 constexpr int kShortThreads = 256;
 constexpr int kShortWaves = kShortThreads / 64;
 constexpr int64_t kShortMax = 16384;
@@ -151,7 +153,9 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
   extern __shared__ uint32_t keys[];  // max_len words
   __shared__ uint32_t hist[kShortBins];
   __shared__ uint32_t sel[kShortMax / 32];  // chosen bin-b keys, by column
-  __shared__ uint32_t ckey[kShortRank], ccol[kShortRank];
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[kShortWaves * kShortRank];  // per-wave lists
+  __shared__ __attribute__((aligned(16))) uint32_t ccol[kShortWaves * kShortRank];
+  __shared__ int s_nb[kShortWaves];
   __shared__ int s_scan[3 * kShortWaves], s_misc[8];
   __shared__ uint32_t s_mm[2 * kShortWaves];
   __shared__ int s_gt[kShortWaves];
@@ -220,30 +224,57 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
   }
   const uint32_t b = (uint32_t)s_misc[0];
   const int need = s_misc[1], nb = s_misc[2];
-  if (nb <= kShortRank) {
-    // list the keys of bin b, then keep those ranked below `need` (key descending, column
-    // ascending)
-    for (int i0 = 0; i0 < n; i0 += kShortThreads) {
-      const int i = i0 + tid;
-      const bool in_b = i < n && digit(keys[i]) == b;
-      const uint64_t m = __ballot(in_b);
-      if (m) {
-        int at = 0;
-        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
-        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
-        if (in_b && at < nb) {
-          ckey[at] = keys[i];
-          ccol[at] = (uint32_t)i;
+  const bool rank_path = nb <= kShortRank;
+  // wave wv owns the contiguous column range [c_lo, c_hi)
+  const int chunk = ((n + kShortWaves - 1) / kShortWaves + 63) & ~63;
+  const int c_lo = min(n, wv * chunk), c_hi = min(n, c_lo + chunk);
+  // one walk: keys above b are counted, keys of b listed (rank path) in this wave's list
+  {
+    int n_gt = 0, n_b = 0;
+    uint32_t *wkey = ckey + wv * kShortRank, *wcol = ccol + wv * kShortRank;
+    for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
+      const int j = j0 + lane;
+      const bool ok = j < c_hi;
+      const uint32_t key = ok ? keys[j] : 0u;
+      const uint32_t d = digit(key);
+      n_gt += __popcll(__ballot(ok && d > b));
+      if (rank_path) {
+        const bool in_b = ok && d == b;
+        const uint64_t m = __ballot(in_b);
+        if (in_b) {
+          const int at = n_b + (int)lanes_below(m);
+          wkey[at] = key;
+          wcol[at] = (uint32_t)j;
         }
+        n_b += __popcll(m);
       }
     }
-    __syncthreads();
+    if (lane == 0) {
+      s_gt[wv] = n_gt;
+      s_nb[wv] = n_b;
+    }
+  }
+  __syncthreads();
+  if (rank_path) {
+    // the lists hold the nb keys of b; keep those ranked below `need` (key descending,
+    // column ascending). Thread t takes the t-th entry of the lists in wave order.
     if (tid < nb) {
-      const uint32_t key = ckey[tid], col = ccol[tid];
+      int w = 0, t = tid;
+      while (w < kShortWaves - 1 && t >= s_nb[w]) t -= s_nb[w++];
+      const uint32_t key = ckey[w * kShortRank + t], col = ccol[w * kShortRank + t];
       int rank = 0;
-      for (int g = 0; g < nb; g++) {
-        const uint32_t kg = ckey[g];
-        rank += (kg > key || (kg == key && ccol[g] < col)) ? 1 : 0;
+      for (int w2 = 0; w2 < kShortWaves; w2++) {
+        const int m2 = s_nb[w2];
+        const uint4 *k4 = reinterpret_cast<const uint4 *>(ckey + w2 * kShortRank);
+        const uint4 *c4 = reinterpret_cast<const uint4 *>(ccol + w2 * kShortRank);
+        // four entries per read (entries past m2 are in the list's space and not counted)
+        for (int g = 0; g < m2; g += 4) {
+          const uint4 kq = k4[g / 4], cq = c4[g / 4];
+          const uint32_t kv[4] = {kq.x, kq.y, kq.z, kq.w}, cv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            rank += (g + e < m2 && (kv[e] > key || (kv[e] == key && cv[e] < col))) ? 1 : 0;
+        }
       }
       if (rank < need) atomicOr(&sel[col >> 5], 1u << (col & 31));
     }
@@ -274,22 +305,24 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
     }
   }
   __syncthreads();
-  // gather: wave wv owns the contiguous column range [c_lo, c_hi)
-  const int chunk = ((n + kShortWaves - 1) / kShortWaves + 63) & ~63;
-  const int c_lo = min(n, wv * chunk), c_hi = min(n, c_lo + chunk);
+  // kept columns of this wave: those above b plus the chosen keys of b (set bits of its
+  // range of the bitmap; a non-empty range starts at a multiple of 64, and no bit past n is
+  // ever set)
+  {
+    int n_sel = 0;
+    if (c_lo < c_hi)
+      for (int wd = c_lo / 32 + lane; wd < (c_hi + 31) / 32; wd += 64) n_sel += __popc(sel[wd]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) n_sel += __shfl_xor(n_sel, o, 64);
+    if (lane == 0) s_gt[wv] += n_sel;  // each wave updates only its own entry
+  }
+  __syncthreads();
+  int out_base = 0;
+  for (int w2 = 0; w2 < wv; w2++) out_base += s_gt[w2];
   auto take = [&](int j) {
     const uint32_t key = keys[j];
     return digit(key) > b || ((sel[j >> 5] >> (j & 31)) & 1u);
   };
-  int n_take = 0;
-  for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
-    const int j = j0 + lane;
-    n_take += __popcll(__ballot(j < c_hi && take(j)));
-  }
-  if (lane == 0) s_gt[wv] = n_take;
-  __syncthreads();
-  int out_base = 0;
-  for (int w2 = 0; w2 < wv; w2++) out_base += s_gt[w2];
   for (int j0 = c_lo; j0 < c_hi; j0 += 64) {
     const int j = j0 + lane;
     const bool t = j < c_hi && take(j);

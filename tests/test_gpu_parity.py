@@ -190,6 +190,26 @@ def test_topk_ties_and_signed_zero(ifp4):
         assert (got[r][m:] == -1).all()
 
 
+@pytest.mark.parametrize("k", [1, 16, 64, 2048])
+def test_topk_short_rows_exact(ifp4, k):
+    """Short-row selection on ragged lengths around the per-wave column ranges (64-column
+    steps, ranges clamped to the row, some empty) equals the oracle's full sort exactly."""
+    rng = np.random.default_rng(11 + k)
+    lens = np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 2049, 2050, 4097, 8191, 16384], np.int32)
+    n = int(lens.max())
+    lg = (rng.standard_normal((len(lens), n)) * 40 + 100).astype(np.float32)
+    lg[3, :50] = lg[3, 60]  # a tie block inside the first range
+    t = to_dev(lg)
+    top = torch.full((len(lens), k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk(t, to_dev(lens), n, k, top)
+    want = oracle.topk(lg.astype(np.float64), lens, k)
+    got = top.cpu().numpy()
+    for r in range(len(lens)):
+        m = min(k, int(lens[r]))
+        assert list(got[r][:m]) == sorted(want[r][:m].tolist()), (r, int(lens[r]))
+        assert (got[r][m:] == -1).all()
+
+
 def test_device_side_errors_flag_and_skip(ifp4):
     case = W.decode_config("decode_tiny")
     bt = case.block_table.copy()
