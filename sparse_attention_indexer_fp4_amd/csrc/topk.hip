@@ -140,7 +140,10 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
 // one contiguous column range: one walk over it counts the keys above b and lists the keys
 // of b in the wave's own part of the list (no shared counter), and after the selection a
 // second walk writes the kept columns in ascending order.
-constexpr int kShortThreads = 256;
+#ifndef IFP4_TOPK_SHORT_THREADS
+#define IFP4_TOPK_SHORT_THREADS 256
+#endif
+constexpr int kShortThreads = IFP4_TOPK_SHORT_THREADS;
 constexpr int kShortWaves = kShortThreads / 64;
 constexpr int64_t kShortMax = 16384;
 constexpr int kShortBins = 1024;
@@ -205,18 +208,24 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
     hist_put(hist, i < n ? digit(keys[i]) : 0u, i < n);
   }
   __syncthreads();
-  // the bin b of the k-th largest key (thread t owns bins 4t .. 4t+3)
+  // the bin b of the k-th largest key (thread t owns bins kPer t .. kPer t + kPer - 1)
   {
-    uint32_t c[4];
+    constexpr int kPer = kShortBins / kShortThreads;
+    static_assert(kPer * kShortThreads == kShortBins, "bins per thread");
+    uint32_t c[kPer];
+    int sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) c[i] = hist[4 * tid + i];
-    int acc = block_suffix_sum<kShortThreads>((int)(c[0] + c[1] + c[2] + c[3]), s_scan);
+    for (int i = 0; i < kPer; i++) {
+      c[i] = hist[kPer * tid + i];
+      sum += (int)c[i];
+    }
+    int acc = block_suffix_sum<kShortThreads>(sum, s_scan);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < kPer; i++) {
       if (acc >= k && acc - (int)c[i] < k) {
-        s_misc[0] = 4 * tid + i;          // b
+        s_misc[0] = kPer * tid + i;         // b
         s_misc[1] = k - (acc - (int)c[i]);  // keys of b to take
-        s_misc[2] = (int)c[i];            // keys in b
+        s_misc[2] = (int)c[i];              // keys in b
       }
       acc -= (int)c[i];
     }
