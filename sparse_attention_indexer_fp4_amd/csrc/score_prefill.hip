@@ -171,39 +171,39 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
   // from every unrolled item and are forced inline: out of line, the row would be passed
   // through private (scratch) memory.
   constexpr int NQS = (NH16 + 3) / 4;
-  __shared__ uint4 q_lds[NW * NH16 * 64];
-  __shared__ float4 w_lds[NW * NH16 * 4];
-  __shared__ uint32_t qs_lds[NW * NQS * 64];
-  uint4 *my_qa = q_lds + wv * NH16 * 64;
-  float4 *my_w = w_lds + wv * NH16 * 4;
-  uint32_t *my_qs = qs_lds + wv * NQS * 64;
-  // (LDS traffic goes through native vector types: copies of the HIP vector structs become
-  // memcpys that keep the row in private memory)
+  // (native vector element types: copies of the HIP vector structs become memcpys that keep
+  // the row in private memory; and every access indexes the arrays themselves, so the
+  // compiler can tell them apart from the ring slots the direct loads write and adds no
+  // wait for those loads before reading the row)
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ u32x4 q_lds[NW * NH16 * 64];
+  __shared__ f32x4 w_lds[NW * NH16 * 4];
+  __shared__ uint32_t qs_lds[NW * NQS * 64];
+  const int qa0 = wv * NH16 * 64, w0i = wv * NH16 * 4, qs0i = wv * NQS * 64;
   auto stage_row = [&](const RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NH16; m++) {
       const uint4 a = Q.qa[0][m];
-      *reinterpret_cast<u32x4 *>(my_qa + m * 64 + lane) = u32x4{a.x, a.y, a.z, a.w};
+      q_lds[qa0 + m * 64 + lane] = u32x4{a.x, a.y, a.z, a.w};
       // all 16 lanes of a group store the same four weights to the same address (a
       // conditional store here would also keep the row in private memory)
       const float4 x = Q.w[0][m];
-      *reinterpret_cast<f32x4 *>(my_w + m * 4 + (lane >> 4)) = f32x4{x.x, x.y, x.z, x.w};
+      w_lds[w0i + m * 4 + (lane >> 4)] = f32x4{x.x, x.y, x.z, x.w};
     }
 #pragma unroll
-    for (int j = 0; j < NQS; j++) my_qs[j * 64 + lane] = Q.qs[0][j];
+    for (int j = 0; j < NQS; j++) qs_lds[qs0i + j * 64 + lane] = Q.qs[0][j];
   };
   auto read_row = [&](RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < NH16; m++) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(my_qa + m * 64 + lane);
+      const u32x4 a = q_lds[qa0 + m * 64 + lane];
       Q.qa[0][m] = make_uint4(a.x, a.y, a.z, a.w);
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(my_w + m * 4 + (lane >> 4));
+      const f32x4 x = w_lds[w0i + m * 4 + (lane >> 4)];
       Q.w[0][m] = make_float4(x.x, x.y, x.z, x.w);
     }
 #pragma unroll
-    for (int j = 0; j < NQS; j++) Q.qs[0][j] = my_qs[j * 64 + lane];
+    for (int j = 0; j < NQS; j++) Q.qs[0][j] = qs_lds[qs0i + j * 64 + lane];
   };
   // The first tile's row is requested before the item table is built and staged after the
   // prologue's copies are issued, so its loads overlap the table's and the first pages'.
@@ -239,9 +239,11 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
     const float v = page_logit<NH16, 1, 0>(pg, R, lane);
     buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
   };
-  // score the B items of group GG: one refill of the query registers from LDS when every
-  // item stays on the current tile, else per item after staging each new tile
-  auto score_group = [&](auto gg) __attribute__((always_inline)) {
+  // score the B items of group GG with the current tile's row R (read from LDS before the
+  // group's refills are issued: the compiler cannot tell the row from the ring slots being
+  // filled and waits for every load in flight before reading it), or, in a group that enters
+  // a new tile, per item after staging each new tile
+  auto score_group = [&](auto gg, const RowRegs<NH16, 1> &R) __attribute__((always_inline)) {
     constexpr int GG = decltype(gg)::value;
     bool same = true;
     static_for<B>([&](auto bb) {
@@ -249,8 +251,6 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
       same = same && (!sok[S] || st[S] == qt);
     });
     if (same) {
-      RowRegs<NH16, 1> R;
-      read_row(R);
       static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}, R); });
     } else {
       static_for<B>([&](auto bb) {
@@ -285,12 +285,14 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
       if (loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (B * (2 * G - 3)));
       __builtin_amdgcn_s_barrier();  // the group landed; the previous group's slots are free
       asm volatile("" ::: "memory");
+      RowRegs<NH16, 1> R;
+      read_row(R);
       constexpr int GR = (GG + G - 1) % G;  // slots of the previous group
       static_for<B>([&](auto bb) {
         constexpr int BB = decltype(bb)::value;
         issue(std::integral_constant<int, GR * B + BB>{}, i0 + (GG + G - 1) * B + BB);
       });
-      score_group(gg);
+      score_group(gg, R);
     });
   }
 }
