@@ -64,7 +64,16 @@ __device__ __forceinline__ int block_exponent(uint32_t amag) {
 
 // This lane's eight bf16 (one uint4) -> four packed bytes (element 2i in the low nibble of
 // byte i) and the block's scale byte; the four lanes of a block must be active together.
+//
+// The codes come from gfx950's scaled conversion (two bf16 -> two E2M1 codes of v / scale
+// per instruction, the first in the low nibble). Probed on the device against the threshold
+// encoder above for every finite bf16 value at block exponents -10..10, it rounds the same
+// way (nearest, ties to the even code, saturating at 6, sign kept), and the exhaustive writer
+// test checks it through the library, at the extreme exponents too. Blocks with e <= -124
+// (largest magnitude below 2^-121) take the threshold encoder: there a bf16 subnormal could
+// reach a nonzero code, and at e = -127 the scale itself is not a normal float.
 __device__ __forceinline__ uint32_t encode_lane8(uint4 in, uint32_t &scale) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const uint32_t w[4] = {in.x, in.y, in.z, in.w};
   uint32_t amag = 0;
 #pragma unroll
@@ -73,10 +82,18 @@ __device__ __forceinline__ uint32_t encode_lane8(uint4 in, uint32_t &scale) {
   amag = max(amag, (uint32_t)__shfl_xor((int)amag, 2, 64));
   const int e = block_exponent(amag);
   scale = (uint32_t)(e + 127);
-  const E2M1Points pts(e);
   uint32_t d = 0;
+  if (e > -124) {
+    const float s = __uint_as_float(scale << 23);  // 2^e, a normal float
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[0]), s, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[1]), s, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[2]), s, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, __builtin_bit_cast(bf16x2, w[3]), s, 3);
+  } else {
+    const E2M1Points pts(e);
 #pragma unroll
-  for (int h = 0; h < 4; h++) d |= (pts.code(w[h] & 0xFFFFu) | (pts.code(w[h] >> 16) << 4)) << (8 * h);
+    for (int h = 0; h < 4; h++) d |= (pts.code(w[h] & 0xFFFFu) | (pts.code(w[h] >> 16) << 4)) << (8 * h);
+  }
   return d;
 }
 

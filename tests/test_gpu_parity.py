@@ -45,7 +45,9 @@ def _all_finite_bf16():
 
 def test_quantizer_exhaustive_bf16(ifp4):
     """Every finite bf16 value alone in its block, in a random block mix, and under fixed
-    block scales 2^e (e = -10..10), through the query arm: bytes equal the oracle's."""
+    block scales 2^e (e = -10..10 and the extremes -127..-121, 100, 125, where bf16
+    subnormals can reach nonzero codes and the scale leaves the normal floats), through the
+    query arm: bytes equal the oracle's."""
     bits = _all_finite_bf16()
     rng = np.random.default_rng(11)
     vecs = []
@@ -53,7 +55,7 @@ def test_quantizer_exhaustive_bf16(ifp4):
     alone[:, 0] = bits
     vecs.append(alone.reshape(-1, 128))
     vecs.append(rng.permutation(np.concatenate([bits, bits[: (-bits.size) % 128]])).reshape(-1, 128))
-    for e in range(-10, 11):
+    for e in list(range(-10, 11)) + [-127, -126, -125, -124, -123, -122, -121, 100, 125]:
         v = W.bf16_to_f32(bits).astype(np.float64)
         sel = bits[np.abs(v) < 2.0 ** (e + 2)]
         blk = np.zeros((sel.size, 32), np.uint16)
