@@ -137,6 +137,7 @@ def check_logits(g: np.ndarray, s: np.ndarray, row_len: np.ndarray, sentinel_nan
     for r in range(g.shape[0]):
         L = int(row_len[r])
         if L:
+            assert np.isfinite(g[r, :L]).all(), f"row {r}: a column below its length {L} is not finite (never written?)"
             err = np.abs(g[r, :L] - s[r, :L])
             bad = err > RTOL * np.abs(s[r, :L])
             if bad.any():
