@@ -232,6 +232,57 @@ def test_device_side_errors_flag_and_skip(ifp4):
         assert np.allclose(lg[r, :L][m], o["s"][r, :L][m], rtol=1e-3, atol=0)
 
 
+def test_prefill_device_side_errors_flag_and_skip(ifp4):
+    """Prefill with block-table entries outside the pool: the scorer flags the step, skips
+    exactly the pages those entries name (their columns keep the sentinel), does not fault,
+    and every other valid logit matches the oracle."""
+    case = W.prefill_config("prefill_tiny", heads=16)
+    kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((case.n_pages, 4, 64), dtype=torch.uint8, device=dev())
+    okp = np.zeros((case.n_pages, 64, 64), np.uint8)
+    oks = np.zeros((case.n_pages, 4, 64), np.uint8)
+    st0, st = case.steps[0], case.steps[1]  # the second step holds requests 0 and 2
+    assert list(st.req_ids) == [0, 2]
+    g0 = gpu_prefill_step(case, st0, kp, ks, run_topk=False)
+    assert g0["err"] == 0
+    oracle_prefill_step(case, st0, okp, oks, scores=False)
+    o = oracle_prefill_step(case, st, okp, oks)
+    # the step's own keys, then a schedule and the scorer over a corrupted table
+    NP, R, H = st.n_rows_padded, len(st.req_ids), case.heads
+    keys, slots = W.step_keys(case, st)
+    qp = torch.empty((NP, H, 64), dtype=torch.uint8, device=dev())
+    qs = torch.empty((NP, H, 4), dtype=torch.uint8, device=dev())
+    ifp4.indexer_fp4_quant_and_cache(bf16_tensor(keys), to_dev(slots), kp, ks, bf16_tensor(st.q), qp, qs)
+    bt = W.step_block_table(case, st).copy()
+    bt[0, 1] = 10_000  # request 0, page 1: outside the pool
+    bt[1, 0] = -3      # request 2, page 0
+    units = ifp4.PREFILL_UNITS
+    sched = torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8, device=dev())
+    row_len = torch.empty(NP, dtype=torch.int32, device=dev())
+    ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, sched, row_len)
+    ld = bt.shape[1] * 64
+    logits = torch.full((NP, ld), float("nan"), dtype=torch.float32, device=dev())
+    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, to_dev(bt), sched, units, NP, row_len, logits)
+    torch.cuda.synchronize()
+    assert ifp4.sched_error(sched) & ifp4.DEV_BAD_PAGE
+    lg = logits.cpu().numpy().astype(np.float64)
+    rl = o["row_len"]
+    skipped = np.zeros_like(lg, bool)
+    skipped[st.cu_rows[0]:st.cu_rows[1], 64:128] = True  # request 0's rows past 64 keys
+    skipped[st.cu_rows[1]:st.cu_rows[2], 0:64] = True    # all of request 2's rows
+    for r in range(NP):
+        L = int(rl[r])
+        if L == 0:
+            continue
+        sk = skipped[r, :L]
+        assert np.isnan(lg[r, :L][sk]).all(), f"row {r}: a skipped page was written"
+        ok = ~sk
+        assert np.isfinite(lg[r, :L][ok]).all(), f"row {r}: a good page was not written"
+        assert np.allclose(lg[r, :L][ok], o["s"][r, :L][ok], rtol=1e-3, atol=0), f"row {r}"
+        assert np.isnan(lg[r, L:]).all()
+    assert (rl[st.cu_rows[0]:st.cu_rows[1]] > 64).any()  # the case does reach page 1 of request 0
+
+
 # ---------------------------------------------------------------------------- prefill scores
 
 @pytest.mark.parametrize("which,heads,units", [("prefill_tiny", 16, 512), ("prefill_tiny", 64, 7),
