@@ -15,8 +15,10 @@ capturable: fixed grids, lengths read on the device, no host reads or allocation
 serving engine would run them. Printed: one JSON line with the throughput (keys scored per
 second over whole steps), the decode scorer's roofline (algorithmic bytes per launch over
 its mean launch time: HIP events around replays of a graph holding the step's 21 scorer
-launches), the prefill path's time per layer and FP4 MFMA roofline (4 requests of
-3420..4213 tokens, 512-token chunks), and the CPU oracle's rate on a bounded sample.
+launches), the same figures per layer for the long decode workloads (16 x 131072 and
+8 x 262144, 8 layers each), the prefill path's time per layer and FP4 MFMA roofline (4
+requests of 3420..4213 tokens, 512-token chunks), and the CPU oracle's rate on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -54,11 +56,11 @@ def decode_scorer_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -> int
     return n_keys * (64 + 4 + 4) + n_pages * 4 + rows * (heads * (64 + 4) + heads * 4 + 4)
 
 
-def build_decode(torch, ifp4, W, layers, units, seed, fp8=False):
-    """The decode workload's layers; with fp8, every layer also gets MXFP8 planes of the same
-    keys and queries (the FP8 comparator)."""
+def build_decode(torch, ifp4, W, layers, units, seed, fp8=False, workload="decode_b8_128k"):
+    """The layers of a decode workload of equal contexts; with fp8, every layer also gets
+    MXFP8 planes of the same keys and queries (the FP8 comparator)."""
     dev = torch.device("cuda:0")
-    case_ctx = W.DECODE_CONFIGS["decode_b8_128k"]
+    case_ctx = W.DECODE_CONFIGS[workload]
     ctx = np.array(case_ctx["ctx"], np.int32)
     H, k = case_ctx["heads"], case_ctx["topk"]
     B = ctx.shape[0]
@@ -208,6 +210,41 @@ def bench_decode(torch, ifp4, W, args):
                 scorer_us=scorer_us, alg_bytes=alg_bytes, achieved_gbs=achieved,
                 writer={"fused_us_per_layer": round(writer_us, 3), "plain_us_per_layer": round(plain_us, 3),
                         "tokens": meta["B"], "heads": meta["H"], "rope_dim": ROPE_DIM})
+
+
+SWEEP_WORKLOADS = ("decode_b16_128k", "decode_b8_256k")
+
+
+def bench_decode_sweep(torch, ifp4, W, args, layers=8):
+    """The long decode workloads, 16 x 131072 and 8 x 262144 (64 heads, top-2048): whole
+    steps (schedule, then per layer fused write + score + top-k) and the scorer alone, per
+    layer. A layer's cache holds 2^21 keys (143 MB), so 8 layers stream from HBM."""
+    out = {}
+    for name in SWEEP_WORKLOADS:
+        L, S, meta = build_decode(torch, ifp4, W, layers, args.units, args.seed, workload=name)
+        for _ in range(args.warmup):
+            decode_step(ifp4, L, S, meta)
+        torch.cuda.synchronize()
+        if ifp4.sched_error(S["sched"]) != 0:
+            raise RuntimeError(f"{name}: device error flags {ifp4.sched_error(S['sched'])}")
+        step_graph = capture(torch, lambda: decode_step(ifp4, L, S, meta))
+        for _ in range(args.warmup):
+            step_graph.replay()
+        step_ms = timed_replays(torch, step_graph, args.steps)
+        scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
+        scorer_graph.replay()
+        scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / layers
+        alg = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
+        gbs = alg / (scorer_us * 1e-6) / 1e9
+        out[name] = {"batch": meta["B"], "context": meta["ctx"], "layers": layers,
+                     "us_per_layer": round(1e3 * step_ms / layers, 3),
+                     "keys_per_s": round(meta["n_keys"] * layers / (step_ms * 1e-3), 1),
+                     "scorer_us": round(scorer_us, 3), "scorer_gbs": round(gbs, 1),
+                     "scorer_frac": round(gbs / PEAK_HBM_GBS, 4), "alg_bytes_per_launch": alg}
+        del step_graph, scorer_graph, L, S
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_prefill(torch, ifp4, W, args):
@@ -390,6 +427,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the long decode workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, a kernel of known traffic "
                          "for scaling hardware byte counters")
@@ -420,6 +458,12 @@ def main():
     print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scorer {d['scorer_us']:.2f} us "
           f"({d['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
     pre = None
+    sweep = None
+    if not args.no_sweep:
+        sweep = bench_decode_sweep(torch, ifp4, W, args)
+        for name, r in sweep.items():
+            print(f"bench: {name} {r['us_per_layer']:.2f} us/layer, scorer {r['scorer_us']:.2f} us "
+                  f"({r['scorer_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
     dcp = bench_dcp_merge(torch, ifp4, args)
     fp8 = None
     if not args.no_fp8:
@@ -469,6 +513,7 @@ def main():
                      "alg_bytes_per_launch": d["alg_bytes"]},
         "cpu_baseline": cpu,
         "writer": d["writer"],
+        "decode_long": sweep,
         "prefill": pre,
         "dcp_merge": dcp,
         "fp8_comparator": fp8,
