@@ -132,7 +132,7 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
 }
 
 // ---------------------------------------------------------------------------------------
-// Rows up to kShortMax keys: one 256-thread workgroup per row (several rows share a CU). The
+// Rows up to kShortMax keys: one workgroup per row (several rows share a CU). The
 // row's keys are staged in LDS with their smallest and largest value; a 1024-bin histogram
 // spread linearly over that range (d = min((key - kmin) >> s, 1023)) finds the bin b that
 // holds the k-th largest key; keys in higher bins are kept and the few keys in b are ranked
@@ -140,19 +140,21 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
 // one contiguous column range: one walk over it counts the keys above b and lists the keys
 // of b in the wave's own part of the list (no shared counter), and after the selection a
 // second walk writes the kept columns in ascending order.
-#ifndef IFP4_TOPK_SHORT_THREADS
-#define IFP4_TOPK_SHORT_THREADS 256
-#endif
-constexpr int kShortThreads = IFP4_TOPK_SHORT_THREADS;
-constexpr int kShortWaves = kShortThreads / 64;
+// Workgroups of 512 threads for launches of at most kWideRows rows, whose rows gain from each
+// row's walks spreading over more waves (prefill steps of 120, 824 and 1784 rows of up to
+// 4.3 K keys: 15.9 -> 11.8, 19.2 -> 17.4, 30.0 -> 27.5 us against 256 threads); 256 threads
+// for launches of more rows, where the two measured alike (2048-row steps: within 0.4 us).
 constexpr int64_t kShortMax = 16384;
 constexpr int kShortBins = 1024;
 constexpr int kShortRank = 256;  // bin-b keys ranked by counting
+constexpr int kWideRows = 2047;
 
+template <int kShortThreads>
 __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len, int64_t max_len,
                                                                 int k, uint32_t *__restrict__ row_hist,
                                                                 int32_t *__restrict__ out, int64_t out_ld) {
+  constexpr int kShortWaves = kShortThreads / 64;
   extern __shared__ uint32_t keys[];  // max_len words
   __shared__ uint32_t hist[kShortBins];
   __shared__ uint32_t sel[kShortMax / 32];  // chosen bin-b keys, by column
@@ -987,7 +989,10 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
     hipError_t e = hipFuncSetAttribute((const void *)topk_finish_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kLdsBudget);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)topk_row_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+      e = hipFuncSetAttribute((const void *)topk_row_kernel<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(4 * kShortMax));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)topk_row_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)(4 * kShortMax));
     if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
     lds_set = true;
@@ -996,8 +1001,12 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
     // rows of at most kShortMax keys, or k >= max_len (every row keeps all its keys and
     // the kernel returns before staging anything)
     const size_t lds = max_len <= kShortMax ? (size_t)(4 * max_len) : 0;
-    hipLaunchKernelGGL(topk_row_kernel, dim3(n_rows), dim3(kShortThreads), lds, st, logits, logits_ld, row_len,
-                       max_len, k, row_hist, topk_idx, topk_ld);
+    if (n_rows <= kWideRows)
+      hipLaunchKernelGGL(topk_row_kernel<512>, dim3(n_rows), dim3(512), lds, st, logits, logits_ld, row_len,
+                         max_len, k, row_hist, topk_idx, topk_ld);
+    else
+      hipLaunchKernelGGL(topk_row_kernel<256>, dim3(n_rows), dim3(256), lds, st, logits, logits_ld, row_len,
+                         max_len, k, row_hist, topk_idx, topk_ld);
     return launch_status("topk");
   }
   if (!workspace || (uintptr_t)workspace % 16 != 0)

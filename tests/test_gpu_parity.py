@@ -192,12 +192,15 @@ def test_topk_ties_and_signed_zero(ifp4):
         assert (got[r][m:] == -1).all()
 
 
+@pytest.mark.parametrize("tile", [1, 150])
 @pytest.mark.parametrize("k", [1, 16, 64, 2048])
-def test_topk_short_rows_exact(ifp4, k):
+def test_topk_short_rows_exact(ifp4, k, tile):
     """Short-row selection on ragged lengths around the per-wave column ranges (64-column
-    steps, ranges clamped to the row, some empty) equals the oracle's full sort exactly."""
+    steps, ranges clamped to the row, some empty) equals the oracle's full sort exactly; 14
+    rows run on 512-thread workgroups, 2100 rows on 256-thread ones."""
     rng = np.random.default_rng(11 + k)
-    lens = np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 2049, 2050, 4097, 8191, 16384], np.int32)
+    lens = np.tile(np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 2049, 2050, 4097, 8191, 16384], np.int32),
+                   tile)
     n = int(lens.max())
     lg = (rng.standard_normal((len(lens), n)) * 40 + 100).astype(np.float32)
     lg[3, :50] = lg[3, 60]  # a tie block inside the first range
