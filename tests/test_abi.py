@@ -53,6 +53,12 @@ def test_size_queries(L):
     assert L.indexer_fp4_decode_sched_bytes(8, 1, 512) == 4 * (8 + 9 + 513 + 3 * 512)
     assert L.indexer_fp4_decode_sched_bytes(-1, 1, 512) < 0
     assert L.indexer_fp4_decode_sched_bytes(8, 1, 0) < 0
+    # a schedule buffer sized for next_n = n serves next_n = 1 (the pages' unit-count invariant
+    # f(n) >= f(1)); here the units are (sequence, page) items, so the size does not depend on
+    # next_n at all
+    for b, u in [(1, 512), (8, 512), (16, 37), (3, 4096)]:
+        sizes = [L.indexer_fp4_decode_sched_bytes(b, n, u) for n in (1, 2, 3, 4)]
+        assert min(sizes) == max(sizes) == sizes[0] > 0, (b, u, sizes)
     # prefill: header + tiles[max] x4 + cum[max+1] + unit_begin[U+1] + unit_tile[U] + req_tile[R+1]
     mt = 2048 // 8 + 4
     assert L.indexer_fp4_prefill_sched_bytes(4, 2048, 4096) == 4 * (8 + 4 * mt + mt + 1 + 4097 + 4096 + 5)
