@@ -468,7 +468,8 @@ def test_graph_replay_bitwise_stable(ifp4, fused):
     """One decode step (schedule, key/query write, scorer, top-k) captured once at fixed
     addresses and replayed under four context-length vectors written in place: every replay
     equals an eager run of the same inputs bit for bit (the schedule is what lets a captured
-    graph follow changing lengths). Eager work and synchronizations run between replays."""
+    graph follow changing lengths), including the capture vector replayed again after the
+    others. Eager work and synchronizations run between replays."""
     B, H, k, max_ctx, units = 4, 64, 2048, 20000, 64
     rng = np.random.default_rng(21)
     pages = -(-max_ctx // 64)
@@ -523,7 +524,9 @@ def test_graph_replay_bitwise_stable(ifp4, fused):
             step(g_out)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    for c in ([4096, 100, 17000, 2049], [20000, 64, 1, 9000], [3000, 19999, 2048, 2047], [65, 12345, 20000, 300]):
+    # the capture batch, three others, then the capture batch again after them
+    for c in ([4096, 100, 17000, 2049], [20000, 64, 1, 9000], [3000, 19999, 2048, 2047], [65, 12345, 20000, 300],
+              [4096, 100, 17000, 2049]):
         _say(f"graph replay ctx={c}")
         set_ctx(c)
         e_out["logits"].fill_(float("nan"))
@@ -542,6 +545,95 @@ def test_graph_replay_bitwise_stable(ifp4, fused):
         assert np.array_equal(g_out["row_len"].cpu().numpy(), np.asarray(c, np.int32))
         if fused:
             assert not g_out["hist"].any().item() and not e_out["hist"].any().item()
+
+
+def test_prefill_graph_replay_bitwise_stable(ifp4):
+    """One prefill step (schedule, scorer, top-k) captured once at fixed addresses and replayed
+    under four request layouts (row splits and chunk start positions written in place; the
+    padded row count is fixed), then the first layout again: every replay equals an eager run
+    of the same inputs bit for bit, padding rows select nothing, and the first layout's logits
+    and top-k match the oracle. Eager work and synchronizations run between replays."""
+    R, NP, H, k, units, lmax = 3, 48, 64, 512, 256, 4160
+    rng = np.random.default_rng(33)
+    pages = lmax // 64
+    n_pages = R * pages + 5
+    bt_np = rng.permutation(n_pages)[:R * pages].astype(np.int32).reshape(R, pages)
+    ld = pages * 64
+    slots = (bt_np.astype(np.int64)[:, :, None] * 64 + np.arange(64)).reshape(-1)
+    keys = W.bf16_bits(rng.standard_normal((R * lmax, 128)).astype(np.float32))
+    qb = W.bf16_bits(rng.standard_normal((NP, H, 128)).astype(np.float32))
+    w_np = rng.random((NP, H), dtype=np.float32)
+    kp = torch.zeros((n_pages, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((n_pages, 4, 64), dtype=torch.uint8, device=dev())
+    qp = torch.empty((NP, H, 64), dtype=torch.uint8, device=dev())
+    qs = torch.empty((NP, H, 4), dtype=torch.uint8, device=dev())
+    ifp4.indexer_fp4_quant_and_cache(bf16_tensor(keys), to_dev(slots), kp, ks, bf16_tensor(qb), qp, qs)
+    bt, w = to_dev(bt_np), to_dev(w_np)
+    cu = torch.zeros(R + 1, dtype=torch.int32, device=dev())
+    sp = torch.zeros(R, dtype=torch.int32, device=dev())
+
+    def buffers():
+        return dict(sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8,
+                                      device=dev()),
+                    row_len=torch.empty(NP, dtype=torch.int32, device=dev()),
+                    logits=torch.full((NP, ld), float("nan"), dtype=torch.float32, device=dev()),
+                    top=torch.full((NP, k), -7, dtype=torch.int32, device=dev()),
+                    ws=torch.zeros(max(ifp4.indexer_topk_workspace_bytes(NP, ld, k), 16), dtype=torch.uint8,
+                                   device=dev()))
+
+    def step(o):
+        ifp4.indexer_fp4_prefill_schedule(cu, sp, NP, units, o["sched"], o["row_len"])
+        ifp4.indexer_fp4_score_prefill(qp, qs, w, kp, ks, bt, o["sched"], units, NP, o["row_len"], o["logits"])
+        ifp4.indexer_topk(o["logits"], o["row_len"], ld, k, o["top"], o["ws"])
+
+    layouts = [([0, 16, 30, 45], [0, 500, 1000]), ([0, 40, 41, 48], [100, 0, 2000]), ([0, 1, 2, 3], [3000, 5, 64]),
+               ([0, 8, 20, 44], [63, 4095, 4000]), ([0, 16, 30, 45], [0, 500, 1000])]
+
+    def set_layout(lay):
+        cu.copy_(to_dev(np.asarray(lay[0], np.int32)))
+        sp.copy_(to_dev(np.asarray(lay[1], np.int32)))
+
+    g_out, e_out = buffers(), buffers()
+    set_layout(layouts[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(g_out)  # warm-up on the capture stream
+        with torch.cuda.graph(graph, stream=side):
+            step(g_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for i, lay in enumerate(layouts):
+        _say(f"prefill graph replay layout={lay}")
+        set_layout(lay)
+        e_out["logits"].fill_(float("nan"))
+        g_out["logits"].fill_(float("nan"))
+        step(e_out)  # eager, same inputs
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert ifp4.sched_error(g_out["sched"]) == 0 and ifp4.sched_error(e_out["sched"]) == 0
+        _, rl = oracle.prefill_geometry(np.asarray(lay[0], np.int32), np.asarray(lay[1], np.int32), NP)
+        assert np.array_equal(g_out["row_len"].cpu().numpy(), rl)
+        gl, el = g_out["logits"].cpu().numpy(), e_out["logits"].cpu().numpy()
+        for r in range(NP):
+            n = int(rl[r])
+            assert np.array_equal(gl[r, :n].view(np.uint32), el[r, :n].view(np.uint32)), f"row {r}: logits differ"
+            assert np.isnan(gl[r, n:]).all(), f"row {r}: written past its length {n}"
+        gtop = g_out["top"].cpu().numpy()
+        assert np.array_equal(gtop, e_out["top"].cpu().numpy())
+        assert (gtop[lay[0][-1]:] == -1).all()  # padding rows select nothing
+        if i == 0:
+            okp = np.zeros((n_pages, 64, 64), np.uint8)
+            oks = np.zeros((n_pages, 4, 64), np.uint8)
+            oracle.quant_and_cache(keys, slots, okp, oks)
+            oqp, oqs = oracle.quant_q(qb)
+            rs, rl0 = oracle.prefill_geometry(np.asarray(lay[0], np.int32), np.asarray(lay[1], np.int32), NP)
+            s0, _ = oracle.score(oqp, oqs, w_np, rs, rl0, okp, oks, bt_np, ld=ld)
+            check_logits(gl, s0, rl0)
+            check_topk(gtop, oracle.topk(s0, rl0, k), s0, rl0, k)
 
 
 # ---------------------------------------------------------------------------- context parallelism
