@@ -373,6 +373,7 @@ constexpr int kWaveCols = kChunk / kLongWaves;      // columns of a chunk held b
 constexpr int kBins = 4096;                         // 12-bit digits
 constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
 constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
+static_assert(kMaxChunks <= kFinishThreads, "the finish gives every chunk at least one thread");
 constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the finish kernel
 constexpr int kSubMax = 8192;                       // candidates of bin b2 staged in LDS
 constexpr int kRankMax = 256;                       // ... ranked by counting
@@ -597,9 +598,11 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   const uint32_t *cc = ccol + (int64_t)cq * kChunk;
   const int64_t len = clamped_len(row_len, r, max_len);
   const int ns_raw = (int)cnt[2 * cq], nc_raw = (int)cnt[2 * cq + 1];
-  uint32_t h2[4];
+  constexpr int kH = kBins / kFinishThreads;  // digit-2 bins per thread
+  static_assert(kH * kFinishThreads == kBins, "bins per thread");
+  uint32_t h2[kH];
 #pragma unroll
-  for (int i = 0; i < 4; i++) h2[i] = g2[4 * tid + i];
+  for (int i = 0; i < kH; i++) h2[i] = g2[kH * tid + i];
   uint32_t sj[kBatch], kk[kBatch], jj[kBatch];
 #pragma unroll
   for (int u = 0; u < kBatch; u++) {
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   if (len <= k) {  // short row: every key is kept (the other kernels left it alone)
     for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
 #pragma unroll
-    for (int i = 0; i < 4; i++) g1[4 * tid + i] = 0u;  // a scorer-filled histogram counts it
+    for (int i = 0; i < kH; i++) g1[kH * tid + i] = 0u;  // a scorer-filled histogram counts it
     return;
   }
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
@@ -629,7 +632,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   // together; the scan's barriers also publish the cleared bitmap
   {
     const bool lead = mine && t0 == 0;
-    int sa = lead ? ns : 0, sb2 = lead ? nc : 0, sh = (int)(h2[0] + h2[1] + h2[2] + h2[3]);
+    int sa = lead ? ns : 0, sb2 = lead ? nc : 0, sh = 0;
+#pragma unroll
+    for (int i = 0; i < kH; i++) sh += (int)h2[i];
     block_suffix_sum3<kFinishThreads>(sa, sb2, sh, s_scan);
     if (tid == 0) {
       s_sure_off[used] = sa;  // totals
@@ -642,11 +647,11 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
     }
     // bin b2 of the (k - sure)-th largest candidate
     const int rem = k - s_sure_off[used];
-    int acc = sh;  // candidates in digit-2 bins >= 4 tid
+    int acc = sh;  // candidates in digit-2 bins >= kH tid
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
+    for (int i = 0; i < kH; i++) {
       if (acc >= rem && acc - (int)h2[i] < rem) {
-        s_misc[0] = 4 * tid + i;               // b2
+        s_misc[0] = kH * tid + i;              // b2
         s_misc[1] = rem - (acc - (int)h2[i]);  // keys of b2 still to take
         s_misc[2] = (int)h2[i];                // keys in b2
       }
@@ -657,9 +662,9 @@ __global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32
   }
   // both histograms are left zero for the next call
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    g1[4 * tid + i] = 0u;
-    g2[4 * tid + i] = 0u;
+  for (int i = 0; i < kH; i++) {
+    g1[kH * tid + i] = 0u;
+    g2[kH * tid + i] = 0u;
   }
   const int n_cand = s_cand_off[used];
   const uint32_t b2 = (uint32_t)s_misc[0];
