@@ -659,6 +659,28 @@ def test_topk_merge_matches_oracle(ifp4, rows, n_cand, k):
         assert (got[r][m:] == -1).all()
 
 
+@pytest.mark.parametrize("mode", ["repeated", "wide"])
+def test_topk_merge_index_ranges(ifp4, mode):
+    """Indices that repeat (the ordering falls back from the LDS bitmap to the sort) and
+    indices spread over [0, 2^31 - 1) (wider than the bitmap) merge as the oracle does."""
+    rows, n_cand, k = 5, 3000, 256
+    rng = np.random.default_rng(7 if mode == "repeated" else 8)
+    sc = rng.standard_normal((rows, n_cand)).astype(np.float32)
+    sc[1] = np.round(sc[1] * 4) / 4  # heavy ties
+    hi = n_cand // 2 if mode == "repeated" else 2**31 - 1
+    ix = rng.integers(0, hi, (rows, n_cand)).astype(np.int32)
+    ix[2, ::5] = -1
+    _say(f"topk_merge index mode={mode}")
+    top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk_merge(to_dev(sc), to_dev(ix), k, top)
+    got = top.cpu().numpy()
+    want = oracle.topk_merge(sc.astype(np.float64), ix, k)
+    for r in range(rows):
+        m = int((want[r] >= 0).sum())
+        assert list(got[r][:m]) == sorted(want[r][:m].tolist()), f"row {r}"
+        assert (got[r][m:] == -1).all()
+
+
 def test_context_parallel_decode_on_one_gpu(ifp4):
     """Context parallelism on one GPU's share: W = 4 page-interleaved shards of every
     sequence are scored by the scorer through their own block tables, each takes a local
