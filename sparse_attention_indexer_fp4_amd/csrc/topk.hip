@@ -348,7 +348,8 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 // Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). A workgroup retires
 // only 64 lanes of arithmetic a cycle, so one workgroup per row would be bound by its own
 // ALUs; each row is cut into chunks of kChunk keys, one workgroup each, and the selection
-// is a two-level radix select over the key bits, in three launches ordered by the stream:
+// is a two-level radix select over the key bits, in three launches ordered by the stream
+// (two when the decode scorer has already filled the digit-1 histograms):
 //   hist     histogram of digit 1 (key bits 31..20) of every chunk, merged into the row's
 //            histogram with one atomic per occupied bin;
 //   collect  every chunk finds the bin b1 that holds the row's k-th largest key and writes,
@@ -362,8 +363,9 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 //            the columns in ascending order and zeroes both histograms for the next call.
 // Device-wide atomics on one cache line serialize, so the merges are kept to one atomic
 // instruction per workgroup and 64-bin block.
-// 512 threads (8 keys each): measured against 1024 and 256 on 8 and 16 rows of 131072 keys
-// (hist + collect + finish 20.9 / 23.9 us, against 21.9 / 29.0 at 1024 and 25.2 / 26.9 at 256)
+// Chunk workgroups of 512 threads (8 keys each): measured against 1024 and 256 on 8 and 16
+// rows of 131072 keys (hist + collect + finish 20.9 / 23.9 us, against 21.9 / 29.0 at 1024
+// and 25.2 / 26.9 at 256).
 constexpr int kLongThreads = 512;
 constexpr int kLongWaves = kLongThreads / 64;
 constexpr int kFinishThreads = 1024;
