@@ -87,8 +87,10 @@ enum {
 #define INDEXER_FP4_MAX_HEADS 128
 #define INDEXER_FP4_TILE_ROWS 8   /* prefill rows per tile; n_rows_padded is a multiple */
 
-/* Message of the last failed call on this host thread ("" if none). [host] */
+/* Message of the last failed call on this host thread ("" if none). [host]
+ * indexer_last_error is the same function under a shorter name. */
 const char *indexer_fp4_last_error(void);
+const char *indexer_last_error(void);
 
 /* ---------------------------------------------------------------------------------
  * Cache write and query quantization ([P2] commit message: the fused writer's FP4
@@ -207,21 +209,24 @@ int indexer_fp4_norm_rope_quant_and_cache(const void *k_bf16, int64_t n_tok, int
  * with q and k the dequantized FP4 values; row r = b*next_n + t reads its sequence's
  * pages through block_table[b]. Columns >= row_len[r] are not written.
  *   sched, row_len  as written by indexer_fp4_decode_schedule for the same batch,
- *                   next_n and n_units (sched's error word may be updated)
+ *                   next_n and n_units (sched's error word may be updated); sched_bytes is
+ *                   the buffer's size, at least indexer_fp4_decode_sched_bytes(batch,
+ *                   next_n, n_units). A buffer whose header names other sizes (stale,
+ *                   zeroed) is not read past its header: the call scores nothing and sets
+ *                   INDEXER_FP4_DEV_BAD_SCHEDULE.
  *   row_hist        optional (NULL: none), uint32 [batch*next_n][4096], 16-byte aligned,
  *                   zero-filled before its first use: the scorer adds the histogram of
  *                   every written logit's top 12 order-key bits (layout private to the
  *                   library), which indexer_topk takes instead of building its own and
  *                   leaves zero-filled again.
- * Errors: EINVAL (n_heads not a multiple of 16 or above 128, batch/next_n/n_units that
- * are not those of the schedule's sizes, negative sizes, misaligned row_hist), ENOSPC
- * (logits_ld < 64*bt_ld or bt_ld <= 0), EARCH, EHIP.
+ * Errors: EINVAL (n_heads not a multiple of 16 or above 128, negative sizes, misaligned
+ * row_hist), ENOSPC (logits_ld < 64*bt_ld, bt_ld <= 0, sched_bytes too small), EARCH, EHIP.
  * --------------------------------------------------------------------------------- */
 int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale,
                              const float *weights, int32_t n_heads, const uint8_t *kv_packed,
                              const uint8_t *kv_scale, int64_t n_pages,
                              const int32_t *block_table, int64_t bt_ld, int32_t batch,
-                             int32_t next_n, void *sched, int32_t n_units,
+                             int32_t next_n, void *sched, int64_t sched_bytes, int32_t n_units,
                              const int32_t *row_len, float *logits, int64_t logits_ld,
                              uint32_t *row_hist, void *stream);
 
@@ -245,7 +250,7 @@ int indexer_fp8_quant_and_cache(const void *k_bf16, int64_t n_tok, int64_t k_ld,
 int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
                              int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
                              int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
-                             int32_t batch, int32_t next_n, void *sched, int32_t n_units,
+                             int32_t batch, int32_t next_n, void *sched, int64_t sched_bytes, int32_t n_units,
                              const int32_t *row_len, float *logits, int64_t logits_ld,
                              uint32_t *row_hist, void *stream);
 
@@ -257,14 +262,16 @@ int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, co
  * rows read nothing and write nothing.
  *   q_packed/q_scale/weights  [n_rows_padded][n_heads]...
  *   sched, row_len            from indexer_fp4_prefill_schedule (same n_req,
- *                             n_rows_padded, n_units)
- * Errors: as decode.
+ *                             n_rows_padded, n_units); sched_bytes at least
+ *                             indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units)
+ * Errors: as decode (a header of other sizes sets INDEXER_FP4_DEV_BAD_SCHEDULE and
+ * nothing is scored).
  * --------------------------------------------------------------------------------- */
 int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
                               const float *weights, int32_t n_heads, const uint8_t *kv_packed,
                               const uint8_t *kv_scale, int64_t n_pages,
                               const int32_t *block_table, int64_t bt_ld, int32_t n_req,
-                              void *sched, int32_t n_units, int32_t n_rows_padded,
+                              void *sched, int64_t sched_bytes, int32_t n_units, int32_t n_rows_padded,
                               const int32_t *row_len, float *logits, int64_t logits_ld,
                               void *stream);
 

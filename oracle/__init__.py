@@ -66,10 +66,9 @@ def _declare(L):
         "oracle_decode_geometry": [P, I32, I32, P, P],
         "oracle_prefill_geometry": [P, P, I32, I32, P, P],
         "oracle_score": [P, P, P, I32, I64, P, P, P, P, I64, P, I64, P, I64, P],
-        "oracle_score_pairs": [P, P, P, I32, P, P, P, P, I64, P, I64, P, P, I64, P],
         "oracle_topk": [P, I64, I64, P, I32, P, I64],
         "oracle_topk_merge": [P, P, I64, I64, I32, I32, P, I64],
-        "oracle_decode_schedule": [P, I32, I32, P, P, P, P, P],
+        "oracle_decode_schedule": [P, I32, I32, P, P, P],
         "oracle_prefill_schedule": [P, P, I32, I32, I32, I32, I32, P, P, P, P, P],
         "oracle_layer_norm": [P, I32, P, P, ctypes.c_float, P],
         "oracle_mx8_encode_blocks": [P, I64, P, P],
@@ -327,23 +326,6 @@ def _score_impl(fn, q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale,
     return out, reads
 
 
-def score_pairs(q_packed, q_scale, w, row_seq, row_len, kv_packed, kv_scale, block_table, rows, cols):
-    qp = _c(q_packed, np.uint8)
-    qs = _c(q_scale, np.uint8)
-    w = _c(w, np.float32)
-    h = qp.shape[1]
-    rs = _c(row_seq, np.int32)
-    rl = _c(row_len, np.int32)
-    bt = _c(block_table, np.int32)
-    r = _c(rows, np.int64)
-    c = _c(cols, np.int64)
-    out = np.zeros(r.shape[0], np.float64)
-    _check(lib().oracle_score_pairs(_p(qp), _p(qs), _p(w), h, _p(rs), _p(rl), _p(kv_packed), _p(kv_scale),
-                                    kv_packed.shape[0], _p(bt), bt.shape[1], _p(r), _p(c), r.shape[0], _p(out)),
-           "score_pairs")
-    return out
-
-
 def topk(s, row_len, k):
     s = _c(s, np.float64)
     rows, ld = s.shape
@@ -371,11 +353,8 @@ def decode_schedule(ctx, n_units):
     cum = np.zeros(b + 1, np.int32)
     ub = np.zeros(n_units + 1, np.int32)
     us = np.zeros(n_units, np.int32)
-    up = np.zeros(n_units, np.int32)
-    ur = np.zeros(n_units, np.int32)
-    _check(lib().oracle_decode_schedule(_p(ctx), b, n_units, _p(cum), _p(ub), _p(us), _p(up), _p(ur)),
-           "decode_schedule")
-    return {"cum_pages": cum, "unit_begin": ub, "unit_seq": us, "unit_page": up, "unit_run": ur}
+    _check(lib().oracle_decode_schedule(_p(ctx), b, n_units, _p(cum), _p(ub), _p(us)), "decode_schedule")
+    return {"cum_pages": cum, "unit_begin": ub, "unit_seq": us}
 
 
 def prefill_schedule(cu_rows, start_pos, n_rows_padded, tile_rows, n_units):

@@ -421,32 +421,6 @@ static int score_fmt(int fmt, const uint8_t *q_packed, const uint8_t *q_scale, c
   return err;
 }
 
-int oracle_score_pairs(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
-                       const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
-                       const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table,
-                       int64_t bt_ld, const int64_t *rows, const int64_t *cols, int64_t n_pairs,
-                       double *out) {
-  if (n_heads <= 0 || n_pairs < 0) return -1;
-  int bad = 0;
-#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
-  for (int64_t i = 0; i < n_pairs; i++) {
-    int64_t r = rows[i], j = cols[i];
-    if (j < 0 || j >= row_len[r] || (j / PAGE_KEYS) >= bt_ld) { bad = 1; continue; }
-    double *qd = (double *)malloc(sizeof(double) * n_heads * KEY_DIM);
-    double kd[KEY_DIM];
-    if (!qd) { bad = 1; continue; }
-    if (dequant_row_q(4, q_packed, q_scale, r, n_heads, qd) ||
-        oracle_dequant_key(kv_packed, kv_scale, n_pages, block_table[(int64_t)row_seq[r] * bt_ld + j / PAGE_KEYS],
-                           (int)(j % PAGE_KEYS), kd)) {
-      bad = 1;
-    } else {
-      out[i] = score_one(qd, &w[r * n_heads], n_heads, kd);
-    }
-    free(qd);
-  }
-  return bad ? -2 : 0;
-}
-
 /* Top-k by a full sort of (score desc, column asc) (R7). The per-row scan is
  * bounded by the row's own length ([P2] review fixes: the top-k bounds its
  * scan by the context, so the logits tail is never read). */
@@ -521,7 +495,7 @@ static void even_split(int64_t n_items, int32_t n_units, int32_t *unit_begin) {
 }
 
 int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, int32_t *cum_pages,
-                           int32_t *unit_begin, int32_t *unit_seq, int32_t *unit_page, int32_t *unit_run) {
+                           int32_t *unit_begin, int32_t *unit_seq) {
   if (batch < 0 || n_units <= 0) return -1;
   cum_pages[0] = 0;
   for (int32_t b = 0; b < batch; b++) {
@@ -533,8 +507,6 @@ int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, i
     int32_t b = 0;
     while (b < batch && cum_pages[b + 1] <= unit_begin[u]) b++;
     unit_seq[u] = b;
-    unit_page[u] = (b < batch) ? unit_begin[u] - cum_pages[b] : 0;  /* page of the first item */
-    unit_run[u] = (b < batch) ? cum_pages[b + 1] - unit_begin[u] : 0; /* items left in sequence b */
   }
   return 0;
 }

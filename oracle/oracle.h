@@ -73,13 +73,6 @@ int oracle_score(const uint8_t *q_packed, const uint8_t *q_scale, const float *w
                  const int32_t *block_table, int64_t bt_ld, double *logits, int64_t ld,
                  int64_t *reads);
 
-/* Same score for an explicit list of (row, column) pairs: out[i] = s[rows[i]][cols[i]]. */
-int oracle_score_pairs(const uint8_t *q_packed, const uint8_t *q_scale, const float *w, int32_t n_heads,
-                       const int32_t *row_seq, const int32_t *row_len, const uint8_t *kv_packed,
-                       const uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table,
-                       int64_t bt_ld, const int64_t *rows, const int64_t *cols, int64_t n_pairs,
-                       double *out);
-
 /* Top-k by full sort: idx[r*idx_ld + i], i < k, holds the column of the i-th
  * largest s[r][j] over j < row_len[r], ties broken by lower column; entries past
  * min(k, row_len[r]) are -1. */
@@ -95,11 +88,9 @@ int oracle_topk_merge(const double *score, const int32_t *index, int64_t ld, int
 /* Decode work split: items are (sequence b, page p < ceil(ctx[b]/64)) in
  * b-major order, cum_pages[b] = first item of b (B+1 entries). Unit u covers
  * items [unit_begin[u], unit_begin[u+1]) with unit_begin[u] = floor(u*W/U);
- * unit_seq[u] = sequence that holds item unit_begin[u] (batch if none), unit_page[u] = that
- * item's page index in it, unit_run[u] = items from it to the end of that sequence (both 0
- * if none). */
+ * unit_seq[u] = sequence that holds item unit_begin[u] (batch if none). */
 int oracle_decode_schedule(const int32_t *ctx, int32_t batch, int32_t n_units, int32_t *cum_pages,
-                           int32_t *unit_begin, int32_t *unit_seq, int32_t *unit_page, int32_t *unit_run);
+                           int32_t *unit_begin, int32_t *unit_seq);
 
 /* Prefill work split: tiles of at most tile_rows rows that stay inside one
  * request's group and start at the group's first row (the last group runs to

@@ -26,6 +26,7 @@ PREFILL_UNITS = 512
 
 EXPORTS = (
     "indexer_fp4_last_error",
+    "indexer_last_error",
     "indexer_fp4_quant_and_cache",
     "indexer_fp4_norm_rope_quant_and_cache",
     "indexer_fp4_decode_sched_bytes",
@@ -62,10 +63,13 @@ def _load() -> ctypes.CDLL:
         "indexer_fp4_decode_schedule": ([P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32], I64),
         "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
-        "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P], ctypes.c_int),
-        "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P], ctypes.c_int),
+        "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P],
+                                     ctypes.c_int),
+        "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I64, I32, I32, P, P, I64, P],
+                                      ctypes.c_int),
         "indexer_fp8_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
-        "indexer_fp8_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P], ctypes.c_int),
+        "indexer_fp8_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P],
+                                     ctypes.c_int),
         "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
         "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P, P], ctypes.c_int),
         "indexer_topk_merge": ([P, P, I64, I32, I32, I32, P, I64, P], ctypes.c_int),
@@ -96,6 +100,10 @@ def _dev(t: torch.Tensor, name: str, dtype=None, contiguous=True):
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _check(rc: int):
@@ -251,8 +259,8 @@ def _score_decode(fn, vec_bytes, q_packed, q_scale, weights, kv_packed, kv_scale
     _check_hist(row_hist, batch * next_n)
     _check(fn(
         _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
-        kv_packed.shape[0], _ptr(block_table), bt_ld, batch, next_n, _ptr(sched), n_units, _ptr(row_len),
-        _ptr(logits), logits.stride(0), _ptr(row_hist), _stream(logits)))
+        kv_packed.shape[0], _ptr(block_table), bt_ld, batch, next_n, _ptr(sched), _nbytes(sched), n_units,
+        _ptr(row_len), _ptr(logits), logits.stride(0), _ptr(row_hist), _stream(logits)))
 
 
 def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, sched, n_units,
@@ -273,8 +281,8 @@ def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, b
     n_req, bt_ld = block_table.shape
     _check(lib.indexer_fp4_score_prefill(
         _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
-        kv_packed.shape[0], _ptr(block_table), bt_ld, n_req, _ptr(sched), n_units, n_rows_padded, _ptr(row_len),
-        _ptr(logits), logits.stride(0), _stream(logits)))
+        kv_packed.shape[0], _ptr(block_table), bt_ld, n_req, _ptr(sched), _nbytes(sched), n_units, n_rows_padded,
+        _ptr(row_len), _ptr(logits), logits.stride(0), _stream(logits)))
 
 
 HIST_BINS = 4096

@@ -56,3 +56,4 @@ int launch_status(const char *what) {
 }  // namespace ifp4
 
 extern "C" const char *indexer_fp4_last_error(void) { return ifp4::g_msg; }
+extern "C" const char *indexer_last_error(void) { return ifp4::g_msg; }

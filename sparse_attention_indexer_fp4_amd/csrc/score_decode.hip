@@ -57,15 +57,21 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   const DecodeSchedLayout L(batch, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
-  const int it0 = sched[L.unit_begin + u];
-  const int it1 = sched[L.unit_begin + u + 1];
+  // The host checked that the buffer holds a schedule of these sizes, so the unit table is
+  // in bounds whatever it contains; its words are only used once the header shows that the
+  // schedule was built for this batch, next_n and unit count (a stale or zeroed buffer is
+  // flagged once, by unit 0, and nothing is scored).
+  const int it0r = sched[L.unit_begin + u];
+  const int it1r = sched[L.unit_begin + u + 1];
+  if (sched[0] != kDecodeMagic || sched[2] != batch || sched[3] != NN || sched[4] != n_units) {
+    if (u == 0 && threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
+    return;
+  }
+  const int items = sched[5];
+  const int it0 = max(it0r, 0), it1 = min(it1r, items);
   if (it0 >= it1) return;  // empty unit: nothing else is touched
   const int lane = threadIdx.x & 63;
   const int wv = uniform(threadIdx.x >> 6);
-  if (sched[0] != kDecodeMagic || sched[2] != batch || sched[3] != NN || sched[4] != n_units) {
-    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
-    return;
-  }
   if (n_pages <= 0) {
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
     return;
@@ -232,8 +238,8 @@ template <class F>
 static int score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights, int32_t n_heads,
                         const uint8_t *kv_packed, const uint8_t *kv_scale, int64_t n_pages,
                         const int32_t *block_table, int64_t bt_ld, int32_t batch, int32_t next_n, void *sched,
-                        int32_t n_units, const int32_t *row_len, float *logits, int64_t logits_ld,
-                        uint32_t *row_hist, void *stream) {
+                        int64_t sched_bytes, int32_t n_units, const int32_t *row_len, float *logits,
+                        int64_t logits_ld, uint32_t *row_hist, void *stream) {
   clear_error();
   if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > INDEXER_FP4_MAX_HEADS)
     return fail(INDEXER_FP4_EINVAL, "n_heads=%d must be a positive multiple of %d and at most %d", n_heads,
@@ -247,6 +253,10 @@ static int score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const f
                 (long long)(bt_ld * kPage));
   if (!sched || !row_len || (batch > 0 && (!q_packed || !q_scale || !weights || !block_table || !logits)))
     return fail(INDEXER_FP4_EINVAL, "score_decode: a required pointer is NULL");
+  const int64_t need = 4 * DecodeSchedLayout(batch, n_units).words;
+  if (sched_bytes < need)
+    return fail(INDEXER_FP4_ENOSPC, "score_decode: sched_bytes=%lld < %lld for batch=%d, n_units=%d",
+                (long long)sched_bytes, (long long)need, batch, n_units);
   if (n_pages > 0 && (!kv_packed || !kv_scale)) return fail(INDEXER_FP4_EINVAL, "score_decode: NULL cache plane");
   if (((uintptr_t)q_packed | (uintptr_t)weights | (uintptr_t)kv_packed | (uintptr_t)kv_scale) % 16 != 0)
     return fail(INDEXER_FP4_EINVAL, "score_decode: q_packed, weights and both planes must be 16-byte aligned");
@@ -268,18 +278,20 @@ static int score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const f
 extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
                                         int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
                                         int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
-                                        int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
-                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
+                                        int32_t next_n, void *sched, int64_t sched_bytes, int32_t n_units,
+                                        const int32_t *row_len, float *logits, int64_t logits_ld,
+                                        uint32_t *row_hist, void *stream) {
   return score_decode<FmtFp4>(q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld,
-                              batch, next_n, sched, n_units, row_len, logits, logits_ld, row_hist, stream);
+                              batch, next_n, sched, sched_bytes, n_units, row_len, logits, logits_ld, row_hist, stream);
 }
 
 // The FP8 comparator: the same scorer over MXFP8 queries and keys (128 bytes a vector).
 extern "C" int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
                                         int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
                                         int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t batch,
-                                        int32_t next_n, void *sched, int32_t n_units, const int32_t *row_len,
-                                        float *logits, int64_t logits_ld, uint32_t *row_hist, void *stream) {
+                                        int32_t next_n, void *sched, int64_t sched_bytes, int32_t n_units,
+                                        const int32_t *row_len, float *logits, int64_t logits_ld,
+                                        uint32_t *row_hist, void *stream) {
   return score_decode<FmtFp8>(q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld,
-                              batch, next_n, sched, n_units, row_len, logits, logits_ld, row_hist, stream);
+                              batch, next_n, sched, sched_bytes, n_units, row_len, logits, logits_ld, row_hist, stream);
 }

@@ -87,27 +87,31 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
   const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
-  const int it0 = sched[L.unit_begin + u];
-  const int it1 = sched[L.unit_begin + u + 1];
+  // The unit table is in bounds (the host checked the buffer's size for these sizes); its
+  // words are used only once the header shows a schedule built for this step's sizes (a
+  // stale or zeroed buffer is flagged once, by unit 0, and nothing is scored).
+  const int it0r = sched[L.unit_begin + u];
+  const int it1r = sched[L.unit_begin + u + 1];
+  if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units) {
+    if (u == 0 && threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
+    return;
+  }
+  const int it0 = max(it0r, 0), it1 = min(it1r, sched[6]);
   if (it0 >= it1) return;  // empty unit (uniform over the workgroup): nothing else is touched
   const int lane = threadIdx.x & 63;
   const int wv = uniform(threadIdx.x >> 6);  // this wave's row inside a tile
-  if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units) {
-    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
-    return;
-  }
   if (n_pages <= 0) {  // the ring always copies some page: there must be one
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
     return;
   }
-  const int n_tiles = sched[5];
+  const int n_tiles = min(sched[5], (int)L.max_tiles);
   const int32_t *tiles = sched_g + L.tiles;  // {first row, rows, request, pages} per tile
   const int32_t *cum = sched_g + L.cum;
   const int n_my = it1 - it0;
   const bool loader = wv < 5;  // waves 0-3 copy key tiles, wave 4 the scale block
 
   // Item table, one lane per item, for 64 items at a time.
-  int tcur = sched[L.unit_tile + u];  // tile of the next item to look up
+  int tcur = min(max(sched[L.unit_tile + u], 0), max(n_tiles - 1, 0));  // tile of the next item to look up
   int tab_base = -64;
   int v_tile = 0, v_page = 0, v_phys = 0, v_need = 0;
   auto fill = [&](int base) {
@@ -315,7 +319,7 @@ using namespace ifp4;
 extern "C" int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
                                          int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
                                          int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t n_req,
-                                         void *sched, int32_t n_units, int32_t n_rows_padded,
+                                         void *sched, int64_t sched_bytes, int32_t n_units, int32_t n_rows_padded,
                                          const int32_t *row_len, float *logits, int64_t logits_ld, void *stream) {
   clear_error();
   if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > INDEXER_FP4_MAX_HEADS)
@@ -331,6 +335,10 @@ extern "C" int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t 
                 (long long)(bt_ld * kPage));
   if (!sched || !row_len || !q_packed || !q_scale || !weights || !block_table || !logits)
     return fail(INDEXER_FP4_EINVAL, "score_prefill: a required pointer is NULL");
+  const int64_t need = 4 * PrefillSchedLayout(n_req, n_rows_padded, n_units).words;
+  if (sched_bytes < need)
+    return fail(INDEXER_FP4_ENOSPC, "score_prefill: sched_bytes=%lld < %lld for n_req=%d, n_rows_padded=%d, n_units=%d",
+                (long long)sched_bytes, (long long)need, n_req, n_rows_padded, n_units);
   if (n_pages > 0 && (!kv_packed || !kv_scale)) return fail(INDEXER_FP4_EINVAL, "score_prefill: NULL cache plane");
   if (((uintptr_t)q_packed | (uintptr_t)weights | (uintptr_t)kv_packed | (uintptr_t)kv_scale) % 16 != 0)
     return fail(INDEXER_FP4_EINVAL, "score_prefill: q_packed, weights and both planes must be 16-byte aligned");

@@ -11,8 +11,9 @@
 // all keys of the row share are skipped), then every key above T is kept together with
 // the lowest-column keys equal to T, and the columns are written in ascending order.
 //
-// Rows up to 16384 keys: one 1024-thread workgroup per row with the row's keys held in
-// LDS. Longer rows: the chunked path further below. Every loop that reads global memory
+// Rows up to 16384 keys: one workgroup per row (512 threads in launches of up to 2047
+// rows, 256 in larger ones) with the row's keys held in LDS. Longer rows: the chunked path
+// further below. Every loop that reads global memory
 // issues all of a thread's loads before it uses them, so a pass costs one memory latency
 // rather than one per element.
 #include "common.h"

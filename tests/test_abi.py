@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
@@ -68,7 +68,10 @@ def test_size_queries(L):
 
 
 def _err(L):
-    return L.indexer_fp4_last_error().decode()
+    msg = L.indexer_fp4_last_error().decode()
+    L.indexer_last_error.restype = ctypes.c_char_p
+    assert L.indexer_last_error().decode() == msg  # the same message under the shorter name
+    return msg
 
 
 def test_host_argument_errors(L):
@@ -83,22 +86,32 @@ def test_host_argument_errors(L):
     L.indexer_fp4_prefill_schedule.argtypes = [P, P, I32, I32, I32, P, I64, P, P]
     assert L.indexer_fp4_prefill_schedule(None, None, 4, 1001, 4096, None, 0, None, None) == -1
     assert "multiple of 8" in _err(L)
-    L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I32, P, P, I64, P, P]
+    L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P]
     # head count not a multiple of 16 (the MFMA tile height)
-    assert L.indexer_fp4_score_decode(None, None, None, 24, None, None, 0, None, 8, 1, 1, None, 512, None,
+    assert L.indexer_fp4_score_decode(None, None, None, 24, None, None, 0, None, 8, 1, 1, None, 0, 512, None,
                                       None, 512, None, None) == -1
     assert "n_heads=24" in _err(L)
     # logits row too short for the block table
-    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 1, 1, None, 512, None,
+    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 1, 1, None, 0, 512, None,
                                       None, 500, None, None) == -2
     assert "logits_ld=500" in _err(L)
+    # a schedule buffer smaller than a schedule of the call's sizes (the unit table would be
+    # read past its end)
+    need = L.indexer_fp4_decode_sched_bytes(1, 1, 512)
+    assert L.indexer_fp4_score_decode(P(16), P(16), P(16), 64, P(16), P(16), 1, P(16), 8, 1, 1, P(16), need - 4,
+                                      512, P(16), P(16), 512, None, None) == -2
+    assert "sched_bytes" in _err(L) and str(need) in _err(L)
     # a row histogram that is not 16-byte aligned
-    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 0, 1, P(16), 512, P(16),
-                                      None, 512, P(20), None) == -1
+    assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 0, 1, P(16), 1 << 20, 512,
+                                      P(16), None, 512, P(20), None) == -1
     assert "row_hist" in _err(L)
-    L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, P, I32, I32, P, P, I64, P]
-    assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, None, 8, 0, None, 512, 8, None,
+    L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, P, I64, I32, I32, P, P, I64, P]
+    assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, None, 8, 0, None, 0, 512, 8, None,
                                        None, 512, None) == -1
+    need = L.indexer_fp4_prefill_sched_bytes(2, 16, 512)
+    assert L.indexer_fp4_score_prefill(P(16), P(16), P(16), 64, P(16), P(16), 1, P(16), 8, 2, P(16), need - 1, 512,
+                                       16, P(16), P(16), 512, None) == -2
+    assert "sched_bytes" in _err(L)
     L.indexer_topk.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, I64, P, P]
     assert L.indexer_topk(None, 100, 4, None, 100, 0, None, 16, None, 0, None, None) == -1
     assert "k=0" in _err(L)

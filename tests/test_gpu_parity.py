@@ -101,8 +101,17 @@ def test_decode_schedule_exact(ifp4, ctx, units, next_n):
     ifp4.indexer_fp4_decode_schedule(to_dev(ctx), next_n, units, sched, row_len)
     got = ifp4.read_decode_schedule(sched, len(ctx), units)
     want = oracle.decode_schedule(ctx, units)
-    for key in ("cum_pages", "unit_begin", "unit_seq", "unit_page", "unit_run"):
+    for key in ("cum_pages", "unit_begin", "unit_seq"):
         assert np.array_equal(got[key], want[key]), key
+    # the library's private per-unit fields (the first item's page in its sequence and the
+    # items left in that sequence) must agree with the oracle's prefix sums
+    cum, ub, us = want["cum_pages"], want["unit_begin"], want["unit_seq"]
+    for u in range(units):
+        b = us[u]
+        if b < len(ctx):
+            assert got["unit_page"][u] == ub[u] - cum[b] and got["unit_run"][u] == cum[b + 1] - ub[u], u
+        else:
+            assert got["unit_page"][u] == 0 and got["unit_run"][u] == 0, u
     assert got["header"][1] == 0
     _, rl = oracle.decode_geometry(ctx, next_n)
     assert np.array_equal(row_len.cpu().numpy(), rl)
@@ -233,6 +242,52 @@ def test_device_side_errors_flag_and_skip(ifp4):
         L = int(o["row_len"][r])
         m = good[r, :L]
         assert np.allclose(lg[r, :L][m], o["s"][r, :L][m], rtol=1e-3, atol=0)
+
+
+def test_stale_or_zeroed_schedule_is_flagged(ifp4):
+    """A schedule buffer that was never built (zero-filled) or was built for other sizes is
+    not trusted: the scorers read only its header, flag INDEXER_FP4_DEV_BAD_SCHEDULE and
+    score nothing (the logits keep their sentinel)."""
+    case = W.decode_config("decode_tiny")
+    g = gpu_decode(case, run_topk=False)
+    units = g["units"]
+    B = case.batch
+    for fill in (0, 0xEE):
+        sched = torch.full((ifp4.indexer_fp4_decode_sched_bytes(B, 1, units),), fill, dtype=torch.uint8, device=dev())
+        sched.view(torch.int32)[1] = 0
+        lg = torch.full_like(g["logits"], float("nan"))
+        ifp4.indexer_fp4_score_decode(g["qp"], g["qs"], to_dev(case.w), g["kp"], g["ks"], to_dev(case.block_table), 1,
+                                      sched, units, g["row_len"], lg)
+        torch.cuda.synchronize()
+        assert ifp4.sched_error(sched) == ifp4.DEV_BAD_SCHEDULE, fill
+        assert torch.isnan(lg).all()
+    # a schedule built for fewer units than the call names: header mismatch, nothing scored
+    small = torch.empty(ifp4.indexer_fp4_decode_sched_bytes(B, 1, units), dtype=torch.uint8, device=dev())
+    rl = torch.empty(B, dtype=torch.int32, device=dev())
+    ifp4.indexer_fp4_decode_schedule(to_dev(case.ctx), 1, units // 2, small, rl)
+    lg = torch.full_like(g["logits"], float("nan"))
+    ifp4.indexer_fp4_score_decode(g["qp"], g["qs"], to_dev(case.w), g["kp"], g["ks"], to_dev(case.block_table), 1,
+                                  small, units, rl, lg)
+    torch.cuda.synchronize()
+    assert ifp4.sched_error(small) == ifp4.DEV_BAD_SCHEDULE
+    assert torch.isnan(lg).all()
+    # prefill: a zeroed buffer
+    pc = W.prefill_config("prefill_tiny", heads=16)
+    st = pc.steps[0]
+    NP, R, H = st.n_rows_padded, len(st.req_ids), pc.heads
+    qp = torch.zeros((NP, H, 64), dtype=torch.uint8, device=dev())
+    qs = torch.zeros((NP, H, 4), dtype=torch.uint8, device=dev())
+    kp = torch.zeros((pc.n_pages, 64, 64), dtype=torch.uint8, device=dev())
+    ks = torch.zeros((pc.n_pages, 4, 64), dtype=torch.uint8, device=dev())
+    bt = W.step_block_table(pc, st)
+    pu = ifp4.PREFILL_UNITS
+    psched = torch.zeros(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, pu), dtype=torch.uint8, device=dev())
+    prl = torch.full((NP,), 5, dtype=torch.int32, device=dev())
+    plg = torch.full((NP, bt.shape[1] * 64), float("nan"), dtype=torch.float32, device=dev())
+    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, to_dev(bt), psched, pu, NP, prl, plg)
+    torch.cuda.synchronize()
+    assert ifp4.sched_error(psched) == ifp4.DEV_BAD_SCHEDULE
+    assert torch.isnan(plg).all()
 
 
 def test_prefill_device_side_errors_flag_and_skip(ifp4):
@@ -724,4 +779,8 @@ def test_context_parallel_decode_on_one_gpu(ifp4):
         cand_i[:, s * k:(s + 1) * k] = torch.where(ok, gi, torch.full_like(gi, -1)).int()
     merged = torch.full((B, k), -7, dtype=torch.int32, device=dev())
     ifp4.indexer_topk_merge(cand_s, cand_i, k, merged)
-    assert np.array_equal(merged.cpu().numpy(), g["top"].cpu().numpy())
+    m = merged.cpu().numpy()
+    assert np.array_equal(m, g["top"].cpu().numpy())
+    # and against the oracle's full sort of its own fp64 scores, up to near-ties of the k-th
+    o = oracle_decode(case)
+    check_topk(m, o["top"], o["s"], o["row_len"], k)

@@ -472,11 +472,39 @@ def test_decode_schedule_covers_every_page_once(ctx, units):
         seq = sch["unit_seq"][u]
         if a < n_items:
             assert sch["cum_pages"][seq] <= a < sch["cum_pages"][seq + 1]
-            assert sch["unit_page"][u] == a - sch["cum_pages"][seq] < pages[seq]
-            assert sch["unit_run"][u] == pages[seq] - sch["unit_page"][u]
         else:
-            assert seq == len(ctx) and sch["unit_page"][u] == 0 and sch["unit_run"][u] == 0
+            assert seq == len(ctx)
     assert (covered == 1).all()
+
+
+def _ints(field):
+    return [int(t) for t in field.split()]
+
+
+def test_schedules_and_geometry_golden():
+    """Hand-worked decode schedules and prefill geometry/tiles (tests/golden/schedules.txt)."""
+    n_dec = n_pre = 0
+    for line in _lines("schedules.txt"):
+        f = [t.strip() for t in line.split(";")]
+        if f[0] == "decode":
+            ctx = np.array(_ints(f[1]), np.int32)
+            sch = oracle.decode_schedule(ctx, int(f[2]))
+            assert list(sch["cum_pages"]) == _ints(f[3])
+            assert list(sch["unit_begin"]) == _ints(f[4])
+            assert list(sch["unit_seq"]) == _ints(f[5])
+            n_dec += 1
+        else:
+            cu, sp = np.array(_ints(f[1]), np.int32), np.array(_ints(f[2]), np.int32)
+            npad, units = int(f[3]), int(f[4])
+            rs, rl = oracle.prefill_geometry(cu, sp, npad)
+            assert list(rs) == _ints(f[5]) and list(rl) == _ints(f[6])
+            sch = oracle.prefill_schedule(cu, sp, npad, 8, units)
+            assert [list(t) for t in sch["tiles"]] == [_ints(t) for t in f[7].split(",")]
+            assert list(sch["cum_items"]) == _ints(f[8])
+            assert list(sch["unit_begin"]) == _ints(f[9])
+            assert list(sch["unit_tile"]) == _ints(f[10])
+            n_pre += 1
+    assert n_dec >= 4 and n_pre >= 2
 
 
 @pytest.mark.parametrize("which", ["prefill_tiny", "prefill_4req"])
