@@ -305,6 +305,24 @@ int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const i
                  void *workspace, int64_t ws_bytes, uint32_t *row_hist, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * indexer_topk without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Same arguments, selection and errors as indexer_topk, except that the
+ * long-row workspace is a fixed array of INDEXER_TOPK_NOALLOC_SCRATCH_BYTES bytes of device
+ * memory owned by the library (one copy per GPU, held until the process ends); a call
+ * whose indexer_topk_workspace_bytes(n_rows, max_len, k) exceeds it returns ENOSPC
+ * (e.g. 16 rows x 131072 keys need 25.7 MB and fit; 32 rows do not). The call allocates
+ * nothing. Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or host threads) race and give undefined selections. The first call
+ * on a GPU (and the first after a call that returned EHIP) clears the array with a fill
+ * kernel on `stream` before selecting.
+ * --------------------------------------------------------------------------------- */
+#define INDEXER_TOPK_NOALLOC_SCRATCH_BYTES (32ll << 20)
+int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
+                         int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, uint32_t *row_hist,
+                         void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Candidate merge for context-parallel decode ([P2] DCP commit: each rank takes a local
  * top-k over its share of a sequence's pages, the ranks exchange candidates, and a merge
  * top-k reads the exchanged fp32 scores).

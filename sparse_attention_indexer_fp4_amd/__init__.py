@@ -40,6 +40,7 @@ EXPORTS = (
     "indexer_topk_workspace_bytes",
     "indexer_topk_merge",
     "indexer_topk",
+    "indexer_topk_noalloc",
 )
 
 
@@ -73,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "indexer_topk_workspace_bytes": ([I32, I64, I32], I64),
         "indexer_topk": ([P, I64, I32, P, I64, I32, P, I64, P, I64, P, P], ctypes.c_int),
         "indexer_topk_merge": ([P, P, I64, I32, I32, I32, P, I64, P], ctypes.c_int),
+        "indexer_topk_noalloc": ([P, I64, I32, P, I64, I32, P, I64, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -321,6 +323,23 @@ def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None, row_hist
     _check(lib.indexer_topk(
         _ptr(logits), logits.stride(0), logits.shape[0], _ptr(row_len), max_len, k, _ptr(topk_idx),
         topk_idx.stride(0), _ptr(workspace), ws_bytes, _ptr(row_hist), _stream(logits)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def indexer_topk_noalloc(logits, row_len, max_len, k, topk_idx, row_hist=None):
+    """indexer_topk with the library's fixed per-GPU scratch array instead of a workspace
+    (allocates nothing; calls that overlap on one GPU race)."""
+    _dev(logits, "logits", torch.float32, contiguous=False)
+    _dev(row_len, "row_len", torch.int32)
+    _dev(topk_idx, "topk_idx", torch.int32, contiguous=False)
+    if logits.stride(1) != 1 or topk_idx.stride(1) != 1:
+        raise ValueError("logits and topk_idx rows must be contiguous")
+    _check_hist(row_hist, logits.shape[0])
+    _check(lib.indexer_topk_noalloc(
+        _ptr(logits), logits.stride(0), logits.shape[0], _ptr(row_len), max_len, k, _ptr(topk_idx),
+        topk_idx.stride(0), _ptr(row_hist), _stream(logits)))
 
 
 def indexer_topk_merge(cand_score, cand_index, k, topk_idx):

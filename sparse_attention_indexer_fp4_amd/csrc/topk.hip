@@ -16,6 +16,8 @@
 // further below. Every loop that reads global memory
 // issues all of a thread's loads before it uses them, so a pass costs one memory latency
 // rather than one per element.
+#include <mutex>
+
 #include "common.h"
 
 namespace ifp4 {
@@ -1012,10 +1014,11 @@ extern "C" int64_t indexer_topk_workspace_bytes(int32_t n_rows, int64_t max_len,
   return 4 * LongWs(n_rows, max_len).words;
 }
 
-extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
-                            int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, void *workspace,
-                            int64_t ws_bytes, uint32_t *row_hist, void *stream) {
-  clear_error();
+// Checks and launches of indexer_topk, on a workspace the caller (or the scratch array below)
+// provides; `ws_what` names it in messages.
+static int topk_check(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
+                      int64_t max_len, int32_t k, const int32_t *topk_idx, int64_t topk_ld, int64_t ws_bytes,
+                      const char *ws_what, const uint32_t *row_hist) {
   if (k <= 0 || n_rows < 0 || max_len < 0)
     return fail(INDEXER_FP4_EINVAL, "topk: k=%d must be > 0, n_rows=%d >= 0, max_len=%lld >= 0", k, n_rows,
                 (long long)max_len);
@@ -1028,10 +1031,20 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   if (topk_ld < k) return fail(INDEXER_FP4_ENOSPC, "topk: topk_ld=%lld < k=%d", (long long)topk_ld, k);
   const int64_t need = indexer_topk_workspace_bytes(n_rows, max_len, k);
   if (ws_bytes < need)
-    return fail(INDEXER_FP4_ENOSPC, "topk: workspace needs %lld bytes, has %lld", (long long)need, (long long)ws_bytes);
+    return fail(INDEXER_FP4_ENOSPC, "topk: n_rows=%d, max_len=%lld, k=%d need %lld bytes of %s, which has %lld",
+                n_rows, (long long)max_len, k, (long long)need, ws_what, (long long)ws_bytes);
   if (n_rows > 0 && (!logits || !row_len || !topk_idx)) return fail(INDEXER_FP4_EINVAL, "topk: NULL pointer");
   if ((uintptr_t)row_hist % 16 != 0) return fail(INDEXER_FP4_EINVAL, "topk: row_hist must be 16-byte aligned");
-  int rc = check_device();
+  return INDEXER_FP4_OK;
+}
+
+static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
+                     int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, void *workspace,
+                     int64_t ws_bytes, const char *ws_what, uint32_t *row_hist, void *stream) {
+  int rc = topk_check(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, ws_bytes, ws_what,
+                      row_hist);
+  if (rc) return rc;
+  rc = check_device();
   if (rc) return rc;
   if (n_rows == 0) return INDEXER_FP4_OK;
   hipStream_t st = (hipStream_t)stream;
@@ -1076,6 +1089,76 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
   hipLaunchKernelGGL(topk_finish_kernel, dim3(n_rows), dim3(kFinishThreads), lds, st, row_len, max_len, k, ws,
                      n_rows, h1, topk_idx, topk_ld);
   return launch_status("topk");
+}
+
+extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,
+                            int64_t max_len, int32_t k, int32_t *topk_idx, int64_t topk_ld, void *workspace,
+                            int64_t ws_bytes, uint32_t *row_hist, void *stream) {
+  clear_error();
+  return topk_impl(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, workspace, ws_bytes,
+                   "workspace", row_hist, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// indexer_topk_noalloc: the same selection with the long-row workspace in a fixed array of
+// device memory that the library owns, for callers that cannot allocate. Each device holds
+// its own copy of the array; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name in host code is a
+// host-side stand-in, not a device address). The kernels leave the array's histograms
+// zeroed after every call, as they leave a caller's workspace; the array is cleared by a fill
+// kernel on its first use on a device and again after a call that failed to launch.
+constexpr int64_t kScratchBytes = INDEXER_TOPK_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) uint32_t scratch[kScratchBytes / 4];
+
+__global__ void scratch_zero_kernel(uint4 *p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64];   // per device: the array's device address, once looked up
+static bool g_scratch_clean[64];  // per device: the array is known to be zero-filled where it must be
+
+extern "C" int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int32_t n_rows,
+                                    const int32_t *row_len, int64_t max_len, int32_t k, int32_t *topk_idx,
+                                    int64_t topk_ld, uint32_t *row_hist, void *stream) {
+  clear_error();
+  int rc = topk_check(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, kScratchBytes,
+                      "the fixed scratch array", row_hist);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  void *ptr = nullptr;
+  bool clean = false;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !g_scratch_ptr[dev]) {
+        g_scratch_ptr[dev] = nullptr;
+        return fail(INDEXER_FP4_EHIP, "topk_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(e));
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+    clean = g_scratch_clean[dev];
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (!clean) {  // a fill kernel, not a memset node, so that a captured graph replays it faithfully
+    hipLaunchKernelGGL(scratch_zero_kernel, dim3(1024), dim3(256), 0, st, (uint4 *)ptr, kScratchBytes / 16);
+    rc = launch_status("topk_noalloc scratch clear");
+    if (rc) return rc;
+  }
+  rc = topk_impl(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, ptr, kScratchBytes,
+                 "scratch", row_hist, stream);
+  // an argument error returns before any launch and leaves the array as it was; a failed
+  // launch may have left it partly written
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch_clean[dev] = rc != INDEXER_FP4_EHIP;
+  return rc;
 }
 
 extern "C" int indexer_topk_merge(const float *cand_score, const int32_t *cand_index, int64_t cand_ld,

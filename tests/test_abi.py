@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), n
     import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
@@ -120,6 +120,11 @@ def test_host_argument_errors(L):
     assert L.indexer_topk(None, 100, 4, None, 200, 32, None, 32, None, 0, None, None) == -1
     assert L.indexer_topk(None, 100, 0, None, 100, 32, None, 32, None, 0, P(20), None) == -1
     assert "row_hist" in _err(L)
+    # the allocation-free top-k refuses sizes whose workspace exceeds its fixed scratch array
+    L.indexer_topk_noalloc.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, P]
+    assert L.indexer_topk_noalloc(None, 1 << 20, 64, None, 1 << 20, 2048, None, 2048, None, None) == -2
+    assert "scratch array" in _err(L) and "n_rows=64" in _err(L)
+    assert L.indexer_topk_noalloc(None, 100, 4, None, 100, 0, None, 16, None, None) == -1
     L.indexer_topk_merge.argtypes = [P, P, I64, I32, I32, I32, P, I64, P]
     assert L.indexer_topk_merge(None, None, 16, 2, 16, 0, None, 16, None) == -1
     assert L.indexer_topk_merge(None, None, 16, 2, 16, 8192, None, 8192, None) == -1
