@@ -276,7 +276,8 @@ def bench_prefill(torch, ifp4, W, args):
             bt=torch.from_numpy(bt).to(dev),
             qp=torch.empty((NP, case.heads, 64), dtype=torch.uint8, device=dev),
             qs=torch.empty((NP, case.heads, 4), dtype=torch.uint8, device=dev),
-            sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8, device=dev),
+            sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units, bt.shape[1]), dtype=torch.uint8,
+                              device=dev),
             row_len=torch.empty(NP, dtype=torch.int32, device=dev),
             logits=torch.empty((NP, ld), dtype=torch.float32, device=dev),
             top=torch.empty((NP, case.topk), dtype=torch.int32, device=dev)))
@@ -284,20 +285,21 @@ def bench_prefill(torch, ifp4, W, args):
     def schedules():
         # published once a step and shared by every layer of the step
         for s in steps:
-            ifp4.indexer_fp4_prefill_schedule(s["cu"], s["sp"], s["NP"], units, s["sched"], s["row_len"])
+            ifp4.indexer_fp4_prefill_schedule(s["cu"], s["sp"], s["NP"], units, s["bt"], kp.shape[0], s["sched"],
+                                              s["row_len"])
 
     def run():
         # one layer: per step the chunk's key/query write, the scorer and the top-k
         for s in steps:
             ifp4.indexer_fp4_quant_and_cache(s["keys"], s["slots"], kp, ks, s["q"], s["qp"], s["qs"])
-            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["bt"], s["sched"], units, s["NP"],
-                                           s["row_len"], s["logits"])
+            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["R"], s["bt"].shape[1], s["sched"],
+                                           units, s["NP"], s["logits"])
             ifp4.indexer_topk(s["logits"], s["row_len"], ld, case.topk, s["top"])
 
     def scorers():
         for s in steps:
-            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["bt"], s["sched"], units, s["NP"],
-                                           s["row_len"], s["logits"])
+            ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["R"], s["bt"].shape[1], s["sched"],
+                                           units, s["NP"], s["logits"])
 
     for _ in range(max(1, args.warmup)):
         schedules()

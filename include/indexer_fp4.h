@@ -85,7 +85,8 @@ enum {
 #define INDEXER_FP4_HEAD_DIM 128  /* index head dimension ([P2] Scope) */
 #define INDEXER_FP4_HEAD_MULT 16  /* n_heads must be a multiple of this ([P2] Scope: MFMA_M) */
 #define INDEXER_FP4_MAX_HEADS 128
-#define INDEXER_FP4_TILE_ROWS 8   /* prefill rows per tile; n_rows_padded is a multiple */
+#define INDEXER_FP4_ROW_MULTIPLE 8 /* a prefill step's n_rows_padded is a multiple of this */
+#define INDEXER_FP4_TILE_ROWS 16   /* prefill rows per tile (a row group is cut into tiles) */
 
 /* Message of the last failed call on this host thread ("" if none). [host]
  * indexer_last_error is the same function under a shorter name. */
@@ -142,20 +143,30 @@ int indexer_fp4_decode_schedule(const int32_t *context_lens, int32_t batch, int3
  * cu_rows[i] and sees keys [0, position] (causal, inclusive). Rows [cu_rows[n_req],
  * n_rows_padded) are padding: they join the last request's group and see no key
  * ([P1] section 3: padding rows fold into the last request's group, sit at position 0
- * and read no key). Each group is cut into tiles of up to 8 rows starting at the
- * group's first row; a work item is (tile, page), tile-major.
- *   cu_rows    int32 [n_req+1], cu_rows[0] = 0, ascending, cu_rows[n_req] <= n_rows_padded
- *   start_pos  int32 [n_req]
- *   n_rows_padded [host] multiple of 8
- *   row_len    int32 [n_rows_padded] output (0 for padding rows)
- * Errors: EINVAL (n_req <= 0, n_rows_padded not a positive multiple of 8, n_units <= 0),
- * ENOSPC, EARCH, EHIP. Device-side: a descending cu_rows or negative start_pos sets
- * INDEXER_FP4_DEV_BAD_LENGTH and empties the schedule.
+ * and read no key). Each group is cut into tiles of up to INDEXER_FP4_TILE_ROWS rows
+ * starting at the group's first row; a work item is (tile, page), tile-major, for the
+ * pages the tile's longest row reaches. The schedule also looks every item's page up in
+ * the block table (request i reads its keys through block_table[i]; [P1] section 3: group
+ * b -> block_tables[b]), once a step for every layer that shares the table, so the scorer
+ * does not read the table; a page the table cannot give (an entry outside [0, n_pages), or
+ * past bt_ld) is recorded as unreadable and flagged in the schedule's error word
+ * (INDEXER_FP4_DEV_BAD_PAGE, INDEXER_FP4_DEV_TABLE_SHORT); its logits are not written.
+ *   cu_rows     int32 [n_req+1], cu_rows[0] = 0, ascending, cu_rows[n_req] <= n_rows_padded
+ *   start_pos   int32 [n_req]
+ *   n_rows_padded [host] a multiple of INDEXER_FP4_ROW_MULTIPLE
+ *   block_table int32 [n_req][bt_ld]: row i = request i of the step
+ *   n_pages     pages in the cache planes the scorer will read
+ *   sched       indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units, bt_ld) bytes
+ *   row_len     int32 [n_rows_padded] output (0 for padding rows)
+ * Errors: EINVAL (n_req <= 0, n_rows_padded not a positive multiple of 8, n_units <= 0,
+ * bt_ld outside 1..2^31-1, n_pages < 0), ENOSPC, EARCH, EHIP. Device-side: a descending
+ * cu_rows or negative start_pos sets INDEXER_FP4_DEV_BAD_LENGTH and empties the schedule.
  * --------------------------------------------------------------------------------- */
-int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, int32_t n_units);
+int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, int32_t n_units, int64_t bt_ld);
 int indexer_fp4_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
-                                 int32_t n_rows_padded, int32_t n_units, void *sched,
-                                 int64_t sched_bytes, int32_t *row_len, void *stream);
+                                 int32_t n_rows_padded, int32_t n_units, const int32_t *block_table,
+                                 int64_t bt_ld, int64_t n_pages, void *sched, int64_t sched_bytes,
+                                 int32_t *row_len, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Fused writer: key LayerNorm and RoPE, then the cache write and query quantization
@@ -256,24 +267,24 @@ int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, co
 
 /* ---------------------------------------------------------------------------------
  * Prefill scorer ([P2] commit message: the FP4 prefill variant; [P1] section 3: the
- * row-group kernel finds a group's page table as group b -> block_tables[b]).
- * Same logit as decode for every valid row of the step; row r of request i reads its
- * keys through block_table[i] (row i of the table = request i of the step). Padding
- * rows read nothing and write nothing.
+ * row-group kernel finds a group's page table as group b -> block_tables[b], which the
+ * schedule has already resolved). Same logit as decode for every valid row of the step;
+ * padding rows read nothing and write nothing; items whose page the schedule marked
+ * unreadable are skipped.
  *   q_packed/q_scale/weights  [n_rows_padded][n_heads]...
- *   sched, row_len            from indexer_fp4_prefill_schedule (same n_req,
- *                             n_rows_padded, n_units); sched_bytes at least
- *                             indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units)
+ *   n_pages, bt_ld, n_req, n_units, n_rows_padded  as given to the schedule call
+ *   sched                     from indexer_fp4_prefill_schedule; sched_bytes its size
+ *   logits                    fp32 [n_rows_padded][logits_ld], logits_ld >= 64*bt_ld
+ * More than 64 heads are scored in passes of 64 heads over the same items (two launches
+ * at 128 heads); the passes after the first add into the logits.
  * Errors: as decode (a header of other sizes sets INDEXER_FP4_DEV_BAD_SCHEDULE and
  * nothing is scored).
  * --------------------------------------------------------------------------------- */
 int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
                               const float *weights, int32_t n_heads, const uint8_t *kv_packed,
-                              const uint8_t *kv_scale, int64_t n_pages,
-                              const int32_t *block_table, int64_t bt_ld, int32_t n_req,
+                              const uint8_t *kv_scale, int64_t n_pages, int64_t bt_ld, int32_t n_req,
                               void *sched, int64_t sched_bytes, int32_t n_units, int32_t n_rows_padded,
-                              const int32_t *row_len, float *logits, int64_t logits_ld,
-                              void *stream);
+                              float *logits, int64_t logits_ld, void *stream);
 
 /* ---------------------------------------------------------------------------------
  * Per-row top-k ([P2] review fixes: top_k_per_row bounds its scan by the row's

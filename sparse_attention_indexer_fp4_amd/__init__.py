@@ -18,11 +18,12 @@ LIB_PATH = os.path.join(_HERE, "libindexer_fp4.so")
 
 PAGE = 64
 HEAD_DIM = 128
-TILE_ROWS = 8
+ROW_MULTIPLE = 8   # a prefill step's padded row count is a multiple of this
+TILE_ROWS = 16     # prefill rows per tile
 DEV_BAD_PAGE, DEV_TABLE_SHORT, DEV_BAD_SCHEDULE, DEV_BAD_LENGTH = 1, 2, 4, 8
 # persistent-grid sizes the scorers default to (units = workgroups)
 DECODE_UNITS = 512
-PREFILL_UNITS = 512
+PREFILL_UNITS = 256  # one 16-wave unit per CU
 
 EXPORTS = (
     "indexer_fp4_last_error",
@@ -62,11 +63,11 @@ def _load() -> ctypes.CDLL:
                                                    P, P, P, F32, P, I32, P, P], ctypes.c_int),
         "indexer_fp4_decode_sched_bytes": ([I32, I32, I32], I64),
         "indexer_fp4_decode_schedule": ([P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
-        "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32], I64),
-        "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, P, P], ctypes.c_int),
+        "indexer_fp4_prefill_sched_bytes": ([I32, I32, I32, I64], I64),
+        "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, I64, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P],
                                      ctypes.c_int),
-        "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, P, I64, I32, P, I64, I32, I32, P, P, I64, P],
+        "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, I64, I32, P, I64, I32, I32, P, I64, P],
                                       ctypes.c_int),
         "indexer_fp8_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
         "indexer_fp8_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P],
@@ -200,8 +201,8 @@ def indexer_fp4_decode_sched_bytes(batch: int, next_n: int, n_units: int) -> int
     return int(lib.indexer_fp4_decode_sched_bytes(batch, next_n, n_units))
 
 
-def indexer_fp4_prefill_sched_bytes(n_req: int, n_rows_padded: int, n_units: int) -> int:
-    return int(lib.indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units))
+def indexer_fp4_prefill_sched_bytes(n_req: int, n_rows_padded: int, n_units: int, bt_ld: int) -> int:
+    return int(lib.indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units, bt_ld))
 
 
 def indexer_fp4_decode_schedule(context_lens, next_n, n_units, sched, row_len):
@@ -214,14 +215,19 @@ def indexer_fp4_decode_schedule(context_lens, next_n, n_units, sched, row_len):
         sched.numel() * sched.element_size(), _ptr(row_len), _stream(sched)))
 
 
-def indexer_fp4_prefill_schedule(cu_rows, start_pos, n_rows_padded, n_units, sched, row_len):
+def indexer_fp4_prefill_schedule(cu_rows, start_pos, n_rows_padded, n_units, block_table, n_pages, sched, row_len):
+    """cu_rows int32 [R+1], start_pos int32 [R], block_table int32 [R, bt_ld] (row i = request i);
+    n_pages: pages of the cache planes the scorer reads. Outputs: sched, row_len int32 [n_rows_padded]."""
     _dev(cu_rows, "cu_rows", torch.int32)
     _dev(start_pos, "start_pos", torch.int32)
+    _dev(block_table, "block_table", torch.int32)
     _dev(sched, "sched")
     _dev(row_len, "row_len", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != start_pos.shape[0]:
+        raise ValueError("block_table must be [n_req, bt_ld]")
     _check(lib.indexer_fp4_prefill_schedule(
-        _ptr(cu_rows), _ptr(start_pos), start_pos.shape[0], n_rows_padded, n_units, _ptr(sched),
-        sched.numel() * sched.element_size(), _ptr(row_len), _stream(sched)))
+        _ptr(cu_rows), _ptr(start_pos), start_pos.shape[0], n_rows_padded, n_units, _ptr(block_table),
+        block_table.shape[1], int(n_pages), _ptr(sched), _nbytes(sched), _ptr(row_len), _stream(sched)))
 
 
 def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched, n_units,
@@ -265,26 +271,23 @@ def _score_decode(fn, vec_bytes, q_packed, q_scale, weights, kv_packed, kv_scale
         _ptr(row_len), _ptr(logits), logits.stride(0), _ptr(row_hist), _stream(logits)))
 
 
-def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, sched, n_units,
-                              n_rows_padded, row_len, logits):
-    """block_table int32 [n_req, W] with row i = request i of the step; q/weights/logits have
-    n_rows_padded rows."""
+def indexer_fp4_score_prefill(q_packed, q_scale, weights, kv_packed, kv_scale, n_req, bt_ld, sched, n_units,
+                              n_rows_padded, logits):
+    """q/weights/logits have n_rows_padded rows; n_req, bt_ld, n_units, n_rows_padded and the cache's
+    page count as given to indexer_fp4_prefill_schedule (which resolved the block table)."""
     _dev(q_packed, "q_packed", torch.uint8)
     _dev(q_scale, "q_scale", torch.uint8)
     _dev(weights, "weights", torch.float32)
     _dev(kv_packed, "kv_packed", torch.uint8)
     _dev(kv_scale, "kv_scale", torch.uint8)
-    _dev(block_table, "block_table", torch.int32)
     _dev(sched, "sched")
-    _dev(row_len, "row_len", torch.int32)
     _dev(logits, "logits", torch.float32, contiguous=False)
     if logits.stride(1) != 1:
         raise ValueError("logits rows must be contiguous")
-    n_req, bt_ld = block_table.shape
     _check(lib.indexer_fp4_score_prefill(
         _ptr(q_packed), _ptr(q_scale), _ptr(weights), q_packed.shape[1], _ptr(kv_packed), _ptr(kv_scale),
-        kv_packed.shape[0], _ptr(block_table), bt_ld, n_req, _ptr(sched), _nbytes(sched), n_units, n_rows_padded,
-        _ptr(row_len), _ptr(logits), logits.stride(0), _stream(logits)))
+        kv_packed.shape[0], int(bt_ld), int(n_req), _ptr(sched), _nbytes(sched), n_units, n_rows_padded,
+        _ptr(logits), logits.stride(0), _stream(logits)))
 
 
 HIST_BINS = 4096
@@ -376,14 +379,21 @@ def read_decode_schedule(sched, batch: int, n_units: int) -> dict:
             "unit_page": w[up:up + n_units].copy(), "unit_run": w[ur:ur + n_units].copy()}
 
 
-def read_prefill_schedule(sched, n_req: int, n_rows_padded: int, n_units: int) -> dict:
+def read_prefill_schedule(sched, n_req: int, n_rows_padded: int, n_units: int, bt_ld: int) -> dict:
+    """Host copy of a prefill schedule: tiles as {first row, rows, request, pages} (the
+    oracle's fields) plus the library's own per-tile, per-unit and per-item words."""
     w = sched.view(torch.int32).cpu().numpy()
     max_tiles = n_rows_padded // TILE_ROWS + n_req
-    tiles = 8
-    cum = tiles + 4 * max_tiles
+    urec = 16
+    tiles = urec + 16 * n_units
+    cum = tiles + 8 * max_tiles
     ub = cum + max_tiles + 1
     ut = ub + n_units + 1
-    n_tiles = int(w[5])
-    return {"header": w[:8].copy(), "tiles": w[tiles:tiles + 4 * n_tiles].reshape(n_tiles, 4).copy(),
+    rt = ut + n_units
+    ip = rt + n_req + 1
+    n_tiles, items = int(w[5]), int(w[6])
+    t8 = w[tiles:tiles + 8 * n_tiles].reshape(n_tiles, 8).copy()
+    return {"header": w[:16].copy(), "tiles": t8[:, [0, 1, 4, 5]].copy(), "tile_words": t8,
             "cum_items": w[cum:cum + n_tiles + 1].copy(), "unit_begin": w[ub:ub + n_units + 1].copy(),
-            "unit_tile": w[ut:ut + n_units].copy()}
+            "unit_tile": w[ut:ut + n_units].copy(), "unit_records": w[urec:tiles].reshape(n_units, 16).copy(),
+            "item_phys": w[ip:ip + items].copy()}

@@ -20,7 +20,7 @@ constexpr int kPageBytes = kPage * kKeyBytes;    // packed plane bytes per page 
 constexpr int kPageScaleBytes = kPage * kGroups; // scale plane bytes per page (256)
 constexpr int kKeyBytes8 = kHeadDim;             // MXFP8 (comparator): E4M3 bytes per key (128)
 constexpr int kPageBytes8 = kPage * kKeyBytes8;  // its packed plane bytes per page (8192)
-constexpr int kTileRows = INDEXER_FP4_TILE_ROWS; // prefill rows per tile
+constexpr int kRowMultiple = INDEXER_FP4_ROW_MULTIPLE; // prefill rows are padded to a multiple of this
 
 // ---- errors (thread-local message, see indexer_fp4_last_error) -------------------------
 int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -50,20 +50,36 @@ struct DecodeSchedLayout {
   }
 };
 
-// Prefill: [0] magic, [1] error word, [2] n_req, [3] n_rows_padded, [4] n_units,
-//          [5] n_tiles, [6] items, [7] tile rows, then tiles[max_tiles] as int4
-//          {first row, rows, request, pages}, cum_items[max_tiles+1],
-//          unit_begin[n_units+1], unit_tile[n_units], req_tile[n_req+1].
+// Prefill: a 16-word header [0] magic, [1] error word, [2] n_req, [3] n_rows_padded,
+// [4] n_units, [5] n_tiles, [6] items, [7] tile rows, [8] bt_ld, [9] n_pages (clamped to
+// INT32_MAX), then
+//   unit records [n_units][16]: {first item, end item, first tile, 0, that tile's record (8
+//                words), physical pages of the unit's first four items (-1 past its end)}
+//   tiles      [max_tiles][8]: {first row, rows, valid rows, position of the first row,
+//                request, pages, first item, 0}
+//   cum_items  [max_tiles+1]  first item of each tile (items are (tile, page), tile-major)
+//   unit_begin [n_units+1], unit_tile [n_units], req_tile [n_req+1]
+//   item_phys  [max_tiles * bt_ld]  physical page of every item, -1 if it cannot be read
+// The block table is resolved here, once a step for every layer that shares it, so a scorer
+// unit needs one scalar load to start its first page copies.
+constexpr int kPrefillTileRows = 16;
+constexpr int kPrefillHdrWords = 16;
+constexpr int kUnitRecWords = 16;
+constexpr int kTileRecWords = 8;
+constexpr int kUnitRecPhys = 4;  // first items whose pages a unit record carries
+
 struct PrefillSchedLayout {
-  int64_t max_tiles, tiles, cum, unit_begin, unit_tile, req_tile, words;
-  __host__ __device__ PrefillSchedLayout(int32_t n_req, int32_t n_rows_padded, int32_t n_units) {
-    max_tiles = (int64_t)n_rows_padded / kTileRows + n_req;
-    tiles = kHdrWords;
-    cum = tiles + 4 * max_tiles;
+  int64_t max_tiles, urec, tiles, cum, unit_begin, unit_tile, req_tile, item_phys, words;
+  __host__ __device__ PrefillSchedLayout(int32_t n_req, int32_t n_rows_padded, int32_t n_units, int64_t bt_ld) {
+    max_tiles = (int64_t)n_rows_padded / kPrefillTileRows + n_req;
+    urec = kPrefillHdrWords;
+    tiles = urec + (int64_t)kUnitRecWords * n_units;
+    cum = tiles + (int64_t)kTileRecWords * max_tiles;
     unit_begin = cum + max_tiles + 1;
     unit_tile = unit_begin + (int64_t)n_units + 1;
     req_tile = unit_tile + n_units;
-    words = req_tile + (int64_t)n_req + 1;
+    item_phys = req_tile + (int64_t)n_req + 1;
+    words = item_phys + max_tiles * bt_ld;
   }
 };
 

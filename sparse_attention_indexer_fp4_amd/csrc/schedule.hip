@@ -110,12 +110,30 @@ __global__ __launch_bounds__(kSchedThreads) void decode_schedule_kernel(const in
 
 __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(
     const int32_t *__restrict__ cu_rows, const int32_t *__restrict__ start_pos, int n_req, int n_rows_padded,
-    int n_units, int32_t *sched, int32_t *__restrict__ row_len) {
+    int n_units, const int32_t *__restrict__ bt, int64_t bt_ld, int64_t n_pages, int32_t *sched,
+    int32_t *__restrict__ row_len) {
   __shared__ int lds[kSchedThreads / 64];
-  const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
+  __shared__ int s_flags;
+  const PrefillSchedLayout L(n_req, n_rows_padded, n_units, bt_ld);
   int32_t *tiles = sched + L.tiles;
   int32_t *cum = sched + L.cum;
   int32_t *req_tile = sched + L.req_tile;
+  int32_t *item_phys = sched + L.item_phys;
+  constexpr int TR = kPrefillTileRows;
+  auto header = [&](int err, int n_tiles, int items) {
+    sched[0] = kPrefillMagic;
+    sched[1] = err;
+    sched[2] = n_req;
+    sched[3] = n_rows_padded;
+    sched[4] = n_units;
+    sched[5] = n_tiles;
+    sched[6] = items;
+    sched[7] = TR;
+    sched[8] = (int32_t)bt_ld;
+    sched[9] = (int32_t)min(n_pages, (int64_t)INT32_MAX);
+    for (int i = 10; i < kPrefillHdrWords; i++) sched[i] = 0;
+  };
+  if (threadIdx.x == 0) s_flags = 0;
   // validate: cu_rows starts at 0, ascends, ends within the padded rows; positions >= 0
   int bad_local = 0;
   for (int i = threadIdx.x; i < n_req; i += kSchedThreads) {
@@ -123,21 +141,17 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(
   }
   if (threadIdx.x == 0 && (cu_rows[0] != 0 || cu_rows[n_req] > n_rows_padded)) bad_local = 1;
   const int bad = __syncthreads_or(bad_local);
-  if (bad) {
+  if (bad) {  // an empty schedule: no unit has work, every row has length 0
     for (int r = threadIdx.x; r < n_rows_padded; r += kSchedThreads) row_len[r] = 0;
     for (int u = threadIdx.x; u <= n_units; u += kSchedThreads) {
       sched[L.unit_begin + u] = 0;
-      if (u < n_units) sched[L.unit_tile + u] = 0;
+      if (u < n_units) {
+        sched[L.unit_tile + u] = 0;
+        for (int j = 0; j < kUnitRecWords; j++) sched[L.urec + (int64_t)kUnitRecWords * u + j] = 0;
+      }
     }
     if (threadIdx.x == 0) {
-      sched[0] = kPrefillMagic;
-      sched[1] = INDEXER_FP4_DEV_BAD_LENGTH;
-      sched[2] = n_req;
-      sched[3] = n_rows_padded;
-      sched[4] = n_units;
-      sched[5] = 0;
-      sched[6] = 0;
-      sched[7] = kTileRows;
+      header(INDEXER_FP4_DEV_BAD_LENGTH, 0, 0);
       cum[0] = 0;
     }
     return;
@@ -149,7 +163,7 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(
     int nt = 0;
     if (i < n_req) {
       const int gend = (i == n_req - 1) ? n_rows_padded : cu_rows[i + 1];
-      nt = (gend - cu_rows[i] + kTileRows - 1) / kTileRows;
+      nt = (gend - cu_rows[i] + TR - 1) / TR;
     }
     int total;
     const int incl = block_inclusive_scan(nt, lds, &total);
@@ -159,42 +173,39 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(
   const int n_tiles = carry;
   if (threadIdx.x == 0) req_tile[0] = 0;
   __syncthreads();
-  // fill tiles and their page counts, then prefix-sum the pages into work items
+  // tile records and their page counts, then the pages' prefix sum (first item per tile)
   carry = 0;
   for (int base = 0; base < n_tiles; base += kSchedThreads) {
     const int t = base + threadIdx.x;
-    int pages = 0;
+    int pages = 0, r0 = 0, nr = 0, nv = 0, pos0 = 0, i = 0;
     if (t < n_tiles) {
-      const int i = count_le(req_tile + 1, n_req - 1, t);  // request whose tiles hold t
-      const int m = t - req_tile[i];
+      i = count_le(req_tile + 1, n_req - 1, t);  // request whose tiles hold t
       const int first = cu_rows[i];
-      const int r0 = first + kTileRows * m;
+      r0 = first + TR * (t - req_tile[i]);
       const int gend = (i == n_req - 1) ? n_rows_padded : cu_rows[i + 1];
-      const int nr = min(kTileRows, gend - r0);
-      const int last_valid = min(r0 + nr, cu_rows[i + 1]) - 1;
-      if (last_valid >= r0) {
-        const int len = start_pos[i] + (last_valid - first) + 1;
-        pages = (len + kPage - 1) / kPage;
-      }
-      reinterpret_cast<int4 *>(tiles)[t] = make_int4(r0, nr, i, pages);
+      nr = min(TR, gend - r0);
+      nv = max(0, min(r0 + nr, cu_rows[i + 1]) - r0);
+      pos0 = start_pos[i] + (r0 - first);
+      if (nv > 0) pages = (pos0 + nv + kPage - 1) / kPage;  // the tile's longest row sees pos0 + nv keys
     }
     int total;
     const int incl = block_inclusive_scan(pages, lds, &total);
-    if (t < n_tiles) cum[t + 1] = carry + incl;
+    if (t < n_tiles) {
+      int32_t *T = tiles + (int64_t)kTileRecWords * t;
+      T[0] = r0;
+      T[1] = nr;
+      T[2] = nv;
+      T[3] = pos0;
+      T[4] = i;
+      T[5] = pages;
+      T[6] = carry + incl - pages;
+      T[7] = 0;
+      cum[t + 1] = carry + incl;
+    }
     carry += total;
   }
   const int items = carry;
-  if (threadIdx.x == 0) {
-    cum[0] = 0;
-    sched[0] = kPrefillMagic;
-    sched[1] = 0;
-    sched[2] = n_req;
-    sched[3] = n_rows_padded;
-    sched[4] = n_units;
-    sched[5] = n_tiles;
-    sched[6] = items;
-    sched[7] = kTileRows;
-  }
+  if (threadIdx.x == 0) cum[0] = 0;
   // rows: causal length = position + 1; padding rows see nothing
   const int n_valid = cu_rows[n_req];
   for (int r = threadIdx.x; r < n_rows_padded; r += kSchedThreads) {
@@ -206,10 +217,46 @@ __global__ __launch_bounds__(kSchedThreads) void prefill_schedule_kernel(
     row_len[r] = len;
   }
   __syncthreads();
+  // every item's physical page: one wave per tile, lanes over its pages; a page the table
+  // cannot give is -1 and flagged (every item of a tile is needed by the tile's longest row)
+  {
+    int flags = 0;
+    const int lane = threadIdx.x & 63;
+    for (int t = threadIdx.x >> 6; t < n_tiles; t += kSchedThreads / 64) {
+      const int32_t *T = tiles + (int64_t)kTileRecWords * t;
+      const int req = T[4], pages = T[5], i0 = T[6];
+      for (int p = lane; p < pages; p += 64) {
+        int phys = -1;
+        if (p < bt_ld) {
+          const int e = bt[(int64_t)req * bt_ld + p];
+          if (e >= 0 && e < n_pages) phys = e;
+          else flags |= INDEXER_FP4_DEV_BAD_PAGE;
+        } else {
+          flags |= INDEXER_FP4_DEV_TABLE_SHORT;
+        }
+        item_phys[i0 + p] = phys;
+      }
+    }
+    if (flags) atomicOr(&s_flags, flags);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) header(s_flags, n_tiles, items);
+  // unit ranges and start records
   for (int u = threadIdx.x; u <= n_units; u += kSchedThreads) {
     const int64_t ib = (int64_t)u * items / n_units;
     sched[L.unit_begin + u] = (int32_t)ib;
-    if (u < n_units) sched[L.unit_tile + u] = count_le(cum + 1, n_tiles, ib);
+    if (u < n_units) {
+      const int ie = (int)(((int64_t)u + 1) * items / n_units);
+      const int t = count_le(cum + 1, n_tiles, ib);
+      sched[L.unit_tile + u] = t;
+      int32_t *R = sched + L.urec + (int64_t)kUnitRecWords * u;
+      R[0] = (int32_t)ib;
+      R[1] = ie;
+      R[2] = t;
+      R[3] = 0;
+      for (int j = 0; j < kTileRecWords; j++) R[4 + j] = t < n_tiles ? tiles[(int64_t)kTileRecWords * t + j] : 0;
+      for (int j = 0; j < kUnitRecPhys; j++) R[12 + j] = (int)ib + j < ie ? item_phys[ib + j] : -1;
+    }
   }
 }
 
@@ -222,9 +269,10 @@ extern "C" int64_t indexer_fp4_decode_sched_bytes(int32_t batch, int32_t next_n,
   return 4 * DecodeSchedLayout(batch, n_units).words;
 }
 
-extern "C" int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, int32_t n_units) {
-  if (n_req <= 0 || n_rows_padded <= 0 || n_units <= 0) return -1;
-  return 4 * PrefillSchedLayout(n_req, n_rows_padded, n_units).words;
+extern "C" int64_t indexer_fp4_prefill_sched_bytes(int32_t n_req, int32_t n_rows_padded, int32_t n_units,
+                                                   int64_t bt_ld) {
+  if (n_req <= 0 || n_rows_padded <= 0 || n_units <= 0 || bt_ld <= 0 || bt_ld > INT32_MAX) return -1;
+  return 4 * PrefillSchedLayout(n_req, n_rows_padded, n_units, bt_ld).words;
 }
 
 extern "C" int indexer_fp4_decode_schedule(const int32_t *context_lens, int32_t batch, int32_t next_n,
@@ -251,23 +299,27 @@ extern "C" int indexer_fp4_decode_schedule(const int32_t *context_lens, int32_t 
 }
 
 extern "C" int indexer_fp4_prefill_schedule(const int32_t *cu_rows, const int32_t *start_pos, int32_t n_req,
-                                            int32_t n_rows_padded, int32_t n_units, void *sched,
-                                            int64_t sched_bytes, int32_t *row_len, void *stream) {
+                                            int32_t n_rows_padded, int32_t n_units, const int32_t *block_table,
+                                            int64_t bt_ld, int64_t n_pages, void *sched, int64_t sched_bytes,
+                                            int32_t *row_len, void *stream) {
   clear_error();
-  if (n_req <= 0 || n_units <= 0 || n_rows_padded <= 0 || n_rows_padded % kTileRows != 0)
+  if (n_req <= 0 || n_units <= 0 || n_rows_padded <= 0 || n_rows_padded % kRowMultiple != 0)
     return fail(INDEXER_FP4_EINVAL,
                 "prefill schedule: n_req=%d must be > 0, n_units=%d > 0, n_rows_padded=%d a positive multiple of %d",
-                n_req, n_units, n_rows_padded, kTileRows);
-  const int64_t need = indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units);
+                n_req, n_units, n_rows_padded, kRowMultiple);
+  if (bt_ld <= 0 || bt_ld > INT32_MAX || n_pages < 0)
+    return fail(INDEXER_FP4_EINVAL, "prefill schedule: bt_ld=%lld in 1..2^31-1, n_pages=%lld >= 0", (long long)bt_ld,
+                (long long)n_pages);
+  const int64_t need = indexer_fp4_prefill_sched_bytes(n_req, n_rows_padded, n_units, bt_ld);
   if (!sched || sched_bytes < need)
     return fail(INDEXER_FP4_ENOSPC, "prefill schedule needs %lld bytes, buffer has %lld", (long long)need,
                 (long long)sched_bytes);
   if ((uintptr_t)sched % 16 != 0) return fail(INDEXER_FP4_EINVAL, "schedule buffer must be 16-byte aligned");
-  if (!cu_rows || !start_pos || !row_len)
-    return fail(INDEXER_FP4_EINVAL, "prefill schedule needs cu_rows, start_pos and row_len");
+  if (!cu_rows || !start_pos || !row_len || !block_table)
+    return fail(INDEXER_FP4_EINVAL, "prefill schedule needs cu_rows, start_pos, block_table and row_len");
   int rc = check_device();
   if (rc) return rc;
   hipLaunchKernelGGL(prefill_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, (hipStream_t)stream, cu_rows,
-                     start_pos, n_req, n_rows_padded, n_units, (int32_t *)sched, row_len);
+                     start_pos, n_req, n_rows_padded, n_units, block_table, bt_ld, n_pages, (int32_t *)sched, row_len);
   return launch_status("prefill_schedule");
 }

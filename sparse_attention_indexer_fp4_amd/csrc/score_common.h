@@ -70,18 +70,20 @@ __device__ __forceinline__ void load_page(PageRegs &P, const uint8_t *__restrict
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Logit of key `lane` of the page for row n: sum over heads of w * ReLU(q . k).
-// The MFMAs of key tile t+1 are issued into a second set of accumulators before the
-// ReLU/weight epilogue of tile t, so the matrix unit works while the VALU reduces.
-template <int NH16, int NN, int N>
+// With DB the MFMAs of key tile t+1 are issued into a second set of accumulators before the
+// ReLU/weight epilogue of tile t, so the matrix unit works while the VALU reduces; without
+// it one set is reused (16 NH16 fewer registers).
+template <int NH16, int NN, int N, bool DB = true>
 __device__ __forceinline__ float page_logit(const PageRegs &P, const RowRegs<NH16, NN> &R, int lane) {
   float acc[4];
-  floatx4 c[2][NH16];
+  constexpr int NB = DB ? 2 : 1;
+  floatx4 c[NB][NH16];
   auto mfmas = [&](auto tt) {
     constexpr int T = decltype(tt)::value;
     static_for<NH16>([&](auto mm) {
       constexpr int M = decltype(mm)::value;
       const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
-      c[T & 1][M] = mfma_fp4<M % 4, T>(R.qa[N][M], P.k[T], zero, R.qs[N][M / 4], P.s);
+      c[T % NB][M] = mfma_fp4<M % 4, T>(R.qa[N][M], P.k[T], zero, R.qs[N][M / 4], P.s);
     });
   };
   auto epilogue = [&](auto tt) {
@@ -89,19 +91,26 @@ __device__ __forceinline__ float page_logit(const PageRegs &P, const RowRegs<NH1
     float a = 0.f;
     static_for<NH16>([&](auto mm) {
       constexpr int M = decltype(mm)::value;
-      a += R.w[N][M].x * relu(c[T & 1][M][0]);
-      a += R.w[N][M].y * relu(c[T & 1][M][1]);
-      a += R.w[N][M].z * relu(c[T & 1][M][2]);
-      a += R.w[N][M].w * relu(c[T & 1][M][3]);
+      a += R.w[N][M].x * relu(c[T % NB][M][0]);
+      a += R.w[N][M].y * relu(c[T % NB][M][1]);
+      a += R.w[N][M].z * relu(c[T % NB][M][2]);
+      a += R.w[N][M].w * relu(c[T % NB][M][3]);
     });
     acc[T] = a;
   };
-  mfmas(std::integral_constant<int, 0>{});
-  static_for<4>([&](auto tt) {
-    constexpr int T = decltype(tt)::value;
-    if constexpr (T + 1 < 4) mfmas(std::integral_constant<int, T + 1>{});
-    epilogue(tt);
-  });
+  if constexpr (DB) {
+    mfmas(std::integral_constant<int, 0>{});
+    static_for<4>([&](auto tt) {
+      constexpr int T = decltype(tt)::value;
+      if constexpr (T + 1 < 4) mfmas(std::integral_constant<int, T + 1>{});
+      epilogue(tt);
+    });
+  } else {
+    static_for<4>([&](auto tt) {
+      mfmas(tt);
+      epilogue(tt);
+    });
+  }
   // lanes 16G..16G+15 hold, for every tile, partial sums over their heads; reduce across
   // the four lane groups so that lane 16G+j ends with tile G's full sum for key j
   const int G = lane >> 4;

@@ -6,27 +6,29 @@
 // and padding rows, folded into the last request's group, read no key. Each valid row r
 // at position p sees keys [0, p] (causal, inclusive).
 //
-// Design for gfx950. Work items are (tile, page) pairs where a tile is up to 8 rows of one
-// request's group (schedule.hip). A unit (workgroup of 8 waves) takes a contiguous range of
-// items; all its waves walk the same items and wave w scores row w of the tile, so one key
-// page feeds 8 rows x n_heads query heads of MFMA work. Pages go through a ring of P slots
-// in LDS filled by direct global-to-LDS loads (no registers held while in flight, so the
-// ring can be deep): four waves each copy one 1 KiB key tile, a fifth the 256-byte scale
-// block, with lane i fetching exactly the 16 bytes that lane i of every wave later reads as
-// its MFMA operand (same layout as the decode scorer's direct loads), so the LDS reads are
-// linear. Items go in groups of B: per group the loader waves wait until their copies have
-// landed (vmcnt counting in issue order), the unit meets at one barrier, the slots of the
-// previous group are refilled P-B items ahead, and every wave scores its row for the whole
-// group from LDS without further synchronisation. Each wave keeps a table of 64 items at a
-// time (tile, page, physical page, whether its row reaches the page), built with one round
-// of per-lane loads. Logits past a row's length fall outside the store's range.
-//
-// Each wave keeps its row's query operands in LDS, in operand order, and refills its
-// registers from there at every group (per item in the rare group that crosses into a new
-// tile, which first stages the new row from global memory). Holding them in registers
-// across groups would put a join after every conditional reload, and the compiler resolves
-// such joins with dozens of register copies per item, a third of the VALU work. The first
-// tile's row is fetched at entry, while the item table is being built.
+// Design for gfx950. Work items are (tile, page) pairs where a tile is up to 16 rows of one
+// request's group; the step's schedule (schedule.hip) has already turned every item into its
+// physical page and gives each unit a start record. A unit is one workgroup of 16 waves, one
+// per row of the tile, and one unit runs per CU (four waves per SIMD, all of one unit, so no
+// unit's waves are starved by another's). The unit takes a contiguous range of items; all its
+// waves walk the same items, so one key page feeds 16 rows x n_heads query heads of MFMA work.
+//   - Pages go through a ring of P slots in LDS filled by direct global-to-LDS loads: four
+//     waves copy one 1 KiB key tile each and a fifth the 256-byte scale block, lane i fetching
+//     exactly the 16 bytes that lane i of every wave later reads as its MFMA operand (the
+//     decode scorer's operand layout), so the LDS reads are linear.
+//   - Items go in groups of B: per group the loader waves wait until their copies have
+//     landed (vmcnt counting in issue order), the unit meets at one barrier, the slots of the
+//     previous group are refilled P-B items ahead, and every wave scores its row for the whole
+//     group from LDS without further synchronisation.
+//   - Each wave holds its row's query operands, scales and weights in registers; they are
+//     reloaded only when the items cross into the next tile (at most a few times per unit).
+//   - The unit's first items come from its start record (one scalar load), so the first page
+//     copies are in flight after a single round trip; the pages of its later items come from
+//     the schedule's item table by scalar loads issued one group ahead.
+// Logits past a row's length fall outside the range-checked store. A unit handles at most 64
+// heads (4 MFMA M-tiles); more heads are scored in further passes over the same schedule that
+// add their partial sums with range-checked atomic adds (one add per logit, so the result does
+// not depend on timing).
 #include "score_common.h"
 
 // pages in the LDS ring of a unit, and items between the unit's barriers (divides the ring)
@@ -40,10 +42,12 @@
 namespace ifp4 {
 
 constexpr int kPrefillMaxRing = 8;
+constexpr int kPrefillWaves = kPrefillTileRows;  // one wave per tile row
+constexpr int kPrefillPassHeads16 = 4;           // M-tiles of 16 heads per pass
 
 // One LDS array per ring slot: with every slot access indexed by a constant the compiler
 // can tell the slots apart and adds no waits of its own between a slot's reads and the
-// loads in flight into other slots.
+// direct loads in flight into other slots.
 #define IFP4_SLOT(I)                                                   \
   __shared__ __attribute__((aligned(16))) uint4 pf_keys##I[kPage * 4]; \
   __shared__ uint32_t pf_scales##I[kPage];
@@ -76,162 +80,117 @@ __device__ __forceinline__ uint32_t *slot_scales() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int NH16, int NW, int P, int B>
-__global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
+// A tile as the scorer tracks it (wave-uniform): its record from the schedule.
+struct TileState {
+  int t, row0, nvalid, pos0, pages, item0;
+};
+
+template <int NH16, bool ADD, int P, int B>
+__global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
-    const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
-    const int32_t *__restrict__ bt_g, int64_t bt_ld, int n_req, int n_rows_padded, int n_units,
-    const int32_t *__restrict__ sched_g, int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g,
+    int head0, const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages, int64_t bt_ld,
+    int n_req, int n_rows_padded, int n_units, const int32_t *__restrict__ sched_g, int32_t *__restrict__ err,
     float *__restrict__ logits, int64_t ld) {
-  static_assert(P <= kPrefillMaxRing && B >= 1 && P % B == 0 && P / B >= 2 && NW >= 5, "ring, groups, loaders");
-  const PrefillSchedLayout L(n_req, n_rows_padded, n_units);
-  const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
+  static_assert(P <= kPrefillMaxRing && B >= 1 && P % B == 0 && P / B >= 2, "ring and groups");
+  const PrefillSchedLayout L(n_req, n_rows_padded, n_units, bt_ld);
+  const const_ptr<int32_t> sched = as_const(sched_g);
   const int u = blockIdx.x;
-  // The unit table is in bounds (the host checked the buffer's size for these sizes); its
-  // words are used only once the header shows a schedule built for this step's sizes (a
-  // stale or zeroed buffer is flagged once, by unit 0, and nothing is scored).
-  const int it0r = sched[L.unit_begin + u];
-  const int it1r = sched[L.unit_begin + u + 1];
-  if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units) {
+  // One scalar round: the header and this unit's start record (in bounds whatever they hold:
+  // the host checked the buffer's size for these sizes). Nothing is used before the header
+  // shows a schedule built for this step's sizes and this pool; a stale or zeroed buffer is
+  // flagged once, by unit 0, and nothing is scored.
+  const const_ptr<int32_t> rec = sched + L.urec + (int64_t)kUnitRecWords * u;
+  int rv[kUnitRecWords];
+#pragma unroll
+  for (int j = 0; j < kUnitRecWords; j++) rv[j] = rec[j];
+  if (sched[0] != kPrefillMagic || sched[2] != n_req || sched[3] != n_rows_padded || sched[4] != n_units ||
+      sched[7] != kPrefillTileRows || sched[8] != (int32_t)bt_ld ||
+      sched[9] != (int32_t)min(n_pages, (int64_t)INT32_MAX)) {
     if (u == 0 && threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
     return;
   }
-  const int it0 = max(it0r, 0), it1 = min(it1r, sched[6]);
-  if (it0 >= it1) return;  // empty unit (uniform over the workgroup): nothing else is touched
+  const int n_tiles = min(sched[5], (int)L.max_tiles);
+  const int items = min(sched[6], (int)(L.max_tiles * bt_ld));
+  const int it0 = max(rv[0], 0), it1 = min(rv[1], items);
+  if (it0 >= it1 || n_tiles <= 0) return;  // empty unit (uniform over the workgroup): nothing else is touched
   const int lane = threadIdx.x & 63;
   const int wv = uniform(threadIdx.x >> 6);  // this wave's row inside a tile
-  if (n_pages <= 0) {  // the ring always copies some page: there must be one
-    if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
-    return;
-  }
-  const int n_tiles = min(sched[5], (int)L.max_tiles);
-  const int32_t *tiles = sched_g + L.tiles;  // {first row, rows, request, pages} per tile
-  const int32_t *cum = sched_g + L.cum;
   const int n_my = it1 - it0;
   const bool loader = wv < 5;  // waves 0-3 copy key tiles, wave 4 the scale block
 
-  // Item table, one lane per item, for 64 items at a time.
-  int tcur = min(max(sched[L.unit_tile + u], 0), max(n_tiles - 1, 0));  // tile of the next item to look up
-  int tab_base = -64;
-  int v_tile = 0, v_page = 0, v_phys = 0, v_need = 0;
-  auto fill = [&](int base) {
-    tab_base = base;
-    const int it = it0 + base + lane;
-    int t = tcur, p = 0, phys = 0, need = 0;
-    if (it < it1) {
-      while (t < n_tiles - 1 && it >= cum[t + 1]) t++;
-      p = it - cum[t];
-      const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * t);
-      need = wv < T.y && row_len[T.x + wv] > p * kPage;
-      if (p < 0) {
-        atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
-        need = 0;
-      } else if (p >= bt_ld) {
-        if (need) atomicOr(err, INDEXER_FP4_DEV_TABLE_SHORT);
-        need = 0;
-      } else {
-        phys = bt_g[(int64_t)T.z * bt_ld + p];
-        if (phys < 0 || phys >= n_pages) {
-          if (need) atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
-          phys = 0;  // a page that exists; nobody scores it
-          need = 0;
-        }
-      }
-    }
-    v_tile = t;
-    v_page = p;
-    v_phys = phys;
-    v_need = need;
-    tcur = __builtin_amdgcn_readlane(t, 63);  // tiles only advance with the items
+  // the current tile (from the start record), and this wave's row in it
+  TileState T;
+  T.t = min(max(rv[2], 0), n_tiles - 1);
+  T.row0 = rv[4];
+  T.nvalid = rv[6];
+  T.pos0 = rv[7];
+  T.pages = rv[9];
+  T.item0 = rv[10];
+  // Physical pages of the unit's items: the first (G-1)B from the start record, the others by
+  // scalar loads from the schedule's item table one group before their copies are issued
+  // (scalar loads wait on their own counter, not behind the copies in flight).
+  constexpr int G = P / B;
+  static_assert((G - 1) * B <= kUnitRecPhys, "the start record holds the prologue's pages");
+  const const_ptr<int32_t> item_phys = sched + L.item_phys + it0;
+  int nphys[B];
+  auto prefetch = [&](int i) {  // pages of items i .. i+B-1 (clamped to the unit's last item)
+    static_for<B>([&](auto bb) { nphys[decltype(bb)::value] = item_phys[min(i + (int)decltype(bb)::value, n_my - 1)]; });
   };
 
-  int st[P], sp[P];
-  bool sok[P];
-  // copy item i (clamped to the unit's last item) into ring slot S, and note what scoring it
-  // needs; every wave records the item, the loader waves issue one direct load each
-  auto issue = [&](auto ss, int i) {
+  // the first item of each ring group's slots, and one bit per slot: its item is scored
+  int gbase[G];
+  uint32_t live_bits = 0;
+  // copy item i (past the unit's last item: that one again) with physical page `phys` into
+  // ring slot S; the loader waves issue one direct load each (a page that cannot be read is
+  // replaced by page 0, which exists, and is not scored)
+  auto issue = [&](auto ss, int i, int phys) {
     constexpr int S = decltype(ss)::value;
-    const bool live = i < n_my;
-    const int ii = live ? i : n_my - 1;
-    if (ii - tab_base >= 64) fill(ii & ~63);
-    const int l = ii - tab_base;
-    const int phys = __builtin_amdgcn_readlane(v_phys, l);
-    st[S] = __builtin_amdgcn_readlane(v_tile, l);
-    sp[S] = __builtin_amdgcn_readlane(v_page, l);
-    sok[S] = live && __builtin_amdgcn_readlane(v_need, l) != 0;
+    if constexpr (S % B == 0) gbase[S / B] = i;
+    const bool live = i < n_my && phys >= 0;
+    live_bits = live ? (live_bits | (1u << S)) : (live_bits & ~(1u << S));
+    const int64_t pg = phys >= 0 ? phys : 0;
     if (wv < 4) {
-      const uint8_t *src = kvp + (int64_t)phys * kPageBytes + 1024 * wv + 64 * (lane & 15) + 16 * (lane >> 4);
+      const uint8_t *src = kvp + pg * kPageBytes + 1024 * wv + 64 * (lane & 15) + 16 * (lane >> 4);
       __builtin_amdgcn_global_load_lds(src, (lds_void *)(slot_keys<S>() + 64 * wv), 16, 0, 0);
     } else if (wv == 4) {
-      const uint8_t *src = kvs + (int64_t)phys * kPageScaleBytes + 4 * lane;
+      const uint8_t *src = kvs + pg * kPageScaleBytes + 4 * lane;
       __builtin_amdgcn_global_load_lds(src, (lds_void *)slot_scales<S>(), 4, 0, 0);
     }
   };
   // a store that writes nothing (empty range): keeps every wave at one store per item
   auto idle_store = [&]() { buffer_store_f32(0.f, buffer_view(logits, 0u), 0u); };
 
-  // This wave's query row in LDS: operands per M-tile and lane, weights per M-tile and lane
-  // group (16 lanes read one address), scale words per lane. The helpers below are called
-  // from every unrolled item and are forced inline: out of line, the row would be passed
-  // through private (scratch) memory.
-  constexpr int NQS = (NH16 + 3) / 4;
-  // (native vector element types: copies of the HIP vector structs become memcpys that keep
-  // the row in private memory; and every access indexes the arrays themselves, so the
-  // compiler can tell them apart from the ring slots the direct loads write and adds no
-  // wait for those loads before reading the row)
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ u32x4 q_lds[NW * NH16 * 64];
-  __shared__ f32x4 w_lds[NW * NH16 * 4];
-  __shared__ uint32_t qs_lds[NW * NQS * 64];
-  const int qa0 = wv * NH16 * 64, w0i = wv * NH16 * 4, qs0i = wv * NQS * 64;
-  auto stage_row = [&](const RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < NH16; m++) {
-      const uint4 a = Q.qa[0][m];
-      q_lds[qa0 + m * 64 + lane] = u32x4{a.x, a.y, a.z, a.w};
-      // all 16 lanes of a group store the same four weights to the same address (a
-      // conditional store here would also keep the row in private memory)
-      const float4 x = Q.w[0][m];
-      w_lds[w0i + m * 4 + (lane >> 4)] = f32x4{x.x, x.y, x.z, x.w};
+  // This wave's query row (operands, scales, weights of this pass's heads) in registers.
+  RowRegs<NH16, 1> R;
+  int row = 0, len = 0;
+  auto load_row = [&](bool wait) __attribute__((always_inline)) {
+    row = T.row0 + wv;
+    len = wv < T.nvalid ? T.pos0 + wv + 1 : 0;
+    if (len > 0) {
+      // the pass's heads [head0, head0 + 16 NH16) of row `row`
+      const uint8_t *q = qp + (int64_t)head0 * kKeyBytes;
+      const uint8_t *s = qs + (int64_t)head0 * kGroups;
+      const float *ww = w + head0;
+      if (wait) load_rows<NH16, 1, true>(R, q, s, ww, row, 1, n_heads, lane);
+      else load_rows<NH16, 1, false>(R, q, s, ww, row, 1, n_heads, lane);
     }
-#pragma unroll
-    for (int j = 0; j < NQS; j++) qs_lds[qs0i + j * 64 + lane] = Q.qs[0][j];
   };
-  auto read_row = [&](RowRegs<NH16, 1> &Q) __attribute__((always_inline)) {
-#pragma unroll
-    for (int m = 0; m < NH16; m++) {
-      const u32x4 a = q_lds[qa0 + m * 64 + lane];
-      Q.qa[0][m] = make_uint4(a.x, a.y, a.z, a.w);
-      const f32x4 x = w_lds[w0i + m * 4 + (lane >> 4)];
-      Q.w[0][m] = make_float4(x.x, x.y, x.z, x.w);
-    }
-#pragma unroll
-    for (int j = 0; j < NQS; j++) Q.qs[0][j] = qs_lds[qs0i + j * 64 + lane];
+  auto next_tile = [&]() __attribute__((always_inline)) {
+    // tiles of no page hold no item, so the next item's tile is found by walking forward
+    T.t = min(T.t + 1, n_tiles - 1);
+    const const_ptr<int32_t> rt = sched + L.tiles + (int64_t)kTileRecWords * T.t;
+    T.row0 = rt[0];
+    T.nvalid = rt[2];
+    T.pos0 = rt[3];
+    T.pages = rt[5];
+    T.item0 = rt[6];
   };
-  // The first tile's row is requested before the item table is built and staged after the
-  // prologue's copies are issued, so its loads overlap the table's and the first pages'.
-  int qt = tcur, row = 0, row_bytes = 0;
-  RowRegs<NH16, 1> Q0;
-  const bool first_row = wv < tiles[4 * qt + 1];
-  if (first_row) {
-    row = tiles[4 * qt] + wv;
-    row_bytes = 4 * max(row_len[row], 0);
-    load_rows<NH16, 1, false>(Q0, qp, qs, w, row, 1, n_heads, lane);
-  }
-  // a new tile for this wave: stage its row (waits for everything in flight; once per tile)
-  auto enter_tile = [&](int t) __attribute__((always_inline)) {
-    qt = t;
-    const int4 T = *reinterpret_cast<const int4 *>(tiles + 4 * qt);
-    row = T.x + wv;  // only called for items this wave scores, so wv < T.y
-    row_bytes = 4 * max(row_len[row], 0);
-    RowRegs<NH16, 1> Q;
-    load_rows<NH16, 1>(Q, qp, qs, w, row, 1, n_heads, lane);
-    stage_row(Q);
-  };
-  auto score = [&](auto ss, const RowRegs<NH16, 1> &R) __attribute__((always_inline)) {
+
+  auto item_of = [&](auto ss) { return min(gbase[decltype(ss)::value / B] + decltype(ss)::value % B, n_my - 1); };
+  auto score = [&](auto ss) __attribute__((always_inline)) {
     constexpr int S = decltype(ss)::value;
-    if (!sok[S]) {
+    const int p = it0 + item_of(ss) - T.item0;  // the item's page within its tile
+    if (!((live_bits >> S) & 1u) || len <= p * kPage) {
       idle_store();
       return;
     }
@@ -239,30 +198,30 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
 #pragma unroll
     for (int t = 0; t < 4; t++) pg.k[t] = slot_keys<S>()[64 * t + lane];
     pg.s = slot_scales<S>()[lane];
-    const uint32_t col = (uint32_t)(sp[S] * kPage + lane);
-    const float v = page_logit<NH16, 1, 0>(pg, R, lane);
-    buffer_store_f32(v, buffer_view(logits + (int64_t)row * ld, (uint32_t)row_bytes), 4u * col);
+    const float v = page_logit<NH16, 1, 0, (NH16 <= 3)>(pg, R, lane);  // one accumulator set at 64 heads (registers)
+    const __amdgpu_buffer_rsrc_t dst = buffer_view(logits + (int64_t)row * ld, 4u * (uint32_t)len);
+    const uint32_t off = 4u * (uint32_t)(p * kPage + lane);
+    if constexpr (ADD) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, dst, (int)off, 0, 0);
+    else buffer_store_f32(v, dst, off);
   };
-  // score the B items of group GG with the current tile's row R (read from LDS before the
-  // group's refills are issued: the compiler cannot tell the row from the ring slots being
-  // filled and waits for every load in flight before reading it), or, in a group that enters
-  // a new tile, per item after staging each new tile
-  auto score_group = [&](auto gg, const RowRegs<NH16, 1> &R) __attribute__((always_inline)) {
+  // score the B items of group GG; a group that reaches into the next tile(s) moves there
+  // item by item (loading the new row waits for every copy in flight: rare, a few times per
+  // unit at most)
+  auto score_group = [&](auto gg) __attribute__((always_inline)) {
     constexpr int GG = decltype(gg)::value;
-    bool same = true;
-    static_for<B>([&](auto bb) {
-      constexpr int S = GG * B + decltype(bb)::value;
-      same = same && (!sok[S] || st[S] == qt);
-    });
-    if (same) {
-      static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}, R); });
+    const int last = it0 + item_of(std::integral_constant<int, GG * B + B - 1>{});  // the group's items ascend
+    if (last < T.item0 + T.pages) {
+      static_for<B>([&](auto bb) { score(std::integral_constant<int, GG * B + decltype(bb)::value>{}); });
     } else {
       static_for<B>([&](auto bb) {
         constexpr int S = GG * B + decltype(bb)::value;
-        if (sok[S] && st[S] != qt) enter_tile(st[S]);
-        RowRegs<NH16, 1> R;
-        read_row(R);
-        score(std::integral_constant<int, S>{}, R);
+        bool moved = false;
+        while (it0 + item_of(std::integral_constant<int, S>{}) >= T.item0 + T.pages && T.t < n_tiles - 1) {
+          next_tile();
+          moved = true;
+        }
+        if (moved) load_row(true);
+        score(std::integral_constant<int, S>{});
       });
     }
   };
@@ -271,15 +230,20 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
   // loader waves wait until the group's copies have landed, the unit meets once, the slots
   // of group k-1 are refilled with group k+G-1, and every wave scores its row for the B
   // items of group k without further synchronisation.
-  constexpr int G = P / B;
-  // Prologue: groups 0 .. G-2, each followed by B idle stores so that a loader wave issues
-  // the same sequence (B loads, then B stores) before every group.
+  // Prologue: groups 0 .. G-2 (pages from the start record), each followed by B idle stores
+  // so that a loader wave issues the same sequence (B loads, then B stores) before every group.
   static_for<G - 1>([&](auto gg) {
     constexpr int GG = decltype(gg)::value;
-    static_for<B>([&](auto bb) { issue(std::integral_constant<int, GG * B + decltype(bb)::value>{}, GG * B + decltype(bb)::value); });
+    static_for<B>([&](auto bb) {
+      constexpr int I = GG * B + decltype(bb)::value;
+      issue(std::integral_constant<int, I>{}, I, I < n_my ? rv[12 + I] : -1);
+    });
     if (loader) static_for<B>([&](auto) { idle_store(); });
   });
-  if (first_row) stage_row(Q0);
+  prefetch((G - 1) * B);
+  // the row's query, in flight with the first copies; its wait (vmcnt 0) also covers them,
+  // and leaves no load the compiler would still have to wait for later
+  load_row(true);
   for (int i0 = 0; i0 < n_my; i0 += P) {
     static_for<G>([&](auto gg) {
       constexpr int GG = decltype(gg)::value;
@@ -289,27 +253,40 @@ __global__ __launch_bounds__(NW * 64) void score_prefill_kernel(
       if (loader) __builtin_amdgcn_s_waitcnt(0x0F70 | (B * (2 * G - 3)));
       __builtin_amdgcn_s_barrier();  // the group landed; the previous group's slots are free
       asm volatile("" ::: "memory");
-      RowRegs<NH16, 1> R;
-      read_row(R);
       constexpr int GR = (GG + G - 1) % G;  // slots of the previous group
+      const int ir = i0 + (GG + G - 1) * B;  // the refill's first item
       static_for<B>([&](auto bb) {
         constexpr int BB = decltype(bb)::value;
-        issue(std::integral_constant<int, GR * B + BB>{}, i0 + (GG + G - 1) * B + BB);
+        issue(std::integral_constant<int, GR * B + BB>{}, ir + BB, nphys[BB]);
       });
-      score_group(gg, R);
+      prefetch(ir + B);
+      score_group(gg);
     });
   }
 }
 
-template <int NH16>
-static void launch_prefill(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
-                           int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
-                           int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched, const int32_t *row_len,
-                           float *logits, int64_t ld) {
-  constexpr int NW = kTileRows, P = IFP4_PREFILL_RING, B = IFP4_PREFILL_GROUP;
-  hipLaunchKernelGGL((score_prefill_kernel<NH16, NW, P, B>), dim3(n_units), dim3(NW * 64), 0, st, qp, qs, w,
-                     n_heads, kvp, kvs, n_pages, bt, bt_ld, n_req, n_rows_padded, n_units, sched, sched + 1, row_len,
+template <int NH16, bool ADD>
+static void launch_prefill_pass(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
+                                int n_heads, int head0, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages,
+                                int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched, float *logits,
+                                int64_t ld) {
+  constexpr int P = IFP4_PREFILL_RING, B = IFP4_PREFILL_GROUP;
+  hipLaunchKernelGGL((score_prefill_kernel<NH16, ADD, P, B>), dim3(n_units), dim3(kPrefillWaves * 64), 0, st, qp, qs,
+                     w, n_heads, head0, kvp, kvs, n_pages, bt_ld, n_req, n_rows_padded, n_units, sched, sched + 1,
                      logits, ld);
+}
+
+template <bool ADD>
+static void launch_prefill(int nh16, hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs,
+                           const float *w, int n_heads, int head0, const uint8_t *kvp, const uint8_t *kvs,
+                           int64_t n_pages, int64_t bt_ld, int n_req, int n_rows_padded, int32_t *sched,
+                           float *logits, int64_t ld) {
+  switch (nh16) {
+#define IFP4_CASE(X) \
+  case X: launch_prefill_pass<X, ADD>(st, n_units, qp, qs, w, n_heads, head0, kvp, kvs, n_pages, bt_ld, n_req, n_rows_padded, sched, logits, ld); break;
+    IFP4_CASE(1) IFP4_CASE(2) IFP4_CASE(3) IFP4_CASE(4)
+#undef IFP4_CASE
+  }
 }
 
 }  // namespace ifp4
@@ -318,40 +295,49 @@ using namespace ifp4;
 
 extern "C" int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale, const float *weights,
                                          int32_t n_heads, const uint8_t *kv_packed, const uint8_t *kv_scale,
-                                         int64_t n_pages, const int32_t *block_table, int64_t bt_ld, int32_t n_req,
-                                         void *sched, int64_t sched_bytes, int32_t n_units, int32_t n_rows_padded,
-                                         const int32_t *row_len, float *logits, int64_t logits_ld, void *stream) {
+                                         int64_t n_pages, int64_t bt_ld, int32_t n_req, void *sched,
+                                         int64_t sched_bytes, int32_t n_units, int32_t n_rows_padded, float *logits,
+                                         int64_t logits_ld, void *stream) {
   clear_error();
   if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > INDEXER_FP4_MAX_HEADS)
     return fail(INDEXER_FP4_EINVAL, "n_heads=%d must be a positive multiple of %d and at most %d", n_heads,
                 INDEXER_FP4_HEAD_MULT, INDEXER_FP4_MAX_HEADS);
-  if (n_req <= 0 || n_units <= 0 || n_pages < 0 || n_rows_padded <= 0 || n_rows_padded % kTileRows != 0)
+  if (n_req <= 0 || n_units <= 0 || n_pages < 0 || n_rows_padded <= 0 || n_rows_padded % kRowMultiple != 0)
     return fail(INDEXER_FP4_EINVAL,
                 "score_prefill: n_req=%d > 0, n_units=%d > 0, n_pages=%lld >= 0, n_rows_padded=%d a positive multiple of %d",
-                n_req, n_units, (long long)n_pages, n_rows_padded, kTileRows);
-  if (bt_ld <= 0) return fail(INDEXER_FP4_ENOSPC, "score_prefill: bt_ld=%lld must be positive", (long long)bt_ld);
+                n_req, n_units, (long long)n_pages, n_rows_padded, kRowMultiple);
+  if (bt_ld <= 0 || bt_ld > INT32_MAX)
+    return fail(INDEXER_FP4_ENOSPC, "score_prefill: bt_ld=%lld must be in 1..2^31-1", (long long)bt_ld);
   if (logits_ld < bt_ld * kPage)
     return fail(INDEXER_FP4_ENOSPC, "score_prefill: logits_ld=%lld < 64*bt_ld=%lld", (long long)logits_ld,
                 (long long)(bt_ld * kPage));
-  if (!sched || !row_len || !q_packed || !q_scale || !weights || !block_table || !logits)
+  if (!sched || !q_packed || !q_scale || !weights || !logits)
     return fail(INDEXER_FP4_EINVAL, "score_prefill: a required pointer is NULL");
-  const int64_t need = 4 * PrefillSchedLayout(n_req, n_rows_padded, n_units).words;
+  const int64_t need = 4 * PrefillSchedLayout(n_req, n_rows_padded, n_units, bt_ld).words;
   if (sched_bytes < need)
-    return fail(INDEXER_FP4_ENOSPC, "score_prefill: sched_bytes=%lld < %lld for n_req=%d, n_rows_padded=%d, n_units=%d",
-                (long long)sched_bytes, (long long)need, n_req, n_rows_padded, n_units);
+    return fail(INDEXER_FP4_ENOSPC, "score_prefill: sched_bytes=%lld < %lld for n_req=%d, n_rows_padded=%d, n_units=%d, "
+                "bt_ld=%lld", (long long)sched_bytes, (long long)need, n_req, n_rows_padded, n_units, (long long)bt_ld);
   if (n_pages > 0 && (!kv_packed || !kv_scale)) return fail(INDEXER_FP4_EINVAL, "score_prefill: NULL cache plane");
   if (((uintptr_t)q_packed | (uintptr_t)weights | (uintptr_t)kv_packed | (uintptr_t)kv_scale) % 16 != 0)
     return fail(INDEXER_FP4_EINVAL, "score_prefill: q_packed, weights and both planes must be 16-byte aligned");
+  if (((uintptr_t)sched | (uintptr_t)logits) % 4 != 0)
+    return fail(INDEXER_FP4_EINVAL, "score_prefill: sched and logits must be 4-byte aligned");
   int rc = check_device();
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   int32_t *sc = (int32_t *)sched;
-  switch (n_heads / 16) {
-#define IFP4_CASE(X) \
-  case X: launch_prefill<X>(st, n_units, q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, n_req, n_rows_padded, sc, row_len, logits, logits_ld); break;
-    IFP4_CASE(1) IFP4_CASE(2) IFP4_CASE(3) IFP4_CASE(4) IFP4_CASE(5) IFP4_CASE(6) IFP4_CASE(7) IFP4_CASE(8)
-#undef IFP4_CASE
+  // heads in passes of at most 64: the first stores, the others add
+  const int nh16 = n_heads / 16;
+  for (int m0 = 0; m0 < nh16; m0 += kPrefillPassHeads16) {
+    const int m = min(kPrefillPassHeads16, nh16 - m0);
+    if (m0 == 0)
+      launch_prefill<false>(m, st, n_units, q_packed, q_scale, weights, n_heads, 16 * m0, kv_packed, kv_scale,
+                            n_pages, bt_ld, n_req, n_rows_padded, sc, logits, logits_ld);
+    else
+      launch_prefill<true>(m, st, n_units, q_packed, q_scale, weights, n_heads, 16 * m0, kv_packed, kv_scale,
+                           n_pages, bt_ld, n_req, n_rows_padded, sc, logits, logits_ld);
+    rc = launch_status("score_prefill");
+    if (rc) return rc;
   }
-  return launch_status("score_prefill");
+  return INDEXER_FP4_OK;
 }
-

@@ -98,11 +98,13 @@ def gpu_prefill_step(case: W.PrefillCase, step: W.PrefillStep, kp, ks, units=Non
     qp = torch.empty((NP, H, 64), dtype=torch.uint8, device=dev())
     qs = torch.empty((NP, H, 4), dtype=torch.uint8, device=dev())
     ifp4.indexer_fp4_quant_and_cache(bf16_tensor(keys), to_dev(slots), kp, ks, bf16_tensor(step.q), qp, qs)
-    sched = torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8, device=dev())
+    sched = torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units, bt.shape[1]), dtype=torch.uint8,
+                        device=dev())
     row_len = torch.empty(NP, dtype=torch.int32, device=dev())
-    ifp4.indexer_fp4_prefill_schedule(to_dev(step.cu_rows), to_dev(step.start_pos), NP, units, sched, row_len)
+    ifp4.indexer_fp4_prefill_schedule(to_dev(step.cu_rows), to_dev(step.start_pos), NP, units, to_dev(bt),
+                                      kp.shape[0], sched, row_len)
     logits = torch.full((NP, ld), fill, dtype=torch.float32, device=dev())
-    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(step.w), kp, ks, to_dev(bt), sched, units, NP, row_len, logits)
+    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(step.w), kp, ks, R, bt.shape[1], sched, units, NP, logits)
     out = dict(qp=qp, qs=qs, sched=sched, row_len=row_len, logits=logits, units=units, ld=ld)
     if run_topk:
         top = torch.full((NP, case.topk), -7, dtype=torch.int32, device=dev())

@@ -59,10 +59,14 @@ def test_size_queries(L):
     for b, u in [(1, 512), (8, 512), (16, 37), (3, 4096)]:
         sizes = [L.indexer_fp4_decode_sched_bytes(b, n, u) for n in (1, 2, 3, 4)]
         assert min(sizes) == max(sizes) == sizes[0] > 0, (b, u, sizes)
-    # prefill: header + tiles[max] x4 + cum[max+1] + unit_begin[U+1] + unit_tile[U] + req_tile[R+1]
-    mt = 2048 // 8 + 4
-    assert L.indexer_fp4_prefill_sched_bytes(4, 2048, 4096) == 4 * (8 + 4 * mt + mt + 1 + 4097 + 4096 + 5)
-    assert L.indexer_fp4_prefill_sched_bytes(0, 2048, 4096) < 0
+    # prefill: 16-word header + unit records [U] x16 + tiles[max] x8 + cum[max+1] + unit_begin[U+1]
+    # + unit_tile[U] + req_tile[R+1] + item pages [max * bt_ld], with max = rows/16 + R tiles
+    L.indexer_fp4_prefill_sched_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    mt = 2048 // 16 + 4
+    assert L.indexer_fp4_prefill_sched_bytes(4, 2048, 256, 68) == \
+        4 * (16 + 16 * 256 + 8 * mt + mt + 1 + 257 + 256 + 5 + mt * 68)
+    assert L.indexer_fp4_prefill_sched_bytes(0, 2048, 256, 68) < 0
+    assert L.indexer_fp4_prefill_sched_bytes(4, 2048, 256, 0) < 0
     assert L.indexer_topk_workspace_bytes(8, 131072, 2048) >= 0
     assert L.indexer_topk_workspace_bytes(8, 131072, 0) < 0
 
@@ -83,9 +87,13 @@ def test_host_argument_errors(L):
     # schedule buffer too small: never silently truncated
     assert L.indexer_fp4_decode_schedule(None, 8, 1, 512, None, 100, None, None) == -2
     assert "needs" in _err(L) and "100" in _err(L)
-    L.indexer_fp4_prefill_schedule.argtypes = [P, P, I32, I32, I32, P, I64, P, P]
-    assert L.indexer_fp4_prefill_schedule(None, None, 4, 1001, 4096, None, 0, None, None) == -1
+    L.indexer_fp4_prefill_schedule.argtypes = [P, P, I32, I32, I32, P, I64, I64, P, I64, P, P]
+    assert L.indexer_fp4_prefill_schedule(None, None, 4, 1001, 4096, None, 68, 100, None, 0, None, None) == -1
     assert "multiple of 8" in _err(L)
+    assert L.indexer_fp4_prefill_schedule(None, None, 4, 1000, 256, None, 0, 100, None, 0, None, None) == -1
+    assert "bt_ld=0" in _err(L)
+    assert L.indexer_fp4_prefill_schedule(P(16), P(16), 4, 1000, 256, P(16), 68, 100, P(16), 64, P(16), None) == -2
+    assert "needs" in _err(L)
     L.indexer_fp4_score_decode.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P]
     # head count not a multiple of 16 (the MFMA tile height)
     assert L.indexer_fp4_score_decode(None, None, None, 24, None, None, 0, None, 8, 1, 1, None, 0, 512, None,
@@ -105,13 +113,16 @@ def test_host_argument_errors(L):
     assert L.indexer_fp4_score_decode(None, None, None, 64, None, None, 0, None, 8, 0, 1, P(16), 1 << 20, 512,
                                       P(16), None, 512, P(20), None) == -1
     assert "row_hist" in _err(L)
-    L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, P, I64, I32, P, I64, I32, I32, P, P, I64, P]
-    assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, None, 8, 0, None, 0, 512, 8, None,
-                                       None, 512, None) == -1
-    need = L.indexer_fp4_prefill_sched_bytes(2, 16, 512)
-    assert L.indexer_fp4_score_prefill(P(16), P(16), P(16), 64, P(16), P(16), 1, P(16), 8, 2, P(16), need - 1, 512,
-                                       16, P(16), P(16), 512, None) == -2
+    L.indexer_fp4_score_prefill.argtypes = [P, P, P, I32, P, P, I64, I64, I32, P, I64, I32, I32, P, I64, P]
+    assert L.indexer_fp4_score_prefill(None, None, None, 64, None, None, 0, 8, 0, None, 0, 512, 8, None, 512,
+                                       None) == -1
+    need = L.indexer_fp4_prefill_sched_bytes(2, 16, 256, 8)
+    assert L.indexer_fp4_score_prefill(P(16), P(16), P(16), 64, P(16), P(16), 1, 8, 2, P(16), need - 1, 256, 16,
+                                       P(16), 512, None) == -2
     assert "sched_bytes" in _err(L)
+    assert L.indexer_fp4_score_prefill(P(16), P(16), P(16), 64, P(16), P(16), 1, 8, 2, P(16), need, 256, 16,
+                                       P(16), 500, None) == -2
+    assert "logits_ld=500" in _err(L)
     L.indexer_topk.argtypes = [P, I64, I32, P, I64, I32, P, I64, P, I64, P, P]
     assert L.indexer_topk(None, 100, 4, None, 100, 0, None, 16, None, 0, None, None) == -1
     assert "k=0" in _err(L)

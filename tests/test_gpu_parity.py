@@ -118,22 +118,47 @@ def test_decode_schedule_exact(ifp4, ctx, units, next_n):
 
 
 @pytest.mark.parametrize("which", ["prefill_tiny", "prefill_4req"])
-@pytest.mark.parametrize("units", [13, 512, 4096])
+@pytest.mark.parametrize("units", [13, 256, 4096])
 def test_prefill_schedule_exact(ifp4, which, units):
     case = W.prefill_config(which, heads=16)
+    TR = ifp4.TILE_ROWS
     for st in case.steps:
         R, NP = len(st.req_ids), st.n_rows_padded
-        sched = torch.full((ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units),), 0xEE, dtype=torch.uint8,
+        bt = W.step_block_table(case, st)
+        bt_ld = bt.shape[1]
+        sched = torch.full((ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units, bt_ld),), 0xEE, dtype=torch.uint8,
                            device=dev())
         row_len = torch.empty(NP, dtype=torch.int32, device=dev())
-        ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, sched, row_len)
-        got = ifp4.read_prefill_schedule(sched, R, NP, units)
-        want = oracle.prefill_schedule(st.cu_rows, st.start_pos, NP, 8, units)
+        ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, to_dev(bt),
+                                          case.n_pages, sched, row_len)
+        got = ifp4.read_prefill_schedule(sched, R, NP, units, bt_ld)
+        want = oracle.prefill_schedule(st.cu_rows, st.start_pos, NP, TR, units)
         assert got["header"][1] == 0
         for key in ("tiles", "cum_items", "unit_begin", "unit_tile"):
             assert np.array_equal(got[key], want[key]), key
-        _, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, NP)
+        rs, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, NP)
         assert np.array_equal(row_len.cpu().numpy(), rl)
+        # the library's own words, against the oracle's tiles, lengths and the block table:
+        # valid rows, first position, first item of every tile; every item's physical page;
+        # every unit's start record
+        cum = want["cum_items"]
+        for t, (r0, nr, req, pages) in enumerate(want["tiles"]):
+            tw = got["tile_words"][t]
+            nv = int((rl[r0:r0 + nr] > 0).sum())
+            assert tw[2] == nv and tw[6] == cum[t], t
+            if nv:
+                assert tw[3] + 1 == rl[r0]
+            for p in range(pages):
+                assert got["item_phys"][cum[t] + p] == bt[req, p], (t, p)
+        ub = want["unit_begin"]
+        for u in range(units):
+            rec = got["unit_records"][u]
+            assert rec[0] == ub[u] and rec[1] == ub[u + 1] and rec[2] == want["unit_tile"][u], u
+            if ub[u] < ub[u + 1]:
+                assert np.array_equal(rec[4:12], got["tile_words"][rec[2]]), u
+            for j in range(4):
+                i = ub[u] + j
+                assert rec[12 + j] == (got["item_phys"][i] if i < ub[u + 1] else -1), (u, j)
 
 
 # ---------------------------------------------------------------------------- decode scores
@@ -281,19 +306,19 @@ def test_stale_or_zeroed_schedule_is_flagged(ifp4):
     ks = torch.zeros((pc.n_pages, 4, 64), dtype=torch.uint8, device=dev())
     bt = W.step_block_table(pc, st)
     pu = ifp4.PREFILL_UNITS
-    psched = torch.zeros(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, pu), dtype=torch.uint8, device=dev())
-    prl = torch.full((NP,), 5, dtype=torch.int32, device=dev())
+    psched = torch.zeros(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, pu, bt.shape[1]), dtype=torch.uint8,
+                         device=dev())
     plg = torch.full((NP, bt.shape[1] * 64), float("nan"), dtype=torch.float32, device=dev())
-    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, to_dev(bt), psched, pu, NP, prl, plg)
+    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, R, bt.shape[1], psched, pu, NP, plg)
     torch.cuda.synchronize()
     assert ifp4.sched_error(psched) == ifp4.DEV_BAD_SCHEDULE
     assert torch.isnan(plg).all()
 
 
 def test_prefill_device_side_errors_flag_and_skip(ifp4):
-    """Prefill with block-table entries outside the pool: the scorer flags the step, skips
-    exactly the pages those entries name (their columns keep the sentinel), does not fault,
-    and every other valid logit matches the oracle."""
+    """Prefill with block-table entries outside the pool: the schedule flags the step, the
+    scorer skips exactly the pages those entries name (their columns keep the sentinel),
+    nothing faults, and every other valid logit matches the oracle."""
     case = W.prefill_config("prefill_tiny", heads=16)
     kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev())
     ks = torch.zeros((case.n_pages, 4, 64), dtype=torch.uint8, device=dev())
@@ -315,12 +340,14 @@ def test_prefill_device_side_errors_flag_and_skip(ifp4):
     bt[0, 1] = 10_000  # request 0, page 1: outside the pool
     bt[1, 0] = -3      # request 2, page 0
     units = ifp4.PREFILL_UNITS
-    sched = torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8, device=dev())
+    sched = torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units, bt.shape[1]), dtype=torch.uint8,
+                        device=dev())
     row_len = torch.empty(NP, dtype=torch.int32, device=dev())
-    ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, sched, row_len)
+    ifp4.indexer_fp4_prefill_schedule(to_dev(st.cu_rows), to_dev(st.start_pos), NP, units, to_dev(bt), case.n_pages,
+                                      sched, row_len)
     ld = bt.shape[1] * 64
     logits = torch.full((NP, ld), float("nan"), dtype=torch.float32, device=dev())
-    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, to_dev(bt), sched, units, NP, row_len, logits)
+    ifp4.indexer_fp4_score_prefill(qp, qs, to_dev(st.w), kp, ks, R, bt.shape[1], sched, units, NP, logits)
     torch.cuda.synchronize()
     assert ifp4.sched_error(sched) & ifp4.DEV_BAD_PAGE
     lg = logits.cpu().numpy().astype(np.float64)
@@ -628,7 +655,7 @@ def test_prefill_graph_replay_bitwise_stable(ifp4):
     sp = torch.zeros(R, dtype=torch.int32, device=dev())
 
     def buffers():
-        return dict(sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units), dtype=torch.uint8,
+        return dict(sched=torch.empty(ifp4.indexer_fp4_prefill_sched_bytes(R, NP, units, pages), dtype=torch.uint8,
                                       device=dev()),
                     row_len=torch.empty(NP, dtype=torch.int32, device=dev()),
                     logits=torch.full((NP, ld), float("nan"), dtype=torch.float32, device=dev()),
@@ -637,8 +664,8 @@ def test_prefill_graph_replay_bitwise_stable(ifp4):
                                    device=dev()))
 
     def step(o):
-        ifp4.indexer_fp4_prefill_schedule(cu, sp, NP, units, o["sched"], o["row_len"])
-        ifp4.indexer_fp4_score_prefill(qp, qs, w, kp, ks, bt, o["sched"], units, NP, o["row_len"], o["logits"])
+        ifp4.indexer_fp4_prefill_schedule(cu, sp, NP, units, bt, n_pages, o["sched"], o["row_len"])
+        ifp4.indexer_fp4_score_prefill(qp, qs, w, kp, ks, R, pages, o["sched"], units, NP, o["logits"])
         ifp4.indexer_topk(o["logits"], o["row_len"], ld, k, o["top"], o["ws"])
 
     layouts = [([0, 16, 30, 45], [0, 500, 1000]), ([0, 40, 41, 48], [100, 0, 2000]), ([0, 1, 2, 3], [3000, 5, 64]),

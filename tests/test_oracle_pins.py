@@ -508,11 +508,13 @@ def test_schedules_and_geometry_golden():
 
 
 @pytest.mark.parametrize("which", ["prefill_tiny", "prefill_4req"])
-def test_prefill_schedule_covers_rows_and_pages_once(which):
+@pytest.mark.parametrize("tile_rows", [8, 16])
+def test_prefill_schedule_covers_rows_and_pages_once(which, tile_rows):
     case = W.prefill_config(which, heads=4)
+    TR = tile_rows
     for st in case.steps:
         units = 4096 if which == "prefill_4req" else 13
-        sch = oracle.prefill_schedule(st.cu_rows, st.start_pos, st.n_rows_padded, 8, units)
+        sch = oracle.prefill_schedule(st.cu_rows, st.start_pos, st.n_rows_padded, TR, units)
         rs, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, st.n_rows_padded)
         tiles = sch["tiles"]
         # every row in exactly one tile; tiles inside one group, aligned to its start
@@ -520,10 +522,10 @@ def test_prefill_schedule_covers_rows_and_pages_once(which):
         R = len(st.req_ids)
         for r0, nr, req, npg in tiles:
             seen[r0:r0 + nr] += 1
-            assert 1 <= nr <= 8
+            assert 1 <= nr <= TR
             first = st.cu_rows[req]
             end = st.n_rows_padded if req == R - 1 else st.cu_rows[req + 1]
-            assert first <= r0 and r0 + nr <= end and (r0 - first) % 8 == 0
+            assert first <= r0 and r0 + nr <= end and (r0 - first) % TR == 0
             assert (rs[r0:r0 + nr] == req).all()
             assert npg == (int(rl[r0:r0 + nr].max()) + 63) // 64
         assert (seen == 1).all()
