@@ -112,6 +112,16 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on XCD b % 8), and each
+// XCD has its own L2. This maps workgroup b to a work index so that consecutive work indices
+// (neighbouring items, which share pages and query rows) run on one XCD: the first n - n % 8
+// indices in 8 contiguous blocks, one per XCD, the rest unchanged.
+__device__ __forceinline__ int xcd_local_index(int b, int n) {
+  constexpr int kXcds = 8;
+  const int n8 = n - n % kXcds;
+  return b < n8 ? (b % kXcds) * (n8 / kXcds) + b / kXcds : b;
+}
+
 // Read-only view in the constant address space: wave-uniform reads through it become scalar
 // loads, which do not wait behind the vector-memory queue (the page prefetches). Only for
 // memory the kernel does not write.

@@ -19,6 +19,24 @@ struct RowRegs {
   float4 w[NN][NH16];                // weights of heads 16m + 4(l/16) + i
 };
 
+// Row `r` into slot n of R (no wait: the compiler waits where the registers are first used,
+// unless the caller waits itself).
+template <int NH16, int NN>
+__device__ __forceinline__ void load_row_into(RowRegs<NH16, NN> &R, int n, const uint8_t *__restrict__ qp,
+                                              const uint8_t *__restrict__ qs, const float *__restrict__ w,
+                                              int64_t r, int n_heads, int lane) {
+  const int hl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < (NH16 + 3) / 4; j++) R.qs[n][j] = 0;
+#pragma unroll
+  for (int m = 0; m < NH16; m++) {
+    const int64_t v = r * n_heads + 16 * m + hl;
+    R.qa[n][m] = *reinterpret_cast<const uint4 *>(qp + v * kKeyBytes + 16 * g);
+    R.qs[n][m / 4] |= (uint32_t)qs[v * kGroups + g] << (8 * (m % 4));
+    R.w[n][m] = *reinterpret_cast<const float4 *>(w + r * n_heads + 16 * m + 4 * g);
+  }
+}
+
 template <int NH16, int NN, bool Wait = true>
 __device__ __forceinline__ void load_rows(RowRegs<NH16, NN> &R, const uint8_t *__restrict__ qp,
                                           const uint8_t *__restrict__ qs, const float *__restrict__ w,
@@ -62,6 +80,16 @@ __device__ __forceinline__ void load_page(PageRegs &P, const uint8_t *__restrict
 #else
   P.s = *reinterpret_cast<const uint32_t *>(kvs + phys * kPageScaleBytes + 4 * lane);
 #endif
+}
+
+// One page as B operands with default (cached) loads: for pages that other waves or units read
+// again soon (prefill: every tile of a request reads the request's pages).
+__device__ __forceinline__ void load_page_cached(PageRegs &P, const uint8_t *__restrict__ kvp,
+                                                 const uint8_t *__restrict__ kvs, int64_t phys, int lane) {
+  const uint8_t *base = kvp + phys * kPageBytes + (lane & 15) * kKeyBytes + (lane >> 4) * 16;
+#pragma unroll
+  for (int t = 0; t < 4; t++) P.k[t] = *reinterpret_cast<const uint4 *>(base + 1024 * t);
+  P.s = *reinterpret_cast<const uint32_t *>(kvs + phys * kPageScaleBytes + 4 * lane);
 }
 
 // ReLU on the float's bits: a negative float is a negative int32, so an integer max with 0
