@@ -247,6 +247,34 @@ def bench_decode_sweep(torch, ifp4, W, args, layers=8):
     return out
 
 
+def bench_decode_latency(torch, ifp4, W, args, layers=21):
+    """Batch 1 at context 4096 (64 heads, top-2048): a latency-bound step. Whole steps
+    (schedule, then per layer fused write + score + top-k) and the scorer alone, per layer, at
+    the pages' two grid sizes: 512 units and 4096 ("Score a DSA sparse indexer in FP4", PR
+    description, Decode grid floor: 2.99 against 8.75 us per layer). Empty units exit before
+    any load, so the larger grid should cost only its extra dispatch."""
+    out = {}
+    for units in (512, 4096):
+        L, S, meta = build_decode(torch, ifp4, W, layers, units, args.seed, workload="decode_b1_4k")
+        for _ in range(args.warmup):
+            decode_step(ifp4, L, S, meta)
+        torch.cuda.synchronize()
+        if ifp4.sched_error(S["sched"]) != 0:
+            raise RuntimeError(f"decode_b1_4k: device error flags {ifp4.sched_error(S['sched'])}")
+        step_graph = capture(torch, lambda: decode_step(ifp4, L, S, meta))
+        for _ in range(args.warmup):
+            step_graph.replay()
+        step_ms = timed_replays(torch, step_graph, args.steps)
+        scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
+        scorer_graph.replay()
+        scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / layers
+        out[f"units_{units}"] = {"us_per_layer": round(1e3 * step_ms / layers, 3), "scorer_us": round(scorer_us, 3)}
+        del step_graph, scorer_graph, L, S
+        torch.cuda.synchronize()
+    return {"workload": "decode_b1_4k", "batch": 1, "context": 4096, "heads": 64, "index_topk": 2048,
+            "layers": layers, **out}
+
+
 def bench_prefill(torch, ifp4, W, args):
     dev = torch.device("cuda:0")
     layers = args.layers
@@ -430,6 +458,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
     ap.add_argument("--no-sweep", action="store_true", help="skip the long decode workloads")
+    ap.add_argument("--no-latency", action="store_true", help="skip the batch-1, 4096-context decode leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, a kernel of known traffic "
                          "for scaling hardware byte counters")
@@ -466,6 +495,12 @@ def main():
         for name, r in sweep.items():
             print(f"bench: {name} {r['us_per_layer']:.2f} us/layer, scorer {r['scorer_us']:.2f} us "
                   f"({r['scorer_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    lat = None
+    if not args.no_latency:
+        lat = bench_decode_latency(torch, ifp4, W, args)
+        print(f"bench: decode_b1_4k {lat['units_512']['us_per_layer']:.2f} / {lat['units_4096']['us_per_layer']:.2f} "
+              f"us/layer at 512 / 4096 units, scorer {lat['units_512']['scorer_us']:.2f} / "
+              f"{lat['units_4096']['scorer_us']:.2f} us", file=sys.stderr, flush=True)
     dcp = bench_dcp_merge(torch, ifp4, args)
     fp8 = None
     if not args.no_fp8:
@@ -515,6 +550,7 @@ def main():
                      "alg_bytes_per_launch": d["alg_bytes"]},
         "cpu_baseline": cpu,
         "writer": d["writer"],
+        "decode_latency": lat,
         "decode_long": sweep,
         "prefill": pre,
         "dcp_merge": dcp,
