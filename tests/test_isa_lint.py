@@ -31,7 +31,7 @@ def _asm(src, out_dir):
 
 
 SCC_WRITER = re.compile(r"^\s+(s_cmp\w*|s_(and|or|xor|andn2|orn2|nand|nor|xnor|not)_b\d+|s_(add|sub|addc|subb)_[ui]32|"
-                        r"s_(min|max)_\w+|s_(lshl|lshr|ashr)\w*|s_bfe\w*|s_abs\w*|s_bitcmp\w*|s_cselect\w*|"
+                        r"s_(min|max)_\w+|s_(lshl|lshr|ashr)\w*|s_bfe\w*|s_abs\w*|s_bitcmp\w*|"
                         r"s_\w+_saveexec\w*|s_mul_i32|s_absdiff\w*|s_bcnt\w*|s_quadmask\w*|s_wqm\w*)\b")
 
 
@@ -61,7 +61,11 @@ def test_lint_flags_the_known_bad_pattern():
     good = "\n".join(["\tv_cmp_eq_u32_e32 vcc, v8, v7", "\ts_cmp_eq_u32 s4, s5", "\ts_cselect_b32 s29, -1, s31"])
     mask = "\n".join(["\ts_and_b64 s[0:1], s[20:21], exec", "\tv_cmp_lt_i32_e32 vcc, v3, v4",
                       "\ts_cselect_b32 s0, s4, 0"])
+    # selects read the condition code without writing it: a chain of them after one compare
+    chain = "\n".join(["\ts_cmp_eq_u32 s27, 0", "\ts_cselect_b32 s54, s10, s11", "\tv_cmp_lt_i32_e32 vcc, v21, v22",
+                       "\ts_cselect_b32 s55, s48, s23"])
     assert suspicious_selects(bad) and not suspicious_selects(good) and not suspicious_selects(mask)
+    assert not suspicious_selects(chain)
 
 
 @pytest.fixture(scope="module")
