@@ -348,105 +348,94 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
 }
 
 // ---------------------------------------------------------------------------------------
-// Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). A workgroup retires
-// only 64 lanes of arithmetic a cycle, so one workgroup per row would be bound by its own
-// ALUs; each row is cut into chunks of kChunk keys, one workgroup each, and the selection
-// is a two-level radix select over the key bits, in three launches ordered by the stream
-// (two when the decode scorer has already filled the digit-1 histograms):
+// Long rows (decode at long context: few rows of 10^5 .. 10^6 keys). One workgroup per row
+// would be bound by one CU's ALUs and memory port, so each row is cut into chunks of kChunk
+// keys, one workgroup each, and the selection is a radix select over the key bits in
+// launches ordered by the stream (two when the decode scorer has already filled the digit-1
+// histograms):
 //   hist     histogram of digit 1 (key bits 31..20) of every chunk, merged into the row's
 //            histogram with one atomic per occupied bin;
-//   collect  every chunk finds the bin b1 that holds the row's k-th largest key and writes,
-//            in column order, its keys above b1 ("sure") and in b1 ("candidates") into its
-//            own region of the workspace with their counts; the candidates are also
-//            histogrammed on digit 2 (key bits 19..8) into the row's second histogram;
-//   finish   (one workgroup per row) finds the digit-2 bin b2 that holds the remaining
-//            k - sure keys, marks sure keys and candidates above b2 in an LDS bitmap of
-//            the row's columns, selects among the few candidates in b2 exactly (by counting
-//            ranks, ties to the lowest columns; radix select when there are many), writes
-//            the columns in ascending order and zeroes both histograms for the next call.
-// Device-wide atomics on one cache line serialize, so the merges are kept to one atomic
-// instruction per workgroup and 64-bin block.
-// Chunk workgroups of 512 threads (8 keys each): measured against 1024 and 256 on 8 and 16
-// rows of 131072 keys (hist + collect + finish 20.9 / 23.9 us, against 21.9 / 29.0 at 1024
-// and 25.2 / 26.9 at 256).
+//   collect  every chunk finds the bin b1 that holds the row's k-th largest key, counts its
+//            keys above b1 ("sure") and writes its keys in b1 ("candidates") into its own
+//            region of the workspace in column order, with both counts and b1;
+//   emit     every chunk again: it reads the counts and candidates of all the row's chunks
+//            and resolves from them, with two LDS histograms over the candidates (key bits
+//            19..8, then 7..0), the row's k-th largest key T and how many keys equal to T are
+//            kept (those of the lowest columns). Its offset in the output is the number of
+//            kept keys of the earlier chunks (their sure keys, their candidates above T and
+//            their share of the keys equal to T); it re-reads its own logits and writes its
+//            kept columns in ascending order. Every chunk of a row resolves T for itself, so
+//            no workgroup waits for another, and it zeroes its share of the row's digit-1
+//            histogram for the next call.
+// The candidates of a row are the keys of one digit-1 bin, an eighth of an octave of logit
+// values: a few thousand at most on the decode workloads, read by every chunk of the row in
+// one round of loads (more are read in further rounds). Device-wide atomics on one cache
+// line serialize, so the histogram merge sends one atomic per occupied bin.
+// Chunk workgroups of 512 threads (8 keys each).
 constexpr int kLongThreads = 512;
 constexpr int kLongWaves = kLongThreads / 64;
-constexpr int kFinishThreads = 1024;
 constexpr int kChunk = 4096;
 constexpr int kPerThread = kChunk / kLongThreads;  // 8
 constexpr int kWaveCols = kChunk / kLongWaves;      // columns of a chunk held by one wave
 constexpr int kBins = 4096;                         // 12-bit digits
-constexpr int64_t kLongMaxLen = 1 << 20;            // the finishing bitmap must fit LDS
+constexpr int64_t kLongMaxLen = 1 << 20;
 constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
-static_assert(kMaxChunks <= kFinishThreads, "the finish gives every chunk at least one thread");
-constexpr int kLdsBudget = 150 * 1024;              // dynamic LDS of the finish kernel
-constexpr int kSubMax = 8192;                       // candidates of bin b2 staged in LDS
-constexpr int kRankMax = 256;                       // ... ranked by counting
+static_assert(kMaxChunks <= kLongThreads, "the emit kernel gives every chunk of a row at least one thread");
+static_assert(kMaxChunks <= 4 * 64, "one wave of the emit kernel sums the chunk counts, four a lane");
+static_assert(kBins == kHistBins, "the digit-1 histograms are the row histograms the decode scorer fills");
+constexpr int kCandPer = 16;    // candidate slots of its chunk a thread of the emit kernel reads at once
+constexpr int kListMax = 8192;  // candidates of a row the emit kernel stages in LDS
+constexpr int kCountWords = 4;  // per chunk: sure count, candidate count, b1, unused
 
-// Workspace words: both row histograms first (zero when a call starts, zeroed again by the
-// finish), then per row the chunk counts and the chunks' regions for sure columns and
-// candidate keys / columns.
+// Workspace words: the row histograms of digit 1 first (used when the decode scorer has not
+// filled them; zero when a call starts and zeroed again by the emit kernel), then per row the
+// chunks' counts and the chunks' candidate regions.
 struct LongWs {
-  int64_t hist1, hist2, counts, sure, ckey, ccol, words;
+  int64_t hist1, counts, ckey, words;
   __host__ __device__ LongWs(int rows, int64_t max_len) {
     const int64_t chunks = (max_len + kChunk - 1) / kChunk;
     const int64_t cap = chunks * kChunk;
     hist1 = 0;
-    hist2 = hist1 + (int64_t)rows * kBins;
-    counts = hist2 + (int64_t)rows * kBins;
-    sure = counts + (int64_t)rows * 2 * chunks;
-    ckey = sure + (int64_t)rows * cap;
-    ccol = ckey + (int64_t)rows * cap;
-    words = ccol + (int64_t)rows * cap;
+    counts = hist1 + (int64_t)rows * kBins;
+    ckey = counts + (int64_t)rows * kCountWords * chunks;
+    words = ckey + (int64_t)rows * cap;
   }
 };
-
-__host__ __device__ inline int long_bitmap_words(int64_t max_len) { return (int)((max_len + 31) / 32); }
-__host__ __device__ inline int long_sub_cap(int64_t max_len) {
-  const int64_t room = ((int64_t)kLdsBudget - 4 * (int64_t)long_bitmap_words(max_len)) / 8;
-  return (int)(room < 0 ? 0 : (room > kSubMax ? kSubMax : room));
-}
 
 __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
   const int64_t len = row_len[r];
   return len < 0 ? 0 : (len > max_len ? max_len : len);
 }
 
-// Adds an LDS histogram's occupied bins into a global one: each wave instruction covers 64
-// consecutive bins, so a workgroup sends at most one atomic instruction per 256-byte block.
-template <int NT>
-__device__ __forceinline__ void hist_flush(const uint32_t *h, uint32_t *g) {
-  for (int b = threadIdx.x; b < kBins; b += NT) {
-    const uint32_t c = h[b];
-    if (c) atomicAdd(&g[b], c);
-  }
+// Inclusive prefix sum over the lanes of a wave (lanes <= this one): DPP shifts within rows of
+// 16 lanes, then row broadcasts across rows (no LDS round trips).
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, into rows 2 and 3
+  return v;
 }
 
-// Suffix sums of three values over the workgroup's threads (threads >= tid), one barrier pair.
+// Inclusive prefix sum of v over the workgroup's threads (threads <= tid); *total gets the
+// sum over all of them. s_w (one word a wave) must not be reused before another barrier.
 template <int NT>
-__device__ __forceinline__ void block_suffix_sum3(int &a, int &b, int &c, int *s_scan) {
+__device__ __forceinline__ int block_prefix_sum(int v, int *s_w, int &total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  v = wave_prefix_sum(v);
+  if (lane == 63) s_w[wv] = v;
+  __syncthreads();
+  int before = 0;
+  total = 0;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int ya = __shfl_down(a, off, 64), yb = __shfl_down(b, off, 64), yc = __shfl_down(c, off, 64);
-    if (lane + off < 64) {
-      a += ya;
-      b += yb;
-      c += yc;
-    }
+  for (int w2 = 0; w2 < NT / 64; w2++) {
+    const int x = s_w[w2];
+    before += w2 < wv ? x : 0;
+    total += x;
   }
-  if (lane == 0) {
-    s_scan[3 * wv] = a;
-    s_scan[3 * wv + 1] = b;
-    s_scan[3 * wv + 2] = c;
-  }
-  __syncthreads();
-  for (int w2 = wv + 1; w2 < NT / 64; w2++) {
-    a += s_scan[3 * w2];
-    b += s_scan[3 * w2 + 1];
-    c += s_scan[3 * w2 + 2];
-  }
-  __syncthreads();
+  return v + before;
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
@@ -481,7 +470,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
                                                                    const int32_t *__restrict__ row_len,
                                                                    int64_t max_len, int k, uint32_t *__restrict__ ws,
                                                                    int rows, const uint32_t *__restrict__ h1) {
-  __shared__ uint32_t h2[kBins];
+  __shared__ uint32_t s_h[kBins];
   __shared__ int s_scan[kLongWaves];
   __shared__ int s_bin;
   __shared__ uint32_t s_ws[kLongWaves], s_wc[kLongWaves];
@@ -502,19 +491,26 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     const int64_t j = start + kWaveCols * wv + 64 * u + lane;
     key[u] = order_key(j < end ? row[j] : 0.f);
   }
-  for (int i = tid; i < kBins; i += kLongThreads) h2[i] = 0u;
-  // the bin of the row's k-th largest key, from the row's digit-1 histogram
+  // the row's digit-1 histogram: read in its slot order (whole lines), put in LDS, then taken
+  // in bin order
   {
-    const uint32_t *gh = h1 + (int64_t)r * kHistBins;
+    const uint4 *gh = reinterpret_cast<const uint4 *>(h1 + (int64_t)r * kHistBins);
+    uint4 *sh = reinterpret_cast<uint4 *>(s_h);
+    for (int i = tid; i < kBins / 4; i += kLongThreads) sh[i] = gh[i];
+  }
+  if (tid == 0) s_bin = 0;  // published by the scan's barriers
+  __syncthreads();
+  {
     constexpr int kPer = kBins / kLongThreads;
     uint32_t cnt[kPer];
     int sum = 0;
-    if (tid == 0) s_bin = 0;  // published by the scan's barriers
 #pragma unroll
-    for (int i = 0; i < kPer; i++) cnt[i] = gh[hist_slot(kPer * tid + i)];
+    for (int i = 0; i < kPer; i++) cnt[i] = s_h[hist_slot(kPer * tid + i)];
 #pragma unroll
     for (int i = 0; i < kPer; i++) sum += (int)cnt[i];
-    int acc = block_suffix_sum<kLongThreads>(sum, s_scan);  // keys in bins >= kPer*tid
+    int tot;
+    const int incl = block_prefix_sum<kLongThreads>(sum, s_scan, tot);
+    int acc = tot - incl + sum;  // keys in bins >= kPer*tid
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
       if (acc >= k && acc - (int)cnt[i] < k) s_bin = kPer * tid + i;
@@ -523,268 +519,311 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     __syncthreads();
   }
   const uint32_t bin1 = (uint32_t)s_bin;
-  uint64_t ms[kPerThread], mc[kPerThread];
+  uint64_t mc[kPerThread];
   uint32_t n_s = 0, n_c = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
     const bool ok = start + kWaveCols * wv + 64 * u + lane < end;
     const uint32_t d = key[u] >> 20;
-    ms[u] = __ballot(ok && d > bin1);
+    n_s += (uint32_t)__popcll(__ballot(ok && d > bin1));
     mc[u] = __ballot(ok && d == bin1);
-    n_s += (uint32_t)__popcll(ms[u]);
     n_c += (uint32_t)__popcll(mc[u]);
-    if (mc[u]) hist_put(h2, (key[u] >> 8) & (kBins - 1), ok && d == bin1);
   }
   if (lane == 0) {
     s_ws[wv] = n_s;
     s_wc[wv] = n_c;
   }
-  __syncthreads();  // also completes h2
-  uint32_t bs = 0, bc = 0, ts = 0, tc = 0;
+  __syncthreads();
+  uint32_t bc = 0, ts = 0, tc = 0;
   for (int w2 = 0; w2 < kLongWaves; w2++) {
-    if (w2 < wv) {
-      bs += s_ws[w2];
-      bc += s_wc[w2];
-    }
+    if (w2 < wv) bc += s_wc[w2];
     ts += s_ws[w2];
     tc += s_wc[w2];
   }
-  uint32_t *sure = ws + L.sure + (int64_t)r * cap + start;
   uint32_t *ckey = ws + L.ckey + (int64_t)r * cap + start;
-  uint32_t *ccol = ws + L.ccol + (int64_t)r * cap + start;
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
-    const uint32_t j = (uint32_t)(start + kWaveCols * wv + 64 * u + lane);
-    if ((ms[u] >> lane) & 1ull) sure[bs + lanes_below(ms[u])] = j;
-    if ((mc[u] >> lane) & 1ull) {
-      ckey[bc + lanes_below(mc[u])] = key[u];
-      ccol[bc + lanes_below(mc[u])] = j;
-    }
-    bs += (uint32_t)__popcll(ms[u]);
+    if ((mc[u] >> lane) & 1ull) ckey[bc + lanes_below(mc[u])] = key[u];
     bc += (uint32_t)__popcll(mc[u]);
   }
   if (tid == 0) {
-    uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
-    cnt[2 * c] = ts;
-    cnt[2 * c + 1] = tc;
+    uint32_t *cnt = ws + L.counts + ((int64_t)r * chunks + c) * kCountWords;
+    cnt[0] = ts;
+    cnt[1] = tc;
+    cnt[2] = bin1;
   }
-  if (tc) hist_flush<kLongThreads>(h2, ws + L.hist2 + (int64_t)r * kBins);
 }
 
-__global__ __launch_bounds__(kFinishThreads) void topk_finish_kernel(const int32_t *__restrict__ row_len,
-                                                                    int64_t max_len, int k, uint32_t *__restrict__ ws,
-                                                                    int rows, uint32_t *__restrict__ h1,
-                                                                    int32_t *__restrict__ out, int64_t out_ld) {
-  // dynamic LDS: bitmap of the row's columns, then the candidates of bin b2 (keys, columns)
-  extern __shared__ uint32_t lds[];
-  __shared__ uint32_t hist[4 * 256];
-  __shared__ int s_scan[3 * (kFinishThreads / 64)], s_misc[8];
-  __shared__ int s_sure_off[kMaxChunks + 1], s_cand_off[kMaxChunks + 1];
-  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-  const LongWs L(rows, max_len);
+__global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__restrict__ logits, int64_t ld,
+                                                                const int32_t *__restrict__ row_len,
+                                                                int64_t max_len, int k,
+                                                                const uint32_t *__restrict__ ws, int rows,
+                                                                uint32_t *__restrict__ h1, int32_t *__restrict__ out,
+                                                                int64_t out_ld) {
+  __shared__ uint32_t s_h2[kBins];
+  __shared__ uint32_t s_h3[256];
+  __shared__ uint32_t s_list[kListMax];
+  __shared__ int s_nc[kMaxChunks], s_ns[kMaxChunks];
+  __shared__ int s_coff[kMaxChunks + 1], s_soff[kMaxChunks + 1];
+  __shared__ int s_wa[kLongWaves], s_wc[4 * kLongWaves];
+  __shared__ int s_sel[4];
+  __shared__ uint32_t s_we[kLongWaves], s_wk[kLongWaves];
+  const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int chunks = (int)((max_len + kChunk - 1) / kChunk);
+  const LongWs L(rows, max_len);
   const int64_t cap = (int64_t)chunks * kChunk;
-  uint32_t *g1 = h1 + (int64_t)r * kHistBins;
-  uint32_t *g2 = ws + L.hist2 + (int64_t)r * kBins;
-  const uint32_t *sure = ws + L.sure + (int64_t)r * cap;
-  const uint32_t *ckey = ws + L.ckey + (int64_t)r * cap;
-  const uint32_t *ccol = ws + L.ccol + (int64_t)r * cap;
-  // Everything the kernel reads is requested at once: the row length, the chunk counts, the
-  // digit-2 histogram and the first entries of each chunk's two lists. Thread group c (tpc
-  // threads) owns chunk c; every chunk's list regions hold kChunk entries and
-  // kBatch * tpc <= kChunk, so reading past a count stays in bounds.
-  constexpr int kBatch = 4;
-  const int tpc = max(1, kFinishThreads / chunks);
-  const int c = tid / tpc, t0 = tid % tpc;
-  const int cq = min(c, chunks - 1);
-  const uint32_t *cnt = ws + L.counts + (int64_t)r * 2 * chunks;
-  const uint32_t *cs = sure + (int64_t)cq * kChunk;
-  const uint32_t *ck = ckey + (int64_t)cq * kChunk;
-  const uint32_t *cc = ccol + (int64_t)cq * kChunk;
   const int64_t len = clamped_len(row_len, r, max_len);
-  const int ns_raw = (int)cnt[2 * cq], nc_raw = (int)cnt[2 * cq + 1];
-  constexpr int kH = kBins / kFinishThreads;  // digit-2 bins per thread
-  static_assert(kH * kFinishThreads == kBins, "bins per thread");
-  uint32_t h2[kH];
-#pragma unroll
-  for (int i = 0; i < kH; i++) h2[i] = g2[kH * tid + i];
-  uint32_t sj[kBatch], kk[kBatch], jj[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; u++) {
-    sj[u] = cs[t0 + u * tpc];
-    kk[u] = ck[t0 + u * tpc];
-    jj[u] = cc[t0 + u * tpc];
+  // the collect kernel has read the row's digit-1 histogram: this chunk's share of it is
+  // zeroed for the next call
+  {
+    const int per = (kHistBins / 4 + chunks - 1) / chunks;
+    uint4 *g = reinterpret_cast<uint4 *>(h1 + (int64_t)r * kHistBins);
+    const int i1 = min(kHistBins / 4, (c + 1) * per);
+    for (int i = c * per + tid; i < i1; i += kLongThreads) g[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   int32_t *o = out + r * out_ld;
-  if (len <= k) {  // short row: every key is kept (the other kernels left it alone)
-    for (int j = tid; j < k; j += kFinishThreads) o[j] = j < len ? j : -1;
-#pragma unroll
-    for (int i = 0; i < kH; i++) g1[kH * tid + i] = 0u;  // a scorer-filled histogram counts it
+  if (len <= k) {  // a row of at most k keys keeps them all (the collect kernel left it alone)
+    const int64_t span = ((int64_t)k + chunks - 1) / chunks;
+    const int64_t j1 = min((int64_t)k, (c + 1) * span);
+    for (int64_t j = c * span + tid; j < j1; j += kLongThreads) o[j] = j < len ? (int32_t)j : -1;
     return;
   }
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
-  const bool mine = c < used;
-  if (tid == 0) {  // defaults if no bin matches (a digit-1 histogram of other logits)
-    s_misc[0] = 0;
-    s_misc[1] = 0;
-    s_misc[2] = 0;
+  if (c >= used) return;
+  // Everything is requested at once: the counts of every chunk of the row, the first
+  // candidates of every chunk's region (tpc threads a chunk, kCandPer slots each; slots past a
+  // chunk's count hold stale words and are dropped once the counts are in) and this chunk's
+  // logits.
+  const int tpc = kLongThreads / used;
+  const int cc = tid / tpc, t0 = tid % tpc;
+  const bool live = cc < used;
+  const int ccq = live ? cc : 0;
+  const uint32_t *cw = ws + L.counts + (int64_t)r * chunks * kCountWords;
+  const uint32_t ns_raw = cw[ccq * kCountWords], nc_raw = cw[ccq * kCountWords + 1];
+  const uint32_t b1 = cw[2] & (kBins - 1);  // chunk 0 holds keys of every long row
+  const uint32_t *ckr = ws + L.ckey + (int64_t)r * cap;
+  uint32_t cand[kCandPer];
+#pragma unroll
+  for (int u = 0; u < kCandPer; u++) {
+    const int i = t0 + u * tpc;
+    cand[u] = i < kChunk ? ckr[(int64_t)ccq * kChunk + i] : 0u;
   }
-  const int ns = mine ? ns_raw : 0, nc = mine ? nc_raw : 0;
-  const int nwords = (int)((len + 31) / 32);
-  uint32_t *bitmap = lds;
-  for (int i = tid; i < nwords; i += kFinishThreads) bitmap[i] = 0u;
-  // chunk offsets (first thread of each group) and digit-2 bins 4 tid .. 4 tid + 3, scanned
-  // together; the scan's barriers also publish the cleared bitmap
-  {
-    const bool lead = mine && t0 == 0;
-    int sa = lead ? ns : 0, sb2 = lead ? nc : 0, sh = 0;
+  const int64_t start = (int64_t)c * kChunk;
+  const int64_t end = min(len, start + kChunk);
+  const int nvalid = (int)(end - start);  // keys of this chunk
+  const float *row = logits + r * ld;
+  uint32_t key[kPerThread];
 #pragma unroll
-    for (int i = 0; i < kH; i++) sh += (int)h2[i];
-    block_suffix_sum3<kFinishThreads>(sa, sb2, sh, s_scan);
-    if (tid == 0) {
-      s_sure_off[used] = sa;  // totals
-      s_cand_off[used] = sb2;
-    }
-    __syncthreads();
-    if (lead) {
-      s_sure_off[c] = s_sure_off[used] - sa;
-      s_cand_off[c] = s_cand_off[used] - sb2;
-    }
-    // bin b2 of the (k - sure)-th largest candidate
-    const int rem = k - s_sure_off[used];
-    int acc = sh;  // candidates in digit-2 bins >= kH tid
-#pragma unroll
-    for (int i = 0; i < kH; i++) {
-      if (acc >= rem && acc - (int)h2[i] < rem) {
-        s_misc[0] = kH * tid + i;              // b2
-        s_misc[1] = rem - (acc - (int)h2[i]);  // keys of b2 still to take
-        s_misc[2] = (int)h2[i];                // keys in b2
-      }
-      acc -= (int)h2[i];
-    }
-    if (tid == 0) s_misc[3] = 0;  // staged candidates of b2
-    __syncthreads();
+  for (int u = 0; u < kPerThread; u++) {
+    const int64_t j = start + kWaveCols * wv + 64 * u + lane;
+    key[u] = order_key(j < end ? row[j] : 0.f);
   }
-  // both histograms are left zero for the next call
-#pragma unroll
-  for (int i = 0; i < kH; i++) {
-    g1[kH * tid + i] = 0u;
-    g2[kH * tid + i] = 0u;
+  for (int i = tid; i < kBins / 4; i += kLongThreads) reinterpret_cast<uint4 *>(s_h2)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 256) s_h3[tid] = 0u;
+  if (tid == 0) {
+    s_sel[0] = -1;  // bin b2, if one holds the (k - sure)-th largest candidate
+    s_sel[1] = 0;
+    s_sel[2] = 0;
+    s_sel[3] = 0;
   }
-  const int n_cand = s_cand_off[used];
-  const uint32_t b2 = (uint32_t)s_misc[0];
-  const int need = s_misc[1], n2 = s_misc[2];
-  const int sub_cap = long_sub_cap(max_len);
-  const bool staged = n2 <= sub_cap;
-  uint32_t *sub_key = lds + long_bitmap_words(max_len);
-  uint32_t *sub_col = sub_key + sub_cap;
-  // sure columns and candidates above b2 go into the bitmap, candidates in b2 into LDS
-  auto place = [&](int t1) {
-#pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int t = t1 + u * tpc;
-      if (t < ns) atomicOr(&bitmap[sj[u] >> 5], 1u << (sj[u] & 31));
-      const bool cand = t < nc;
-      const uint32_t d2 = (kk[u] >> 8) & (kBins - 1);
-      if (cand && d2 > b2) atomicOr(&bitmap[jj[u] >> 5], 1u << (jj[u] & 31));
-      const bool in_b2 = cand && d2 == b2;
-      const uint64_t m = __ballot(in_b2 && staged);
-      if (m) {
-        int at = 0;
-        if (lane == 0) at = atomicAdd(&s_misc[3], __popcll(m));
-        at = __builtin_amdgcn_readfirstlane(at) + (int)lanes_below(m);
-        if (in_b2 && at < n2) {
-          sub_key[at] = kk[u];
-          sub_col[at] = jj[u];
-        }
-      }
-    }
-  };
-  place(t0);
-  // chunks with more entries than the first batch covered (rare)
-  for (int t1 = t0 + kBatch * tpc; __syncthreads_or(t1 < ns || t1 < nc); t1 += kBatch * tpc) {
-#pragma unroll
-    for (int u = 0; u < kBatch; u++) {
-      const int t = t1 + u * tpc;
-      sj[u] = t < ns ? cs[t] : 0u;
-      kk[u] = t < nc ? ck[t] : 0u;
-      jj[u] = t < nc ? cc[t] : 0u;
-    }
-    place(t1);
+  const int nc = live ? (int)min(nc_raw, (uint32_t)kChunk) : 0;
+  const int ns = live ? (int)min(ns_raw, (uint32_t)kChunk) : 0;
+  if (live && t0 == 0) {
+    s_nc[cc] = nc;
+    s_ns[cc] = ns;
   }
   __syncthreads();
-  // g-th candidate of the row (list split over chunks), for the radix fallback below: the
-  // chunk is found for the wave's first lane by bisection and advanced per lane
-  auto locate = [&](int g) {
-    const int g0 = __builtin_amdgcn_readfirstlane(g);
-    int lo = 0, hi = used;  // largest c with offset <= g0
+  // offsets of the chunks' candidates in the row's list and of their sure keys: one wave,
+  // four chunks a lane
+  if (wv == 0) {
+    int a[4], b[4], sa = 0, sb = 0;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int x = 4 * lane + i;
+      a[i] = x < used ? s_nc[x] : 0;
+      b[i] = x < used ? s_ns[x] : 0;
+      sa += a[i];
+      sb += b[i];
+    }
+    int ra = wave_prefix_sum(sa) - sa, rb = wave_prefix_sum(sb) - sb;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int x = 4 * lane + i;
+      if (x < used) {
+        s_coff[x] = ra;
+        s_soff[x] = rb;
+      }
+      ra += a[i];
+      rb += b[i];
+    }
+    if (lane == 63) {  // the totals
+      s_coff[used] = ra;
+      s_soff[used] = rb;
+    }
+  }
+  __syncthreads();
+  const int n_cand = s_coff[used], sure_all = s_soff[used];
+  const int cand_bef = s_coff[c], sure_bef = s_soff[c];
+  // The row's candidates in chunk (that is column) order, in LDS when they fit; otherwise read
+  // from the workspace wherever they are needed.
+  const bool staged = n_cand <= kListMax;
+  const int E = kCandPer * tpc;  // slots of a chunk held in registers
+  if (staged) {
+    const int off = s_coff[ccq];
+#pragma unroll
+    for (int u = 0; u < kCandPer; u++) {
+      const int i = t0 + u * tpc;
+      if (i < nc) s_list[off + i] = cand[u];
+    }
+    // the rest of chunks with more candidates than slots (rare), by the chunk's own threads
+    for (int i = E + t0; i < nc; i += tpc) s_list[off + i] = ckr[(int64_t)ccq * kChunk + i];
+    __syncthreads();
+  }
+  auto cand_at = [&](int g) -> uint32_t {
+    if (staged) return s_list[g];
+    int lo = 0, hi = used;  // the chunk x with s_coff[x] <= g < s_coff[x + 1]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_cand_off[mid] <= g0) lo = mid;
+      if (s_coff[mid] <= g) lo = mid;
       else hi = mid;
     }
-    int c = lo;
-    while (c + 1 < used && s_cand_off[c + 1] <= g) c++;
-    return (int64_t)c * kChunk + (g - s_cand_off[c]);
+    return ckr[(int64_t)lo * kChunk + (g - s_coff[lo])];
   };
-  // the `need` largest candidates of b2, ties to the lowest columns
-  if (staged && n2 <= kRankMax) {
-    if (tid < n2) {
-      const uint32_t key = sub_key[tid], col = sub_col[tid];
-      int rank = 0;
-      for (int g = 0; g < n2; g++) {
-        const uint32_t kg = sub_key[g];
-        rank += (kg > key || (kg == key && sub_col[g] < col)) ? 1 : 0;
+  // bin b2 (key bits 19..8) of the need-th largest candidate, then its low byte (plain LDS
+  // atomics: the candidates' digits are nearly all distinct, and rows of ties that put many
+  // on one digit only cost conflicts)
+  const int need = k - sure_all;
+  for (int g = tid; g < n_cand; g += kLongThreads) atomicAdd(&s_h2[(cand_at(g) >> 8) & (kBins - 1)], 1u);
+  __syncthreads();
+  {
+    constexpr int kPer = kBins / kLongThreads;
+    static_assert(kPer == 8, "two 16-byte reads a thread");
+    const uint4 lo = reinterpret_cast<const uint4 *>(s_h2)[2 * tid];
+    const uint4 hi = reinterpret_cast<const uint4 *>(s_h2)[2 * tid + 1];
+    const int cnt[kPer] = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) sum += cnt[i];
+    int tot;
+    const int incl = block_prefix_sum<kLongThreads>(sum, s_wa, tot);
+    int acc = tot - incl + sum;  // candidates in bins >= kPer*tid
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      if (acc >= need && acc - cnt[i] < need) {
+        s_sel[0] = kPer * tid + i;
+        s_sel[1] = need - (acc - cnt[i]);  // candidates of b2 still to take
       }
-      if (rank < need) atomicOr(&bitmap[col >> 5], 1u << (col & 31));
+      acc -= cnt[i];
     }
-  } else {
-    // radix select over the low 8 key bits (the top 24 are b1 and b2): from the staged list,
-    // or straight from the candidate lists, where keys outside b2 do not match the prefix
-    const int n_sel = staged ? n2 : n_cand;
-    auto key_at = [&](int g) { return staged ? sub_key[g] : ckey[locate(g)]; };
-    auto col_at = [&](int g) { return staged ? sub_col[g] : ccol[locate(g)]; };
-    const uint32_t prefix = (ckey[locate(0)] & 0xFFF00000u) | (b2 << 8);
-    int rem = need, n_eq = 0;
-    const uint32_t T = block_select<kFinishThreads>(n_sel, key_at, prefix, 0xFFFFFF00u, 8, &rem, &n_eq, hist, s_scan,
-                                                    s_misc + 4);
-    uint32_t cut = 0xFFFFFFFFu;  // keys equal to T with column <= cut are kept
-    if (rem < n_eq) {            // keep the rem lowest columns: the largest 2^20 - 1 - column
-      int rem2 = rem, n_eq2 = 0;
-      const uint32_t sel = block_select<kFinishThreads>(
-          n_sel, [&](int g) { return key_at(g) == T ? (0xFFFFFu - col_at(g)) : 0xFFFFFFFFu; }, 0u, 0xFFF00000u, 20,
-          &rem2, &n_eq2, hist, s_scan, s_misc + 4);
-      cut = 0xFFFFFu - sel;
+    __syncthreads();
+  }
+  uint32_t T;
+  int rem;  // keys equal to T that are kept
+  const int b2 = s_sel[0];
+  if (b2 >= 0) {
+    const int need2 = s_sel[1];
+    for (int g = tid; g < n_cand; g += kLongThreads) {
+      const uint32_t v = cand_at(g);
+      if ((int)((v >> 8) & (kBins - 1)) == b2) atomicAdd(&s_h3[v & 255u], 1u);
     }
-    for (int g = tid; g < n_sel; g += kFinishThreads) {
-      const uint32_t key = key_at(g);
-      const uint32_t j = col_at(g);
-      if (key > T || (key == T && j <= cut)) atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    __syncthreads();
+    if (wv == 0) {  // 256 bins, four a lane
+      const uint4 q = reinterpret_cast<const uint4 *>(s_h3)[lane];
+      const int cnt[4] = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      const int incl = wave_prefix_sum(sum);
+      int acc = __builtin_amdgcn_readlane(incl, 63) - incl + sum;  // candidates of b2 in bins >= 4 lane
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (acc >= need2 && acc - cnt[i] < need2) {
+          s_sel[2] = 4 * lane + i;
+          s_sel[3] = need2 - (acc - cnt[i]);
+        }
+        acc -= cnt[i];
+      }
+    }
+    __syncthreads();
+    T = (b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)s_sel[2];
+    rem = s_sel[3];
+  } else if (need <= 0) {  // more sure keys than k (a histogram of other logits): no candidate
+    T = 0xFFFFFFFFu;
+    rem = 0;
+  } else {  // fewer candidates than needed: all of them
+    T = 0u;
+    rem = INT32_MAX;
+  }
+  // candidates above T and equal to T: in the whole row and before this chunk (wave counts
+  // from ballots, summed over the waves)
+  int above_all = 0, eq_all = 0, above_bef = 0, eq_bef = 0;
+  {
+    int na = 0, ne = 0, nab = 0, neb = 0;
+    for (int g0 = 64 * wv; g0 < n_cand; g0 += kLongThreads) {
+      const int g = g0 + lane;
+      const bool ok = g < n_cand;
+      const uint32_t x = ok ? cand_at(g) : 0u;
+      const uint64_t ma = __ballot(ok && x > T), me = __ballot(ok && x == T), mb = __ballot(g < cand_bef);
+      na += __popcll(ma);
+      ne += __popcll(me);
+      nab += __popcll(ma & mb);
+      neb += __popcll(me & mb);
+    }
+    if (lane == 0) {
+      s_wc[4 * wv] = na;
+      s_wc[4 * wv + 1] = ne;
+      s_wc[4 * wv + 2] = nab;
+      s_wc[4 * wv + 3] = neb;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w2 = 0; w2 < kLongWaves; w2++) {
+      above_all += s_wc[4 * w2];
+      eq_all += s_wc[4 * w2 + 1];
+      above_bef += s_wc[4 * w2 + 2];
+      eq_bef += s_wc[4 * w2 + 3];
     }
   }
-  __syncthreads();
-  // columns out in ascending order: each thread owns a contiguous run of bitmap words
-  const int per = (nwords + kFinishThreads - 1) / kFinishThreads;
-  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  int bits = 0;
-  for (int i = w0; i < w1; i++) bits += __popc(bitmap[i]);
-  // exclusive prefix over threads = total - suffix(tid); the total is exactly k when the
-  // selection is consistent, and the bounds below hold either way
-  const int suffix = block_suffix_sum<kFinishThreads>(bits, s_scan);
-  if (tid == 0) s_misc[7] = suffix;
-  __syncthreads();
-  const int total = s_misc[7];
-  int pos = total - suffix;
-  for (int i = w0; i < w1; i++) {
-    uint32_t m = bitmap[i];
-    while (m) {
-      const int b = __ffs(m) - 1;
-      m &= m - 1;
-      if (pos >= 0 && pos < k) o[pos] = 32 * i + b;
-      pos++;
-    }
+  const int total = sure_all + above_all + min(eq_all, rem);
+  const int pre = sure_bef + above_bef + min(eq_bef, rem);
+  const int rem_c = max(0, rem - eq_bef);  // keys equal to T this chunk may keep, lowest columns first
+  // this chunk's keys equal to T in column order (wave-major), then the kept keys
+  uint64_t me[kPerThread];
+  uint32_t n_e = 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
+    me[u] = __ballot(ok && (key[u] >> 20) == b1 && key[u] == T);
+    n_e += (uint32_t)__popcll(me[u]);
   }
-  for (int j = max(total, 0) + tid; j < k; j += kFinishThreads) o[j] = -1;
+  if (lane == 0) s_we[wv] = n_e;
+  __syncthreads();
+  int e_run = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kLongWaves; w2++) e_run += w2 < wv ? (int)s_we[w2] : 0;
+  uint64_t mk[kPerThread];
+  uint32_t n_k = 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
+    const uint32_t d = key[u] >> 20;
+    const bool eq = (me[u] >> lane) & 1ull;
+    const bool keep = ok && (d > b1 || (d == b1 && key[u] > T) || (eq && e_run + (int)lanes_below(me[u]) < rem_c));
+    e_run += (int)__popcll(me[u]);
+    mk[u] = __ballot(keep);
+    n_k += (uint32_t)__popcll(mk[u]);
+  }
+  if (lane == 0) s_wk[wv] = n_k;
+  __syncthreads();
+  int pos = pre;
+#pragma unroll
+  for (int w2 = 0; w2 < kLongWaves; w2++) pos += w2 < wv ? (int)s_wk[w2] : 0;
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) {
+    const int at = pos + (int)lanes_below(mk[u]);
+    if (((mk[u] >> lane) & 1ull) && at >= 0 && at < k) o[at] = (int32_t)(start + kWaveCols * wv + 64 * u + lane);
+    pos += (int)__popcll(mk[u]);
+  }
+  if (c == used - 1)  // a selection short of k (a histogram of other logits) is padded
+    for (int j = max(total, 0) + tid; j < k; j += kLongThreads) o[j] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1048,14 +1087,11 @@ static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, con
   if (rc) return rc;
   if (n_rows == 0) return INDEXER_FP4_OK;
   hipStream_t st = (hipStream_t)stream;
-  // both kernels size their dynamic LDS from max_len; raise the launch limit once
+  // the short-row kernels size their dynamic LDS from max_len; raise the launch limit once
   static bool lds_set = false;
   if (!lds_set) {
-    hipError_t e = hipFuncSetAttribute((const void *)topk_finish_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       kLdsBudget);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)topk_row_kernel<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(4 * kShortMax));
+    hipError_t e = hipFuncSetAttribute((const void *)topk_row_kernel<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(4 * kShortMax));
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void *)topk_row_kernel<512>, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)(4 * kShortMax));
@@ -1078,7 +1114,6 @@ static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, con
     return fail(INDEXER_FP4_EINVAL, "topk: rows up to %lld keys need a 16-byte aligned workspace", (long long)max_len);
   uint32_t *ws = (uint32_t *)workspace;
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
-  const size_t lds = 4 * ((size_t)long_bitmap_words(max_len) + 2 * (size_t)long_sub_cap(max_len));
   // the digit-1 histograms: filled by the decode scorer, or built here in the workspace
   uint32_t *h1 = row_hist ? row_hist : ws + LongWs(n_rows, max_len).hist1;
   if (!row_hist)
@@ -1086,8 +1121,8 @@ static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, con
                        max_len, k, h1);
   hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld,
                      row_len, max_len, k, ws, n_rows, h1);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3(n_rows), dim3(kFinishThreads), lds, st, row_len, max_len, k, ws,
-                     n_rows, h1, topk_idx, topk_ld);
+  hipLaunchKernelGGL(topk_emit_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
+                     max_len, k, ws, n_rows, h1, topk_idx, topk_ld);
   return launch_status("topk");
 }
 

@@ -505,9 +505,10 @@ def test_topk_long_rows_exact(ifp4, n, k):
 
 
 def test_topk_long_rows_second_level_paths(ifp4):
-    """Rows built so the k-th key's second-level bin holds (a) a few thousand keys (radix select
-    staged in LDS), (b) a handful with exact ties at the threshold (ranking by counting), (c) more
-    than LDS holds (radix select straight from the chunk lists); rows of odd stride."""
+    """Rows built so that the k-th key's digit-1 bin holds (a) a few thousand keys clustered in a
+    few digit-2 bins, (b) exact ties at the threshold spread over every chunk, (c) far more
+    candidates than one round of the emit kernel's reads covers (further rounds from the
+    workspace); rows of odd stride."""
     n, k = 131072, 2048
     rng = np.random.default_rng(11)
     lg = rng.random((4, n)).astype(np.float32)
@@ -523,7 +524,7 @@ def test_topk_long_rows_second_level_paths(ifp4):
     _topk_exact(ifp4, lg, rl, k, n, pad=1)
 
 
-def test_topk_long_row_at_the_bitmap_limit(ifp4):
+def test_topk_long_row_at_the_length_limit(ifp4):
     n, k = 1 << 20, 2048
     rng = np.random.default_rng(1)
     lg = rng.standard_normal((2, n)).astype(np.float32)
