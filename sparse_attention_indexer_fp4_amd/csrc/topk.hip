@@ -560,13 +560,13 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
                                                                 const uint32_t *__restrict__ ws, int rows,
                                                                 uint32_t *__restrict__ h1, int32_t *__restrict__ out,
                                                                 int64_t out_ld) {
-  __shared__ uint32_t s_h2[kBins];
-  __shared__ uint32_t s_h3[256];
+  __shared__ uint32_t s_h2[kBins], s_h2b[kBins];  // all candidates; those of earlier chunks
+  __shared__ uint32_t s_h3[256], s_h3b[256];
   __shared__ uint32_t s_list[kListMax];
   __shared__ int s_nc[kMaxChunks], s_ns[kMaxChunks];
   __shared__ int s_coff[kMaxChunks + 1], s_soff[kMaxChunks + 1];
-  __shared__ int s_wa[kLongWaves], s_wc[4 * kLongWaves];
-  __shared__ int s_sel[4];
+  __shared__ int s_wa[2 * kLongWaves];
+  __shared__ int s_sel[8];
   __shared__ uint32_t s_we[kLongWaves], s_wk[kLongWaves];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int chunks = (int)((max_len + kChunk - 1) / kChunk);
@@ -618,14 +618,15 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
     const int64_t j = start + kWaveCols * wv + 64 * u + lane;
     key[u] = order_key(j < end ? row[j] : 0.f);
   }
-  for (int i = tid; i < kBins / 4; i += kLongThreads) reinterpret_cast<uint4 *>(s_h2)[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < 256) s_h3[tid] = 0u;
-  if (tid == 0) {
-    s_sel[0] = -1;  // bin b2, if one holds the (k - sure)-th largest candidate
-    s_sel[1] = 0;
-    s_sel[2] = 0;
-    s_sel[3] = 0;
+  for (int i = tid; i < kBins / 4; i += kLongThreads) {
+    reinterpret_cast<uint4 *>(s_h2)[i] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4 *>(s_h2b)[i] = make_uint4(0u, 0u, 0u, 0u);
   }
+  if (tid < 256) {
+    s_h3[tid] = 0u;
+    s_h3b[tid] = 0u;
+  }
+  if (tid < 8) s_sel[tid] = tid == 0 ? -1 : 0;  // s_sel[0]: bin b2, if one holds the (k - sure)-th largest candidate
   const int nc = live ? (int)min(nc_raw, (uint32_t)kChunk) : 0;
   const int ns = live ? (int)min(ns_raw, (uint32_t)kChunk) : 0;
   if (live && t0 == 0) {
@@ -679,126 +680,143 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
     for (int i = E + t0; i < nc; i += tpc) s_list[off + i] = ckr[(int64_t)ccq * kChunk + i];
     __syncthreads();
   }
-  auto cand_at = [&](int g) -> uint32_t {
-    if (staged) return s_list[g];
-    int lo = 0, hi = used;  // the chunk x with s_coff[x] <= g < s_coff[x + 1]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_coff[mid] <= g) lo = mid;
-      else hi = mid;
+  // f(g, key) for the row's candidates g = tid, tid + kLongThreads, ... (two loops, so that
+  // the staged one reads LDS with LDS instructions only)
+  auto for_cands = [&](auto f) {
+    if (staged) {
+      for (int g = tid; g < n_cand; g += kLongThreads) f(g, s_list[g]);
+    } else {
+      for (int g = tid; g < n_cand; g += kLongThreads) {
+        int lo = 0, hi = used;  // the chunk x with s_coff[x] <= g < s_coff[x + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (s_coff[mid] <= g) lo = mid;
+          else hi = mid;
+        }
+        f(g, ckr[(int64_t)lo * kChunk + (g - s_coff[lo])]);
+      }
     }
-    return ckr[(int64_t)lo * kChunk + (g - s_coff[lo])];
   };
-  // bin b2 (key bits 19..8) of the need-th largest candidate, then its low byte (plain LDS
-  // atomics: the candidates' digits are nearly all distinct, and rows of ties that put many
-  // on one digit only cost conflicts)
+  // Bin b2 (key bits 19..8) of the need-th largest candidate, then its low byte b3; the
+  // candidates of earlier chunks are counted alongside, so the same scans also give how many
+  // of them lie above T and equal T (plain LDS atomics: the candidates' digits are nearly all
+  // distinct, and rows of ties that put many on one digit only cost conflicts).
   const int need = k - sure_all;
-  for (int g = tid; g < n_cand; g += kLongThreads) atomicAdd(&s_h2[(cand_at(g) >> 8) & (kBins - 1)], 1u);
+  for_cands([&](int g, uint32_t v) {
+    const uint32_t d = (v >> 8) & (kBins - 1);
+    atomicAdd(&s_h2[d], 1u);
+    if (g < cand_bef) atomicAdd(&s_h2b[d], 1u);
+  });
   __syncthreads();
   {
     constexpr int kPer = kBins / kLongThreads;
     static_assert(kPer == 8, "two 16-byte reads a thread");
     const uint4 lo = reinterpret_cast<const uint4 *>(s_h2)[2 * tid];
     const uint4 hi = reinterpret_cast<const uint4 *>(s_h2)[2 * tid + 1];
+    const uint4 lob = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid];
+    const uint4 hib = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid + 1];
     const int cnt[kPer] = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) sum += cnt[i];
-    int tot;
-    const int incl = block_prefix_sum<kLongThreads>(sum, s_wa, tot);
-    int acc = tot - incl + sum;  // candidates in bins >= kPer*tid
+    const int cnb[kPer] = {(int)lob.x, (int)lob.y, (int)lob.z, (int)lob.w,
+                           (int)hib.x, (int)hib.y, (int)hib.z, (int)hib.w};
+    int sum = 0, sumb = 0;
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
-      if (acc >= need && acc - cnt[i] < need) {
-        s_sel[0] = kPer * tid + i;
-        s_sel[1] = need - (acc - cnt[i]);  // candidates of b2 still to take
-      }
+      sum += cnt[i];
+      sumb += cnb[i];
+    }
+    int tot, totb;
+    const int incl = block_prefix_sum<kLongThreads>(sum, s_wa, tot);
+    const int inclb = block_prefix_sum<kLongThreads>(sumb, s_wa + kLongWaves, totb);
+    int acc = tot - incl + sum, accb = totb - inclb + sumb;  // in bins >= kPer*tid
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
       acc -= cnt[i];
+      accb -= cnb[i];
+      if (acc + cnt[i] >= need && acc < need) {
+        s_sel[0] = kPer * tid + i;
+        s_sel[1] = need - acc;  // candidates of b2 still to take
+        s_sel[4] = accb;        // earlier chunks' candidates above b2
+      }
     }
     __syncthreads();
   }
   uint32_t T;
-  int rem;  // keys equal to T that are kept
+  int rem;            // keys equal to T that are kept
+  int eq_all, above_bef, eq_bef;
   const int b2 = s_sel[0];
   if (b2 >= 0) {
     const int need2 = s_sel[1];
-    for (int g = tid; g < n_cand; g += kLongThreads) {
-      const uint32_t v = cand_at(g);
-      if ((int)((v >> 8) & (kBins - 1)) == b2) atomicAdd(&s_h3[v & 255u], 1u);
-    }
+    for_cands([&](int g, uint32_t v) {
+      if ((int)((v >> 8) & (kBins - 1)) == b2) {
+        atomicAdd(&s_h3[v & 255u], 1u);
+        if (g < cand_bef) atomicAdd(&s_h3b[v & 255u], 1u);
+      }
+    });
     __syncthreads();
     if (wv == 0) {  // 256 bins, four a lane
       const uint4 q = reinterpret_cast<const uint4 *>(s_h3)[lane];
+      const uint4 qb = reinterpret_cast<const uint4 *>(s_h3b)[lane];
       const int cnt[4] = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3];
-      const int incl = wave_prefix_sum(sum);
-      int acc = __builtin_amdgcn_readlane(incl, 63) - incl + sum;  // candidates of b2 in bins >= 4 lane
+      const int cnb[4] = {(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w};
+      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3], sumb = cnb[0] + cnb[1] + cnb[2] + cnb[3];
+      const int incl = wave_prefix_sum(sum), inclb = wave_prefix_sum(sumb);
+      int acc = __builtin_amdgcn_readlane(incl, 63) - incl + sum;  // b2's candidates in bins >= 4 lane
+      int accb = __builtin_amdgcn_readlane(inclb, 63) - inclb + sumb;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        if (acc >= need2 && acc - cnt[i] < need2) {
-          s_sel[2] = 4 * lane + i;
-          s_sel[3] = need2 - (acc - cnt[i]);
-        }
         acc -= cnt[i];
+        accb -= cnb[i];
+        if (acc + cnt[i] >= need2 && acc < need2) {
+          s_sel[2] = 4 * lane + i;
+          s_sel[3] = need2 - acc;  // keys equal to T that are kept
+          s_sel[5] = accb;         // earlier chunks' candidates of b2 above T
+          s_sel[6] = cnb[i];       // earlier chunks' keys equal to T
+          s_sel[7] = cnt[i];       // keys equal to T
+        }
       }
     }
     __syncthreads();
     T = (b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)s_sel[2];
     rem = s_sel[3];
+    above_bef = s_sel[4] + s_sel[5];
+    eq_bef = s_sel[6];
+    eq_all = s_sel[7];
   } else if (need <= 0) {  // more sure keys than k (a histogram of other logits): no candidate
     T = 0xFFFFFFFFu;
     rem = 0;
-  } else {  // fewer candidates than needed: all of them
+    eq_all = above_bef = eq_bef = 0;
+  } else {  // fewer candidates than needed: all of them (all counted as above T)
     T = 0u;
     rem = INT32_MAX;
+    eq_all = eq_bef = 0;
+    above_bef = cand_bef;
   }
-  // candidates above T and equal to T: in the whole row and before this chunk (wave counts
-  // from ballots, summed over the waves)
-  int above_all = 0, eq_all = 0, above_bef = 0, eq_bef = 0;
-  {
-    int na = 0, ne = 0, nab = 0, neb = 0;
-    for (int g0 = 64 * wv; g0 < n_cand; g0 += kLongThreads) {
-      const int g = g0 + lane;
-      const bool ok = g < n_cand;
-      const uint32_t x = ok ? cand_at(g) : 0u;
-      const uint64_t ma = __ballot(ok && x > T), me = __ballot(ok && x == T), mb = __ballot(g < cand_bef);
-      na += __popcll(ma);
-      ne += __popcll(me);
-      nab += __popcll(ma & mb);
-      neb += __popcll(me & mb);
-    }
-    if (lane == 0) {
-      s_wc[4 * wv] = na;
-      s_wc[4 * wv + 1] = ne;
-      s_wc[4 * wv + 2] = nab;
-      s_wc[4 * wv + 3] = neb;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int w2 = 0; w2 < kLongWaves; w2++) {
-      above_all += s_wc[4 * w2];
-      eq_all += s_wc[4 * w2 + 1];
-      above_bef += s_wc[4 * w2 + 2];
-      eq_bef += s_wc[4 * w2 + 3];
-    }
-  }
-  const int total = sure_all + above_all + min(eq_all, rem);
+  const int total = b2 >= 0 ? k : (need <= 0 ? sure_all : sure_all + n_cand);
   const int pre = sure_bef + above_bef + min(eq_bef, rem);
   const int rem_c = max(0, rem - eq_bef);  // keys equal to T this chunk may keep, lowest columns first
+  // Keys equal to T are ranked by column only where the kept ones stop among them; otherwise
+  // they are all kept (the usual case: T is unique) or none is.
+  const bool rank_t = rem_c > 0 && rem < eq_all;
+  const bool keep_t = rem > 0 && rem >= eq_all;
   // this chunk's keys equal to T in column order (wave-major), then the kept keys
   uint64_t me[kPerThread];
-  uint32_t n_e = 0;
-#pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
-    me[u] = __ballot(ok && (key[u] >> 20) == b1 && key[u] == T);
-    n_e += (uint32_t)__popcll(me[u]);
-  }
-  if (lane == 0) s_we[wv] = n_e;
-  __syncthreads();
   int e_run = 0;
+  if (rank_t) {
+    uint32_t n_e = 0;
 #pragma unroll
-  for (int w2 = 0; w2 < kLongWaves; w2++) e_run += w2 < wv ? (int)s_we[w2] : 0;
+    for (int u = 0; u < kPerThread; u++) {
+      const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
+      me[u] = __ballot(ok && (key[u] >> 20) == b1 && key[u] == T);
+      n_e += (uint32_t)__popcll(me[u]);
+    }
+    if (lane == 0) s_we[wv] = n_e;
+    __syncthreads();
+#pragma unroll
+    for (int w2 = 0; w2 < kLongWaves; w2++) e_run += w2 < wv ? (int)s_we[w2] : 0;
+  } else {
+#pragma unroll
+    for (int u = 0; u < kPerThread; u++) me[u] = 0;
+  }
   uint64_t mk[kPerThread];
   uint32_t n_k = 0;
 #pragma unroll
@@ -806,7 +824,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
     const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
     const uint32_t d = key[u] >> 20;
     const bool eq = (me[u] >> lane) & 1ull;
-    const bool keep = ok && (d > b1 || (d == b1 && key[u] > T) || (eq && e_run + (int)lanes_below(me[u]) < rem_c));
+    const bool keep = ok && (d > b1 || (d == b1 && (key[u] > T || (keep_t && key[u] == T))) ||
+                             (eq && e_run + (int)lanes_below(me[u]) < rem_c));
     e_run += (int)__popcll(me[u]);
     mk[u] = __ballot(keep);
     n_k += (uint32_t)__popcll(mk[u]);
