@@ -475,29 +475,34 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   __shared__ int s_bin;
   __shared__ uint32_t s_ws[kLongWaves], s_wc[kLongWaves];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t len = clamped_len(row_len, r, max_len);
   const int64_t start = (int64_t)c * kChunk;
-  if (len <= k || start >= len) return;
+  // Every load goes out before the row length is known (a second memory round trip
+  // otherwise): the chunk's logits (columns clamped into the row; those past its length are
+  // masked below) and the row's digit-1 histogram, read in its slot order (whole lines).
+  // Wave wv holds the chunk's columns [kWaveCols wv, kWaveCols (wv + 1)) in 64-column steps,
+  // so wave-major order is column order.
+  const float *row = logits + r * ld;
+  float lv[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) lv[u] = row[min(start + kWaveCols * wv + 64 * u + lane, max_len - 1)];
+  static_assert(kBins / 4 == 2 * kLongThreads, "two 16-byte histogram reads a thread");
+  const uint4 *gh = reinterpret_cast<const uint4 *>(h1 + (int64_t)r * kHistBins);
+  const uint4 hv0 = gh[tid], hv1 = gh[tid + kLongThreads];
+  // A chunk past the row's length, or of a row of at most k keys (left to the emit kernel),
+  // runs through with no key counted and writes nothing: an early return here would let the
+  // compiler move the loads above behind the length's round trip.
+  const int64_t len = clamped_len(row_len, r, max_len);
+  const bool active = len > k && start < len;
   const LongWs L(rows, max_len);
   const int64_t chunks = (max_len + kChunk - 1) / kChunk;
   const int64_t cap = chunks * kChunk;
-  const float *row = logits + r * ld;
-  const int64_t end = min(len, start + kChunk);
-  // wave wv holds the chunk's columns [kWaveCols wv, kWaveCols (wv + 1)) in 64-column steps,
-  // so wave-major order is column order
+  const int64_t end = active ? min(len, start + kChunk) : start;
   uint32_t key[kPerThread];
 #pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + kWaveCols * wv + 64 * u + lane;
-    key[u] = order_key(j < end ? row[j] : 0.f);
-  }
-  // the row's digit-1 histogram: read in its slot order (whole lines), put in LDS, then taken
-  // in bin order
-  {
-    const uint4 *gh = reinterpret_cast<const uint4 *>(h1 + (int64_t)r * kHistBins);
-    uint4 *sh = reinterpret_cast<uint4 *>(s_h);
-    for (int i = tid; i < kBins / 4; i += kLongThreads) sh[i] = gh[i];
-  }
+  for (int u = 0; u < kPerThread; u++) key[u] = order_key(lv[u]);
+  // the histogram goes to LDS in slot order and is taken in bin order
+  reinterpret_cast<uint4 *>(s_h)[tid] = hv0;
+  reinterpret_cast<uint4 *>(s_h)[tid + kLongThreads] = hv1;
   if (tid == 0) s_bin = 0;  // published by the scan's barriers
   __syncthreads();
   {
@@ -546,7 +551,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     if ((mc[u] >> lane) & 1ull) ckey[bc + lanes_below(mc[u])] = key[u];
     bc += (uint32_t)__popcll(mc[u]);
   }
-  if (tid == 0) {
+  if (tid == 0 && active) {
     uint32_t *cnt = ws + L.counts + ((int64_t)r * chunks + c) * kCountWords;
     cnt[0] = ts;
     cnt[1] = tc;
@@ -572,6 +577,29 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   const int chunks = (int)((max_len + kChunk - 1) / kChunk);
   const LongWs L(rows, max_len);
   const int64_t cap = (int64_t)chunks * kChunk;
+  // Everything is requested at once, before the row length is known (a second memory round
+  // trip otherwise): the counts of every chunk of the row, the first candidates of every
+  // chunk's region (tpc threads a chunk, kCandPer slots each; slots past a chunk's count hold
+  // stale words and are dropped once the counts are in) and this chunk's logits (columns
+  // clamped into the row, those past its length masked).
+  const int tpc_log = 9 - (32 - __clz(chunks - 1));  // tpc: the power of two <= kLongThreads / chunks
+  const int tpc = 1 << tpc_log;
+  const int cc = tid >> tpc_log, t0 = tid & (tpc - 1);
+  const int ccq = min(cc, chunks - 1);
+  const uint32_t *cw = ws + L.counts + (int64_t)r * chunks * kCountWords;
+  const uint32_t ns_raw = cw[ccq * kCountWords], nc_raw = cw[ccq * kCountWords + 1];
+  const uint32_t b1 = cw[2] & (kBins - 1);  // chunk 0 holds keys of every long row
+  const uint32_t *ckr = ws + L.ckey + (int64_t)r * cap;
+  const uint32_t *ckc = ckr + (int64_t)ccq * kChunk;
+  uint32_t cand[kCandPer];
+#pragma unroll
+  for (int u = 0; u < kCandPer; u++) cand[u] = ckc[min(t0 + u * tpc, kChunk - 1)];  // (slots past kChunk unused)
+  const int64_t start = (int64_t)c * kChunk;
+  const float *row = logits + r * ld;
+  float lv[kPerThread];
+#pragma unroll
+  for (int u = 0; u < kPerThread; u++) lv[u] = row[min(start + kWaveCols * wv + 64 * u + lane, max_len - 1)];
+  asm volatile("" ::: "memory");  // (keeps the length check, and its wait, behind the loads)
   const int64_t len = clamped_len(row_len, r, max_len);
   // the collect kernel has read the row's digit-1 histogram: this chunk's share of it is
   // zeroed for the next call
@@ -590,34 +618,12 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   }
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
   if (c >= used) return;
-  // Everything is requested at once: the counts of every chunk of the row, the first
-  // candidates of every chunk's region (tpc threads a chunk, kCandPer slots each; slots past a
-  // chunk's count hold stale words and are dropped once the counts are in) and this chunk's
-  // logits.
-  const int tpc = kLongThreads / used;
-  const int cc = tid / tpc, t0 = tid % tpc;
   const bool live = cc < used;
-  const int ccq = live ? cc : 0;
-  const uint32_t *cw = ws + L.counts + (int64_t)r * chunks * kCountWords;
-  const uint32_t ns_raw = cw[ccq * kCountWords], nc_raw = cw[ccq * kCountWords + 1];
-  const uint32_t b1 = cw[2] & (kBins - 1);  // chunk 0 holds keys of every long row
-  const uint32_t *ckr = ws + L.ckey + (int64_t)r * cap;
-  uint32_t cand[kCandPer];
-#pragma unroll
-  for (int u = 0; u < kCandPer; u++) {
-    const int i = t0 + u * tpc;
-    cand[u] = i < kChunk ? ckr[(int64_t)ccq * kChunk + i] : 0u;
-  }
-  const int64_t start = (int64_t)c * kChunk;
   const int64_t end = min(len, start + kChunk);
   const int nvalid = (int)(end - start);  // keys of this chunk
-  const float *row = logits + r * ld;
   uint32_t key[kPerThread];
 #pragma unroll
-  for (int u = 0; u < kPerThread; u++) {
-    const int64_t j = start + kWaveCols * wv + 64 * u + lane;
-    key[u] = order_key(j < end ? row[j] : 0.f);
-  }
+  for (int u = 0; u < kPerThread; u++) key[u] = order_key(lv[u]);
   for (int i = tid; i < kBins / 4; i += kLongThreads) {
     reinterpret_cast<uint4 *>(s_h2)[i] = make_uint4(0u, 0u, 0u, 0u);
     reinterpret_cast<uint4 *>(s_h2b)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -782,11 +788,11 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
     eq_bef = s_sel[6];
     eq_all = s_sel[7];
   } else if (need <= 0) {  // more sure keys than k (a histogram of other logits): no candidate
-    T = 0xFFFFFFFFu;
+    T = (b1 << 20) | 0xFFFFFu;
     rem = 0;
     eq_all = above_bef = eq_bef = 0;
   } else {  // fewer candidates than needed: all of them (all counted as above T)
-    T = 0u;
+    T = b1 << 20;
     rem = INT32_MAX;
     eq_all = eq_bef = 0;
     above_bef = cand_bef;
@@ -798,7 +804,9 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   // they are all kept (the usual case: T is unique) or none is.
   const bool rank_t = rem_c > 0 && rem < eq_all;
   const bool keep_t = rem > 0 && rem >= eq_all;
-  // this chunk's keys equal to T in column order (wave-major), then the kept keys
+  // this chunk's keys equal to T in column order (wave-major), then the kept keys: T holds
+  // b1 in its top bits, so keys above T are the sure keys and the candidates above T (the
+  // predicates are combined without short-circuits, which would branch per key)
   uint64_t me[kPerThread];
   int e_run = 0;
   if (rank_t) {
@@ -806,7 +814,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
 #pragma unroll
     for (int u = 0; u < kPerThread; u++) {
       const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
-      me[u] = __ballot(ok && (key[u] >> 20) == b1 && key[u] == T);
+      me[u] = __ballot(ok & (key[u] == T));
       n_e += (uint32_t)__popcll(me[u]);
     }
     if (lane == 0) s_we[wv] = n_e;
@@ -822,10 +830,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) {
     const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
-    const uint32_t d = key[u] >> 20;
     const bool eq = (me[u] >> lane) & 1ull;
-    const bool keep = ok && (d > b1 || (d == b1 && (key[u] > T || (keep_t && key[u] == T))) ||
-                             (eq && e_run + (int)lanes_below(me[u]) < rem_c));
+    const bool keep = ok & ((key[u] > T) | (keep_t & (key[u] == T)) | (eq & (e_run + (int)lanes_below(me[u]) < rem_c)));
     e_run += (int)__popcll(me[u]);
     mk[u] = __ballot(keep);
     n_k += (uint32_t)__popcll(mk[u]);
