@@ -5,7 +5,9 @@ A step is one decode step of the indexer over 21 layers at batch 8 x context 131
 index heads x 128, index_topk 2048): the decode schedule is published once, then every
 layer writes its 8 new keys and quantizes its queries with the fused writer (key LayerNorm,
 RoPE on keys and query heads, MXFP4 write, weights_mqa: indexer_fp4_norm_rope_quant_and_cache),
-scores all keys (indexer_fp4_score_decode) and selects the top-k (indexer_topk). Each layer
+scores all keys (indexer_fp4_score_decode) and selects the top-k (indexer_topk); --fused-write
+runs the writer's work inside the scorer instead (indexer_fp4_write_and_score_decode, one
+launch). Each layer
 has its own key cache (21 x 78 MB), so the scan streams from HBM instead of the 256 MB
 last-level cache. The pages' indexer has 21 layers ("Score a DSA sparse indexer in FP4",
 PR description: 21 layers x 5.8 us of grid overhead a step).
@@ -13,9 +15,9 @@ PR description: 21 layers x 5.8 us of grid overhead a step).
 Steps run as replays of a HIP graph captured from the library calls (the calls are
 capturable: fixed grids, lengths read on the device, no host reads or allocations), as a
 serving engine would run them. Printed: one JSON line with the throughput (keys scored per
-second over whole steps), the decode scorer's roofline (algorithmic bytes per launch over
-its mean launch time: HIP events around replays of a graph holding the step's 21 scorer
-launches), the same figures per layer for the long decode workloads (16 x 131072 and
+second over whole steps), the roofline of the step's scoring kernel (algorithmic bytes per
+launch over its mean launch time: HIP events around replays of a graph holding the step's 21
+scoring launches), the same figures per layer for the long decode workloads (16 x 131072 and
 8 x 262144, 8 layers each), the prefill path's time per layer and FP4 MFMA roofline (4
 requests of 3420..4213 tokens, 512-token chunks), and the CPU oracle's rate on a bounded
 sample.
@@ -54,6 +56,15 @@ def decode_scorer_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -> int
     bytes read once and its fp32 logit written once; one block-table entry per page; per
     row the quantized query (64 + 4 bytes per head), its fp32 head weights and its length."""
     return n_keys * (64 + 4 + 4) + n_pages * 4 + rows * (heads * (64 + 4) + heads * 4 + 4)
+
+
+def decode_write_score_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -> int:
+    """Algorithmic HBM bytes of one write-and-score launch: the scorer's keys, table entries,
+    logits and lengths as above, and per row the writer's inputs instead of the quantized
+    query: the bf16 query heads, the fp32 weights, the bf16 new key, its position, slot and
+    rotary table row, and the new key's 68 cache bytes written."""
+    return (n_keys * (64 + 4 + 4) + n_pages * 4 +
+            rows * (heads * 256 + heads * 4 + 4 + 256 + 8 + 8 + 4 * ROPE_DIM + 68))
 
 
 def build_decode(torch, ifp4, W, layers, units, seed, fp8=False, workload="decode_b8_128k"):
@@ -119,19 +130,31 @@ def build_decode(torch, ifp4, W, layers, units, seed, fp8=False, workload="decod
     )
     torch.cuda.synchronize()
     meta = dict(B=B, H=H, k=k, ctx=int(ctx[0]), n_keys=int(ctx.astype(np.int64).sum()), n_pages_read=need,
-                ld=ld, units=units)
+                ld=ld, units=units, separate_writer=True)
     return L, shared, meta
 
 
 def decode_step(ifp4, L, S, meta):
-    """One decode step over all layers: schedule once, then per layer write + score + select."""
+    """One decode step over all layers: schedule once, then per layer write + score (one launch,
+    or two with separate_writer) and select."""
     units, ld, k = meta["units"], meta["ld"], meta["k"]
     ifp4.indexer_fp4_decode_schedule(S["ctx"], 1, units, S["sched"], S["row_len"])
     for lay in L:
-        write_decode(ifp4, lay, S)
-        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
-                                      units, S["row_len"], S["logits"], S["hist"])
+        if meta["separate_writer"]:
+            write_decode(ifp4, lay, S)
+            ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1,
+                                          S["sched"], units, S["row_len"], S["logits"], S["hist"])
+        else:
+            write_and_score(ifp4, lay, S, meta, S["hist"])
         ifp4.indexer_topk(S["logits"], S["row_len"], ld, k, S["top"], S["ws"], S["hist"])
+
+
+def write_and_score(ifp4, lay, S, meta, hist):
+    """A layer's fused write and its scores in one launch."""
+    ifp4.indexer_fp4_write_and_score_decode(
+        lay["knew"], S["new_slots"], lay["kp"], lay["ks"], lay["q"], lay["w"], S["bt"], S["sched"], meta["units"],
+        S["row_len"], S["logits"], positions=S["positions"], cos_sin=S["cos_sin"], rope_dim=ROPE_DIM,
+        k_norm_weight=lay["gamma"], k_norm_bias=lay["beta"], eps=1e-6, weight_scale=WEIGHT_SCALE, row_hist=hist)
 
 
 def write_decode(ifp4, lay, S):
@@ -143,11 +166,15 @@ def write_decode(ifp4, lay, S):
         q_packed=lay["qp"], q_scale=lay["qs"], weights=lay["w"], weight_scale=WEIGHT_SCALE, weights_mqa=lay["wm"])
 
 
-def decode_scorers(ifp4, L, S, meta):
-    """The step's 21 scorer launches alone (one per layer cache), histogram included."""
+def decode_scorers(ifp4, L, S, meta, plain=False):
+    """The step's 21 scoring launches alone (one per layer cache), histogram included: the
+    kernel the step runs (write-and-score), or with plain the scorer on quantized rows."""
     for lay in L:
-        ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1, S["sched"],
-                                      meta["units"], S["row_len"], S["logits"], S["hist_scorer"])
+        if plain or meta["separate_writer"]:
+            ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1,
+                                          S["sched"], meta["units"], S["row_len"], S["logits"], S["hist_scorer"])
+        else:
+            write_and_score(ifp4, lay, S, meta, S["hist_scorer"])
 
 
 def capture(torch, fn):
@@ -178,8 +205,17 @@ def timed_replays(torch, g, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def scoring_bytes(meta):
+    """Algorithmic bytes of the kernel decode_scorers times."""
+    f = decode_scorer_bytes if meta["separate_writer"] else decode_write_score_bytes
+    return f(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
+
+
 def bench_decode(torch, ifp4, W, args):
     L, S, meta = build_decode(torch, ifp4, W, args.layers, args.units, args.seed)
+    meta["separate_writer"] = not args.fused_write
+    for lay in L:  # the quantized rows the plain scorer reads
+        write_decode(ifp4, lay, S)
     for _ in range(args.warmup):
         decode_step(ifp4, L, S, meta)
     torch.cuda.synchronize()
@@ -191,10 +227,15 @@ def bench_decode(torch, ifp4, W, args):
     wall0 = time.perf_counter()
     ms_per_step = timed_replays(torch, step_graph, args.steps)
     wall = time.perf_counter() - wall0
-    # the dominant kernel alone: 21 scorer launches per replay, averaged over the replays
+    # the dominant kernel alone: 21 scoring launches per replay, averaged over the replays
     scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
     scorer_graph.replay()
     scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / args.layers
+    plain_scorer_us = scorer_us
+    if not meta["separate_writer"]:  # the scorer on quantized rows, beside the writing one
+        plain_scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta, plain=True))
+        plain_scorer_graph.replay()
+        plain_scorer_us = 1e3 * timed_replays(torch, plain_scorer_graph, args.steps) / args.layers
     # the step's other per-layer kernel: the fused writer (and the plain writer beside it)
     writer_graph = capture(torch, lambda: [write_decode(ifp4, lay, S) for lay in L])
     writer_us = 1e3 * timed_replays(torch, writer_graph, args.steps) / args.layers
@@ -204,10 +245,13 @@ def bench_decode(torch, ifp4, W, args):
     for lay in L:  # leave the fused write's outputs in place
         write_decode(ifp4, lay, S)
     keys_per_step = meta["n_keys"] * args.layers
-    alg_bytes = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
+    alg_bytes = scoring_bytes(meta)
     achieved = alg_bytes / (scorer_us * 1e-6) / 1e9
+    plain_bytes = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
     return dict(meta=meta, ms_per_step=ms_per_step, wall_s=wall, keys_per_s=keys_per_step / (ms_per_step * 1e-3),
                 scorer_us=scorer_us, alg_bytes=alg_bytes, achieved_gbs=achieved,
+                plain_scorer={"us": round(plain_scorer_us, 3), "alg_bytes_per_launch": plain_bytes,
+                              "frac": round(plain_bytes / (plain_scorer_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
                 writer={"fused_us_per_layer": round(writer_us, 3), "plain_us_per_layer": round(plain_us, 3),
                         "tokens": meta["B"], "heads": meta["H"], "rope_dim": ROPE_DIM})
 
@@ -222,6 +266,7 @@ def bench_decode_sweep(torch, ifp4, W, args, layers=8):
     out = {}
     for name in SWEEP_WORKLOADS:
         L, S, meta = build_decode(torch, ifp4, W, layers, args.units, args.seed, workload=name)
+        meta["separate_writer"] = not args.fused_write
         for _ in range(args.warmup):
             decode_step(ifp4, L, S, meta)
         torch.cuda.synchronize()
@@ -234,7 +279,7 @@ def bench_decode_sweep(torch, ifp4, W, args, layers=8):
         scorer_graph = capture(torch, lambda: decode_scorers(ifp4, L, S, meta))
         scorer_graph.replay()
         scorer_us = 1e3 * timed_replays(torch, scorer_graph, args.steps) / layers
-        alg = decode_scorer_bytes(meta["n_keys"], meta["n_pages_read"], meta["B"], meta["H"])
+        alg = scoring_bytes(meta)
         gbs = alg / (scorer_us * 1e-6) / 1e9
         out[name] = {"batch": meta["B"], "context": meta["ctx"], "layers": layers,
                      "us_per_layer": round(1e3 * step_ms / layers, 3),
@@ -256,6 +301,7 @@ def bench_decode_latency(torch, ifp4, W, args, layers=21):
     out = {}
     for units in (512, 4096):
         L, S, meta = build_decode(torch, ifp4, W, layers, units, args.seed, workload="decode_b1_4k")
+        meta["separate_writer"] = not args.fused_write
         for _ in range(args.warmup):
             decode_step(ifp4, L, S, meta)
         torch.cuda.synchronize()
@@ -459,6 +505,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
     ap.add_argument("--no-sweep", action="store_true", help="skip the long decode workloads")
     ap.add_argument("--no-latency", action="store_true", help="skip the batch-1, 4096-context decode leg")
+    ap.add_argument("--fused-write", action="store_true",
+                    help="decode steps run the writer's work inside the scorer (one launch a layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy, a kernel of known traffic "
                          "for scaling hardware byte counters")
@@ -486,8 +534,9 @@ def main():
     print(f"bench: decode 8 x 131072, {args.layers} layers, steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     d = bench_decode(torch, ifp4, W, args)
-    print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scorer {d['scorer_us']:.2f} us "
-          f"({d['achieved_gbs']:.0f} GB/s)", file=sys.stderr, flush=True)
+    print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scoring kernel {d['scorer_us']:.2f} us "
+          f"({d['achieved_gbs']:.0f} GB/s), plain scorer {d['plain_scorer']['us']:.2f} us, writer "
+          f"{d['writer']['fused_us_per_layer']:.2f} us", file=sys.stderr, flush=True)
     pre = None
     sweep = None
     if not args.no_sweep:
@@ -546,8 +595,9 @@ def main():
         "decode_scorer_keys_per_s": round(d["meta"]["n_keys"] / (d["scorer_us"] * 1e-6), 1),
         "roofline": {"bound": "hbm", "achieved": round(d["achieved_gbs"], 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(d["achieved_gbs"] / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "score_decode", "launch_us_mean": round(d["scorer_us"], 3),
-                     "alg_bytes_per_launch": d["alg_bytes"]},
+                     "kernel": "write_and_score_decode" if args.fused_write else "score_decode",
+                     "launch_us_mean": round(d["scorer_us"], 3), "alg_bytes_per_launch": d["alg_bytes"]},
+        "plain_scorer": d["plain_scorer"],
         "cpu_baseline": cpu,
         "writer": d["writer"],
         "decode_latency": lat,

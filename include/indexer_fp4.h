@@ -266,6 +266,35 @@ int indexer_fp8_score_decode(const uint8_t *q_packed, const uint8_t *q_scale, co
                              uint32_t *row_hist, void *stream);
 
 /* ---------------------------------------------------------------------------------
+ * Write and score in one launch ([P2] PR description, Performance: the FP4 path runs
+ * exactly one kernel more than the FP8 one, the fused writer; here that writer's work is
+ * done by the decode scorer itself). For next_n = 1 only: the result equals
+ * indexer_fp4_norm_rope_quant_and_cache on (k_bf16, q_bf16, weights) with n_tok = batch
+ * followed by indexer_fp4_score_decode on its outputs: the cache planes receive the same
+ * bytes at slot_mapping, and logits and row_hist the same values. The quantized query rows
+ * stay inside the launch (no q_packed, q_scale or weights_mqa output).
+ *   k_bf16 ... all_q   as for indexer_fp4_norm_rope_quant_and_cache, with n_tok = batch
+ *                      (row b is sequence b); n_heads a multiple of 16, at most 128
+ *   kv_packed ... row_hist  as for indexer_fp4_score_decode with next_n = 1; the
+ *                      schedule must be built with next_n = 1
+ * Each sequence's new key is written by the wave that scores the sequence's last page,
+ * before it loads that page: slot_mapping[b] must be the slot of position row_len[b] - 1
+ * of sequence b (its block-table page, as the decode step writes it); a key written to
+ * another slot is still written but not necessarily seen by this call's scores.
+ * Device flags as both: INDEXER_FP4_DEV_BAD_POSITION and _SLOT_OUT_OF_POOL (key skipped)
+ * go to the schedule's error word.
+ * Errors: EINVAL (n_heads, rope_dim, eps, k_ld, bias without weight, NULL or misaligned
+ * pointers), ENOSPC (bt_ld, logits_ld, sched_bytes), EARCH, EHIP.
+ * --------------------------------------------------------------------------------- */
+int indexer_fp4_write_and_score_decode(
+    const void *k_bf16, int64_t k_ld, const float *k_norm_weight, const float *k_norm_bias, float eps,
+    const int64_t *positions, const float *cos_sin, int64_t max_pos, int32_t rope_dim, int32_t rope_interleaved,
+    const int64_t *slot_mapping, const void *q_bf16, const float *weights, float weight_scale, int32_t all_q,
+    int32_t n_heads, uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+    int32_t batch, void *sched, int64_t sched_bytes, int32_t n_units, const int32_t *row_len, float *logits,
+    int64_t logits_ld, uint32_t *row_hist, void *stream);
+
+/* ---------------------------------------------------------------------------------
  * Prefill scorer ([P2] commit message: the FP4 prefill variant; [P1] section 3: the
  * row-group kernel finds a group's page table as group b -> block_tables[b], which the
  * schedule has already resolved). Same logit as decode for every valid row of the step;

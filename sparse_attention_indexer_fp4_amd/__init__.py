@@ -21,6 +21,7 @@ HEAD_DIM = 128
 ROW_MULTIPLE = 8   # a prefill step's padded row count is a multiple of this
 TILE_ROWS = 16     # prefill rows per tile
 DEV_BAD_PAGE, DEV_TABLE_SHORT, DEV_BAD_SCHEDULE, DEV_BAD_LENGTH = 1, 2, 4, 8
+DEV_BAD_POSITION, DEV_SLOT_OUT_OF_POOL = 16, 32
 # persistent-grid sizes the scorers default to (units = workgroups)
 DECODE_UNITS = 512
 PREFILL_UNITS = 256  # one 16-wave unit per CU
@@ -35,6 +36,7 @@ EXPORTS = (
     "indexer_fp4_prefill_sched_bytes",
     "indexer_fp4_prefill_schedule",
     "indexer_fp4_score_decode",
+    "indexer_fp4_write_and_score_decode",
     "indexer_fp4_score_prefill",
     "indexer_fp8_quant_and_cache",
     "indexer_fp8_score_decode",
@@ -67,6 +69,8 @@ def _load() -> ctypes.CDLL:
         "indexer_fp4_prefill_schedule": ([P, P, I32, I32, I32, P, I64, I64, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_decode": ([P, P, P, I32, P, P, I64, P, I64, I32, I32, P, I64, I32, P, P, I64, P, P],
                                      ctypes.c_int),
+        "indexer_fp4_write_and_score_decode": ([P, I64, P, P, F32, P, P, I64, I32, I32, P, P, P, F32, I32, I32, P, P,
+                                                I64, P, I64, I32, P, I64, I32, P, P, I64, P, P], ctypes.c_int),
         "indexer_fp4_score_prefill": ([P, P, P, I32, P, P, I64, I64, I32, P, I64, I32, I32, P, I64, P],
                                       ctypes.c_int),
         "indexer_fp8_quant_and_cache": ([P, I64, I64, P, P, P, I64, P, I64, I32, P, P, P], ctypes.c_int),
@@ -239,6 +243,50 @@ def indexer_fp4_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, bl
     row_histogram) that the scorer fills for indexer_topk."""
     _score_decode(lib.indexer_fp4_score_decode, 64, q_packed, q_scale, weights, kv_packed, kv_scale, block_table,
                   next_n, sched, n_units, row_len, logits, row_hist)
+
+
+def indexer_fp4_write_and_score_decode(k, slot_mapping, kv_packed, kv_scale, q, weights, block_table, sched, n_units,
+                                       row_len, logits, positions=None, cos_sin=None, rope_dim=0, interleaved=False,
+                                       k_norm_weight=None, k_norm_bias=None, eps=1e-6, weight_scale=1.0, all_q=False,
+                                       row_hist=None):
+    """The fused writer and the decode scorer in one launch (next_n = 1): k [B, >=128] bf16 and
+    q [B, H, 128] bf16 with weights fp32 [B, H] are normalized, rotated and quantized as
+    indexer_fp4_norm_rope_quant_and_cache does (each key to its slot), and the sequences'
+    logits written as indexer_fp4_score_decode writes them from the quantized rows."""
+    _dev(k, "k", torch.bfloat16, contiguous=False)
+    if k.dim() != 2 or k.stride(1) != 1:
+        raise ValueError("k must be 2-D with unit stride along the head dimension")
+    for t, name, dt in ((slot_mapping, "slot_mapping", torch.int64), (kv_packed, "kv_packed", torch.uint8),
+                        (kv_scale, "kv_scale", torch.uint8), (q, "q", torch.bfloat16),
+                        (weights, "weights", torch.float32), (block_table, "block_table", torch.int32),
+                        (row_len, "row_len", torch.int32)):
+        _dev(t, name, dt)
+    _dev(sched, "sched")
+    _dev(logits, "logits", torch.float32, contiguous=False)
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    if kv_packed.dim() != 3 or kv_packed.shape[1:] != (64, 64):
+        raise ValueError("kv_packed must be [n_pages, 64, 64]")
+    batch, bt_ld = block_table.shape
+    if q.dim() != 3 or q.shape[0] != batch or q.shape[2] != HEAD_DIM or k.shape[0] != batch:
+        raise ValueError("q must be [B, H, 128] and k [B, >=128] for the table's B sequences")
+    max_pos = 0
+    if rope_dim:
+        _dev(positions, "positions", torch.int64)
+        _dev(cos_sin, "cos_sin", torch.float32)
+        if cos_sin.dim() != 2 or cos_sin.shape[1] != rope_dim:
+            raise ValueError("cos_sin must be [max_pos, rope_dim]")
+        max_pos = cos_sin.shape[0]
+    for t, name in ((k_norm_weight, "k_norm_weight"), (k_norm_bias, "k_norm_bias")):
+        if t is not None:
+            _dev(t, name, torch.float32)
+    _check_hist(row_hist, batch)
+    _check(lib.indexer_fp4_write_and_score_decode(
+        _ptr(k), k.stride(0), _ptr(k_norm_weight), _ptr(k_norm_bias), float(eps), _ptr(positions), _ptr(cos_sin),
+        max_pos, int(rope_dim), int(bool(interleaved)), _ptr(slot_mapping), _ptr(q), _ptr(weights),
+        float(weight_scale), int(bool(all_q)), q.shape[1], _ptr(kv_packed), _ptr(kv_scale), kv_packed.shape[0],
+        _ptr(block_table), bt_ld, batch, _ptr(sched), _nbytes(sched), n_units, _ptr(row_len), _ptr(logits),
+        logits.stride(0), _ptr(row_hist), _stream(logits)))
 
 
 def indexer_fp8_score_decode(q_packed, q_scale, weights, kv_packed, kv_scale, block_table, next_n, sched, n_units,

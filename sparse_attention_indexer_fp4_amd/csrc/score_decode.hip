@@ -28,6 +28,7 @@
 // extra time: rows of the unit's first sequence (nearly all its items) are counted in LDS and
 // added to the device histogram at the end, the rare pages of later sequences straight into
 // device memory.
+#include "quant_common.h"
 #include "score_common.h"
 
 // waves per unit and pages in flight per wave (tuned on MI355X at 8 x 131072, 64 heads)
@@ -46,14 +47,180 @@ struct SlottedHist {
   __device__ __forceinline__ uint32_t &operator[](uint32_t b) const { return g[hist_slot(b)]; }
 };
 
-template <class F, int NH16, int NN, int NW, int D>
+// The step's writer work, for the entry point that writes the step's key and query rows
+// itself (next_n = 1): the arguments of indexer_fp4_norm_rope_quant_and_cache.
+struct StepWrite {
+  const uint16_t *k;          // [batch][k_ld] bf16: each sequence's new key
+  int64_t k_ld;
+  const float *gamma, *beta;  // k_norm (gamma NULL: none)
+  float eps;
+  const int64_t *positions;   // [batch] rotary positions
+  const float *cos_sin;       // [max_pos][rope_dim]
+  int64_t max_pos;
+  int rope_dim;
+  int interleaved;
+  const int64_t *slots;       // [batch] cache slot of each new key
+  const uint16_t *q;          // [batch][n_heads][128] bf16
+  const float *weights;       // [batch][n_heads]
+  float weight_scale;
+  int all_q;
+  uint8_t *kvp, *kvs;         // the cache planes, written
+};
+
+// A sequence's area in LDS: its quantized query heads (codes [H][64], scales [H][4], weights
+// [H] -- what the writer stores as q_packed, q_scale, weights_mqa) and its new key (codes
+// [64], scales [4], then whether the writer would store it and its slot).
+constexpr int kQVecBytes = kKeyBytes + kGroups + 4;
+constexpr int kKeyAreaBytes = 80;
+__host__ __device__ constexpr int seq_area_bytes(int n_heads) { return n_heads * kQVecBytes + kKeyAreaBytes; }
+
+// The inputs of lane-tasks first + task0 + kb * stride (16 lanes a query head, stride a
+// multiple of 16), and of the sequence's key for the lanes whose task0 is below 16.
+template <int KB>
+struct SeqLoad {
+  uint4 raw[KB];
+  float wv[KB];
+  uint4 kraw;
+  float gm[8], bt[8];
+  float c[8], sn[8];
+  int64_t pos, slot;
+};
+
+template <int KB>
+__device__ __forceinline__ void seq_load(SeqLoad<KB> &Q, const StepWrite W, int b, int n_heads, int task0, int stride,
+                                         int first, bool key) {
+  const int l = task0 & 15;
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+    const int h = min((first + task0 + kb * stride) >> 4, n_heads - 1);
+    Q.raw[kb] = *reinterpret_cast<const uint4 *>(W.q + ((int64_t)b * n_heads + h) * kHeadDim + 8 * l);
+    Q.wv[kb] = W.weights[(int64_t)b * n_heads + h];
+  }
+  Q.pos = W.rope_dim > 0 ? W.positions[b] : 0;
+  Q.slot = W.slots[b];
+  if (key) {
+    Q.kraw = *reinterpret_cast<const uint4 *>(W.k + (int64_t)b * W.k_ld + 8 * l);
+    if (W.gamma) {
+      const float4 g0 = *reinterpret_cast<const float4 *>(W.gamma + 8 * l);
+      const float4 g1 = *reinterpret_cast<const float4 *>(W.gamma + 8 * l + 4);
+      Q.gm[0] = g0.x, Q.gm[1] = g0.y, Q.gm[2] = g0.z, Q.gm[3] = g0.w;
+      Q.gm[4] = g1.x, Q.gm[5] = g1.y, Q.gm[6] = g1.z, Q.gm[7] = g1.w;
+      if (W.beta) {
+        const float4 b0 = *reinterpret_cast<const float4 *>(W.beta + 8 * l);
+        const float4 b1 = *reinterpret_cast<const float4 *>(W.beta + 8 * l + 4);
+        Q.bt[0] = b0.x, Q.bt[1] = b0.y, Q.bt[2] = b0.z, Q.bt[3] = b0.w;
+        Q.bt[4] = b1.x, Q.bt[5] = b1.y, Q.bt[6] = b1.z, Q.bt[7] = b1.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; j++) Q.bt[j] = 0.f;
+      }
+    }
+  }
+}
+
+// ... the rotary angles of the sequence's position (a second round: the table row waits for
+// the position) ...
+template <int KB>
+__device__ __forceinline__ void seq_angles(SeqLoad<KB> &Q, const StepWrite W, int task0) {
+  const int l = task0 & 15;
+  const bool bad_pos = W.rope_dim > 0 && (Q.pos < 0 || Q.pos >= W.max_pos);
+  if (W.rope_dim > 0 && 8 * l < W.rope_dim)
+    rope_angles(W.cos_sin + (bad_pos ? 0 : Q.pos) * W.rope_dim, l, W.rope_dim, W.interleaved != 0, Q.c, Q.sn);
+}
+
+// ... then the query heads and the key quantized into the sequence's area.
+template <int KB>
+__device__ __forceinline__ void seq_store(SeqLoad<KB> &Q, const StepWrite W, int n_heads, int64_t n_pages,
+                                          uint8_t *area, int task0, int stride, int first, bool key) {
+  const int l = task0 & 15, g = l >> 2;
+  const bool bad_pos = W.rope_dim > 0 && (Q.pos < 0 || Q.pos >= W.max_pos);
+  const bool live = !bad_pos && (Q.slot >= 0 || W.all_q != 0);
+#pragma unroll
+  for (int kb = 0; kb < KB; kb++) {
+    const int i = first + task0 + kb * stride;
+    if (i >= 16 * n_heads) break;  // uniform over the head's 16 lanes
+    const int h = i >> 4;
+    uint32_t sc = 0, d = 0;
+    if (live) d = norm_rope_encode(Q.raw[kb], l, false, Q.gm, Q.bt, 0.f, W.rope_dim, W.interleaved != 0, Q.c, Q.sn, sc);
+    *reinterpret_cast<uint32_t *>(area + h * kKeyBytes + 4 * l) = d;
+    if ((l & 3) == 0) area[n_heads * kKeyBytes + h * kGroups + g] = (uint8_t)sc;
+    if (l == 0)
+      reinterpret_cast<float *>(area + n_heads * (kKeyBytes + kGroups))[h] = live ? W.weight_scale * Q.wv[kb] : 0.f;
+  }
+  if (key) {  // the writer stores the key when its position and slot are good
+    uint8_t *ka = area + n_heads * kQVecBytes;
+    const bool store = !bad_pos && Q.slot >= 0 && Q.slot < n_pages * kPage;
+    uint32_t sc = 0;
+    const uint32_t d = norm_rope_encode(Q.kraw, l, W.gamma != nullptr, Q.gm, Q.bt, W.eps, W.rope_dim,
+                                        W.interleaved != 0, Q.c, Q.sn, sc);
+    *reinterpret_cast<uint32_t *>(ka + 4 * l) = d;
+    if ((l & 3) == 0) ka[kKeyBytes + g] = (uint8_t)sc;
+    if (l == 0) {
+      reinterpret_cast<int32_t *>(ka + 68)[0] = (store ? 1 : 0) | (bad_pos ? 2 : 0);
+      *reinterpret_cast<int64_t *>(ka + 72) = Q.slot;
+    }
+  }
+}
+
+// The scorer on the page that holds the sequence's new key: the key's codes and scales go
+// into the page's operand registers at its position p (the lanes of key p % 16 of tile
+// p / 16), and the wave stores them at the key's slot, as the writer would. Nothing is
+// patched unless the slot is that position of this page (the writer would have written the
+// key elsewhere, and this page keeps what it holds).
+__device__ __forceinline__ void patch_new_key(PageRegs &P, const uint8_t *ka, int p, int64_t phys, const StepWrite W,
+                                              int64_t n_pages, int32_t *err, int lane) {
+  const int flags = reinterpret_cast<const int32_t *>(ka + 68)[0];
+  const int64_t slot = *reinterpret_cast<const int64_t *>(ka + 72);
+  if (lane == 0 && (flags & 2)) atomicOr(err, INDEXER_FP4_DEV_BAD_POSITION);
+  if (lane == 0 && !(flags & 2) && slot >= n_pages * kPage) atomicOr(err, INDEXER_FP4_DEV_SLOT_OUT_OF_POOL);
+  if (!(flags & 1)) return;
+  if (lane < 16) {  // the writer's store
+    const int g = lane >> 2;
+    const int64_t page = slot / kPage;
+    const int sp = (int)(slot % kPage);
+    *reinterpret_cast<uint32_t *>(W.kvp + slot * kKeyBytes + 4 * lane) = *reinterpret_cast<const uint32_t *>(ka + 4 * lane);
+    if ((lane & 3) == 0) W.kvs[(page * kGroups + g) * kPage + (sp % 16) * 4 + sp / 16] = ka[kKeyBytes + g];
+  }
+  if (slot != phys * kPage + p) return;
+  const int t = p >> 4;  // uniform
+  if ((lane & 15) == (p & 15)) {
+    const uint4 v = *reinterpret_cast<const uint4 *>(ka + 16 * (lane >> 4));
+    if (t == 0) P.k[0] = v;
+    else if (t == 1) P.k[1] = v;
+    else if (t == 2) P.k[2] = v;
+    else P.k[3] = v;
+    P.s = (P.s & ~(0xFFu << (8 * t))) | ((uint32_t)ka[kKeyBytes + (lane >> 4)] << (8 * t));
+  }
+}
+
+// One query row from a sequence's area (what load_rows reads from memory).
+template <int NH16, int NN>
+__device__ __forceinline__ void rows_from_area(RowRegs<NH16, NN> &R, const uint8_t *area, int n_heads, int lane) {
+  const int hl = lane & 15, g = lane >> 4;
+  const uint8_t *aqs = area + n_heads * kKeyBytes;
+  const float *aw = reinterpret_cast<const float *>(area + n_heads * (kKeyBytes + kGroups));
+#pragma unroll
+  for (int j = 0; j < (NH16 + 3) / 4; j++) R.qs[0][j] = 0;
+#pragma unroll
+  for (int m = 0; m < NH16; m++) {
+    const int v = 16 * m + hl;
+    R.qa[0][m] = *reinterpret_cast<const uint4 *>(area + v * kKeyBytes + 16 * g);
+    R.qs[0][m / 4] |= (uint32_t)aqs[v * kGroups + g] << (8 * (m % 4));
+    R.w[0][m] = *reinterpret_cast<const float4 *>(aw + 16 * m + 4 * g);
+  }
+}
+
+template <class F, int NH16, int NN, int NW, int D, bool WR>
 __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     const uint8_t *__restrict__ qp, const uint8_t *__restrict__ qs, const float *__restrict__ w, int n_heads,
     const uint8_t *__restrict__ kvp, const uint8_t *__restrict__ kvs, int64_t n_pages,
     const int32_t *__restrict__ bt_g, int64_t bt_ld, int batch, int n_units, const int32_t *__restrict__ sched_g,
     int32_t *__restrict__ err, const int32_t *__restrict__ row_len_g, float *__restrict__ logits, int64_t ld,
-    uint32_t *__restrict__ row_hist) {
-  extern __shared__ uint32_t uh[];  // [NN][kHistBins] with a row histogram
+    uint32_t *__restrict__ row_hist, const StepWrite Wr_arg) {
+  static_assert(!WR || (NN == 1 && NH16 <= 8), "the writing scorer takes one row a sequence, up to 128 heads");
+  const StepWrite Wr = Wr_arg;  // (a copy: no address of the kernel argument is taken)
+  // dynamic LDS: [NN][kHistBins] with a row histogram; then, when writing, query areas
+  extern __shared__ uint32_t uh[];
   const DecodeSchedLayout L(batch, n_units);
   const const_ptr<int32_t> sched = as_const(sched_g), row_len = as_const(row_len_g);
   const int u = blockIdx.x;
@@ -82,11 +249,12 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     if (threadIdx.x == 0) atomicOr(err, INDEXER_FP4_DEV_BAD_SCHEDULE);
     return;
   }
-  if (fuse) {
-    for (int i = threadIdx.x; i < NN * kHistBins / 4; i += NW * 64)
-      reinterpret_cast<uint4 *>(uh)[i] = make_uint4(0u, 0u, 0u, 0u);
-    __syncthreads();
-  }
+  // Writing: the query heads of the unit's first sequence (one lane-task each, 16 a head) are
+  // requested right after the first pages and quantized into the unit's LDS area while those
+  // are in flight.
+  uint8_t *qarea = reinterpret_cast<uint8_t *>(uh + (fuse ? NN * kHistBins : 0));
+  const int area_bytes = seq_area_bytes(n_heads);
+  constexpr int KBC = WR ? (16 * 16 * NH16 + NW * 64 - 1) / (NW * 64) : 1;
   // this wave's contiguous share of the unit's items (none for some waves of a short unit,
   // which still meet the workgroup's barriers)
   const int per = (it1 - it0 + NW - 1) / NW;
@@ -96,25 +264,31 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   const int32_t *cum = sched_g + L.cum;
 
   // Item table, one lane per item, for 64 items at a time: sequence, page index within
-  // it, and physical page (-1 if the page cannot be read). Built with one round of
-  // per-lane loads instead of a chain of dependent scalar loads per page.
+  // it, and physical page (-1 if the page cannot be read); when writing, whether the item is
+  // its sequence's last page (the one that holds the step's new key). Built with one round
+  // of per-lane loads instead of a chain of dependent scalar loads per page.
   int seq0 = sched[L.unit_seq + u];  // sequence of the unit's first item
   const int page0 = sched[L.unit_page + u];
   const int run0 = sched[L.unit_run + u];
+  const int end0 = WR ? sched[L.cum + min(seq0, batch - 1) + 1] : 0;  // past the first sequence's last item
   int tab_base = -64;
   int v_seq = 0, v_page = 0, v_phys = -1;
-  auto fill = [&](int base) {
+  bool v_last = false;
+  auto fill = [&](int base) __attribute__((always_inline)) {
     tab_base = base;
     const int it = w0 + base + lane;
     int b = seq0, p = 0, phys = -1;
+    bool last = false;
     if (it < w1) {
       const int k = it - it0;  // items past the unit's first one
       if (k < run0) {          // still in the unit's first sequence: no lookup
         b = sched[L.unit_seq + u];
         p = page0 + k;
+        if constexpr (WR) last = it + 1 == end0;
       } else {
         while (b < batch - 1 && it >= cum[b + 1]) b++;
         p = it - cum[b];
+        if constexpr (WR) last = it + 1 == cum[b + 1];
       }
       if (p >= 0 && p < bt_ld) {
         phys = bt_g[(int64_t)b * bt_ld + p];
@@ -129,9 +303,9 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     v_seq = b;
     v_page = p;
     v_phys = phys;
+    v_last = last;
     seq0 = __builtin_amdgcn_readlane(b, 63);  // sequences only advance with the items
   };
-
   // Software pipeline over a ring of D pages: scoring slot K overlaps the loads of the
   // other D-1 slots. Every slot refill is unconditional -- past the wave's last item it
   // reloads that item (a cache hit) and its logits are dropped -- so the compiler waits
@@ -139,7 +313,9 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   typename F::Page P[D];
   int sb[D], sp[D];
   bool sok[D];
-  auto issue = [&](auto kk, int i) {
+  bool slast[D];     // writing: the slot holds its sequence's last page
+  int64_t sphys[D];  // writing: its physical page
+  auto issue = [&](auto kk, int i) __attribute__((always_inline)) {
     constexpr int K = decltype(kk)::value;
     const bool live = i < n_my;
     const int ii = live ? i : n_my - 1;
@@ -149,15 +325,40 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     sb[K] = __builtin_amdgcn_readlane(v_seq, l);
     sp[K] = __builtin_amdgcn_readlane(v_page, l);
     sok[K] = live && phys >= 0;
+    if constexpr (WR) {
+      slast[K] = live && __builtin_amdgcn_readlane((int)v_last, l) != 0;
+      sphys[K] = phys;
+    }
     F::page(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);
   };
   typename F::template Rows<NH16, NN> R;
   int qb = -1;
-  auto score = [&](auto kk) {
+  uint8_t *warea = qarea + (1 + wv) * area_bytes;  // this wave's area, for other sequences
+  auto score = [&](auto kk) __attribute__((always_inline)) {
     constexpr int K = decltype(kk)::value;
     if (sb[K] != qb) {  // a new sequence: its query rows (waits for everything in flight)
       qb = sb[K];
-      F::template rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
+      if constexpr (WR) {
+        if (qb == qs0) {
+          rows_from_area<NH16, NN>(R, qarea, n_heads, lane);
+        } else {  // quantized by this wave alone, two lane-tasks a lane at a time
+          for (int first = 0; first < 16 * n_heads; first += 2 * 64) {
+            SeqLoad<2> Qw;
+            seq_load<2>(Qw, Wr, qb, n_heads, lane, 64, first, first == 0 && lane < 16);
+            seq_angles<2>(Qw, Wr, lane);
+            seq_store<2>(Qw, Wr, n_heads, n_pages, warea, lane, 64, first, first == 0 && lane < 16);
+          }
+          rows_from_area<NH16, NN>(R, warea, n_heads, lane);
+        }
+      } else {
+        F::template rows<NH16, NN>(R, qp, qs, w, (int64_t)qb * NN, NN, n_heads, lane);
+      }
+    }
+    if constexpr (WR) {  // the page that holds the sequence's new key
+      if (slast[K]) {
+        const int p = (row_len[qb] - 1) & (kPage - 1);
+        patch_new_key(P[K], (qb == qs0 ? qarea : warea) + n_heads * kQVecBytes, p, sphys[K], Wr, n_pages, err, lane);
+      }
     }
     const uint32_t col = (uint32_t)(sp[K] * kPage + lane);
     static_for<NN>([&](auto nn) {
@@ -177,9 +378,24 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
     });
   };
 
+  // Writing: the first sequence's query heads and key are requested with the item table
+  // (one lane-task each, 16 a head; the key by the first 16 lanes), its rotary table row ahead
+  // of the first pages, and all of it quantized while those pages are in flight.
+  SeqLoad<KBC> Q0;
+  if constexpr (WR) seq_load<KBC>(Q0, Wr, qs0, n_heads, threadIdx.x, NW * 64, 0, threadIdx.x < 16);
+  if (n_my > 0) fill(0);
+  if constexpr (WR) seq_angles<KBC>(Q0, Wr, threadIdx.x);
   if (n_my > 0) {
     // the first pages are in flight before the query rows are fetched
     static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
+  }
+  if constexpr (WR) seq_store<KBC>(Q0, Wr, n_heads, n_pages, qarea, threadIdx.x, NW * 64, 0, threadIdx.x < 16);
+  if (fuse) {
+    for (int i = threadIdx.x; i < NN * kHistBins / 4; i += NW * 64)
+      reinterpret_cast<uint4 *>(uh)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (fuse || WR) __syncthreads();  // the histogram cleared, the query area written
+  if (n_my > 0) {
     for (int i0 = 0; i0 < n_my; i0 += D) {
       static_for<D>([&](auto kk) {
         score(kk);
@@ -197,23 +413,25 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   }
 }
 
-template <class F, int NH16, int NN>
+template <class F, int NH16, int NN, bool WR = false>
 static int launch_decode(hipStream_t st, int n_units, const uint8_t *qp, const uint8_t *qs, const float *w,
                           int n_heads, const uint8_t *kvp, const uint8_t *kvs, int64_t n_pages, const int32_t *bt,
                           int64_t bt_ld, int batch, int32_t *sched, const int32_t *row_len, float *logits,
-                          int64_t ld, uint32_t *row_hist) {
+                          int64_t ld, uint32_t *row_hist, const StepWrite &Wr = StepWrite{}) {
   constexpr int NW = IFP4_DECODE_WAVES, D = IFP4_DECODE_RING;
-  constexpr size_t kHistLds = (size_t)NN * kHistBins * 4;
+  // dynamic LDS: the histogram, then (writing) the unit's and each wave's query area
+  const size_t lds = (row_hist ? (size_t)NN * kHistBins * 4 : 0) + (WR ? (size_t)(1 + NW) * seq_area_bytes(n_heads) : 0);
   static bool lds_set = false;  // raise the dynamic LDS limit once per instantiation
-  if (row_hist && !lds_set) {
-    const hipError_t e = hipFuncSetAttribute((const void *)score_decode_kernel<F, NH16, NN, NW, D>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHistLds);
+  if (!lds_set) {
+    const size_t most = (size_t)NN * kHistBins * 4 + (WR ? (size_t)(1 + NW) * seq_area_bytes(16 * NH16) : 0);
+    const hipError_t e = hipFuncSetAttribute((const void *)score_decode_kernel<F, NH16, NN, NW, D, WR>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)most);
     if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "score_decode: hipFuncSetAttribute: %s", hipGetErrorString(e));
     lds_set = true;
   }
-  hipLaunchKernelGGL((score_decode_kernel<F, NH16, NN, NW, D>), dim3(n_units), dim3(NW * 64), row_hist ? kHistLds : 0,
-                     st, qp, qs, w, n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len,
-                     logits, ld, row_hist);
+  hipLaunchKernelGGL((score_decode_kernel<F, NH16, NN, NW, D, WR>), dim3(n_units), dim3(NW * 64), lds, st, qp, qs, w,
+                     n_heads, kvp, kvs, n_pages, bt, bt_ld, batch, n_units, sched, sched + 1, row_len, logits, ld,
+                     row_hist, Wr);
   return INDEXER_FP4_OK;
 }
 
@@ -283,6 +501,66 @@ extern "C" int indexer_fp4_score_decode(const uint8_t *q_packed, const uint8_t *
                                         uint32_t *row_hist, void *stream) {
   return score_decode<FmtFp4>(q_packed, q_scale, weights, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld,
                               batch, next_n, sched, sched_bytes, n_units, row_len, logits, logits_ld, row_hist, stream);
+}
+
+// Write and score in one launch (next_n = 1): the scorer quantizes its query rows itself and
+// writes each sequence's new key from the wave that scores the key's page, before loading it.
+extern "C" int indexer_fp4_write_and_score_decode(
+    const void *k_bf16, int64_t k_ld, const float *k_norm_weight, const float *k_norm_bias, float eps,
+    const int64_t *positions, const float *cos_sin, int64_t max_pos, int32_t rope_dim, int32_t rope_interleaved,
+    const int64_t *slot_mapping, const void *q_bf16, const float *weights, float weight_scale, int32_t all_q,
+    int32_t n_heads, uint8_t *kv_packed, uint8_t *kv_scale, int64_t n_pages, const int32_t *block_table, int64_t bt_ld,
+    int32_t batch, void *sched, int64_t sched_bytes, int32_t n_units, const int32_t *row_len, float *logits,
+    int64_t logits_ld, uint32_t *row_hist, void *stream) {
+  clear_error();
+  if (n_heads <= 0 || n_heads % INDEXER_FP4_HEAD_MULT != 0 || n_heads > 128)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: n_heads=%d must be a positive multiple of %d and at most 128",
+                n_heads, INDEXER_FP4_HEAD_MULT);
+  if (batch < 0 || n_units <= 0 || n_pages < 0)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: batch=%d >= 0, n_units=%d > 0, n_pages=%lld >= 0", batch,
+                n_units, (long long)n_pages);
+  if (rope_dim < 0 || rope_dim > kHeadDim || rope_dim % 16 != 0)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: rope_dim=%d must be a multiple of 16 in 0..%d", rope_dim,
+                kHeadDim);
+  if (!k_norm_weight && k_norm_bias)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: k_norm_bias without k_norm_weight");
+  if (!(eps >= 0.f)) return fail(INDEXER_FP4_EINVAL, "write_and_score: eps must be >= 0");
+  if (k_ld < kHeadDim || k_ld % 8 != 0)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: k_ld=%lld must be >= %d and a multiple of 8", (long long)k_ld,
+                kHeadDim);
+  if (bt_ld <= 0) return fail(INDEXER_FP4_ENOSPC, "write_and_score: bt_ld=%lld must be positive", (long long)bt_ld);
+  if (logits_ld < bt_ld * kPage)
+    return fail(INDEXER_FP4_ENOSPC, "write_and_score: logits_ld=%lld < 64*bt_ld=%lld", (long long)logits_ld,
+                (long long)(bt_ld * kPage));
+  if (!sched || !row_len ||
+      (batch > 0 && (!k_bf16 || !slot_mapping || !q_bf16 || !weights || !block_table || !logits || !kv_packed ||
+                     !kv_scale)))
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: a required pointer is NULL");
+  if (batch > 0 && rope_dim > 0 && (!positions || !cos_sin || max_pos <= 0))
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: rope_dim=%d needs positions and a cos/sin table", rope_dim);
+  if (((uintptr_t)k_bf16 | (uintptr_t)q_bf16 | (uintptr_t)kv_packed | (uintptr_t)kv_scale | (uintptr_t)cos_sin |
+       (uintptr_t)k_norm_weight | (uintptr_t)k_norm_bias | (uintptr_t)row_hist) % 16 != 0)
+    return fail(INDEXER_FP4_EINVAL, "write_and_score: k, q, both planes, cos_sin, k_norm_weight, k_norm_bias and "
+                                    "row_hist must be 16-byte aligned");
+  const int64_t need = 4 * DecodeSchedLayout(batch, n_units).words;
+  if (sched_bytes < need)
+    return fail(INDEXER_FP4_ENOSPC, "write_and_score: sched_bytes=%lld < %lld for batch=%d, n_units=%d",
+                (long long)sched_bytes, (long long)need, batch, n_units);
+  int rc = check_device();
+  if (rc) return rc;
+  if (batch == 0) return INDEXER_FP4_OK;
+  const StepWrite W{(const uint16_t *)k_bf16, k_ld, k_norm_weight, k_norm_bias, eps, positions, cos_sin, max_pos,
+                    rope_dim, rope_interleaved != 0, slot_mapping, (const uint16_t *)q_bf16, weights, weight_scale,
+                    all_q != 0, kv_packed, kv_scale};
+  hipStream_t st = (hipStream_t)stream;
+  int32_t *sc = (int32_t *)sched;
+  switch (n_heads / 16) {
+#define IFP4_CASE(X) \
+  case X: rc = launch_decode<FmtFp4, X, 1, true>(st, n_units, nullptr, nullptr, nullptr, n_heads, kv_packed, kv_scale, n_pages, block_table, bt_ld, batch, sc, row_len, logits, logits_ld, row_hist, W); break;
+    IFP4_CASE(1) IFP4_CASE(2) IFP4_CASE(3) IFP4_CASE(4) IFP4_CASE(5) IFP4_CASE(6) IFP4_CASE(7) IFP4_CASE(8)
+#undef IFP4_CASE
+  }
+  return rc ? rc : launch_status("write_and_score_decode");
 }
 
 // The FP8 comparator: the same scorer over MXFP8 queries and keys (128 bytes a vector).

@@ -40,7 +40,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(L, n), n
     import sparse_attention_indexer_fp4_amd as pkg_module  # noqa: F401  (binding loads too)
@@ -163,3 +163,22 @@ def test_host_argument_errors(L):
     assert call(k_ld=120) == -1 and "k_ld=120" in _err(L)
     assert call(q=P(16), heads=0) == -1 and "n_heads=0" in _err(L)
     assert call(n_tok=-1) == -1
+    L.indexer_fp4_write_and_score_decode.argtypes = [P, I64, P, P, F32, P, P, I64, I32, I32, P, P, P, F32, I32, I32,
+                                                     P, P, I64, P, I64, I32, P, I64, I32, P, P, I64, P, P]
+    ws_fn = L.indexer_fp4_write_and_score_decode
+
+    def ws_call(heads=64, rope_dim=0, k_ld=128, bias=None, weight=None, eps=1e-6, k=P(16), bt_ld=4, ld=256,
+                sched_bytes=1 << 20, batch=2, positions=None, cs=None, max_pos=0):
+        return ws_fn(k, k_ld, weight, bias, eps, positions, cs, max_pos, rope_dim, 0, P(16), P(16), P(16), 1.0, 0,
+                     heads, P(16), P(16), 8, P(16), bt_ld, batch, P(16), sched_bytes, 16, P(16), P(16), ld, None, None)
+    assert ws_call(heads=144) == -1 and "n_heads=144" in _err(L)
+    assert ws_call(heads=24) == -1
+    assert ws_call(rope_dim=24) == -1 and "rope_dim=24" in _err(L)
+    assert ws_call(rope_dim=64) == -1 and "cos/sin" in _err(L)
+    assert ws_call(bias=P(16)) == -1 and "bias" in _err(L)
+    assert ws_call(weight=P(16), eps=-1.0) == -1 and "eps" in _err(L)
+    assert ws_call(k_ld=120) == -1 and "k_ld=120" in _err(L)
+    assert ws_call(k=None) == -1 and "NULL" in _err(L)
+    assert ws_call(ld=200) == -2 and "logits_ld=200" in _err(L)
+    assert ws_call(sched_bytes=16) == -2 and "sched_bytes=16" in _err(L)
+    assert ws_call(k=P(8)) == -1 and "aligned" in _err(L)
