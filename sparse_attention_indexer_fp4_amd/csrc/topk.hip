@@ -42,6 +42,37 @@ __device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
   return v;
 }
 
+// Inclusive prefix sum over the lanes of a wave (lanes <= this one): DPP shifts within rows of
+// 16 lanes, then row broadcasts across rows (no LDS round trips).
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, into rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, into rows 2 and 3
+  return v;
+}
+
+// Inclusive prefix sum of v over the workgroup's threads (threads <= tid); *total gets the
+// sum over all of them. s_w (one word a wave) must not be reused before another barrier.
+template <int NT>
+__device__ __forceinline__ int block_prefix_sum(int v, int *s_w, int &total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  v = wave_prefix_sum(v);
+  if (lane == 63) s_w[wv] = v;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NT / 64; w2++) {
+    const int x = s_w[w2];
+    before += w2 < wv ? x : 0;
+    total += x;
+  }
+  return v + before;
+}
+
 // Histogram increment of digit d (for lanes with `active`). Keys of one row cluster in a
 // few digits, so plain LDS atomics from a wave would mostly hit one address and serialize;
 // the two most common digits of the wave are added once each by a leader lane.
@@ -224,7 +255,9 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
       c[i] = hist[kPer * tid + i];
       sum += (int)c[i];
     }
-    int acc = block_suffix_sum<kShortThreads>(sum, s_scan);
+    int tot;
+    const int incl = block_prefix_sum<kShortThreads>(sum, s_scan, tot);
+    int acc = tot - incl + sum;  // keys in bins >= kPer*tid
 #pragma unroll
     for (int i = 0; i < kPer; i++) {
       if (acc >= k && acc - (int)c[i] < k) {
@@ -405,37 +438,6 @@ struct LongWs {
 __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
   const int64_t len = row_len[r];
   return len < 0 ? 0 : (len > max_len ? max_len : len);
-}
-
-// Inclusive prefix sum over the lanes of a wave (lanes <= this one): DPP shifts within rows of
-// 16 lanes, then row broadcasts across rows (no LDS round trips).
-__device__ __forceinline__ int wave_prefix_sum(int v) {
-  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
-  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, into rows 1 and 3
-  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, into rows 2 and 3
-  return v;
-}
-
-// Inclusive prefix sum of v over the workgroup's threads (threads <= tid); *total gets the
-// sum over all of them. s_w (one word a wave) must not be reused before another barrier.
-template <int NT>
-__device__ __forceinline__ int block_prefix_sum(int v, int *s_w, int &total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  v = wave_prefix_sum(v);
-  if (lane == 63) s_w[wv] = v;
-  __syncthreads();
-  int before = 0;
-  total = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < NT / 64; w2++) {
-    const int x = s_w[w2];
-    before += w2 < wv ? x : 0;
-    total += x;
-  }
-  return v + before;
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
