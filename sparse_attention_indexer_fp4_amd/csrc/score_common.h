@@ -97,6 +97,22 @@ __device__ __forceinline__ void load_page_cached(PageRegs &P, const uint8_t *__r
 // canonicalization as an IEEE float max would need).
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Cross-lane sum of a page's per-tile partial sums: lane 16G + j holds acc[t] = its head
+// group G's part of key 16t + j's logit; afterwards lane 16G + j holds key 16G + j's full sum.
+// gfx950's lane-swap moves do it in VALU (no LDS round trip): a 32-lane swap of acc[0] with
+// acc[2] leaves every lane its own and its partner's (lane ^ 32) sum of the tile it keeps
+// (0 or 1 in the low half, 2 or 3 in the high half), likewise acc[1] with acc[3]; a 16-lane
+// swap of the two results then pairs lane groups G and G ^ 1. Each addition adds a lane's own
+// term and its partner's, so the result is the same whichever operand the swap returns first.
+__device__ __forceinline__ float reduce_tiles(const float (&acc)[4]) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]), __float_as_uint(acc[2]), false, false);
+  const float kx = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[1]), __float_as_uint(acc[3]), false, false);
+  const float ky = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+  const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(kx), __float_as_uint(ky), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
 // Logit of key `lane` of the page for row n: sum over heads of w * ReLU(q . k).
 // With DB the MFMAs of key tile t+1 are issued into a second set of accumulators before the
 // ReLU/weight epilogue of tile t, so the matrix unit works while the VALU reduces; without
@@ -141,15 +157,7 @@ __device__ __forceinline__ float page_logit(const PageRegs &P, const RowRegs<NH1
   }
   // lanes 16G..16G+15 hold, for every tile, partial sums over their heads; reduce across
   // the four lane groups so that lane 16G+j ends with tile G's full sum for key j
-  const int G = lane >> 4;
-  const bool lo = G < 2;
-  float kx = lo ? acc[0] : acc[2];
-  float ky = lo ? acc[1] : acc[3];
-  kx += __shfl_xor(lo ? acc[2] : acc[0], 32, 64);
-  ky += __shfl_xor(lo ? acc[3] : acc[1], 32, 64);
-  const bool odd = G & 1;
-  const float keep = odd ? ky : kx;
-  return keep + __shfl_xor(odd ? kx : ky, 16, 64);
+  return reduce_tiles(acc);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -248,15 +256,7 @@ __device__ __forceinline__ float page_logit8(const PageRegs8 &P, const RowRegs8<
     if constexpr (T + 1 < 4) mfmas(std::integral_constant<int, T + 1>{});
     epilogue(tt);
   });
-  const int G = lane >> 4;
-  const bool lo = G < 2;
-  float kx = lo ? acc[0] : acc[2];
-  float ky = lo ? acc[1] : acc[3];
-  kx += __shfl_xor(lo ? acc[2] : acc[0], 32, 64);
-  ky += __shfl_xor(lo ? acc[3] : acc[1], 32, 64);
-  const bool odd = G & 1;
-  const float keep = odd ? ky : kx;
-  return keep + __shfl_xor(odd ? kx : ky, 16, 64);
+  return reduce_tiles(acc);
 }
 
 // Element-format policies of the decode scorer.

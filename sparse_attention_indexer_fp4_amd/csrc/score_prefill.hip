@@ -19,7 +19,9 @@
 //     is fetched once per CU;
 //   - each wave keeps D pages in flight in a register ring and runs on its own: no LDS, no
 //     barrier, so the waves of a SIMD drift apart and one's MFMAs run while another reduces;
-//   - the two rows share the page registers, and their MFMAs and epilogues interleave.
+//   - the two rows share the page registers, and their MFMAs and epilogues interleave;
+//   - an item's logits are stored after its slot's refill is issued, so waiting for a page
+//     never waits for a store's completion.
 // The unit's first items come from its start record (one scalar load), so the first pages are
 // in flight after a single round trip; the pages of later items come from the schedule's item
 // table by scalar loads issued D items ahead. Each wave's two query rows sit in registers and
@@ -96,9 +98,11 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
   // the ring: pages in registers, the unit-relative item each slot holds
   PageRegs P[D];
   int sitem[D];
+  bool sok[D];  // the slot's page was resolved (an unresolved item stores nothing)
   auto issue = [&](auto kk, int i, int phys) {
     constexpr int K = decltype(kk)::value;
     sitem[K] = i;
+    sok[K] = phys >= 0;
     load_page_cached(P[K], kvp, kvs, phys >= 0 ? phys : 0, lane);  // page 0 exists; an unreadable page is not scored
   };
   int sphys[D];  // pages of the next refill of each slot, loaded one round ahead
@@ -135,6 +139,12 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
     T.item0 = rt[6];
   };
 
+  // the last scored item's logits, stored after the slot's refill is issued: the refill's
+  // loads then sit behind the stores in the memory counter, and the wait for the next slot's
+  // page never includes a store's completion
+  float s_v[RPW];
+  __amdgpu_buffer_rsrc_t s_dst[RPW];
+  uint32_t s_off = 0;
   auto score = [&](auto kk) __attribute__((always_inline)) {
     constexpr int K = decltype(kk)::value;
     const int i = sitem[K];
@@ -145,34 +155,24 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
     }
     const int p = it0 + min(i, n_my - 1) - T.item0;  // the item's page within its tile
     // an item past the unit's last, or whose page the schedule could not resolve, stores nothing
-    const bool ok = i < n_my && item_phys[min(i, n_my - 1)] >= 0;
+    const bool ok = i < n_my && sok[K];
     float v[RPW];
     static_for<RPW>([&](auto jj) { v[decltype(jj)::value] = page_logit<NH16, RPW, decltype(jj)::value, true>(P[K], R, lane); });
-    const uint32_t off = 4u * (uint32_t)(p * kPage + lane);
+    s_off = 4u * (uint32_t)(p * kPage + lane);
     static_for<RPW>([&](auto jj) {
       constexpr int J = decltype(jj)::value;
       const uint32_t bytes = ok ? 4u * (uint32_t)max(len[J], 0) : 0u;
-      const __amdgpu_buffer_rsrc_t dst = buffer_view(logits + (int64_t)row[J] * ld, bytes);
-      if constexpr (ADD) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v[J], dst, (int)off, 0, 0);
-      else buffer_store_f32(v[J], dst, off);
+      s_dst[J] = buffer_view(logits + (int64_t)row[J] * ld, bytes);
+      s_v[J] = v[J];
     });
   };
-
-  // Progress balance: the two waves of a SIMD (w and w + 4) score the same items for different
-  // rows, and the hardware issues the older wave first, so one would finish long before the
-  // other and leave its SIMD to a single wave. Each wave publishes how many items it has
-  // scored and takes a higher priority while it is behind its partner.
-  __shared__ int s_done[kPrefillWaves];
-  int done = 0;
-  auto balance = [&]() __attribute__((always_inline)) {
-    s_done[wv] = done;
-    const int other = s_done[wv ^ 4];
-    if (done < other) __builtin_amdgcn_s_setprio(2);
-    else if (done == other) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
+  auto store = [&]() __attribute__((always_inline)) {
+    static_for<RPW>([&](auto jj) {
+      constexpr int J = decltype(jj)::value;
+      if constexpr (ADD) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s_v[J], s_dst[J], (int)s_off, 0, 0);
+      else buffer_store_f32(s_v[J], s_dst[J], s_off);
+    });
   };
-  if (lane == 0) s_done[wv] = 0;
-  __syncthreads();
 
   // the first D pages from the start record, then the query rows (their wait also covers the
   // pages), then the loop: score slot K, refill it D items ahead
@@ -186,10 +186,9 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
     static_for<D>([&](auto kk) {
       constexpr int K = decltype(kk)::value;
       score(kk);
-      done++;
-      balance();
       const int nxt = i0 + K + D;
       issue(kk, nxt, sphys[K]);
+      store();
       sphys[K] = next_phys(nxt + D);
     });
   }
