@@ -11,9 +11,9 @@
 // all keys of the row share are skipped), then every key above T is kept together with
 // the lowest-column keys equal to T, and the columns are written in ascending order.
 //
-// Rows up to 16384 keys: one workgroup per row (512 threads in launches of up to 2047
-// rows, 256 in larger ones) with the row's keys held in LDS. Longer rows: the chunked path
-// further below. Every loop that reads global memory
+// Rows up to 6144 keys: one workgroup per row with the row's keys in registers; up to 16384
+// keys: one workgroup per row with the row's keys held in LDS (512 threads in launches of up
+// to 2047 rows, 256 in larger ones). Longer rows: the chunked path further below. Every loop that reads global memory
 // issues all of a thread's loads before it uses them, so a pass costs one memory latency
 // rather than one per element.
 #include <mutex>
@@ -377,6 +377,230 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
     const int pos = out_base + (int)lanes_below(tk);
     if (t && pos < k) o[pos] = j;  // exactly k are taken; the bound is insurance
     out_base += __popcll(tk);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Rows up to kRegMax keys (prefill chunks of a few thousand keys a row, short decode rows):
+// the row's keys stay in registers, so a workgroup holds no LDS copy of them and every row
+// of a 2048-row launch is resident at once. The row is cut into one contiguous column range
+// per wave (a multiple of 64 columns, the last ones possibly empty); lane l of wave w holds
+// the columns c_w + 64 u + l. The exact k-th largest key T comes first: a 1024-bin
+// histogram spread linearly over the row's [min, max], then, while the bin that holds T has
+// more than kShortRank keys, histograms of the next 10 bits of key - min over that bin's
+// keys, and finally the bin's keys ranked by counting (or nothing more when a bin is one
+// value). Each wave then counts its keys above and equal to T, and one walk in column order
+// writes every key above T and the lowest-column keys equal to T.
+constexpr int64_t kRegMax = 6144;
+// Launches of up to kRegWideRows rows take 512-thread workgroups (a row's passes spread over
+// 8 waves), larger ones 256 threads: either way every workgroup of a launch up to 2048 rows
+// is resident at once on 256 CUs (32 waves a CU).
+constexpr int kRegWideRows = 1024;
+
+template <int NT, int R>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void topk_reg_kernel(
+    const float *__restrict__ logits, int64_t ld, const int32_t *__restrict__ row_len, int64_t max_len, int k,
+    uint32_t *__restrict__ row_hist, int32_t *__restrict__ out, int64_t out_ld) {
+  constexpr int NW = NT / 64;
+  static_assert(NW * 64 * R == kRegMax, "the launch shapes cover kRegMax keys");
+  __shared__ uint32_t hist[kShortBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lst[NW * kShortRank];  // per-wave candidate keys
+  __shared__ int s_scan[NW], s_nb[NW], s_gt[NW], s_eq[NW], s_misc[4];
+  __shared__ uint32_t s_mm[2 * NW];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t len64 = row_len[r];
+  len64 = len64 < 0 ? 0 : (len64 > max_len ? max_len : len64);
+  const int n = (int)len64;
+  int32_t *o = out + r * out_ld;
+  if (row_hist)  // not used for rows this short: left zero for the next scorer call
+    for (int i = tid; i < kHistBins; i += NT) row_hist[r * kHistBins + i] = 0u;
+  if (n <= k) {  // every key is kept
+    for (int j = tid; j < k; j += NT) o[j] = j < n ? j : -1;
+    return;
+  }
+  // this wave's columns [c0, c1) in ns slots of 64 (wave-uniform); all loads in one round
+  const int chunk = ((n + NW - 1) / NW + 63) & ~63;
+  const int c0 = min(n, wv * chunk), c1 = min(n, c0 + chunk);
+  const int ns = (c1 - c0 + 63) >> 6;
+  const __amdgpu_buffer_rsrc_t src = buffer_view(const_cast<float *>(logits + r * ld), 4u * (uint32_t)n);
+  uint32_t key[R];
+#pragma unroll
+  for (int u = 0; u < R; u++)
+    key[u] = u < ns ? __builtin_amdgcn_raw_buffer_load_b32(src, 4 * (c0 + 64 * u + lane), 0, 0) : 0u;
+  for (int i = tid; i < kShortBins; i += NT) hist[i] = 0u;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  const int lim = c1 - c0 - lane;  // the lane's slot u holds a column iff 64 u < lim
+#pragma unroll
+  for (int u = 0; u < R; u++) {
+    if (u < ns) {
+      const bool ok = 64 * u < lim;
+      const uint32_t kk = order_key(__uint_as_float(key[u]));
+      key[u] = ok ? kk : 0u;
+      kmax = max(kmax, key[u]);
+      kmin = min(kmin, ok ? kk : 0xFFFFFFFFu);
+    }
+  }
+  block_minmax<NT>(kmin, kmax, s_mm);  // its barriers also publish the cleared histogram
+  // From here on a key is held as key - kmin, and a lane of the last slot past the row's end
+  // as 0, the row's smallest value: it sorts below or ties with every key of the row and
+  // comes after all of them in column order, so it is never among the k kept (the
+  // lowest-column keys win ties) and needs no mask below. Slots u >= ns hold nothing and are
+  // skipped.
+#pragma unroll
+  for (int u = 0; u < R; u++) key[u] = max(key[u], kmin) - kmin;
+  // the bin of the want-th largest counted key: s_misc[0] bin, [1] keys in higher bins, [2] in it
+  auto find_bin = [&](int want) __attribute__((always_inline)) {
+    constexpr int kPer = kShortBins / NT;
+    uint32_t c[kPer];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      c[i] = hist[kPer * tid + i];
+      sum += (int)c[i];
+    }
+    int tot;
+    const int incl = block_prefix_sum<NT>(sum, s_scan, tot);
+    int acc = tot - incl + sum;  // keys in bins >= kPer * tid
+#pragma unroll
+    for (int i = 0; i < kPer; i++) {
+      if (acc >= want && acc - (int)c[i] < want) {
+        s_misc[0] = kPer * tid + i;
+        s_misc[1] = acc - (int)c[i];
+        s_misc[2] = (int)c[i];
+      }
+      acc -= (int)c[i];
+    }
+    __syncthreads();
+  };
+  // level 0: bins over the whole range (key - kmin < 2^bl)
+  const int bl = 32 - __clz((int)(kmax - kmin));
+  int sh = bl > 10 ? bl - 10 : 0;
+#pragma unroll
+  for (int u = 0; u < R; u++)
+    if (u < ns) atomicAdd(&hist[key[u] >> sh], 1u);
+  __syncthreads();
+  find_bin(k);
+  uint32_t pre = (uint32_t)s_misc[0] << sh;  // bits of T - kmin under pmask
+  uint32_t pmask = top_bits_mask(32 - sh);
+  int need = k - s_misc[1], nb = s_misc[2];  // keys of the bin still to take; keys in it
+  // further levels while the bin is crowded
+  while (nb > kShortRank && sh > 0) {
+    const int s2 = sh > 10 ? sh - 10 : 0;
+    const uint32_t dm = (1u << (sh - s2)) - 1u;
+    __syncthreads();  // every thread has read s_misc and the histogram of the last level
+    for (int i = tid; i < kShortBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < R; u++)
+      if (u < ns) hist_put(hist, (key[u] >> s2) & dm, (key[u] & pmask) == pre);
+    __syncthreads();
+    find_bin(need);
+    pre |= (uint32_t)s_misc[0] << s2;
+    pmask |= dm << s2;
+    need -= s_misc[1];
+    nb = s_misc[2];
+    sh = s2;
+  }
+  uint32_t T;  // T - kmin
+  if (sh == 0) {
+    T = pre;  // the bin is one value
+  } else {
+    // rank the bin's keys by counting: the need-th largest of them is T
+    int cnt = 0;
+    uint32_t *wl = lst + wv * kShortRank;
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      if (u < ns) {
+        const bool in = (key[u] & pmask) == pre;
+        const uint64_t m = __ballot(in);
+        if (in) wl[cnt + (int)lanes_below(m)] = key[u];
+        cnt += __popcll(m);
+      }
+    }
+    if (lane == 0) s_nb[wv] = cnt;
+    __syncthreads();
+    if (tid < nb) {
+      int w = 0, t = tid;
+      while (w < NW - 1 && t >= s_nb[w]) t -= s_nb[w++];
+      const uint32_t mine = lst[w * kShortRank + t];
+      int g = 0, e = 0;
+      for (int w2 = 0; w2 < NW; w2++) {
+        const int m2 = s_nb[w2];
+        const uint4 *k4 = reinterpret_cast<const uint4 *>(lst + w2 * kShortRank);
+        for (int q = 0; q < m2; q += 4) {  // four entries a read; those past m2 are not counted
+          const uint4 kq = k4[q / 4];
+          const uint32_t kv[4] = {kq.x, kq.y, kq.z, kq.w};
+#pragma unroll
+          for (int x = 0; x < 4; x++) {
+            g += (q + x < m2 && kv[x] > mine) ? 1 : 0;
+            e += (q + x < m2 && kv[x] == mine) ? 1 : 0;
+          }
+        }
+      }
+      if (g < need && g + e >= need) s_misc[3] = (int)mine;  // every such thread holds T
+    }
+    __syncthreads();
+    T = (uint32_t)s_misc[3];
+  }
+  // keys above and equal to T, per wave
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < R; u++) {
+    if (u < ns) {
+      gt += __popcll(__ballot(key[u] > T));
+      eq += __popcll(__ballot(key[u] == T));
+    }
+  }
+  if (lane == 0) {
+    s_gt[wv] = gt;
+    s_eq[wv] = eq;
+  }
+  __syncthreads();
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NW; w2++) {
+    n_gt += s_gt[w2];
+    n_eq += s_eq[w2];
+  }
+  const int need_t = k - n_gt;  // keys equal to T kept, those of the lowest columns
+  int out_base = 0, eq_run = 0;
+  for (int w2 = 0; w2 < wv; w2++) {
+    out_base += s_gt[w2] + min(max(need_t - eq_run, 0), s_eq[w2]);
+    eq_run += s_eq[w2];
+  }
+  // the lane's first column, recomputed here: held from the start, the compiler would keep
+  // every column index of the walk in its own register all along
+  int j0 = c0 + lane;
+  asm volatile("" : "+v"(j0));
+  // stores through a view of the row's k outputs: a lane that keeps nothing stores past it
+  // and is dropped, so the walk has no branches on lanes (exactly k keys are kept)
+  const __amdgpu_buffer_rsrc_t dst = buffer_view(o, 4u * (uint32_t)k);
+  if (n_eq == need_t) {  // every key equal to T is kept (T is usually one key)
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      if (u < ns) {
+        const bool keep = key[u] >= T;
+        const uint64_t km = __ballot(keep);
+        const uint32_t off = keep ? 4u * (uint32_t)(out_base + (int)lanes_below(km)) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(j0 + 64 * u), dst, (int)off, 0, 0);
+        out_base += __popcll(km);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < R; u++) {
+      if (u < ns) {
+        const bool is_eq = key[u] == T;
+        const uint64_t em = __ballot(is_eq);
+        const bool keep = key[u] > T || (is_eq && eq_run + (int)lanes_below(em) < need_t);
+        const uint64_t km = __ballot(keep);
+        const uint32_t off = keep ? 4u * (uint32_t)(out_base + (int)lanes_below(km)) : 0xFFFFFFF0u;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(j0 + 64 * u), dst, (int)off, 0, 0);
+        out_base += __popcll(km);
+        eq_run += __popcll(em);
+      }
+    }
   }
 }
 
@@ -1124,6 +1348,15 @@ static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, con
                               (int)(4 * kShortMax));
     if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk: hipFuncSetAttribute: %s", hipGetErrorString(e));
     lds_set = true;
+  }
+  if (max_len <= kRegMax) {
+    if (n_rows <= kRegWideRows)
+      hipLaunchKernelGGL((topk_reg_kernel<512, 12>), dim3(n_rows), dim3(512), 0, st, logits, logits_ld, row_len,
+                         max_len, k, row_hist, topk_idx, topk_ld);
+    else
+      hipLaunchKernelGGL((topk_reg_kernel<256, 24>), dim3(n_rows), dim3(256), 0, st, logits, logits_ld, row_len,
+                         max_len, k, row_hist, topk_idx, topk_ld);
+    return launch_status("topk");
   }
   if (!use_long_path(max_len, k)) {
     // rows of at most kShortMax keys, or k >= max_len (every row keeps all its keys and

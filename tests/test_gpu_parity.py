@@ -226,15 +226,19 @@ def test_topk_ties_and_signed_zero(ifp4):
         assert (got[r][m:] == -1).all()
 
 
+@pytest.mark.parametrize("max_len", [16384, 6144])
 @pytest.mark.parametrize("tile", [1, 150])
 @pytest.mark.parametrize("k", [1, 16, 64, 2048])
-def test_topk_short_rows_exact(ifp4, k, tile):
+def test_topk_short_rows_exact(ifp4, k, tile, max_len):
     """Short-row selection on ragged lengths around the per-wave column ranges (64-column
     steps, ranges clamped to the row, some empty) equals the oracle's full sort exactly; 14
-    rows run on 512-thread workgroups, 2100 rows on 256-thread ones."""
+    rows run on 512-thread workgroups, 2100 rows on 256-thread ones. Rows of at most 6144
+    keys (max_len 6144) take the register-resident kernel, longer ones the LDS one."""
     rng = np.random.default_rng(11 + k)
-    lens = np.tile(np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 2049, 2050, 4097, 8191, 16384], np.int32),
-                   tile)
+    base = np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 2049, 2050, 4097, 8191, 16384], np.int32)
+    if max_len == 6144:
+        base = np.array([65, 70, 100, 129, 191, 255, 256, 257, 1000, 1535, 1537, 2049, 4097, 6144], np.int32)
+    lens = np.tile(base, tile)
     n = int(lens.max())
     lg = (rng.standard_normal((len(lens), n)) * 40 + 100).astype(np.float32)
     lg[3, :50] = lg[3, 60]  # a tie block inside the first range
@@ -530,6 +534,29 @@ def test_topk_long_row_at_the_length_limit(ifp4):
     lg = rng.standard_normal((2, n)).astype(np.float32)
     lg[1] = np.repeat(rng.standard_normal(n // 1024).astype(np.float32), 1024)  # blocks of ties
     _topk_exact(ifp4, lg, np.array([n, n - 1], np.int32), k, n)
+
+
+@pytest.mark.parametrize("n,k", [(6144, 2048), (4213, 2048), (16000, 2048)])
+def test_topk_crowded_threshold_bin(ifp4, n, k):
+    """Rows whose k-th key sits in a crowded bin of the first histogram: thousands of keys in a
+    tiny band (further 10-bit levels, then ranking), the band made of a few exact values
+    (levels down to one value), exact ties straddling the cut across waves, and the k-th key
+    equal to the row's minimum."""
+    rng = np.random.default_rng(n + 7)
+    rows = 6
+    lg = (rng.standard_normal((rows, n)) * 30.0).astype(np.float32)
+    band = rng.permutation(n)[:3000]
+    lg[0, band] = 7.5 + 1e-4 * rng.random(3000)
+    lg[1, band] = 7.5 + 1e-6 * rng.integers(0, 5, 3000)
+    lg[2, :] = -1.0
+    lg[2, rng.permutation(n)[:k // 2]] = 2.0   # the cut falls inside the ties at -1
+    lg[3] = np.abs(lg[3]) + 1.0
+    lg[3, rng.permutation(n)[:n - k + 10]] = 1.0  # the k-th key is the row minimum, tied
+    lg[4, band] = np.float32(2.0 ** -126)       # a band near the smallest normal
+    lg[5] = np.where(rng.random(n) < 0.5, 0.0, -0.0)
+    rl = np.array([n, n - 1, n, n - 63, n - 64 * 7, n], np.int32)
+    _topk_exact(ifp4, lg, rl, k, n)
+    _topk_exact(ifp4, lg[::-1].copy(), rl, k, n)
 
 
 @pytest.mark.parametrize("n,k", [(3000, 64), (16000, 2048), (131072, 2048)])
