@@ -67,12 +67,13 @@ def decode_write_score_bytes(n_keys: int, n_pages: int, rows: int, heads: int) -
             rows * (heads * 256 + heads * 4 + 4 + 256 + 8 + 8 + 4 * ROPE_DIM + 68))
 
 
-def build_decode(torch, ifp4, W, layers, units, seed, fp8=False, workload="decode_b8_128k"):
-    """The layers of a decode workload of equal contexts; with fp8, every layer also gets
-    MXFP8 planes of the same keys and queries (the FP8 comparator)."""
+def build_decode(torch, ifp4, W, layers, units, seed, fp8=False, workload="decode_b8_128k", contexts=None):
+    """The layers of a decode workload of equal contexts (the named workload's, or `contexts`
+    with its heads and top-k); with fp8, every layer also gets MXFP8 planes of the same keys
+    and queries (the FP8 comparator)."""
     dev = torch.device("cuda:0")
     case_ctx = W.DECODE_CONFIGS[workload]
-    ctx = np.array(case_ctx["ctx"], np.int32)
+    ctx = np.array(case_ctx["ctx"] if contexts is None else contexts, np.int32)
     H, k = case_ctx["heads"], case_ctx["topk"]
     B = ctx.shape[0]
     rng = np.random.default_rng(seed)
@@ -292,6 +293,48 @@ def bench_decode_sweep(torch, ifp4, W, args, layers=8):
     return out
 
 
+SIZE_CONTEXTS = (32768, 65536, 131072, 262144)  # 8 rows each: 2^18 .. 2^21 keys a launch
+
+
+def bench_scorer_sizes(torch, ifp4, W, args, layers=21):
+    """The decode scorer alone at 2^18, 2^19, 2^20 and 2^21 keys a launch (8 rows of 32768 to
+    262144 keys, 64 heads, 21 layer caches so every launch streams from HBM), with and without
+    the top-k's first-digit histogram. A least-squares line of time against keys splits a
+    launch into its fixed part and its per-key part."""
+    rows = []
+    for c in SIZE_CONTEXTS:
+        L, S, meta = build_decode(torch, ifp4, W, layers, args.units, args.seed, contexts=[c] * 8)
+        for _ in range(max(1, args.warmup)):
+            decode_step(ifp4, L, S, meta)
+        torch.cuda.synchronize()
+        row = {"keys": meta["n_keys"], "context": c, "alg_bytes_per_launch": scoring_bytes(meta)}
+        for hist in (True, False):
+            def scorers():
+                for lay in L:
+                    ifp4.indexer_fp4_score_decode(lay["qp"], lay["qs"], lay["wm"], lay["kp"], lay["ks"], S["bt"], 1,
+                                                  S["sched"], meta["units"], S["row_len"], S["logits"],
+                                                  S["hist_scorer"] if hist else None)
+            g = capture(torch, scorers)
+            g.replay()
+            us = 1e3 * timed_replays(torch, g, args.steps) / layers
+            row["us_hist" if hist else "us_plain"] = round(us, 3)
+            del g
+        row["frac_hist"] = round(row["alg_bytes_per_launch"] / (row["us_hist"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+        rows.append(row)
+        print(f"bench: scorer at {row['keys']} keys: {row['us_hist']:.2f} us with the histogram, "
+              f"{row['us_plain']:.2f} us without", file=sys.stderr, flush=True)
+        del L, S
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    fit = {}
+    x = np.array([r["keys"] for r in rows], np.float64)
+    for key in ("us_hist", "us_plain"):
+        y = np.array([r[key] for r in rows], np.float64)
+        slope, icpt = np.polyfit(x, y, 1)
+        fit[key] = {"fixed_us": round(float(icpt), 3), "us_per_2e20_keys": round(float(slope) * 2 ** 20, 3)}
+    return {"rows": 8, "heads": 64, "layers": layers, "sizes": rows, "fit": fit}
+
+
 def bench_decode_latency(torch, ifp4, W, args, layers=21):
     """Batch 1 at context 4096 (64 heads, top-2048): a latency-bound step. Whole steps
     (schedule, then per layer fused write + score + top-k) and the scorer alone, per layer, at
@@ -505,6 +548,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
     ap.add_argument("--no-sweep", action="store_true", help="skip the long decode workloads")
     ap.add_argument("--no-latency", action="store_true", help="skip the batch-1, 4096-context decode leg")
+    ap.add_argument("--scorer-sizes", action="store_true",
+                    help="also time the decode scorer alone at 2^18 .. 2^21 keys a launch (fixed and per-key parts)")
     ap.add_argument("--fused-write", action="store_true",
                     help="decode steps run the writer's work inside the scorer (one launch a layer)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -550,6 +595,13 @@ def main():
         print(f"bench: decode_b1_4k {lat['units_512']['us_per_layer']:.2f} / {lat['units_4096']['us_per_layer']:.2f} "
               f"us/layer at 512 / 4096 units, scorer {lat['units_512']['scorer_us']:.2f} / "
               f"{lat['units_4096']['scorer_us']:.2f} us", file=sys.stderr, flush=True)
+    sizes = None
+    if args.scorer_sizes:
+        sizes = bench_scorer_sizes(torch, ifp4, W, args)
+        f = sizes["fit"]
+        print(f"bench: scorer fit: {f['us_hist']['fixed_us']:.2f} us fixed + {f['us_hist']['us_per_2e20_keys']:.2f} us "
+              f"per 2^20 keys with the histogram, {f['us_plain']['fixed_us']:.2f} + "
+              f"{f['us_plain']['us_per_2e20_keys']:.2f} without", file=sys.stderr, flush=True)
     dcp = bench_dcp_merge(torch, ifp4, args)
     fp8 = None
     if not args.no_fp8:
@@ -602,6 +654,7 @@ def main():
         "writer": d["writer"],
         "decode_latency": lat,
         "decode_long": sweep,
+        "scorer_sizes": sizes,
         "prefill": pre,
         "dcp_merge": dcp,
         "fp8_comparator": fp8,
