@@ -502,22 +502,27 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
     nb = s_misc[2];
     sh = s2;
   }
+  // One pass over the slots: per wave, the keys in bins above T's and the keys of T's bin,
+  // the latter listed when they still have to be ranked.
+  int gt = 0, cnt = 0;
+  uint32_t *wl = lst + wv * kShortRank;
+#pragma unroll
+  for (int u = 0; u < R; u++) {
+    if (u < ns) {
+      const uint32_t hi = key[u] & pmask;
+      gt += __popcll(__ballot(hi > pre));
+      const uint64_t m = __ballot(hi == pre);
+      if (sh > 0 && m != 0 && hi == pre) wl[cnt + (int)lanes_below(m)] = key[u];
+      cnt += __popcll(m);
+    }
+  }
   uint32_t T;  // T - kmin
+  int eq;      // this wave's keys equal to T
   if (sh == 0) {
     T = pre;  // the bin is one value
+    eq = cnt;
   } else {
     // rank the bin's keys by counting: the need-th largest of them is T
-    int cnt = 0;
-    uint32_t *wl = lst + wv * kShortRank;
-#pragma unroll
-    for (int u = 0; u < R; u++) {
-      if (u < ns) {
-        const bool in = (key[u] & pmask) == pre;
-        const uint64_t m = __ballot(in);
-        if (in) wl[cnt + (int)lanes_below(m)] = key[u];
-        cnt += __popcll(m);
-      }
-    }
     if (lane == 0) s_nb[wv] = cnt;
     __syncthreads();
     if (tid < nb) {
@@ -542,14 +547,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
     }
     __syncthreads();
     T = (uint32_t)s_misc[3];
-  }
-  // keys above and equal to T, per wave
-  int gt = 0, eq = 0;
-#pragma unroll
-  for (int u = 0; u < R; u++) {
-    if (u < ns) {
-      gt += __popcll(__ballot(key[u] > T));
-      eq += __popcll(__ballot(key[u] == T));
+    // the wave's own listed keys above and equal to T
+    eq = 0;
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+      const bool ok = i0 + lane < cnt;
+      const uint32_t x = ok ? wl[i0 + lane] : 0u;
+      gt += __popcll(__ballot(ok && x > T));
+      eq += __popcll(__ballot(ok && x == T));
     }
   }
   if (lane == 0) {
