@@ -335,6 +335,51 @@ def bench_scorer_sizes(torch, ifp4, W, args, layers=21):
     return {"rows": 8, "heads": 64, "layers": layers, "sizes": rows, "fit": fit}
 
 
+PROBE_MODES = ("two MFMA waves a SIMD", "two VALU waves a SIMD", "one MFMA and one VALU wave a SIMD",
+               "two waves a SIMD doing both", "one MFMA wave a SIMD", "one VALU wave a SIMD")
+
+
+def mfma_valu_probe(torch, iters=4096, blocks=256):
+    """The scorers' instruction mix alone (libindexer_fp4_probe.so, one 8-wave workgroup per CU):
+    per mode the launch time and the shader clocks per iteration of the MFMA role (waves 0-3)
+    and the other role (waves 4-7). An iteration is 16 FP4 MFMAs 16x16x128 and/or the page
+    epilogue's 128 VALU operations."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "libindexer_fp4_probe.so"))
+    lib.indexer_fp4_probe_mfma_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.indexer_fp4_probe_mfma_valu.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    g = torch.Generator().manual_seed(5)
+    inp = torch.randint(0, 2 ** 31 - 1, (4096,), generator=g, dtype=torch.int32).to(dev)
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(blocks * 16, dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = []
+    for mode, name in enumerate(PROBE_MODES):
+        for rep in range(2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            rc = lib.indexer_fp4_probe_mfma_valu(mode, iters, blocks, inp.data_ptr(), out.data_ptr(), cyc.data_ptr(),
+                                                 stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"mfma/valu probe mode {mode}: error {rc}")
+        c = cyc.view(blocks, 8, 2).cpu().numpy().astype(np.float64)
+        clk = c[:, :, 0] / iters
+        wall_us = c[:, :, 1] / 100.0  # 100 MHz
+        mhz = float(np.median(c[:, :4, 0] / (c[:, :4, 1] * 10.0)) * 1e3)
+        res.append({"mode": mode, "waves": name, "launch_us": round(e0.elapsed_time(e1) * 1e3, 1),
+                    "clk_per_iter_waves_0_3": round(float(clk[:, :4].mean()), 1),
+                    "clk_per_iter_waves_4_7": round(float(clk[:, 4:].mean()), 1),
+                    "wave_us_0_3": round(float(wall_us[:, :4].mean()), 1),
+                    "wave_us_4_7": round(float(wall_us[:, 4:].mean()), 1), "clock_mhz": round(mhz)})
+        print(f"bench: probe mode {mode} ({name}): {res[-1]['launch_us']} us, clk/iter {res[-1]['clk_per_iter_waves_0_3']}"
+              f" / {res[-1]['clk_per_iter_waves_4_7']}, {res[-1]['clock_mhz']} MHz", file=sys.stderr, flush=True)
+    return {"iters": iters, "blocks": blocks, "modes": res}
+
+
 def bench_decode_latency(torch, ifp4, W, args, layers=21):
     """Batch 1 at context 4096 (64 heads, top-2048): a latency-bound step. Whole steps
     (schedule, then per layer fused write + score + top-k) and the scorer alone, per layer, at
@@ -548,6 +593,8 @@ def main():
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 comparator")
     ap.add_argument("--no-sweep", action="store_true", help="skip the long decode workloads")
     ap.add_argument("--no-latency", action="store_true", help="skip the batch-1, 4096-context decode leg")
+    ap.add_argument("--mfma-valu-probe", action="store_true",
+                    help="run only the MFMA/VALU instruction-mix probe and print its JSON line")
     ap.add_argument("--scorer-sizes", action="store_true",
                     help="also time the decode scorer alone at 2^18 .. 2^21 keys a launch (fixed and per-key parts)")
     ap.add_argument("--fused-write", action="store_true",
@@ -567,6 +614,9 @@ def main():
     import sparse_attention_indexer_fp4_amd as ifp4
     import workloads as W
 
+    if args.mfma_valu_probe:
+        print(json.dumps({"probe": "mfma_valu", **mfma_valu_probe(torch)}), flush=True)
+        return
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)

@@ -12,6 +12,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libindexer_fp4.so")
 SOURCES = ["errors.hip", "quant_cache.hip", "schedule.hip", "score_decode.hip", "score_prefill.hip", "topk.hip"]
+# a measurement kernel of its own (bench.py --mfma-valu-probe), kept out of the product library
+PROBE_SOURCE = "probe_mfma_valu.hip"
+PROBE_LIB_PATH = os.path.join(HERE, "libindexer_fp4_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -39,17 +42,22 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
-    """Compile every source and link libindexer_fp4.so; always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path):
+    tmp = path + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(jobs: int = 8) -> str:
+    """Compile every source and link libindexer_fp4.so (and the probe library); always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PROBE_SOURCE]))
+    _link(objs[:-1], LIB_PATH)
+    _link(objs[-1:], PROBE_LIB_PATH)
     return LIB_PATH
 
 
