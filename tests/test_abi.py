@@ -48,6 +48,24 @@ def test_every_declared_symbol_is_exported(L):
     assert set(pkg_module.EXPORTS) == set(names)
 
 
+def test_probe_library_loads_and_rejects_bad_arguments():
+    """The instruction-mix probe (bench.py --mfma-valu-probe) is a library of its own: it loads,
+    exports its one entry point, and rejects a mode or size out of range before any device call."""
+    path = os.path.join(ROOT, "sparse_attention_indexer_fp4_amd", "libindexer_fp4_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    P = ctypes.CDLL(path)
+    f = P.indexer_fp4_probe_mfma_valu
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 4
+    f.restype = ctypes.c_int
+    buf = ctypes.c_void_p(16)  # never dereferenced: every call below fails its checks first
+    assert f(6, 10, 1, buf, buf, buf, None) == -1
+    assert f(-1, 10, 1, buf, buf, buf, None) == -1
+    assert f(0, 0, 1, buf, buf, buf, None) == -1
+    assert f(0, 10, 0, buf, buf, buf, None) == -1
+    assert f(0, 10, 1, None, buf, buf, None) == -1
+
+
 def test_size_queries(L):
     # decode: 8-word header + cum[B+1] + unit_begin[U+1] + unit_seq/unit_page/unit_run[U]
     assert L.indexer_fp4_decode_sched_bytes(8, 1, 512) == 4 * (8 + 9 + 513 + 3 * 512)
