@@ -146,6 +146,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(void *base, uint32
 __device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)byte_offset, 0, IFP4_STORE_POLICY);
 }
+// The same store with the non-temporal hint (cache-policy bit 1 on gfx950): for output that is
+// not read again by the kernel and would otherwise push data the kernel does reuse out of L2.
+__device__ __forceinline__ void buffer_store_f32_nt(float v, __amdgpu_buffer_rsrc_t rsrc, uint32_t byte_offset) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rsrc, (int)byte_offset, 0, 2);
+}
 
 // Order-preserving 32-bit key of a float (flip the sign bit of non-negative values, invert
 // negative ones; -0.0 is folded onto +0.0): a > b as floats iff key(a) > key(b).

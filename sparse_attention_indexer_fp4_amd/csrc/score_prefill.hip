@@ -21,7 +21,9 @@
 //     barrier, so the waves of a SIMD drift apart and one's MFMAs run while another reduces;
 //   - the two rows share the page registers, and their MFMAs and epilogues interleave;
 //   - an item's logits are stored after its slot's refill is issued, so waiting for a page
-//     never waits for a store's completion.
+//     never waits for a store's completion, and with the non-temporal hint: a step writes
+//     tens of MB of logits, which would otherwise push the step's key pages (read again and
+//     again by every tile of their request) out of L2.
 // The unit's first items come from its start record (one scalar load), so the first pages are
 // in flight after a single round trip; the pages of later items come from the schedule's item
 // table by scalar loads issued D items ahead. Each wave's two query rows sit in registers and
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(kPrefillWaves * 64) void score_prefill_kernel(
     static_for<RPW>([&](auto jj) {
       constexpr int J = decltype(jj)::value;
       if constexpr (ADD) __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(s_v[J], s_dst[J], (int)s_off, 0, 0);
-      else buffer_store_f32(s_v[J], s_dst[J], s_off);
+      else buffer_store_f32_nt(s_v[J], s_dst[J], s_off);
     });
   };
 
