@@ -403,12 +403,18 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
       });
     }
   }
-  if (fuse) {  // occupied bins only, one device atomic each
+  if (fuse) {  // occupied bins only, one device atomic each; four bins a 16-byte LDS read
     __syncthreads();
     uint32_t *g = row_hist + (int64_t)qs0 * NN * kHistBins;
-    for (int i = threadIdx.x; i < NN * kHistBins; i += NW * 64) {
-      const uint32_t c = uh[i];
-      if (c) atomicAdd(&g[(i / kHistBins) * kHistBins + hist_slot(i % kHistBins)], c);
+    for (int i4 = threadIdx.x; i4 < NN * kHistBins / 4; i4 += NW * 64) {
+      const uint4 c4 = reinterpret_cast<const uint4 *>(uh)[i4];
+      if ((c4.x | c4.y | c4.z | c4.w) == 0u) continue;
+      const uint32_t cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = 4 * i4 + e;
+        if (cv[e]) atomicAdd(&g[(i / kHistBins) * kHistBins + hist_slot(i % kHistBins)], cv[e]);
+      }
     }
   }
 }
