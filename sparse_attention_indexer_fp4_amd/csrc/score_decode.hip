@@ -81,14 +81,28 @@ struct SeqLoad {
   uint4 raw[KB];
   float wv[KB];
   uint4 kraw;
-  float gm[8], bt[8];
+  float4 g[2], be[2];  // k_norm weight and bias as loaded (selected where they are used)
+  float4 ang[4];       // the rotary row's cos and sin as loaded (arranged where they are used)
   float c[8], sn[8];
   int64_t pos, slot;
 };
 
+// The sequence's position and slot (the rotary table row waits for the position) ...
+// (scalar loads, b being wave-uniform: they count on their own counter, apart from the vector
+// loads in flight)
 template <int KB>
-__device__ __forceinline__ void seq_load(SeqLoad<KB> &Q, const StepWrite W, int b, int n_heads, int task0, int stride,
-                                         int first, bool key) {
+__device__ __forceinline__ void seq_load_pos(SeqLoad<KB> &Q, const StepWrite W, int b) {
+  const int64_t pos = as_const(W.rope_dim > 0 ? W.positions : W.slots)[b];
+  Q.pos = W.rope_dim > 0 ? pos : 0;
+  Q.slot = as_const(W.slots)[b];
+}
+
+// ... and its query heads' and key's inputs. Every lane loads the key's (the lanes whose task0
+// is below 16 use them): loads under a lane condition would make the compiler wait for them
+// where the branch ends.
+template <int KB>
+__device__ __forceinline__ void seq_load_data(SeqLoad<KB> &Q, const StepWrite W, int b, int n_heads, int task0,
+                                              int stride, int first) {
   const int l = task0 & 15;
 #pragma unroll
   for (int kb = 0; kb < KB; kb++) {
@@ -96,26 +110,22 @@ __device__ __forceinline__ void seq_load(SeqLoad<KB> &Q, const StepWrite W, int 
     Q.raw[kb] = *reinterpret_cast<const uint4 *>(W.q + ((int64_t)b * n_heads + h) * kHeadDim + 8 * l);
     Q.wv[kb] = W.weights[(int64_t)b * n_heads + h];
   }
-  Q.pos = W.rope_dim > 0 ? W.positions[b] : 0;
-  Q.slot = W.slots[b];
-  if (key) {
-    Q.kraw = *reinterpret_cast<const uint4 *>(W.k + (int64_t)b * W.k_ld + 8 * l);
-    if (W.gamma) {
-      const float4 g0 = *reinterpret_cast<const float4 *>(W.gamma + 8 * l);
-      const float4 g1 = *reinterpret_cast<const float4 *>(W.gamma + 8 * l + 4);
-      Q.gm[0] = g0.x, Q.gm[1] = g0.y, Q.gm[2] = g0.z, Q.gm[3] = g0.w;
-      Q.gm[4] = g1.x, Q.gm[5] = g1.y, Q.gm[6] = g1.z, Q.gm[7] = g1.w;
-      if (W.beta) {
-        const float4 b0 = *reinterpret_cast<const float4 *>(W.beta + 8 * l);
-        const float4 b1 = *reinterpret_cast<const float4 *>(W.beta + 8 * l + 4);
-        Q.bt[0] = b0.x, Q.bt[1] = b0.y, Q.bt[2] = b0.z, Q.bt[3] = b0.w;
-        Q.bt[4] = b1.x, Q.bt[5] = b1.y, Q.bt[6] = b1.z, Q.bt[7] = b1.w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; j++) Q.bt[j] = 0.f;
-      }
-    }
-  }
+  Q.kraw = *reinterpret_cast<const uint4 *>(W.k + (int64_t)b * W.k_ld + 8 * l);
+  // the k_norm parameters with no condition on the loads either: a missing one is read from
+  // the query rows instead (in bounds) and not used
+  const float *gp = W.gamma ? W.gamma : reinterpret_cast<const float *>(W.q);
+  const float *bp = W.beta ? W.beta : gp;
+  Q.g[0] = *reinterpret_cast<const float4 *>(gp + 8 * l);
+  Q.g[1] = *reinterpret_cast<const float4 *>(gp + 8 * l + 4);
+  Q.be[0] = *reinterpret_cast<const float4 *>(bp + 8 * l);
+  Q.be[1] = *reinterpret_cast<const float4 *>(bp + 8 * l + 4);
+}
+
+template <int KB>
+__device__ __forceinline__ void seq_load(SeqLoad<KB> &Q, const StepWrite W, int b, int n_heads, int task0, int stride,
+                                         int first) {
+  seq_load_pos<KB>(Q, W, b);
+  seq_load_data<KB>(Q, W, b, n_heads, task0, stride, first);
 }
 
 // ... the rotary angles of the sequence's position (a second round: the table row waits for
@@ -124,8 +134,36 @@ template <int KB>
 __device__ __forceinline__ void seq_angles(SeqLoad<KB> &Q, const StepWrite W, int task0) {
   const int l = task0 & 15;
   const bool bad_pos = W.rope_dim > 0 && (Q.pos < 0 || Q.pos >= W.max_pos);
-  if (W.rope_dim > 0 && 8 * l < W.rope_dim)
-    rope_angles(W.cos_sin + (bad_pos ? 0 : Q.pos) * W.rope_dim, l, W.rope_dim, W.interleaved != 0, Q.c, Q.sn);
+  // Four 16-byte loads for either pair layout, with no condition on them (a load under a
+  // condition, even a uniform one, makes the compiler wait for it where the branches meet);
+  // lanes past the rotary part load lane 0's angles and do not use them. seq_arrange_angles
+  // puts them in place once they are needed.
+  if (W.rope_dim > 0) {
+    const float *row = W.cos_sin + (bad_pos ? 0 : Q.pos) * W.rope_dim;
+    const int la = 8 * l < W.rope_dim ? l : 0, half = W.rope_dim >> 1;
+    const int o0 = W.interleaved ? 4 * la : (8 * la) % half;
+    const int o1 = W.interleaved ? 4 * la : o0 + 4;
+    Q.ang[0] = *reinterpret_cast<const float4 *>(row + o0);
+    Q.ang[1] = *reinterpret_cast<const float4 *>(row + o1);
+    Q.ang[2] = *reinterpret_cast<const float4 *>(row + half + o0);
+    Q.ang[3] = *reinterpret_cast<const float4 *>(row + half + o1);
+  }
+}
+
+// The loaded angles as rope8 takes them (rope_angles' arrangement): interleaved pairs use
+// each of the four values twice, half-split pairs the eight in order.
+template <int KB>
+__device__ __forceinline__ void seq_arrange_angles(SeqLoad<KB> &Q, const StepWrite W) {
+  const float a0[4] = {Q.ang[0].x, Q.ang[0].y, Q.ang[0].z, Q.ang[0].w};
+  const float a1[4] = {Q.ang[1].x, Q.ang[1].y, Q.ang[1].z, Q.ang[1].w};
+  const float s0[4] = {Q.ang[2].x, Q.ang[2].y, Q.ang[2].z, Q.ang[2].w};
+  const float s1[4] = {Q.ang[3].x, Q.ang[3].y, Q.ang[3].z, Q.ang[3].w};
+  const bool il = W.interleaved != 0;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    Q.c[j] = il ? a0[j >> 1] : (j < 4 ? a0[j] : a1[j - 4]);
+    Q.sn[j] = il ? s0[j >> 1] : (j < 4 ? s0[j] : s1[j - 4]);
+  }
 }
 
 // ... then the query heads and the key quantized into the sequence's area.
@@ -135,13 +173,14 @@ __device__ __forceinline__ void seq_store(SeqLoad<KB> &Q, const StepWrite W, int
   const int l = task0 & 15, g = l >> 2;
   const bool bad_pos = W.rope_dim > 0 && (Q.pos < 0 || Q.pos >= W.max_pos);
   const bool live = !bad_pos && (Q.slot >= 0 || W.all_q != 0);
+  if (W.rope_dim > 0) seq_arrange_angles<KB>(Q, W);
 #pragma unroll
   for (int kb = 0; kb < KB; kb++) {
     const int i = first + task0 + kb * stride;
     if (i >= 16 * n_heads) break;  // uniform over the head's 16 lanes
     const int h = i >> 4;
     uint32_t sc = 0, d = 0;
-    if (live) d = norm_rope_encode(Q.raw[kb], l, false, Q.gm, Q.bt, 0.f, W.rope_dim, W.interleaved != 0, Q.c, Q.sn, sc);
+    if (live) d = norm_rope_encode(Q.raw[kb], l, false, Q.c, Q.c, 0.f, W.rope_dim, W.interleaved != 0, Q.c, Q.sn, sc);
     *reinterpret_cast<uint32_t *>(area + h * kKeyBytes + 4 * l) = d;
     if ((l & 3) == 0) area[n_heads * kKeyBytes + h * kGroups + g] = (uint8_t)sc;
     if (l == 0)
@@ -150,8 +189,14 @@ __device__ __forceinline__ void seq_store(SeqLoad<KB> &Q, const StepWrite W, int
   if (key) {  // the writer stores the key when its position and slot are good
     uint8_t *ka = area + n_heads * kQVecBytes;
     const bool store = !bad_pos && Q.slot >= 0 && Q.slot < n_pages * kPage;
+    const float gm[8] = {Q.g[0].x, Q.g[0].y, Q.g[0].z, Q.g[0].w, Q.g[1].x, Q.g[1].y, Q.g[1].z, Q.g[1].w};
+    float bt[8] = {Q.be[0].x, Q.be[0].y, Q.be[0].z, Q.be[0].w, Q.be[1].x, Q.be[1].y, Q.be[1].z, Q.be[1].w};
+    if (!W.beta) {
+#pragma unroll
+      for (int j = 0; j < 8; j++) bt[j] = 0.f;
+    }
     uint32_t sc = 0;
-    const uint32_t d = norm_rope_encode(Q.kraw, l, W.gamma != nullptr, Q.gm, Q.bt, W.eps, W.rope_dim,
+    const uint32_t d = norm_rope_encode(Q.kraw, l, W.gamma != nullptr, gm, bt, W.eps, W.rope_dim,
                                         W.interleaved != 0, Q.c, Q.sn, sc);
     *reinterpret_cast<uint32_t *>(ka + 4 * l) = d;
     if ((l & 3) == 0) ka[kKeyBytes + g] = (uint8_t)sc;
@@ -274,10 +319,15 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   int tab_base = -64;
   int v_seq = 0, v_page = 0, v_phys = -1;
   bool v_last = false;
-  auto fill = [&](int base) __attribute__((always_inline)) {
+  // in two halves, so that the writing scorer can issue other loads between the table entries'
+  // request and their use: every lane loads an entry of the table (clamped into it), and the
+  // check afterwards keeps the ones of real items
+  int f_raw = 0, f_b = 0, f_p = 0;
+  bool f_in = false, f_ok = false, f_last = false;
+  auto fill_issue = [&](int base) __attribute__((always_inline)) {
     tab_base = base;
     const int it = w0 + base + lane;
-    int b = seq0, p = 0, phys = -1;
+    int b = seq0, p = 0;
     bool last = false;
     if (it < w1) {
       const int k = it - it0;  // items past the unit's first one
@@ -290,21 +340,37 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
         p = it - cum[b];
         if constexpr (WR) last = it + 1 == cum[b + 1];
       }
-      if (p >= 0 && p < bt_ld) {
-        phys = bt_g[(int64_t)b * bt_ld + p];
+    }
+    const int64_t bc = min(max(b, 0), batch - 1), pc = min(max((int64_t)p, (int64_t)0), bt_ld - 1);
+    f_raw = bt_g[bc * bt_ld + pc];
+    f_b = b;
+    f_p = p;
+    f_in = it < w1;
+    f_ok = p >= 0 && p < bt_ld;
+    f_last = last;
+  };
+  auto fill_check = [&]() __attribute__((always_inline)) {
+    int phys = -1;
+    if (f_in) {
+      if (f_ok) {
+        phys = f_raw;
         if (phys < 0 || phys >= n_pages) {
           atomicOr(err, INDEXER_FP4_DEV_BAD_PAGE);
           phys = -1;
         }
       } else {
-        atomicOr(err, p < 0 ? INDEXER_FP4_DEV_BAD_SCHEDULE : INDEXER_FP4_DEV_TABLE_SHORT);
+        atomicOr(err, f_p < 0 ? INDEXER_FP4_DEV_BAD_SCHEDULE : INDEXER_FP4_DEV_TABLE_SHORT);
       }
     }
-    v_seq = b;
-    v_page = p;
+    v_seq = f_b;
+    v_page = f_p;
     v_phys = phys;
-    v_last = last;
-    seq0 = __builtin_amdgcn_readlane(b, 63);  // sequences only advance with the items
+    v_last = f_last;
+    seq0 = __builtin_amdgcn_readlane(f_b, 63);  // sequences only advance with the items
+  };
+  auto fill = [&](int base) __attribute__((always_inline)) {
+    fill_issue(base);
+    fill_check();
   };
   // Software pipeline over a ring of D pages: scoring slot K overlaps the loads of the
   // other D-1 slots. Every slot refill is unconditional -- past the wave's last item it
@@ -318,7 +384,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   auto issue = [&](auto kk, int i) __attribute__((always_inline)) {
     constexpr int K = decltype(kk)::value;
     const bool live = i < n_my;
-    const int ii = live ? i : n_my - 1;
+    const int ii = live ? i : max(n_my - 1, 0);  // (a wave with no item loads the table's first entry, dropped)
     if (ii - tab_base >= 64) fill(ii & ~63);
     const int l = ii - tab_base;
     const int phys = __builtin_amdgcn_readlane(v_phys, l);
@@ -344,7 +410,7 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
         } else {  // quantized by this wave alone, two lane-tasks a lane at a time
           for (int first = 0; first < 16 * n_heads; first += 2 * 64) {
             SeqLoad<2> Qw;
-            seq_load<2>(Qw, Wr, qb, n_heads, lane, 64, first, first == 0 && lane < 16);
+            seq_load<2>(Qw, Wr, qb, n_heads, lane, 64, first);
             seq_angles<2>(Qw, Wr, lane);
             seq_store<2>(Qw, Wr, n_heads, n_pages, warea, lane, 64, first, first == 0 && lane < 16);
           }
@@ -382,14 +448,28 @@ __global__ __launch_bounds__(NW * 64) void score_decode_kernel(
   // (one lane-task each, 16 a head; the key by the first 16 lanes), its rotary table row ahead
   // of the first pages, and all of it quantized while those pages are in flight.
   SeqLoad<KBC> Q0;
-  if constexpr (WR) seq_load<KBC>(Q0, Wr, qs0, n_heads, threadIdx.x, NW * 64, 0, threadIdx.x < 16);
-  if (n_my > 0) fill(0);
-  if constexpr (WR) seq_angles<KBC>(Q0, Wr, threadIdx.x);
-  if (n_my > 0) {
-    // the first pages are in flight before the query rows are fetched
+  if constexpr (WR) {
+    // Loads go out in the order they are needed (the vector memory counter completes in
+    // order, so a wait for one load is a wait for every older one): the position (a scalar
+    // load, on its own counter), the table entries, the rotary row (its wait covers the
+    // position only), the query and key inputs; then the first pages (their wait covers the
+    // table) and the quantization, whose inputs are all older than the pages. A wave with no
+    // item still issues its first pages (page 0, dropped), so no load sits under a condition
+    // the compiler would have to merge.
+    seq_load_pos<KBC>(Q0, Wr, qs0);
+    fill_issue(0);
+    asm volatile("" ::: "memory");
+    seq_angles<KBC>(Q0, Wr, threadIdx.x);
+    asm volatile("" ::: "memory");
+    seq_load_data<KBC>(Q0, Wr, qs0, n_heads, threadIdx.x, NW * 64, 0);
+    asm volatile("" ::: "memory");
+    fill_check();
+    static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
+    seq_store<KBC>(Q0, Wr, n_heads, n_pages, qarea, threadIdx.x, NW * 64, 0, threadIdx.x < 16);
+  } else if (n_my > 0) {
+    fill(0);
     static_for<D>([&](auto kk) { issue(kk, decltype(kk)::value); });
   }
-  if constexpr (WR) seq_store<KBC>(Q0, Wr, n_heads, n_pages, qarea, threadIdx.x, NW * 64, 0, threadIdx.x < 16);
   if (fuse) {
     for (int i = threadIdx.x; i < NN * kHistBins / 4; i += NW * 64)
       reinterpret_cast<uint4 *>(uh)[i] = make_uint4(0u, 0u, 0u, 0u);
