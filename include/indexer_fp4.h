@@ -325,11 +325,10 @@ int indexer_fp4_score_prefill(const uint8_t *q_packed, const uint8_t *q_scale,
  * rest of the row, up to k, is -1. Logits must be finite.
  *   row_len    int32 [n_rows] (e.g. a schedule's row_len output)
  *   workspace  indexer_topk_workspace_bytes(n_rows, max_len, k) bytes (0 when every
- *              row fits one workgroup: max_len <= 16384 or k >= max_len). It must be
- *              zero-filled before its first use; every call that returns OK leaves it
- *              zero-filled again, so one buffer serves any number of calls on one
- *              stream. Calls that share it must not overlap; after an EHIP error zero
- *              it again.
+ *              row fits one workgroup: max_len <= 16384 or k >= max_len). Its contents
+ *              when a call starts do not matter (a call writes every word it reads
+ *              first), so one buffer serves any number of calls, of any shapes, on one
+ *              stream. Calls that share it must not overlap.
  *   row_hist   optional (NULL: none): the histogram indexer_fp4_score_decode filled for
  *              exactly these logits and rows; it replaces one pass of this call and is
  *              left zero-filled. A histogram of other logits gives a meaningless (though
@@ -351,11 +350,9 @@ int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_rows, const i
  * long-row workspace is a fixed array of INDEXER_TOPK_NOALLOC_SCRATCH_BYTES bytes of device
  * memory owned by the library (one copy per GPU, held until the process ends); a call
  * whose indexer_topk_workspace_bytes(n_rows, max_len, k) exceeds it returns ENOSPC
- * (e.g. 16 rows x 131072 keys need 25.7 MB and fit; 32 rows do not). The call allocates
- * nothing. Every call on one GPU shares that GPU's array: calls that overlap on one GPU
- * (different streams, or host threads) race and give undefined selections. The first call
- * on a GPU (and the first after a call that returned EHIP) clears the array with a fill
- * kernel on `stream` before selecting.
+ * (e.g. 16 rows x 131072 keys need 8.7 MB and fit; 64 rows, 34.6 MB, do not). The call
+ * allocates nothing. Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (different streams, or host threads) race and give undefined selections.
  * --------------------------------------------------------------------------------- */
 #define INDEXER_TOPK_NOALLOC_SCRATCH_BYTES (32ll << 20)
 int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int32_t n_rows, const int32_t *row_len,

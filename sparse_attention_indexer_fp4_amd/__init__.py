@@ -361,8 +361,8 @@ def indexer_topk_workspace_bytes(n_rows: int, max_len: int, k: int) -> int:
 def indexer_topk(logits, row_len, max_len, k, topk_idx, workspace=None, row_hist=None):
     """logits fp32 [rows, LD]; row_len int32 [rows]; topk_idx int32 [rows, >=k] (output).
 
-    workspace: uint8 device buffer of indexer_topk_workspace_bytes(...) bytes, zero-filled
-    before its first use (each successful call leaves it zeroed again).
+    workspace: uint8 device buffer of indexer_topk_workspace_bytes(...) bytes, any contents
+    (a call writes every word it reads first).
     row_hist: the histogram indexer_fp4_score_decode filled for these logits (left zeroed)."""
     _dev(logits, "logits", torch.float32, contiguous=False)
     _dev(row_len, "row_len", torch.int32)

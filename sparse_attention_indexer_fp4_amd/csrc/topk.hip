@@ -615,19 +615,28 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
 // launches ordered by the stream (two when the decode scorer has already filled the digit-1
 // histograms):
 //   hist     histogram of digit 1 (key bits 31..20) of every chunk, merged into the row's
-//            histogram with one atomic per occupied bin;
+//            histogram with one atomic per occupied bin (after a fill kernel clears it);
 //   collect  every chunk finds the bin b1 that holds the row's k-th largest key, counts its
 //            keys above b1 ("sure") and writes its keys in b1 ("candidates") into its own
 //            region of the workspace in column order, with both counts and b1;
 //   emit     every chunk again: it reads the counts and candidates of all the row's chunks
-//            and resolves from them, with two LDS histograms over the candidates (key bits
-//            19..8, then 7..0), the row's k-th largest key T and how many keys equal to T are
-//            kept (those of the lowest columns). Its offset in the output is the number of
-//            kept keys of the earlier chunks (their sure keys, their candidates above T and
-//            their share of the keys equal to T); it re-reads its own logits and writes its
-//            kept columns in ascending order. Every chunk of a row resolves T for itself, so
-//            no workgroup waits for another, and it zeroes its share of the row's digit-1
+//            (into registers: group cc of threads holds chunk cc's) and resolves from them,
+//            with LDS histograms over the candidates (key bits 19..8, then 7..0 unless T's
+//            bin of bits 19..8 is taken whole, as it is when it holds one candidate), the
+//            row's k-th largest key T and how many keys equal to T are kept (those of the
+//            lowest columns). Its offset in the output is the number of kept keys of the
+//            earlier chunks (their sure keys, their candidates above T and their share of the
+//            keys equal to T), which the same histograms count when they are restricted to
+//            the earlier chunks' candidates; it re-reads its own logits and writes its kept
+//            columns in ascending order. Every chunk of a row resolves T for itself, so no
+//            workgroup waits for another, and it zeroes its share of the row's digit-1
 //            histogram for the next call.
+// Each step after the loads is a barrier-separated phase of about half a microsecond, so
+// the emit kernel keeps them few: the counts' sums share the first histogram's barrier, the
+// two histograms' scans share one, and the candidates never go through LDS. (One launch
+// where the last chunk of a row to finish selects, after a device-wide counter, measured
+// slower: the stores and loads that make the lists visible across the chip's L2s, and the
+// counter's atomics, cost more than the launch they save.)
 // The candidates of a row are the keys of one digit-1 bin, an eighth of an octave of logit
 // values: a few thousand at most on the decode workloads, read by every chunk of the row in
 // one round of loads (more are read in further rounds). Device-wide atomics on one cache
@@ -642,15 +651,14 @@ constexpr int kBins = 4096;                         // 12-bit digits
 constexpr int64_t kLongMaxLen = 1 << 20;
 constexpr int kMaxChunks = (int)(kLongMaxLen / kChunk);
 static_assert(kMaxChunks <= kLongThreads, "the emit kernel gives every chunk of a row at least one thread");
-static_assert(kMaxChunks <= 4 * 64, "one wave of the emit kernel sums the chunk counts, four a lane");
 static_assert(kBins == kHistBins, "the digit-1 histograms are the row histograms the decode scorer fills");
 constexpr int kCandPer = 16;    // candidate slots of its chunk a thread of the emit kernel reads at once
-constexpr int kListMax = 8192;  // candidates of a row the emit kernel stages in LDS
 constexpr int kCountWords = 4;  // per chunk: sure count, candidate count, b1, unused
 
 // Workspace words: the row histograms of digit 1 first (used when the decode scorer has not
-// filled them; zero when a call starts and zeroed again by the emit kernel), then per row the
-// chunks' counts and the chunks' candidate regions.
+// filled them), then per row the chunks' counts and the chunks' candidate regions. A call
+// writes each word before it reads it, so the workspace may hold anything when a call
+// starts (another call's lists, of another shape, included).
 struct LongWs {
   int64_t hist1, counts, ckey, words;
   __host__ __device__ LongWs(int rows, int64_t max_len) {
@@ -666,6 +674,11 @@ struct LongWs {
 __device__ __forceinline__ int64_t clamped_len(const int32_t *row_len, int r, int64_t max_len) {
   const int64_t len = row_len[r];
   return len < 0 ? 0 : (len > max_len ? max_len : len);
+}
+
+__global__ void zero_fill_kernel(uint4 *p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 __global__ __launch_bounds__(kLongThreads) void topk_hist_kernel(const float *__restrict__ logits, int64_t ld,
@@ -789,18 +802,47 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
   }
 }
 
+// Wave-wide sum, returned to every lane (the DPP prefix sum's last lane: no LDS round trips).
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63); }
+
+// Inclusive prefix sums of a and b over the workgroup's threads, with one barrier; ta and tb
+// get the totals. s_w (two words a wave) must not be reused before another barrier.
+template <int NT>
+__device__ __forceinline__ void block_prefix_sum2(int &a, int &b, int *s_w, int &ta, int &tb) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  a = wave_prefix_sum(a);
+  b = wave_prefix_sum(b);
+  if (lane == 63) {
+    s_w[wv] = a;
+    s_w[NT / 64 + wv] = b;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0;
+  ta = tb = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < NT / 64; w2++) {
+    const int x = s_w[w2], y = s_w[NT / 64 + w2];
+    ba += w2 < wv ? x : 0;
+    bb += w2 < wv ? y : 0;
+    ta += x;
+    tb += y;
+  }
+  a += ba;
+  b += bb;
+}
+
 __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__restrict__ logits, int64_t ld,
                                                                 const int32_t *__restrict__ row_len,
                                                                 int64_t max_len, int k,
                                                                 const uint32_t *__restrict__ ws, int rows,
                                                                 uint32_t *__restrict__ h1, int32_t *__restrict__ out,
                                                                 int64_t out_ld) {
-  __shared__ uint32_t s_h2[kBins], s_h2b[kBins];  // all candidates; those of earlier chunks
-  __shared__ uint32_t s_h3[256], s_h3b[256];
-  __shared__ uint32_t s_list[kListMax];
-  __shared__ int s_nc[kMaxChunks], s_ns[kMaxChunks];
-  __shared__ int s_coff[kMaxChunks + 1], s_soff[kMaxChunks + 1];
-  __shared__ int s_wa[2 * kLongWaves];
+  // the candidates' digit 2 (key bits 19..8) and low byte: of all chunks, and of the chunks
+  // before this one
+  __shared__ __attribute__((aligned(16))) uint32_t s_h2[kBins], s_h2b[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t s_h3[256], s_h3b[256];
+  __shared__ int s_red[4 * kLongWaves];
+  __shared__ int s_scan[2 * kLongWaves];
   __shared__ int s_sel[8];
   __shared__ uint32_t s_we[kLongWaves], s_wk[kLongWaves];
   const int r = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -808,10 +850,11 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   const LongWs L(rows, max_len);
   const int64_t cap = (int64_t)chunks * kChunk;
   // Everything is requested at once, before the row length is known (a second memory round
-  // trip otherwise): the counts of every chunk of the row, the first candidates of every
-  // chunk's region (tpc threads a chunk, kCandPer slots each; slots past a chunk's count hold
-  // stale words and are dropped once the counts are in) and this chunk's logits (columns
-  // clamped into the row, those past its length masked).
+  // trip otherwise): the counts of every chunk of the row and the first candidates of every
+  // chunk's region (group cc of tpc threads holds chunk cc's slots t0 + tpc u, u < kCandPer,
+  // in one wave or part of one; slots past a chunk's count hold stale words and are dropped
+  // once the counts are in), and this chunk's logits (columns clamped into the row, those
+  // past its length masked).
   const int tpc_log = 9 - (32 - __clz(chunks - 1));  // tpc: the power of two <= kLongThreads / chunks
   const int tpc = 1 << tpc_log;
   const int cc = tid >> tpc_log, t0 = tid & (tpc - 1);
@@ -819,8 +862,7 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   const uint32_t *cw = ws + L.counts + (int64_t)r * chunks * kCountWords;
   const uint32_t ns_raw = cw[ccq * kCountWords], nc_raw = cw[ccq * kCountWords + 1];
   const uint32_t b1 = cw[2] & (kBins - 1);  // chunk 0 holds keys of every long row
-  const uint32_t *ckr = ws + L.ckey + (int64_t)r * cap;
-  const uint32_t *ckc = ckr + (int64_t)ccq * kChunk;
+  const uint32_t *ckc = ws + L.ckey + (int64_t)r * cap + (int64_t)ccq * kChunk;
   uint32_t cand[kCandPer];
 #pragma unroll
   for (int u = 0; u < kCandPer; u++) cand[u] = ckc[min(t0 + u * tpc, kChunk - 1)];  // (slots past kChunk unused)
@@ -830,6 +872,17 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) lv[u] = row[min(start + kWaveCols * wv + 64 * u + lane, max_len - 1)];
   asm volatile("" ::: "memory");  // (keeps the length check, and its wait, behind the loads)
+  // the histograms are cleared while the loads are in flight
+  static_assert(kBins / 4 == 2 * kLongThreads, "two 16-byte stores a thread and histogram");
+  reinterpret_cast<uint4 *>(s_h2)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4 *>(s_h2)[tid + kLongThreads] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4 *>(s_h2b)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  reinterpret_cast<uint4 *>(s_h2b)[tid + kLongThreads] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < 64) {
+    reinterpret_cast<uint4 *>(s_h3)[tid] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4 *>(s_h3b)[tid] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
   const int64_t len = clamped_len(row_len, r, max_len);
   // the collect kernel has read the row's digit-1 histogram: this chunk's share of it is
   // zeroed for the next call
@@ -848,194 +901,151 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   }
   const int used = (int)((len + kChunk - 1) / kChunk);  // chunks that hold keys of this row
   if (c >= used) return;
-  const bool live = cc < used;
+  const bool live = cc < used, before = cc < c;  // chunk cc holds keys; it precedes this one
   const int64_t end = min(len, start + kChunk);
   const int nvalid = (int)(end - start);  // keys of this chunk
   uint32_t key[kPerThread];
 #pragma unroll
   for (int u = 0; u < kPerThread; u++) key[u] = order_key(lv[u]);
-  for (int i = tid; i < kBins / 4; i += kLongThreads) {
-    reinterpret_cast<uint4 *>(s_h2)[i] = make_uint4(0u, 0u, 0u, 0u);
-    reinterpret_cast<uint4 *>(s_h2b)[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (tid < 256) {
-    s_h3[tid] = 0u;
-    s_h3b[tid] = 0u;
-  }
-  if (tid < 8) s_sel[tid] = tid == 0 ? -1 : 0;  // s_sel[0]: bin b2, if one holds the (k - sure)-th largest candidate
   const int nc = live ? (int)min(nc_raw, (uint32_t)kChunk) : 0;
   const int ns = live ? (int)min(ns_raw, (uint32_t)kChunk) : 0;
-  if (live && t0 == 0) {
-    s_nc[cc] = nc;
-    s_ns[cc] = ns;
-  }
-  __syncthreads();
-  // offsets of the chunks' candidates in the row's list and of their sure keys: one wave,
-  // four chunks a lane
-  if (wv == 0) {
-    int a[4], b[4], sa = 0, sb = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int x = 4 * lane + i;
-      a[i] = x < used ? s_nc[x] : 0;
-      b[i] = x < used ? s_ns[x] : 0;
-      sa += a[i];
-      sb += b[i];
-    }
-    int ra = wave_prefix_sum(sa) - sa, rb = wave_prefix_sum(sb) - sb;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int x = 4 * lane + i;
-      if (x < used) {
-        s_coff[x] = ra;
-        s_soff[x] = rb;
-      }
-      ra += a[i];
-      rb += b[i];
-    }
-    if (lane == 63) {  // the totals
-      s_coff[used] = ra;
-      s_soff[used] = rb;
-    }
-  }
-  __syncthreads();
-  const int n_cand = s_coff[used], sure_all = s_soff[used];
-  const int cand_bef = s_coff[c], sure_bef = s_soff[c];
-  // The row's candidates in chunk (that is column) order, in LDS when they fit; otherwise read
-  // from the workspace wherever they are needed.
-  const bool staged = n_cand <= kListMax;
   const int E = kCandPer * tpc;  // slots of a chunk held in registers
-  if (staged) {
-    const int off = s_coff[ccq];
-#pragma unroll
-    for (int u = 0; u < kCandPer; u++) {
-      const int i = t0 + u * tpc;
-      if (i < nc) s_list[off + i] = cand[u];
-    }
-    // the rest of chunks with more candidates than slots (rare), by the chunk's own threads
-    for (int i = E + t0; i < nc; i += tpc) s_list[off + i] = ckr[(int64_t)ccq * kChunk + i];
-    __syncthreads();
-  }
-  // f(g, key) for the row's candidates g = tid, tid + kLongThreads, ... (two loops, so that
-  // the staged one reads LDS with LDS instructions only)
+  // f(v) for every candidate v of chunk cc held by this thread: the registers, then (chunks
+  // with more candidates than slots, rare) the rest from the workspace
   auto for_cands = [&](auto f) {
-    if (staged) {
-      for (int g = tid; g < n_cand; g += kLongThreads) f(g, s_list[g]);
-    } else {
-      for (int g = tid; g < n_cand; g += kLongThreads) {
-        int lo = 0, hi = used;  // the chunk x with s_coff[x] <= g < s_coff[x + 1]
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (s_coff[mid] <= g) lo = mid;
-          else hi = mid;
-        }
-        f(g, ckr[(int64_t)lo * kChunk + (g - s_coff[lo])]);
-      }
-    }
+#pragma unroll
+    for (int u = 0; u < kCandPer; u++)
+      if (t0 + u * tpc < nc) f(cand[u]);
+    for (int i = E + t0; i < nc; i += tpc) f(ckc[i]);
   };
-  // Bin b2 (key bits 19..8) of the need-th largest candidate, then its low byte b3; the
-  // candidates of earlier chunks are counted alongside, so the same scans also give how many
-  // of them lie above T and equal T (plain LDS atomics: the candidates' digits are nearly all
-  // distinct, and rows of ties that put many on one digit only cost conflicts).
-  const int need = k - sure_all;
-  for_cands([&](int g, uint32_t v) {
-    const uint32_t d = (v >> 8) & (kBins - 1);
-    atomicAdd(&s_h2[d], 1u);
-    if (g < cand_bef) atomicAdd(&s_h2b[d], 1u);
-  });
-  __syncthreads();
+  // The sure keys and candidates of the row and of the chunks before this one (group
+  // leaders' counts summed over the workgroup), and the candidates' digit 2 (plain LDS
+  // atomics: their digits are nearly all distinct, and rows of ties only cost conflicts),
+  // under one barrier.
   {
-    constexpr int kPer = kBins / kLongThreads;
-    static_assert(kPer == 8, "two 16-byte reads a thread");
-    const uint4 lo = reinterpret_cast<const uint4 *>(s_h2)[2 * tid];
-    const uint4 hi = reinterpret_cast<const uint4 *>(s_h2)[2 * tid + 1];
-    const uint4 lob = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid];
-    const uint4 hib = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid + 1];
-    const int cnt[kPer] = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    const int cnb[kPer] = {(int)lob.x, (int)lob.y, (int)lob.z, (int)lob.w,
-                           (int)hib.x, (int)hib.y, (int)hib.z, (int)hib.w};
-    int sum = 0, sumb = 0;
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      sum += cnt[i];
-      sumb += cnb[i];
+    const bool lead = t0 == 0;
+    const int a0 = wave_sum(lead ? ns : 0), a1 = wave_sum(lead && before ? ns : 0);
+    const int a2 = wave_sum(lead ? nc : 0), a3 = wave_sum(lead && before ? nc : 0);
+    if (lane == 0) {
+      s_red[wv] = a0;
+      s_red[kLongWaves + wv] = a1;
+      s_red[2 * kLongWaves + wv] = a2;
+      s_red[3 * kLongWaves + wv] = a3;
     }
-    int tot, totb;
-    const int incl = block_prefix_sum<kLongThreads>(sum, s_wa, tot);
-    const int inclb = block_prefix_sum<kLongThreads>(sumb, s_wa + kLongWaves, totb);
-    int acc = tot - incl + sum, accb = totb - inclb + sumb;  // in bins >= kPer*tid
-#pragma unroll
-    for (int i = 0; i < kPer; i++) {
-      acc -= cnt[i];
-      accb -= cnb[i];
-      if (acc + cnt[i] >= need && acc < need) {
-        s_sel[0] = kPer * tid + i;
-        s_sel[1] = need - acc;  // candidates of b2 still to take
-        s_sel[4] = accb;        // earlier chunks' candidates above b2
-      }
-    }
-    __syncthreads();
-  }
-  uint32_t T;
-  int rem;            // keys equal to T that are kept
-  int eq_all, above_bef, eq_bef;
-  const int b2 = s_sel[0];
-  if (b2 >= 0) {
-    const int need2 = s_sel[1];
-    for_cands([&](int g, uint32_t v) {
-      if ((int)((v >> 8) & (kBins - 1)) == b2) {
-        atomicAdd(&s_h3[v & 255u], 1u);
-        if (g < cand_bef) atomicAdd(&s_h3b[v & 255u], 1u);
-      }
+    for_cands([&](uint32_t v) {
+      const uint32_t d = (v >> 8) & (kBins - 1);
+      atomicAdd(&s_h2[d], 1u);
+      if (before) atomicAdd(&s_h2b[d], 1u);
     });
     __syncthreads();
-    if (wv == 0) {  // 256 bins, four a lane
-      const uint4 q = reinterpret_cast<const uint4 *>(s_h3)[lane];
-      const uint4 qb = reinterpret_cast<const uint4 *>(s_h3b)[lane];
-      const int cnt[4] = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
-      const int cnb[4] = {(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w};
-      const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3], sumb = cnb[0] + cnb[1] + cnb[2] + cnb[3];
-      const int incl = wave_prefix_sum(sum), inclb = wave_prefix_sum(sumb);
-      int acc = __builtin_amdgcn_readlane(incl, 63) - incl + sum;  // b2's candidates in bins >= 4 lane
-      int accb = __builtin_amdgcn_readlane(inclb, 63) - inclb + sumb;
+  }
+  int sure_all = 0, sure_bef = 0, n_cand = 0, cand_bef = 0;
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
+  for (int w2 = 0; w2 < kLongWaves; w2++) {
+    sure_all += s_red[w2];
+    sure_bef += s_red[kLongWaves + w2];
+    n_cand += s_red[2 * kLongWaves + w2];
+    cand_bef += s_red[3 * kLongWaves + w2];
+  }
+  const int need = k - sure_all;  // candidates to take after the sure keys
+  uint32_t T;                     // the k-th largest key, or a bound that selects the same keys
+  bool keep_eq;                   // every key equal to T is kept (else the lowest-column rem_all)
+  int rem_all = 0;                // keys equal to T that are kept, when not all are
+  int eq_bef = 0;                 // keys equal to T in earlier chunks
+  int kept_bef;                   // candidates of earlier chunks that are kept (ties included)
+  if (need <= 0) {  // more sure keys than k (a histogram of other logits): no candidate
+    T = (b1 << 20) | 0xFFFFFu;
+    keep_eq = false;
+    kept_bef = 0;
+  } else if (need >= n_cand) {  // every candidate (short of k when fewer)
+    T = b1 << 20;
+    keep_eq = true;
+    kept_bef = cand_bef;
+  } else {
+    {  // the digit-2 bin b2 of the need-th largest candidate
+      constexpr int kPer = kBins / kLongThreads;
+      static_assert(kPer == 8, "two 16-byte reads a thread");
+      const uint4 lo = reinterpret_cast<const uint4 *>(s_h2)[2 * tid];
+      const uint4 hi = reinterpret_cast<const uint4 *>(s_h2)[2 * tid + 1];
+      const uint4 lob = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid];
+      const uint4 hib = reinterpret_cast<const uint4 *>(s_h2b)[2 * tid + 1];
+      const int cnt[kPer] = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int cnb[kPer] = {(int)lob.x, (int)lob.y, (int)lob.z, (int)lob.w,
+                             (int)hib.x, (int)hib.y, (int)hib.z, (int)hib.w};
+      int sum = 0, sumb = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; i++) {
+        sum += cnt[i];
+        sumb += cnb[i];
+      }
+      int incl = sum, inclb = sumb, tot, totb;
+      block_prefix_sum2<kLongThreads>(incl, inclb, s_scan, tot, totb);
+      int acc = tot - incl + sum, accb = totb - inclb + sumb;  // in bins >= kPer*tid
+#pragma unroll
+      for (int i = 0; i < kPer; i++) {
         acc -= cnt[i];
         accb -= cnb[i];
-        if (acc + cnt[i] >= need2 && acc < need2) {
-          s_sel[2] = 4 * lane + i;
-          s_sel[3] = need2 - acc;  // keys equal to T that are kept
-          s_sel[5] = accb;         // earlier chunks' candidates of b2 above T
-          s_sel[6] = cnb[i];       // earlier chunks' keys equal to T
-          s_sel[7] = cnt[i];       // keys equal to T
+        if (acc + cnt[i] >= need && acc < need) {
+          s_sel[0] = kPer * tid + i;
+          s_sel[1] = need - acc;  // candidates of b2 still to take
+          s_sel[2] = accb;        // earlier chunks' candidates above b2
+          s_sel[3] = cnt[i];      // candidates in b2
+          s_sel[4] = cnb[i];      // earlier chunks' candidates in b2
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
-    T = (b1 << 20) | ((uint32_t)b2 << 8) | (uint32_t)s_sel[2];
-    rem = s_sel[3];
-    above_bef = s_sel[4] + s_sel[5];
-    eq_bef = s_sel[6];
-    eq_all = s_sel[7];
-  } else if (need <= 0) {  // more sure keys than k (a histogram of other logits): no candidate
-    T = (b1 << 20) | 0xFFFFFu;
-    rem = 0;
-    eq_all = above_bef = eq_bef = 0;
-  } else {  // fewer candidates than needed: all of them (all counted as above T)
-    T = b1 << 20;
-    rem = INT32_MAX;
-    eq_all = eq_bef = 0;
-    above_bef = cand_bef;
+    const uint32_t hi20 = (b1 << 12) | (uint32_t)s_sel[0];
+    const int need2 = s_sel[1];
+    if (need2 == s_sel[3]) {  // b2 is kept whole (the usual case: it holds one candidate)
+      T = hi20 << 8;
+      keep_eq = true;
+      kept_bef = s_sel[2] + s_sel[4];
+    } else {  // its low byte
+      const int above_b2 = s_sel[2];
+      for_cands([&](uint32_t v) {
+        if ((v >> 8) == hi20) {
+          atomicAdd(&s_h3[v & 255u], 1u);
+          if (before) atomicAdd(&s_h3b[v & 255u], 1u);
+        }
+      });
+      __syncthreads();
+      if (wv == 0) {  // 256 bins, four a lane
+        const uint4 q = reinterpret_cast<const uint4 *>(s_h3)[lane];
+        const uint4 qb = reinterpret_cast<const uint4 *>(s_h3b)[lane];
+        const int cnt[4] = {(int)q.x, (int)q.y, (int)q.z, (int)q.w};
+        const int cnb[4] = {(int)qb.x, (int)qb.y, (int)qb.z, (int)qb.w};
+        const int sum = cnt[0] + cnt[1] + cnt[2] + cnt[3], sumb = cnb[0] + cnb[1] + cnb[2] + cnb[3];
+        const int incl = wave_prefix_sum(sum), inclb = wave_prefix_sum(sumb);
+        int acc = __builtin_amdgcn_readlane(incl, 63) - incl + sum;  // b2's candidates in bins >= 4 lane
+        int accb = __builtin_amdgcn_readlane(inclb, 63) - inclb + sumb;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          acc -= cnt[i];
+          accb -= cnb[i];
+          if (acc + cnt[i] >= need2 && acc < need2) {
+            s_sel[5] = 4 * lane + i;
+            s_sel[6] = need2 - acc;  // keys equal to T that are kept
+            s_sel[7] = accb;         // earlier chunks' candidates of b2 above T
+            s_red[0] = cnb[i];       // earlier chunks' keys equal to T
+            s_red[1] = cnt[i];       // keys equal to T
+          }
+        }
+      }
+      __syncthreads();
+      T = (hi20 << 8) | (uint32_t)s_sel[5];
+      rem_all = s_sel[6];
+      eq_bef = s_red[0];
+      keep_eq = rem_all >= s_red[1];
+      kept_bef = above_b2 + s_sel[7] + min(eq_bef, rem_all);
+    }
   }
-  const int total = b2 >= 0 ? k : (need <= 0 ? sure_all : sure_all + n_cand);
-  const int pre = sure_bef + above_bef + min(eq_bef, rem);
-  const int rem_c = max(0, rem - eq_bef);  // keys equal to T this chunk may keep, lowest columns first
-  // Keys equal to T are ranked by column only where the kept ones stop among them; otherwise
-  // they are all kept (the usual case: T is unique) or none is.
-  const bool rank_t = rem_c > 0 && rem < eq_all;
-  const bool keep_t = rem > 0 && rem >= eq_all;
-  // this chunk's keys equal to T in column order (wave-major), then the kept keys: T holds
-  // b1 in its top bits, so keys above T are the sure keys and the candidates above T (the
+  const int total = min(k, need <= 0 ? sure_all : sure_all + min(need, n_cand));
+  const int pre = sure_bef + kept_bef;
+  // Keys equal to T are ranked by column only where the kept ones stop among them.
+  const int rem_c = keep_eq ? 0 : max(0, rem_all - eq_bef);  // this chunk's ties that are kept
+  const bool rank_t = rem_c > 0;
+  // this chunk's keys equal to T in column order (wave-major), then the kept keys (the
   // predicates are combined without short-circuits, which would branch per key)
   uint64_t me[kPerThread];
   int e_run = 0;
@@ -1061,7 +1071,8 @@ __global__ __launch_bounds__(kLongThreads) void topk_emit_kernel(const float *__
   for (int u = 0; u < kPerThread; u++) {
     const bool ok = kWaveCols * wv + 64 * u + lane < nvalid;
     const bool eq = (me[u] >> lane) & 1ull;
-    const bool keep = ok & ((key[u] > T) | (keep_t & (key[u] == T)) | (eq & (e_run + (int)lanes_below(me[u]) < rem_c)));
+    const bool keep =
+        ok & ((key[u] > T) | (keep_eq & (key[u] == T)) | (eq & (e_run + (int)lanes_below(me[u]) < rem_c)));
     e_run += (int)__popcll(me[u]);
     mk[u] = __ballot(keep);
     n_k += (uint32_t)__popcll(mk[u]);
@@ -1380,9 +1391,13 @@ static int topk_impl(const float *logits, int64_t logits_ld, int32_t n_rows, con
   const unsigned chunks = (unsigned)((max_len + kChunk - 1) / kChunk);
   // the digit-1 histograms: filled by the decode scorer, or built here in the workspace
   uint32_t *h1 = row_hist ? row_hist : ws + LongWs(n_rows, max_len).hist1;
-  if (!row_hist)
+  if (!row_hist) {  // cleared first: the workspace may hold another call's lists there
+    const int64_t n16 = (int64_t)n_rows * kBins / 4;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)std::min<int64_t>(1024, (n16 + 255) / 256)), dim3(256), 0, st,
+                       (uint4 *)h1, n16);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
                        max_len, k, h1);
+  }
   hipLaunchKernelGGL(topk_collect_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld,
                      row_len, max_len, k, ws, n_rows, h1);
   hipLaunchKernelGGL(topk_emit_kernel, dim3(chunks, n_rows), dim3(kLongThreads), 0, st, logits, logits_ld, row_len,
@@ -1403,20 +1418,13 @@ extern "C" int indexer_topk(const float *logits, int64_t logits_ld, int32_t n_ro
 // device memory that the library owns, for callers that cannot allocate. Each device holds
 // its own copy of the array; host code reaches it only through the address
 // hipGetSymbolAddress returns for the current device (the array's name in host code is a
-// host-side stand-in, not a device address). The kernels leave the array's histograms
-// zeroed after every call, as they leave a caller's workspace; the array is cleared by a fill
-// kernel on its first use on a device and again after a call that failed to launch.
+// host-side stand-in, not a device address). As with a caller's workspace, a call writes
+// each word of the array it reads first, so the array needs no clearing.
 constexpr int64_t kScratchBytes = INDEXER_TOPK_NOALLOC_SCRATCH_BYTES;
 static __device__ __attribute__((aligned(256))) uint32_t scratch[kScratchBytes / 4];
 
-__global__ void scratch_zero_kernel(uint4 *p, int64_t n16) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = make_uint4(0u, 0u, 0u, 0u);
-}
-
 static std::mutex g_scratch_mu;
-static void *g_scratch_ptr[64];   // per device: the array's device address, once looked up
-static bool g_scratch_clean[64];  // per device: the array is known to be zero-filled where it must be
+static void *g_scratch_ptr[64];  // per device: the array's device address, once looked up
 
 extern "C" int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int32_t n_rows,
                                     const int32_t *row_len, int64_t max_len, int32_t k, int32_t *topk_idx,
@@ -1431,7 +1439,6 @@ extern "C" int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int3
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail(INDEXER_FP4_EHIP, "topk_noalloc: hipGetDevice: %s", hipGetErrorString(e));
   void *ptr = nullptr;
-  bool clean = false;
   {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
@@ -1443,21 +1450,9 @@ extern "C" int indexer_topk_noalloc(const float *logits, int64_t logits_ld, int3
       }
     }
     ptr = g_scratch_ptr[dev];
-    clean = g_scratch_clean[dev];
   }
-  hipStream_t st = (hipStream_t)stream;
-  if (!clean) {  // a fill kernel, not a memset node, so that a captured graph replays it faithfully
-    hipLaunchKernelGGL(scratch_zero_kernel, dim3(1024), dim3(256), 0, st, (uint4 *)ptr, kScratchBytes / 16);
-    rc = launch_status("topk_noalloc scratch clear");
-    if (rc) return rc;
-  }
-  rc = topk_impl(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, ptr, kScratchBytes,
-                 "scratch", row_hist, stream);
-  // an argument error returns before any launch and leaves the array as it was; a failed
-  // launch may have left it partly written
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  g_scratch_clean[dev] = rc != INDEXER_FP4_EHIP;
-  return rc;
+  return topk_impl(logits, logits_ld, n_rows, row_len, max_len, k, topk_idx, topk_ld, ptr, kScratchBytes,
+                   "scratch", row_hist, stream);
 }
 
 extern "C" int indexer_topk_merge(const float *cand_score, const int32_t *cand_index, int64_t cand_ld,

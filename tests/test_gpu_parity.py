@@ -536,6 +536,23 @@ def test_topk_long_row_at_the_length_limit(ifp4):
     _topk_exact(ifp4, lg, np.array([n, n - 1], np.int32), k, n)
 
 
+def test_topk_workspace_shared_across_shapes(ifp4):
+    """One workspace for calls of different shapes, never cleared: a call with more rows finds
+    an earlier call's candidate lists where it builds its own digit-1 histograms, and every
+    selection must still be exact. Fewer rows first, then more rows at other lengths, then
+    fewer again."""
+    rng = np.random.default_rng(5)
+    calls = [(3, 40000, 2048), (16, 131072, 2048), (2, 262144, 512), (9, 20000, 64)]
+    size = max(ifp4.indexer_topk_workspace_bytes(r, n, k) for r, n, k in calls)
+    ws = torch.zeros(size, dtype=torch.uint8, device=dev())
+    for rows, n, k in calls:
+        _say(f"shared workspace: {rows} rows x {n} keys, k={k}")
+        lg = rng.standard_normal((rows, n)).astype(np.float32)
+        lg[0] = np.round(lg[0] * 8.0) / 8.0  # ties at the threshold
+        rl = np.array([n - (i * 997) % (n // 2) for i in range(rows)], np.int32)
+        _topk_exact(ifp4, lg, rl, k, n, ws)
+
+
 @pytest.mark.parametrize("n,k", [(6144, 2048), (4213, 2048), (16000, 2048)])
 def test_topk_crowded_threshold_bin(ifp4, n, k):
     """Rows whose k-th key sits in a crowded bin of the first histogram: thousands of keys in a

@@ -43,7 +43,7 @@ def _no_alloc(ifp4, lg, rl, max_len, k, hist=None):
 
 def test_noalloc_matches_workspace_topk(ifp4):
     k = 2048
-    # call 1: 16 rows of up to 131072 keys (25.7 MB of scratch), ragged lengths
+    # call 1: 16 rows of up to 131072 keys (8.7 MB of scratch), ragged lengths
     rows, ld = 16, 131072
     assert ifp4.indexer_topk_workspace_bytes(rows, ld, k) <= ifp4.NOALLOC_SCRATCH_BYTES
     lg = _logits(rows, ld, 1)
