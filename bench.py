@@ -463,6 +463,14 @@ def bench_prefill(torch, ifp4, W, args):
             ifp4.indexer_fp4_score_prefill(s["qp"], s["qs"], s["w"], kp, ks, s["R"], s["bt"].shape[1], s["sched"],
                                            units, s["NP"], s["logits"])
 
+    def writers():
+        for s in steps:
+            ifp4.indexer_fp4_quant_and_cache(s["keys"], s["slots"], kp, ks, s["q"], s["qp"], s["qs"])
+
+    def topks():
+        for s in steps:
+            ifp4.indexer_topk(s["logits"], s["row_len"], ld, case.topk, s["top"])
+
     for _ in range(max(1, args.warmup)):
         schedules()
         run()
@@ -474,12 +482,15 @@ def bench_prefill(torch, ifp4, W, args):
     layer_us = 1e3 * timed_replays(torch, layer_graph, reps) + sched_us / layers
     scorer_graph = capture(torch, scorers)
     scorer_us = 1e3 * timed_replays(torch, scorer_graph, reps)
+    writer_us = 1e3 * timed_replays(torch, capture(torch, writers), reps)
+    topk_us = 1e3 * timed_replays(torch, capture(torch, topks), reps)
     flops = 16384 * pairs
     tflops = flops / (scorer_us * 1e-6) / 1e12
     return dict(workload="prefill_4req", lengths=[int(x) for x in case.lengths], chunk=case.chunk,
                 steps=len(steps), causal_pairs=pairs, us_per_layer=round(layer_us, 2),
                 schedule_us_per_pass=round(sched_us, 2), layers_sharing_schedule=layers,
-                scorer_us_per_layer=round(scorer_us, 2), keys_scored_per_s=pairs / (layer_us * 1e-6),
+                scorer_us_per_layer=round(scorer_us, 2), writer_us_per_layer=round(writer_us, 2),
+                topk_us_per_layer=round(topk_us, 2), keys_scored_per_s=pairs / (layer_us * 1e-6),
                 scorer_keys_per_s=round(pairs / (scorer_us * 1e-6), 1),
                 roofline={"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_FP4_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_FP4_TFLOPS, 4)})
@@ -660,7 +671,8 @@ def main():
               flush=True)
     if not args.no_prefill:
         pre = bench_prefill(torch, ifp4, W, args)
-        print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us",
+        print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us, "
+              f"writer {pre['writer_us_per_layer']:.1f} us, top-k {pre['topk_us_per_layer']:.1f} us",
               file=sys.stderr, flush=True)
 
     # HBM traffic of the scorer from rocprofv3 counters, valid only for the kernel they were taken on
