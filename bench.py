@@ -19,8 +19,8 @@ second over whole steps), the roofline of the step's scoring kernel (algorithmic
 launch over its mean launch time: HIP events around replays of a graph holding the step's 21
 scoring launches), the same figures per layer for the long decode workloads (16 x 131072 and
 8 x 262144, 8 layers each), the prefill path's time per layer and FP4 MFMA roofline (4
-requests of 3420..4213 tokens, 512-token chunks), and the CPU oracle's rate on a bounded
-sample.
+requests of 3420..4213 tokens, 512-token chunks; and the same requests as a stream of steps
+of at most 512 tokens in all), and the CPU oracle's rate on a bounded sample.
 """
 from __future__ import annotations
 
@@ -409,10 +409,10 @@ def bench_decode_latency(torch, ifp4, W, args, layers=21):
             "layers": layers, **out}
 
 
-def bench_prefill(torch, ifp4, W, args):
+def bench_prefill(torch, ifp4, W, args, workload="prefill_4req"):
     dev = torch.device("cuda:0")
     layers = args.layers
-    case = W.prefill_config("prefill_4req", seed=args.seed)
+    case = W.prefill_config(workload, seed=args.seed)
     units = args.prefill_units
     kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev)
     ks = torch.zeros((case.n_pages, 4, 64), dtype=torch.uint8, device=dev)
@@ -486,7 +486,7 @@ def bench_prefill(torch, ifp4, W, args):
     topk_us = 1e3 * timed_replays(torch, capture(torch, topks), reps)
     flops = 16384 * pairs
     tflops = flops / (scorer_us * 1e-6) / 1e12
-    return dict(workload="prefill_4req", lengths=[int(x) for x in case.lengths], chunk=case.chunk,
+    return dict(workload=workload, lengths=[int(x) for x in case.lengths], chunk=case.chunk,
                 steps=len(steps), causal_pairs=pairs, us_per_layer=round(layer_us, 2),
                 schedule_us_per_pass=round(sched_us, 2), layers_sharing_schedule=layers,
                 scorer_us_per_layer=round(scorer_us, 2), writer_us_per_layer=round(writer_us, 2),
@@ -643,7 +643,7 @@ def main():
     print(f"bench: decode {d['ms_per_step']:.3f} ms/step, scoring kernel {d['scorer_us']:.2f} us "
           f"({d['achieved_gbs']:.0f} GB/s), plain scorer {d['plain_scorer']['us']:.2f} us, writer "
           f"{d['writer']['fused_us_per_layer']:.2f} us", file=sys.stderr, flush=True)
-    pre = None
+    pre = pre_mbt = None
     sweep = None
     if not args.no_sweep:
         sweep = bench_decode_sweep(torch, ifp4, W, args)
@@ -671,9 +671,11 @@ def main():
               flush=True)
     if not args.no_prefill:
         pre = bench_prefill(torch, ifp4, W, args)
-        print(f"bench: prefill {pre['us_per_layer']:.1f} us/layer, scorer {pre['scorer_us_per_layer']:.1f} us, "
-              f"writer {pre['writer_us_per_layer']:.1f} us, top-k {pre['topk_us_per_layer']:.1f} us",
-              file=sys.stderr, flush=True)
+        pre_mbt = bench_prefill(torch, ifp4, W, args, "prefill_4req_mbt512")
+        for nm, r in (("prefill", pre), ("prefill, 512-token step budget", pre_mbt)):
+            print(f"bench: {nm}: {r['steps']} steps, {r['us_per_layer']:.1f} us/layer, scorer "
+                  f"{r['scorer_us_per_layer']:.1f} us, writer {r['writer_us_per_layer']:.1f} us, top-k "
+                  f"{r['topk_us_per_layer']:.1f} us", file=sys.stderr, flush=True)
 
     # HBM traffic of the scorer from rocprofv3 counters, valid only for the kernel they were taken on
     traffic = None
@@ -718,6 +720,7 @@ def main():
         "decode_long": sweep,
         "scorer_sizes": sizes,
         "prefill": pre,
+        "prefill_mbt512": pre_mbt,
         "dcp_merge": dcp,
         "fp8_comparator": fp8,
     }

@@ -377,7 +377,9 @@ def test_prefill_device_side_errors_flag_and_skip(ifp4):
 @pytest.mark.parametrize("which,heads,units", [("prefill_tiny", 16, 512), ("prefill_tiny", 64, 7),
                                                ("prefill_tiny", 64, 4096), ("prefill_tiny", 32, 13),
                                                ("prefill_tiny", 128, 512),
-                                               ("prefill_4req", 64, 512)])  # full size, as benched
+                                               ("prefill_tiny_mbt", 16, 13), ("prefill_tiny_mbt", 64, 512),
+                                               ("prefill_4req", 64, 512),  # full size, as benched
+                                               ("prefill_4req_mbt512", 64, 512)])
 def test_prefill_scores_and_topk(ifp4, which, heads, units):
     case = W.prefill_config(which, heads=heads)
     kp = torch.zeros((case.n_pages, 64, 64), dtype=torch.uint8, device=dev())

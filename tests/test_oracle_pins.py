@@ -507,13 +507,13 @@ def test_schedules_and_geometry_golden():
     assert n_dec >= 4 and n_pre >= 2
 
 
-@pytest.mark.parametrize("which", ["prefill_tiny", "prefill_4req"])
+@pytest.mark.parametrize("which", ["prefill_tiny", "prefill_tiny_mbt", "prefill_4req", "prefill_4req_mbt512"])
 @pytest.mark.parametrize("tile_rows", [8, 16])
 def test_prefill_schedule_covers_rows_and_pages_once(which, tile_rows):
     case = W.prefill_config(which, heads=4)
     TR = tile_rows
     for st in case.steps:
-        units = 4096 if which == "prefill_4req" else 13
+        units = 4096 if which.startswith("prefill_4req") else 13
         sch = oracle.prefill_schedule(st.cu_rows, st.start_pos, st.n_rows_padded, TR, units)
         rs, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, st.n_rows_padded)
         tiles = sch["tiles"]

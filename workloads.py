@@ -134,7 +134,10 @@ def decode_config(name: str, seed: int = 0, **kw) -> DecodeCase:
 
 # ---------------------------------------------------------------------------------------
 # Prefill: requests of length U[2634, 4295] (the prompt-length range of the pages'
-# accuracy runs), chunked at 512 tokens per step, all live requests co-scheduled.
+# accuracy runs), chunked at 512 tokens per step, all live requests co-scheduled; or, as
+# the secondary stream, steps of at most 512 tokens in all (a scheduler's token budget),
+# filled by the live requests in order, so requests are cut mid-way and a step can hold
+# the end of one request and the start of the next.
 
 def prefill_lengths(n_req=4, lo=2634, hi=4295, multiple=8):
     """First seed s = 0, 1, ... whose draw has a total that is not a multiple of 8,
@@ -176,7 +179,7 @@ class PrefillCase:
 
 
 def prefill_case(lengths, heads=64, topk=2048, chunk=512, seed=0, pad_multiple=8,
-                 swizzle_sensitive=False, name="prefill") -> PrefillCase:
+                 swizzle_sensitive=False, name="prefill", budget=None) -> PrefillCase:
     L = np.asarray(lengths, np.int32)
     rk, rp, rq, rw, ru = _streams(seed, 5)
     keys = [normal_bf16(rk, (int(n), HEAD_DIM)) for n in L]
@@ -193,6 +196,10 @@ def prefill_case(lengths, heads=64, topk=2048, chunk=512, seed=0, pad_multiple=8
     while (done < L).any():
         live = np.nonzero(done < L)[0].astype(np.int32)
         adv = np.minimum(chunk, L[live] - done[live]).astype(np.int32)
+        if budget is not None:  # first come, first served up to the step's token budget
+            left = np.maximum(budget - (np.cumsum(adv) - adv), 0)
+            adv = np.minimum(adv, left).astype(np.int32)
+            live, adv = live[adv > 0], adv[adv > 0]
         cu = np.zeros(live.shape[0] + 1, np.int32)
         cu[1:] = np.cumsum(adv)
         n_rows = int(cu[-1])
@@ -209,9 +216,16 @@ def prefill_config(name: str = "prefill_4req", seed: int = 0, **kw) -> PrefillCa
     if name == "prefill_4req":
         L, _ = prefill_lengths()
         p = dict(lengths=L, heads=64, topk=2048, chunk=512)
+    elif name == "prefill_4req_mbt512":
+        L, _ = prefill_lengths()
+        p = dict(lengths=L, heads=64, topk=2048, chunk=512, budget=512)
     elif name == "prefill_tiny":
         # three short requests, 48-row chunks: several chunks, ragged groups, padding rows
         p = dict(lengths=[70, 5, 133], heads=16, topk=64, chunk=48)
+    elif name == "prefill_tiny_mbt":
+        # the same requests under a 60-token step budget: requests cut mid-way, steps that
+        # end one request and start the next
+        p = dict(lengths=[70, 5, 133], heads=16, topk=64, chunk=48, budget=60)
     else:
         raise KeyError(name)
     p.update(kw)
