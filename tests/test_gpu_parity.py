@@ -429,6 +429,35 @@ def _order_hist(lg, n):
     return out
 
 
+def test_topk_with_a_histogram_of_other_logits(ifp4):
+    """A row histogram built from other logits (the interface allows it: a meaningless but
+    in-bounds, -1-padded selection): histograms of far larger values (no key lies at or above
+    the chosen bin: nothing is selected), of far smaller ones (every key lies above it: the
+    lowest-column k are kept) and of a shuffled row's half (mixed counts). Every selection is
+    valid (ascending distinct columns of the row, then -1), and the workspace and histograms
+    serve a correct call afterwards."""
+    n, k, rows = 131072, 2048, 4
+    rng = np.random.default_rng(31)
+    lg = rng.standard_normal((rows, n)).astype(np.float32)
+    rl = np.array([n, n - 1, 70000, n], np.int32)
+    other = np.stack([lg[0] + 1e4, lg[1] - 1e4, rng.permutation(lg[2])[:n] * 0.5, lg[3][::-1] * 3.0])
+    hist = torch.from_numpy(_order_hist(other, rl).astype(np.uint32).view(np.int32)).to(dev())
+    ws = torch.zeros(ifp4.indexer_topk_workspace_bytes(rows, n, k), dtype=torch.uint8, device=dev())
+    top = torch.full((rows, k), -7, dtype=torch.int32, device=dev())
+    ifp4.indexer_topk(to_dev(lg), to_dev(rl), n, k, top, ws, hist)
+    torch.cuda.synchronize()
+    got = top.cpu().numpy()
+    for r in range(rows):
+        sel = got[r][got[r] >= 0]
+        m = len(sel)
+        assert (got[r][m:] == -1).all(), f"row {r}: -1 only after the selection"
+        assert (np.diff(sel) > 0).all() and (sel < rl[r]).all(), f"row {r}: ascending columns of the row"
+    assert (got[0] == -1).all()                            # no key at or above the bin: nothing kept
+    assert list(got[1]) == list(range(k))                  # every key above the bin: lowest columns
+    assert int(torch.count_nonzero(hist).item()) == 0      # the histograms are left zeroed
+    _topk_exact(ifp4, lg, rl, k, n, ws)                    # the same workspace, no histogram: exact
+
+
 FUSED_CASES = [
     dict(name="long_ragged", ctx=[20000, 9000, 131, 2625], heads=64, topk=2048),
     dict(name="long_next_n2", ctx=[17000, 30000], heads=32, topk=2048, next_n=2),
