@@ -142,16 +142,34 @@ __device__ __forceinline__ int shared_bits(uint32_t kmin, uint32_t kmax) { retur
 // conditional move that read a stale condition code and returned ~0u for sb = 6.
 __device__ __forceinline__ uint32_t top_bits_mask(int sb) { return (uint32_t)~(0xFFFFFFFFull >> sb); }
 
+// Wave-wide min and max in the last lane (the prefix pattern of wave_prefix_sum, with the
+// identity of each operation for lanes that have no source): DPP moves, no LDS round trips.
+__device__ __forceinline__ uint32_t wave_min_last(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_last(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 // Block-wide min and max, returned to every thread.
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uint32_t *s_mm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off, 64));
-  }
-  if (lane == 0) {
+  kmin = wave_min_last(kmin);
+  kmax = wave_max_last(kmax);
+  if (lane == 63) {
     s_mm[2 * wv] = kmin;
     s_mm[2 * wv + 1] = kmax;
   }
