@@ -7,15 +7,15 @@
 //
 // Exact selection by radix select on order-preserving 32-bit keys (flip the sign bit of
 // non-negative floats, invert negative ones; -0.0 is folded onto +0.0): histogram passes
-// over 8-bit digits narrow the key of the k-th largest value to one value T (bits that
-// all keys of the row share are skipped), then every key above T is kept together with
-// the lowest-column keys equal to T, and the columns are written in ascending order.
+// over digits of the keys (each path's width is given with it below) narrow the key of the
+// k-th largest value to one value T, then every key above T is kept together with the
+// lowest-column keys equal to T, and the columns are written in ascending order.
 //
 // Rows up to 6144 keys: one workgroup per row with the row's keys in registers; up to 16384
 // keys: one workgroup per row with the row's keys held in LDS (512 threads in launches of up
-// to 2047 rows, 256 in larger ones). Longer rows: the chunked path further below. Every loop that reads global memory
-// issues all of a thread's loads before it uses them, so a pass costs one memory latency
-// rather than one per element.
+// to 2047 rows, 256 in larger ones). Longer rows: the chunked path further below. Every loop
+// that reads global memory issues all of a thread's loads before it uses them, so a pass
+// costs one memory latency rather than one per element.
 #include <mutex>
 
 #include "common.h"
