@@ -839,3 +839,74 @@ def test_fp8_scores_equal_fp4_scores_on_fp4_representable_data():
     for t, s in enumerate(case.slots[:50]):  # and the keys decode to the same values
         assert np.array_equal(oracle.dequant8_key(kp8, ks8, s // 64, s % 64),
                               oracle.dequant_key(kp4, ks4, s // 64, s % 64))
+
+
+# ---------------------------------------------------------------------------- planted mistakes
+
+def test_parity_checks_catch_planted_mistakes():
+    """The checks the GPU parity tests apply reject outputs with a planted mistake (planted in
+    the oracle's own outputs, on the CPU): a row scored one key too far or one key short (an
+    off-by-one context), a padding row that reads keys, and top-k lists with a shifted index,
+    an index past the row or a duplicate. The unmodified outputs pass."""
+    from helpers import check_logits, check_topk
+
+    def rejects(f):
+        try:
+            f()
+        except AssertionError:
+            return True
+        return False
+
+    # decode: an off-by-one context either way
+    case = W.decode_config("decode_tiny")
+    qp, qs = oracle.quant_q(case.q)
+    kp = np.zeros((case.n_pages, 64, 64), np.uint8)
+    ks = np.zeros((case.n_pages, 4, 64), np.uint8)
+    oracle.quant_and_cache(case.keys, case.slots, kp, ks)
+    rs, rl = oracle.decode_geometry(case.ctx)
+    ld = case.block_table.shape[1] * 64
+    s, _ = oracle.score(qp, qs, case.w, rs, rl, kp, ks, case.block_table, ld=ld)
+    assert not rejects(lambda: check_logits(s, s, rl))
+    rl_long, rl_short = rl.copy(), rl - 1
+    rl_long[0] += 1  # (row 0 has room in its last page and in the logits row)
+    assert rl[0] % 64 != 0 and rl[0] < ld
+    s_long, _ = oracle.score(qp, qs, case.w, rs, rl_long, kp, ks, case.block_table, ld=ld)
+    s_short, _ = oracle.score(qp, qs, case.w, rs, rl_short, kp, ks, case.block_table, ld=ld)
+    assert rejects(lambda: check_logits(s_long, s, rl))
+    assert rejects(lambda: check_logits(s_short, s, rl))
+    # top-k: a shifted index, an index past the row, a duplicate
+    k = case.topk
+    top = oracle.topk(s, rl, k)
+    assert not rejects(lambda: check_topk(top, top, s, rl, k))
+    r = int(np.argmax(rl))
+    n = min(k, int(rl[r]))
+    order = np.argsort(-s[r, :int(rl[r])], kind="stable")
+    out_of_set = int(order[-1])  # the row's smallest score, far from the k-th
+    bad = top.copy()
+    bad[r, 0] = out_of_set
+    assert rejects(lambda: check_topk(bad, top, s, rl, k))
+    bad = top.copy()
+    bad[r, n - 1] = int(rl[r])
+    assert rejects(lambda: check_topk(bad, top, s, rl, k))
+    bad = top.copy()
+    bad[r, 1] = bad[r, 0]
+    assert rejects(lambda: check_topk(bad, top, s, rl, k))
+    # prefill: a padding row scored as if it saw keys
+    pc = W.prefill_config("prefill_tiny")
+    kp = np.zeros((pc.n_pages, 64, 64), np.uint8)
+    ks = np.zeros((pc.n_pages, 4, 64), np.uint8)
+    st = pc.steps[0]
+    k_, sl = W.step_keys(pc, st)
+    oracle.quant_and_cache(k_, sl, kp, ks)
+    rs, rl = oracle.prefill_geometry(st.cu_rows, st.start_pos, st.n_rows_padded)
+    qp, qs = oracle.quant_q(st.q)
+    bt = W.step_block_table(pc, st)
+    ld = int(pc.lengths.max())
+    s, _ = oracle.score(qp, qs, st.w, rs, rl, kp, ks, bt, ld=ld)
+    assert not rejects(lambda: check_logits(s, s, rl))
+    pad = int(st.n_rows)  # the first padding row
+    assert rl[pad] == 0
+    rl_read = rl.copy()
+    rl_read[pad] = 5
+    s_read, _ = oracle.score(qp, qs, st.w, rs, rl_read, kp, ks, bt, ld=ld)
+    assert rejects(lambda: check_logits(s_read, s, rl))
