@@ -26,22 +26,6 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Inclusive suffix sum of v over the workgroup's threads (threads >= tid).
-template <int NT>
-__device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_down(v, off, 64);
-    if (lane + off < 64) v += y;
-  }
-  if (lane == 0) s_scan[wv] = v;
-  __syncthreads();
-  for (int w2 = wv + 1; w2 < NT / 64; w2++) v += s_scan[w2];
-  __syncthreads();
-  return v;
-}
-
 // Inclusive prefix sum over the lanes of a wave (lanes <= this one): DPP shifts within rows of
 // 16 lanes, then row broadcasts across rows (no LDS round trips).
 __device__ __forceinline__ int wave_prefix_sum(int v) {
@@ -51,6 +35,24 @@ __device__ __forceinline__ int wave_prefix_sum(int v) {
   v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
   v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, into rows 1 and 3
   v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, into rows 2 and 3
+  return v;
+}
+
+// Wave-wide sum, returned to every lane (the DPP prefix sum's last lane: no LDS round trips).
+__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63); }
+
+// Inclusive suffix sum of v over the workgroup's threads (threads >= tid): within a wave,
+// the wave's total less the prefix before this lane.
+template <int NT>
+__device__ __forceinline__ int block_suffix_sum(int v, int *s_scan) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int incl = wave_prefix_sum(v);
+  const int wtot = __builtin_amdgcn_readlane(incl, 63);
+  v = wtot - incl + v;
+  if (lane == 0) s_scan[wv] = wtot;
+  __syncthreads();
+  for (int w2 = wv + 1; w2 < NT / 64; w2++) v += s_scan[w2];
+  __syncthreads();
   return v;
 }
 
@@ -377,8 +379,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
     int n_sel = 0;
     if (c_lo < c_hi)
       for (int wd = c_lo / 32 + lane; wd < (c_hi + 31) / 32; wd += 64) n_sel += __popc(sel[wd]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) n_sel += __shfl_xor(n_sel, o, 64);
+    n_sel = wave_sum(n_sel);
     if (lane == 0) s_gt[wv] += n_sel;  // each wave updates only its own entry
   }
   __syncthreads();
@@ -819,9 +820,6 @@ __global__ __launch_bounds__(kLongThreads) void topk_collect_kernel(const float 
     cnt[2] = bin1;
   }
 }
-
-// Wave-wide sum, returned to every lane (the DPP prefix sum's last lane: no LDS round trips).
-__device__ __forceinline__ int wave_sum(int v) { return __builtin_amdgcn_readlane(wave_prefix_sum(v), 63); }
 
 // Inclusive prefix sums of a and b over the workgroup's threads, with one barrier; ta and tb
 // get the totals. s_w (two words a wave) must not be reused before another barrier.
