@@ -1149,21 +1149,38 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
   uint32_t *keys = lds, *idx = lds + n_cand, *buf = lds + 2 * n_cand;
   const int P2 = merge_sort_len(k);
   uint32_t *bm = buf + P2;
-  // stage; an empty slot (index < 0) gets index 0xFFFFFFFF and never counts
+  // stage; an empty slot (index < 0) gets index 0xFFFFFFFF and never counts. All of a
+  // thread's loads go out before any is used (slots past n_cand load the last candidate and
+  // are dropped): a loop that used each load before the next waited one round trip a slot.
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, imin = 0xFFFFFFFFu, imax = 0u;
   int nv = 0;
-  for (int c = tid; c < n_cand; c += kMergeThreads) {
-    const int32_t ix = index[r * ld + c];
-    const bool ok = ix >= 0;
-    const uint32_t key = order_key(score[r * ld + c]);
-    keys[c] = key;
-    idx[c] = ok ? (uint32_t)ix : 0xFFFFFFFFu;
-    if (ok) {
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
-      imin = min(imin, (uint32_t)ix);
-      imax = max(imax, (uint32_t)ix);
-      nv++;
+  constexpr int kStage = kMergeMaxCand / kMergeThreads;  // candidate slots a thread holds
+  if (n_cand > 0) {
+    int32_t ixv[kStage];
+    float scv[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; u++) {
+      const int64_t c = r * ld + min(tid + u * kMergeThreads, n_cand - 1);
+      ixv[u] = index[c];
+      scv[u] = score[c];
+    }
+#pragma unroll
+    for (int u = 0; u < kStage; u++) {
+      const int c = tid + u * kMergeThreads;
+      if (c < n_cand) {
+        const int32_t ix = ixv[u];
+        const bool ok = ix >= 0;
+        const uint32_t key = order_key(scv[u]);
+        keys[c] = key;
+        idx[c] = ok ? (uint32_t)ix : 0xFFFFFFFFu;
+        if (ok) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+          imin = min(imin, (uint32_t)ix);
+          imax = max(imax, (uint32_t)ix);
+          nv++;
+        }
+      }
     }
   }
   for (int i = tid; i < kMergeBins; i += kMergeThreads) hist[i] = 0u;
