@@ -1204,7 +1204,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
   const int bl = 32 - __clz((int)(kmax - kmin));
   const int sh = bl > 10 ? bl - 10 : 0;
   auto digit = [&](uint32_t key) { return min((key - kmin) >> sh, (uint32_t)(kMergeBins - 1)); };
-  uint32_t b = 0;
+  uint32_t pre_b = 0, pmask_b = 0;  // T's bin: the bits of key - kmin its keys share
   if (nv > k) {
     for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
       const int c = c0 + tid;
@@ -1222,12 +1222,47 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
       }
       __syncthreads();
     }
-    b = (uint32_t)s_misc[0];
-    const int need = s_misc[1], nb = s_misc[2];
-    if (nb <= kShortRank) {
+    // the bits of key - kmin that every key of T's bin shares (pre under pmask); further
+    // linear levels of 10 bits over that bin's keys while it is crowded
+    uint32_t pre = (uint32_t)s_misc[0] << sh;
+    uint32_t pmask = top_bits_mask(32 - sh);
+    int need = s_misc[1], nb = s_misc[2];
+    int sc = sh;
+    while (nb > kShortRank && sc > 0) {
+      const int s2 = sc > 10 ? sc - 10 : 0;
+      const uint32_t dm = (1u << (sc - s2)) - 1u;
+      __syncthreads();  // every thread has read s_misc and the last level's histogram
+      hist[tid] = 0u;
+      __syncthreads();
       for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
         const int c = c0 + tid;
-        const bool in_b = c < n_cand && idx[c] != 0xFFFFFFFFu && digit(keys[c]) == b;
+        const bool ok = c < n_cand && idx[c] != 0xFFFFFFFFu && ((keys[c] - kmin) & pmask) == pre;
+        hist_put(hist, ok ? ((keys[c] - kmin) >> s2) & dm : 0u, ok);
+      }
+      __syncthreads();
+      {
+        const uint32_t h = hist[tid];
+        const int acc = block_suffix_sum<kMergeThreads>((int)h, s_scan);
+        if (acc >= need && acc - (int)h < need) {
+          s_misc[0] = tid;
+          s_misc[1] = need - (acc - (int)h);
+          s_misc[2] = (int)h;
+        }
+        __syncthreads();
+      }
+      pre |= (uint32_t)s_misc[0] << s2;
+      pmask |= dm << s2;
+      need = s_misc[1];
+      nb = s_misc[2];
+      sc = s2;
+    }
+    pre_b = pre;
+    pmask_b = pmask;
+    auto in_bin = [&](int c) { return idx[c] != 0xFFFFFFFFu && ((keys[c] - kmin) & pmask) == pre; };
+    if (nb <= kShortRank) {  // the bin's keys ranked by counting
+      for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
+        const int c = c0 + tid;
+        const bool in_b = c < n_cand && in_bin(c);
         const uint64_t m = __ballot(in_b);
         if (m) {
           int at = 0;
@@ -1249,28 +1284,16 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
         }
         if (rank < need) atomicOr(&chosen[cpos[tid] >> 5], 1u << (cpos[tid] & 31));
       }
-    } else {
-      const uint32_t other = b == 0 ? 0xFFFFFFFFu : 0u;
-      auto off_of = [&](int c) {
-        return (idx[c] != 0xFFFFFFFFu && digit(keys[c]) == b) ? keys[c] - kmin : other;
-      };
-      int rem = need, n_eq = 0;
-      const uint32_t T = kmin + block_select<kMergeThreads>(n_cand, off_of, b << sh, top_bits_mask(32 - sh), sh,
-                                                            &rem, &n_eq, hist, s_scan, s_misc + 4);
-      uint32_t cut = 0xFFFFFFFFu;  // keys equal to T with index <= cut are kept
-      if (rem < n_eq) {            // the rem smallest indices: the largest 2^31 - 1 - index
-        int rem2 = rem, n_eq2 = 0;
-        const uint32_t sel = block_select<kMergeThreads>(
-            n_cand,
-            [&](int c) { return (idx[c] != 0xFFFFFFFFu && keys[c] == T) ? (0x7FFFFFFFu - idx[c]) : 0xFFFFFFFFu; },
-            0u, 0x80000000u, 31, &rem2, &n_eq2, hist, s_scan, s_misc + 4);
-        cut = 0x7FFFFFFFu - sel;
-      }
-      for (int c = tid; c < n_cand; c += kMergeThreads) {
-        const uint32_t key = keys[c];
-        if (idx[c] != 0xFFFFFFFFu && digit(key) == b && (key > T || (key == T && idx[c] <= cut)))
-          atomicOr(&chosen[c >> 5], 1u << (c & 31));
-      }
+    } else {  // a crowded bin of one value T: its need smallest indices
+      const uint32_t T = kmin + pre;
+      int rem2 = need, n_eq2 = 0;
+      const uint32_t sel = block_select<kMergeThreads>(
+          n_cand,
+          [&](int c) { return (idx[c] != 0xFFFFFFFFu && keys[c] == T) ? (0x7FFFFFFFu - idx[c]) : 0xFFFFFFFFu; },
+          0u, 0x80000000u, 31, &rem2, &n_eq2, hist, s_scan, s_misc + 4);
+      const uint32_t cut = 0x7FFFFFFFu - sel;  // keys equal to T with index <= cut are kept
+      for (int c = tid; c < n_cand; c += kMergeThreads)
+        if (idx[c] != 0xFFFFFFFFu && keys[c] == T && idx[c] <= cut) atomicOr(&chosen[c >> 5], 1u << (c & 31));
     }
     __syncthreads();
   }
@@ -1278,7 +1301,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
   for (int c0 = 0; c0 < n_cand; c0 += kMergeThreads) {
     const int c = c0 + tid;
     bool t = c < n_cand && idx[c] != 0xFFFFFFFFu;
-    if (t && nv > k) t = digit(keys[c]) > b || ((chosen[c >> 5] >> (c & 31)) & 1u);
+    if (t && nv > k) t = ((keys[c] - kmin) & pmask_b) > pre_b || ((chosen[c >> 5] >> (c & 31)) & 1u);
     const uint64_t m = __ballot(t);
     if (m) {
       int at = 0;
