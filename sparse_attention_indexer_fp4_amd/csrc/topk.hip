@@ -1142,7 +1142,7 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
   __shared__ uint32_t chosen[kMergeMaxCand / 32];  // chosen candidates of bin b, by position
   __shared__ uint32_t ckey[kShortRank], cpos[kShortRank];
   __shared__ int s_scan[3 * kMergeWaves], s_misc[8];
-  __shared__ uint32_t s_mm[2 * kMergeWaves];
+  __shared__ uint32_t s_red[8 * kMergeWaves];
   __shared__ int s_gathered;  // indices gathered for the sort (block_select uses s_misc[4..6])
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1189,17 +1189,35 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(const float *
     s_misc[3] = 0;  // bin-b candidates listed
     s_gathered = 0;
   }
-  block_minmax<kMergeThreads>(kmin, kmax, s_mm);
-  block_minmax<kMergeThreads>(imin, imax, s_mm);
+  {  // the block's key and index ranges and valid count: DPP reductions, one LDS exchange
+    const int wv = tid >> 6;
+    const uint32_t a0 = wave_min_last(kmin), a1 = wave_max_last(kmax);
+    const uint32_t a2 = wave_min_last(imin), a3 = wave_max_last(imax);
+    const int a4 = wave_prefix_sum(nv);
+    if (lane == 63) {
+      s_red[8 * wv] = a0;
+      s_red[8 * wv + 1] = a1;
+      s_red[8 * wv + 2] = a2;
+      s_red[8 * wv + 3] = a3;
+      s_red[8 * wv + 4] = (uint32_t)a4;
+    }
+    __syncthreads();
+    nv = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kMergeWaves; w2++) {
+      kmin = min(kmin, s_red[8 * w2]);
+      kmax = max(kmax, s_red[8 * w2 + 1]);
+      imin = min(imin, s_red[8 * w2 + 2]);
+      imax = max(imax, s_red[8 * w2 + 3]);
+      nv += (int)s_red[8 * w2 + 4];
+    }
+  }
   // the chosen indices are put in order through a bitmap over [imin, imax] when it fits LDS
   const int span_words = imin <= imax ? (int)min(((uint64_t)(imax - imin) + 32) / 32, (uint64_t)bm_words + 1) : 0;
   const bool use_bm = span_words > 0 && span_words <= bm_words;
   if (use_bm)
     for (int i = tid; i < span_words; i += kMergeThreads) bm[i] = 0u;
-  nv = block_suffix_sum<kMergeThreads>(nv, s_scan);
-  if (tid == 0) s_misc[7] = nv;
   __syncthreads();
-  nv = s_misc[7];
   const int take_n = min(k, nv);
   const int bl = 32 - __clz((int)(kmax - kmin));
   const int sh = bl > 10 ? bl - 10 : 0;
