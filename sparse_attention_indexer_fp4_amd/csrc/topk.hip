@@ -165,7 +165,9 @@ __device__ __forceinline__ uint32_t wave_max_last(uint32_t v) {
   return v;
 }
 
-// Block-wide min and max, returned to every thread.
+// Block-wide min and max, returned to every thread, with one barrier (which also publishes
+// whatever the block wrote to LDS before the call). s_mm (two words a wave) is read after
+// the barrier, so it must not be written again by this launch.
 template <int NT>
 __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uint32_t *s_mm) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -182,7 +184,6 @@ __device__ __forceinline__ void block_minmax(uint32_t &kmin, uint32_t &kmax, uin
     kmin = min(kmin, s_mm[2 * w2]);
     kmax = max(kmax, s_mm[2 * w2 + 1]);
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------------------
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(kShortThreads) void topk_row_kernel(const float *__
   const int nwords = (n + 31) / 32;
   for (int i = tid; i < nwords; i += kShortThreads) sel[i] = 0u;
   if (tid == 0) s_misc[3] = 0;
-  block_minmax<kShortThreads>(kmin, kmax, s_mm);  // its barriers publish all of the above
+  block_minmax<kShortThreads>(kmin, kmax, s_mm);  // its barrier publishes all of the above
   const int bl = 32 - __clz((int)(kmax - kmin));
   const int sh = bl > 10 ? bl - 10 : 0;
   auto digit = [&](uint32_t key) { return min((key - kmin) >> sh, (uint32_t)(kShortBins - 1)); };
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void to
       kmin = min(kmin, ok ? kk : 0xFFFFFFFFu);
     }
   }
-  block_minmax<NT>(kmin, kmax, s_mm);  // its barriers also publish the cleared histogram
+  block_minmax<NT>(kmin, kmax, s_mm);  // its barrier also publishes the cleared histogram
   // From here on a key is held as key - kmin, and a lane of the last slot past the row's end
   // as 0, the row's smallest value: it sorts below or ties with every key of the row and
   // comes after all of them in column order, so it is never among the k kept (the
